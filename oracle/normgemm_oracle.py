@@ -1,0 +1,155 @@
+"""Plain float64 definitions of the norm-fused GEMM operations.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path.
+
+Sources (cited by page title and section):
+
+* "Free normalization fusion" (aixai.ru blog, Russian), section "Lazy
+  Pre-Norm": the fused product is C = rmsnorm(A) @ B with rmsnorm(A) equal to
+  A times the per-row inverse root-mean-square, and the row scale commutes
+  with the matrix product.
+* Same page, section "Multi-CTA Norm Fusion": any normalization splits into a
+  per-row reduction (rstd, or mean and variance) followed by an elementwise
+  apply; this is the form of the GEMM-epilogue norms.
+* "RMSNorm fusion on Ascend" (gsyq.cn, Chinese), section 1.1 (LayerNorm: mean,
+  biased variance over the H elements of a row, (x - mean)/sqrt(var + eps),
+  then gamma * x_norm + beta) and section 1.2 (RMSNorm: x / sqrt(mean(x^2) +
+  eps) * gamma).  The extracted text lost the "+" before eps; eps is read as
+  added inside the square root, which the page's own code sample confirms.
+
+H, the length a row is normalized over, is K for the Lazy Pre-Norm form (a
+row of A) and N for the GEMM-epilogue forms (a row of A @ B).
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import numpy as np
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact decode of raw bfloat16 bit patterns (uint16) to float64."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16, nearest with ties to even.
+
+    Rounds directly from float64 (no intermediate float32 rounding), so the
+    result is the bfloat16 value nearest to ``x``.  Used only to express the
+    precision of a bfloat16 output in the tests.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                       # x = m * 2**e, 0.5 <= |m| < 1
+    # bfloat16 keeps 8 significant bits: scale the mantissa to [128, 256).
+    q = np.rint(m * 256.0)                   # numpy rint rounds ties to even
+    y = np.ldexp(q / 256.0, e).astype(np.float32)
+    return (y.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _f64(x) -> np.ndarray:
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return bf16_to_f64(x)
+    return x.astype(np.float64)
+
+
+def gemm(A, B) -> np.ndarray:
+    """X = A @ B in float64.  A is [M, K], B is [K, N] (logical layout)."""
+    A = _f64(A)
+    B = _f64(B)
+    return A @ B
+
+
+def rms_norm_rows(X, eps: float, gamma=None) -> Tuple[np.ndarray, np.ndarray]:
+    """RMSNorm of each row of X (section 1.2 of the Ascend page).
+
+    ms = (1/H) * sum_i x_i^2,  rstd = 1/sqrt(ms + eps),  y = x * rstd * gamma.
+    Returns (Y, rstd).  gamma is per column; None means 1.
+    """
+    X = _f64(X)
+    H = X.shape[1]
+    ms = np.sum(X * X, axis=1) / H
+    rstd = 1.0 / np.sqrt(ms + eps)
+    Y = X * rstd[:, None]
+    if gamma is not None:
+        Y = Y * _f64(gamma)[None, :]
+    return Y, rstd
+
+
+def layer_norm_rows(X, eps: float, gamma=None, beta=None
+                    ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """LayerNorm of each row of X (section 1.1 of the Ascend page).
+
+    mean = (1/H) sum_i x_i,  var = (1/H) sum_i (x_i - mean)^2 (biased, two
+    passes),  rstd = 1/sqrt(var + eps),  y = (x - mean) * rstd * gamma + beta.
+    Returns (Y, mean, rstd).  gamma/beta are per column; None means 1 / 0.
+    """
+    X = _f64(X)
+    H = X.shape[1]
+    mean = np.sum(X, axis=1) / H
+    D = X - mean[:, None]
+    var = np.sum(D * D, axis=1) / H
+    rstd = 1.0 / np.sqrt(var + eps)
+    Y = D * rstd[:, None]
+    if gamma is not None:
+        Y = Y * _f64(gamma)[None, :]
+    if beta is not None:
+        Y = Y + _f64(beta)[None, :]
+    return Y, mean, rstd
+
+
+def rmsnorm_gemm_lazy(A, B, eps: float) -> Tuple[np.ndarray, np.ndarray]:
+    """C = rmsnorm(A) @ B for RMSNorm without affine ("Lazy Pre-Norm" section).
+
+    The definition is computed as written: each row of A is normalized over
+    its K elements first (unrounded float64), then multiplied by B.  The fused
+    kernel's reordering (A @ B) * rstd is equal in exact arithmetic; it is not
+    used here.  Returns (C, rstd) with rstd per row of A.
+    """
+    A_hat, rstd = rms_norm_rows(A, eps)
+    return A_hat @ _f64(B), rstd
+
+
+def gemm_rmsnorm(A, B, eps: float, gamma=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Y = RMSNorm(A @ B) over each full output row (H = N), optional gamma.
+
+    The epilogue form of the "Multi-CTA Norm Fusion" section: reduce each
+    whole row of the product, then apply.  Returns (Y, rstd).
+    """
+    return rms_norm_rows(gemm(A, B), eps, gamma)
+
+
+def gemm_layernorm(A, B, eps: float, gamma=None, beta=None
+                   ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Y = LayerNorm(A @ B) over each full output row (H = N), optional affine.
+
+    Returns (Y, mean, rstd).
+    """
+    return layer_norm_rows(gemm(A, B), eps, gamma, beta)
+
+
+def norm(X, kind: str, eps: float, gamma=None, beta=None):
+    """Standalone row norm of X: kind 'rms' or 'layer'.
+
+    Returns (Y, mean_or_None, rstd).
+    """
+    if kind == "rms":
+        if beta is not None:
+            raise ValueError("RMSNorm has no beta")
+        Y, rstd = rms_norm_rows(X, eps, gamma)
+        return Y, None, rstd
+    if kind == "layer":
+        return layer_norm_rows(X, eps, gamma, beta)
+    raise ValueError(f"unknown norm kind {kind!r}")
+
+
+def rel_err(got, ref) -> float:
+    """max |got - ref| / (1 + |ref|) over all elements (0.0 for empty)."""
+    got = _f64(got)
+    ref = _f64(ref)
+    if ref.size == 0:
+        return 0.0
+    return float(np.max(np.abs(got - ref) / (1.0 + np.abs(ref))))
