@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the norm-fused GEMM path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME|all]
+
+A step is one call of the fused kernel over one batch of the workload's
+synthetic bf16 inputs (seeded, see workloads/).  The default workload is the
+GEMM + LayerNorm epilogue case (A 65536x512 @ B 512x128, N = 128: the
+single-workgroup row tile).  Inputs sit in HBM before the timed region;
+several input/output copies are rotated so that the 256 MB Infinity Cache
+cannot serve a step from the previous step's data.
+
+Printed: one JSON line with the fused kernel's throughput (TFLOP/s of the GEMM,
+2*M*N*K per step), its share of the bf16 MFMA peak, the share of standalone
+norm latency it hides against the unfused ng_gemm + ng_norm pair, its roofline
+position (HBM- or MFMA-bound), and the CPU oracle's throughput on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+RIDGE_FLOP_PER_BYTE = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+DEFAULT_WORKLOAD = workloads.WORKLOADS[1].name
+ROTATE_BYTES = 768 << 20     # input+output copies rotated per step exceed this
+METRIC = ("fused norm-GEMM bf16 TFLOP/s (% MFMA peak) + % norm latency hidden vs unfused")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="workload name, or 'all' for one line per workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w: workloads.Workload) -> int:
+    """Compulsory HBM bytes of one fused call: A, B and C once, plus gamma/beta."""
+    b = 2 * (w.M * w.K + w.K * w.N + w.M * w.N)
+    b += 2 * w.N * (int(w.gamma) + int(w.beta))
+    return b
+
+
+def norm_bytes(w: workloads.Workload) -> int:
+    """Standalone norm of the unfused pair: read + write the normalized matrix."""
+    rows, cols = (w.M, w.K) if w.op == workloads.OP_LAZY else (w.M, w.N)
+    return 4 * rows * cols
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "normalization_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(w: workloads.Workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % w.name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+class Bench:
+    def __init__(self, w: workloads.Workload, seed: int = 0):
+        import numpy as np
+        import torch
+
+        import normalization_gemm_amd as ng
+        self.torch, self.ng, self.np = torch, ng, np
+        self.w = w
+        x = workloads.workload_inputs(w, seed)
+        dev = torch.device("cuda:0")
+
+        def up(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
+                torch.bfloat16)
+
+        per_copy = 2 * (w.M * w.K + w.M * w.N) + (2 * w.M * w.K if w.op == workloads.OP_LAZY else 0)
+        self.R = max(1, min(8, math.ceil(ROTATE_BYTES / per_copy)))
+        A0 = up(x.A)
+        self.A = [A0] + [A0.clone() for _ in range(self.R - 1)]
+        self.B = up(x.B)
+        self.gamma = up(x.gamma) if x.gamma is not None else None
+        self.beta = up(x.beta) if x.beta is not None else None
+        self.C = [torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev) for _ in range(self.R)]
+        # unfused pair intermediates
+        if w.op == workloads.OP_LAZY:
+            self.An = [torch.empty_like(A0) for _ in range(self.R)]
+        self.ws = None
+        op = {workloads.OP_LAZY: ng.NG_OP_RMSNORM_GEMM_LAZY,
+              workloads.OP_GEMM_RMSNORM: ng.NG_OP_GEMM_RMSNORM,
+              workloads.OP_GEMM_LAYERNORM: ng.NG_OP_GEMM_LAYERNORM}[w.op]
+        nb = ng.ng_workspace_bytes(op, w.M, w.N, w.K)
+        if nb:
+            self.ws = ng.Workspace(nb, dev)
+        del x
+        torch.cuda.synchronize()
+
+    # one fused call on rotation slot i
+    def fused(self, i):
+        w, ng, r = self.w, self.ng, i % self.R
+        if w.op == workloads.OP_LAZY:
+            ng.rmsnorm_gemm_lazy(self.A[r], self.B, eps=w.eps, out=self.C[r])
+        elif w.op == workloads.OP_GEMM_RMSNORM:
+            ng.gemm_rmsnorm(self.A[r], self.B, self.gamma, eps=w.eps, out=self.C[r],
+                            workspace=self.ws)
+        else:
+            ng.gemm_layernorm(self.A[r], self.B, self.gamma, self.beta, eps=w.eps,
+                              out=self.C[r], workspace=self.ws)
+
+    def gemm_only(self, i):
+        r = i % self.R
+        src = self.An[r] if self.w.op == workloads.OP_LAZY else self.A[r]
+        self.ng.gemm(src, self.B, out=self.C[r])
+
+    def norm_only(self, i):
+        w, ng, r = self.w, self.ng, i % self.R
+        if w.op == workloads.OP_LAZY:
+            ng.norm(self.A[r], "rms", eps=w.eps, out=self.An[r])
+        elif w.op == workloads.OP_GEMM_RMSNORM:
+            ng.norm(self.C[r], "rms", self.gamma, eps=w.eps, out=self.C[r])
+        else:
+            ng.norm(self.C[r], "layer", self.gamma, self.beta, eps=w.eps, out=self.C[r])
+
+    def pair(self, i):
+        if self.w.op == workloads.OP_LAZY:
+            self.norm_only(i)
+            self.gemm_only(i)
+        else:
+            self.gemm_only(i)
+            self.norm_only(i)
+
+    def time_launches(self, fn, steps, warmup):
+        """Per-launch durations (ms) from HIP events on the launch stream, and
+        the wall time of the whole timed loop (ms)."""
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        t0 = time.perf_counter()
+        ev[0].record()
+        for i in range(steps):
+            fn(i)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        return per, wall, ev[0].elapsed_time(ev[steps])
+
+
+def cpu_baseline(w: workloads.Workload, target_s: float):
+    """The CPU oracle (untuned) on a row sample of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    rows = min(w.M, 256)
+    x = workloads.make_inputs(rows, w.N, w.K, seed=1, row_scale=w.row_scale, gamma=w.gamma,
+                              beta=w.beta)
+    done_rows, t_total = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        if w.op == workloads.OP_LAZY:
+            oracle.rmsnorm_gemm_lazy(x.A, x.B, w.eps)
+        elif w.op == workloads.OP_GEMM_RMSNORM:
+            oracle.gemm_rmsnorm(x.A, x.B, w.eps, x.gamma)
+        else:
+            oracle.gemm_layernorm(x.A, x.B, w.eps, x.gamma, x.beta)
+        t_total += time.perf_counter() - t0
+        done_rows += rows
+        if t_total >= target_s or done_rows >= w.M:
+            break
+        if t_total < target_s / 8 and rows < w.M:
+            rows = min(w.M, rows * 4)
+            x = workloads.make_inputs(rows, w.N, w.K, seed=1, row_scale=w.row_scale,
+                                      gamma=w.gamma, beta=w.beta)
+    flops = 2.0 * done_rows * w.N * w.K
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": "%d output rows of %s (fp64 NumPy GEMM + explicit norm, %.1f s)"
+                      % (done_rows, w.name, t_total)}
+
+
+def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: float):
+    import numpy as np
+    torch_mod = __import__("torch")
+    b = Bench(w)
+    # headline: the fused kernel, steps timed with a sync on both sides
+    per, wall_ms, ev_ms = b.time_launches(b.fused, steps, warmup)
+    per_g, _, ev_g = b.time_launches(b.gemm_only, steps, warmup)
+    per_n, _, ev_n = b.time_launches(b.norm_only, steps, warmup)
+    per_p, _, ev_p = b.time_launches(b.pair, steps, warmup)
+    t_fused = ev_ms / steps
+    t_gemm = ev_g / steps
+    t_norm = ev_n / steps
+    t_pair = ev_p / steps
+    flops = float(w.flops)
+    tflops = flops * steps / (wall_ms * 1e-3) / 1e12
+    kern_tflops = flops / (t_fused * 1e-3) / 1e12
+    ai = flops / algorithmic_bytes(w)
+    hbm_bound = ai < RIDGE_FLOP_PER_BYTE
+    if hbm_bound:
+        achieved = algorithmic_bytes(w) / (t_fused * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(kern_tflops, 1), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(kern_tflops / MFMA_PEAK_TFLOPS, 4)}
+    roof["traffic"] = measured_traffic(w)
+    roof["kernel"] = {workloads.OP_LAZY: "gemm_kernel<Lazy>",
+                      workloads.OP_GEMM_RMSNORM: "gemm_kernel<RowNorm>",
+                      workloads.OP_GEMM_LAYERNORM: "gemm_kernel<RowNorm>"}[w.op]
+    roof["avg_launch_us"] = round(t_fused * 1e3, 2)
+    roof["algorithmic_bytes"] = algorithmic_bytes(w)
+    hidden = (t_gemm + t_norm - t_fused) / t_norm * 100.0
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall_ms / steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bf16, shapes and distributions of the named workload)",
+        "config": {"workload": w.name, "op": w.op, "M": w.M, "N": w.N, "K": w.K, "eps": w.eps,
+                   "gamma": w.gamma, "beta": w.beta, "b_layout": "kn",
+                   "rotated_copies": b.R},
+        "mfma_peak_pct": round(kern_tflops / MFMA_PEAK_TFLOPS * 100.0, 2),
+        "norm_hidden_pct": round(hidden, 1),
+        "unfused": {"gemm_us": round(t_gemm * 1e3, 2), "norm_us": round(t_norm * 1e3, 2),
+                    "pair_us": round(t_pair * 1e3, 2), "fused_us": round(t_fused * 1e3, 2),
+                    "norm_gbs": round(norm_bytes(w) / (t_norm * 1e-3) / 1e9, 1),
+                    "fused_median_us": round(float(np.median(per)) * 1e3, 2)},
+        "roofline": roof,
+    }
+    del b
+    torch_mod.cuda.empty_cache()
+    if with_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, cpu_s)
+    return line
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested); run with --gpus 1" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    names = [w.name for w in workloads.WORKLOADS] if args.workload == "all" else [args.workload]
+    for name in names:
+        w = workloads.WORKLOAD_BY_NAME[name]
+        small = w.flops < 1e11
+        steps = args.steps if args.steps is not None else (200 if small else 20)
+        warmup = args.warmup if args.warmup is not None else (20 if small else 5)
+        line = run(w, steps, warmup, not args.no_cpu_baseline, args.cpu_seconds)
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

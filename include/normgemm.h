@@ -1,0 +1,151 @@
+/*
+ * libnormgemm -- normalization fused into bf16 GEMM on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Every matrix is a dense row-major array of raw bfloat16 bit patterns
+ * (uint16_t) in device memory; statistics are float32 in device memory.  All
+ * device pointers are owned by the caller.  The library never allocates or
+ * frees memory and never synchronizes on the compute calls: each call checks
+ * its arguments on the host (before any HIP call), enqueues its kernel(s) on
+ * `stream` (a hipStream_t; NULL means the null stream) and returns.  Device
+ * faults surface at the caller's next synchronization, as in HIP.
+ *
+ * Common argument rules (violations return NG_ERR_INVALID_ARG unless noted):
+ *   - M >= 0 (M == 0 is a no-op that returns NG_OK), N >= 1, K >= 1 and each
+ *     at most 2^24;
+ *   - N and K must be multiples of 8 (16-byte rows) -> else NG_ERR_UNSUPPORTED;
+ *   - eps finite and >= 0;
+ *   - every matrix pointer non-NULL (A and C, or X and Y, may be NULL when
+ *     M, or rows, is 0) and 16-byte aligned; gamma/beta (when given) 16-byte
+ *     aligned; the float32 statistic outputs 4-byte aligned;
+ *   - b_layout is NG_B_KN (B stored [K, N], N contiguous) or NG_B_NK (B stored
+ *     [N, K], K contiguous: a Linear layer's weight).
+ * Outputs must not overlap inputs.
+ *
+ * Accuracy: bf16 inputs, fp32 accumulation and fp32 row statistics, outputs
+ * rounded to bf16 (nearest, ties to even).  Against a float64 evaluation of
+ * the plain definition every output element satisfies
+ * |out - exact| <= 1e-2 * (1 + |exact|).
+ */
+#ifndef NORMGEMM_H
+#define NORMGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t ng_bf16; /* raw bfloat16 bits */
+
+typedef enum {
+  NG_OK = 0,
+  NG_ERR_INVALID_ARG = 1, /* NULL/misaligned pointer, bad size, bad eps or enum */
+  NG_ERR_UNSUPPORTED = 2, /* valid request this build does not tile (N or K not a multiple of 8, ...) */
+  NG_ERR_WORKSPACE = 3,   /* workspace NULL, too small or misaligned */
+  NG_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  NG_ERR_TIMEOUT = 5      /* a cross-workgroup wait gave up (reported by ng_workspace_status) */
+} ng_status;
+
+enum { NG_NORM_RMS = 0, NG_NORM_LAYER = 1 };
+enum { NG_B_KN = 0, NG_B_NK = 1 };
+enum {
+  NG_OP_RMSNORM_GEMM_LAZY = 0,
+  NG_OP_GEMM_RMSNORM = 1,
+  NG_OP_GEMM_LAYERNORM = 2,
+  NG_OP_GEMM = 3,
+  NG_OP_NORM = 4
+};
+
+/*
+ * Lazy Pre-Norm: C = rmsnorm(A) @ B for RMSNorm without affine parameters.
+ * ("Free normalization fusion", aixai.ru, section "Lazy Pre-Norm": the
+ * per-row scale rstd commutes with the product, so C = (A @ B) * rstd(A); the
+ * sum of squares of each row of A accumulates inside the GEMM k-loop and the
+ * scaling runs in the epilogue.)
+ *   rstd[m] = 1 / sqrt((1/K) * sum_k A[m,k]^2 + eps)
+ *   C[m,n]  = rstd[m] * sum_k A[m,k] * B[k,n]
+ * A: [M, K]; B: see b_layout; C: [M, N] bf16 out.
+ * rstd_out: float32 [M] or NULL.  Needs no workspace.
+ */
+int ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N,
+                         int64_t K, int b_layout, float eps, float* rstd_out, void* stream);
+
+/*
+ * GEMM with an RMSNorm epilogue over each full output row (H = N):
+ *   X = A @ B;  rstd[m] = 1 / sqrt((1/N) sum_n X[m,n]^2 + eps);
+ *   C[m,n] = X[m,n] * rstd[m] * gamma[n]        (gamma NULL means 1)
+ * ("RMSNorm fusion on Ascend", gsyq.cn, section 1.2 for the norm; "Free
+ * normalization fusion", section "Multi-CTA Norm Fusion" for reducing a row
+ * that several workgroups share, then applying.)  Rows with N <= 256 are
+ * normalized inside one workgroup; wider rows merge per-row fp32 partials
+ * across workgroups through `workspace`, which must hold
+ * ng_workspace_bytes(NG_OP_GEMM_RMSNORM, M, N, K) bytes (0 means none needed),
+ * be 256-byte aligned and be zero-filled before its first use (see
+ * ng_workspace_reset); calls leave it ready for the next call.  One workspace
+ * must not be used by two calls that may run concurrently.
+ * gamma: bf16 [N] or NULL.  rstd_out: float32 [M] or NULL.
+ */
+int ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,
+                    int64_t M, int64_t N, int64_t K, int b_layout, float eps, float* rstd_out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * GEMM with a LayerNorm epilogue over each full output row (H = N):
+ *   X = A @ B;  mean[m] = (1/N) sum_n X[m,n];
+ *   var[m] = (1/N) sum_n (X[m,n] - mean[m])^2   (biased);
+ *   rstd[m] = 1 / sqrt(var[m] + eps);
+ *   C[m,n] = (X[m,n] - mean[m]) * rstd[m] * gamma[n] + beta[n]
+ * (gamma NULL means 1, beta NULL means 0).  ("RMSNorm fusion on Ascend",
+ * section 1.1; "Free normalization fusion", section "Multi-CTA Norm Fusion".)
+ * Workspace rules as for ng_gemm_rmsnorm with NG_OP_GEMM_LAYERNORM.
+ * mean_out, rstd_out: float32 [M] or NULL.
+ */
+int ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
+                      const ng_bf16* beta, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+                      int b_layout, float eps, float* mean_out, float* rstd_out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Plain GEMM, the matrix half of the unfused baseline: C = A @ B (bf16 out,
+ * fp32 accumulation).
+ */
+int ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+            int b_layout, void* stream);
+
+/*
+ * Standalone row norm, the other half of the unfused baseline.  X, Y: [rows,
+ * cols] bf16 (Y may equal X for an in-place norm).  kind NG_NORM_RMS or
+ * NG_NORM_LAYER with the formulas above (H = cols).  beta must be NULL for
+ * RMS.  cols must be a multiple of 8 and at most 65536 (else
+ * NG_ERR_UNSUPPORTED).  mean_out (LayerNorm only) and rstd_out: float32
+ * [rows] or NULL.
+ */
+int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* Y,
+            int64_t rows, int64_t cols, int kind, float eps, float* mean_out, float* rstd_out,
+            void* stream);
+
+/* Workspace bytes `op` needs for this shape (0 when it needs none). */
+size_t ng_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
+
+/* Zero-fill a workspace on `stream` with a fill kernel (graph-capture safe). */
+int ng_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Synchronizes `stream`, then reads the workspace's error word: NG_OK, or
+ * NG_ERR_TIMEOUT if a cross-workgroup wait in an earlier call gave up (its
+ * output is then undefined and the workspace must be reset).
+ */
+int ng_workspace_status(const void* workspace, void* stream);
+
+/* Static description of a status code. */
+const char* ng_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* ng_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NORMGEMM_H */

@@ -1,0 +1,215 @@
+"""normalization_gemm_amd: norm-fused bf16 GEMM on MI355X (gfx950).
+
+Thin Python layer over libnormgemm (include/normgemm.h).  PyTorch provides
+device memory and streams only: every step runs in the library's HIP kernels.
+There is no CPU or PyTorch fallback; a missing library or a CPU tensor is an
+error.
+
+Raw C-ABI calls (integer pointers, status codes) live in ``_lib`` under the C
+names (``ng_rmsnorm_gemm_lazy``, ...).  The tensor helpers below allocate the
+outputs with torch, launch on the current stream and raise NormGemmError on a
+non-zero status.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    NG_B_KN, NG_B_NK, NG_NORM_LAYER, NG_NORM_RMS, NG_OK,
+    NG_OP_GEMM, NG_OP_GEMM_LAYERNORM, NG_OP_GEMM_RMSNORM, NG_OP_NORM, NG_OP_RMSNORM_GEMM_LAZY,
+    ng_gemm, ng_gemm_layernorm, ng_gemm_rmsnorm, ng_last_error, ng_norm, ng_rmsnorm_gemm_lazy,
+    ng_status_string, ng_workspace_bytes, ng_workspace_reset, ng_workspace_status,
+)
+
+__all__ = [
+    "NormGemmError", "rmsnorm_gemm_lazy", "gemm_rmsnorm", "gemm_layernorm", "gemm", "norm",
+    "Workspace", "library_path",
+]
+
+
+class NormGemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, ng_status_string(status), ng_last_error()))
+
+
+def library_path() -> str:
+    _lib.load()
+    return _lib.LIB_PATH
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(status: int, where: str):
+    if status != NG_OK:
+        raise NormGemmError(status, where)
+
+
+def _dev_bf16(t, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU (got %s)" % (name, t.device))
+    if t.dtype != torch.bfloat16:
+        raise TypeError("%s must be bfloat16 (got %s)" % (name, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _layout(b_layout):
+    if b_layout in ("kn", NG_B_KN):
+        return NG_B_KN
+    if b_layout in ("nk", NG_B_NK):
+        return NG_B_NK
+    raise ValueError("b_layout must be 'kn' or 'nk'")
+
+
+def _shapes(A, B, lay):
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be 2-D")
+    M, K = A.shape
+    if lay == NG_B_KN:
+        K2, N = B.shape
+    else:
+        N, K2 = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ: A %s, B %s" % (tuple(A.shape), tuple(B.shape)))
+    return M, N, K
+
+
+class Workspace:
+    """Device scratch for the cross-workgroup epilogue (zeroed once here; the
+    kernels leave it zeroed).  One workspace must not serve two calls that
+    can run at the same time."""
+
+    def __init__(self, nbytes: int, device=None):
+        torch = _torch()
+        self.nbytes = max(int(nbytes), 256)
+        self.buf = torch.zeros(self.nbytes, dtype=torch.uint8,
+                               device=device if device is not None else "cuda")
+
+    def ptr(self):
+        return self.buf.data_ptr()
+
+    def status(self, stream=None) -> int:
+        return ng_workspace_status(self.ptr(), _stream(stream))
+
+
+_ws_cache = {}
+
+
+def _workspace(op, M, N, K, device, workspace):
+    need = ng_workspace_bytes(op, M, N, K)
+    if need == 0:
+        return None, 0
+    if workspace is not None:
+        return workspace.ptr(), workspace.nbytes
+    key = (str(device),)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.nbytes < need:
+        ws = Workspace(need, device)
+        _ws_cache[key] = ws
+    return ws.ptr(), ws.nbytes
+
+
+def rmsnorm_gemm_lazy(A, B, *, eps: float = 1e-6, b_layout="kn", out=None, rstd_out=None,
+                      stream=None):
+    """C = rmsnorm(A) @ B (RMSNorm without affine) as (A @ B) * rstd(A)."""
+    torch = _torch()
+    _dev_bf16(A, "A"); _dev_bf16(B, "B")
+    lay = _layout(b_layout)
+    M, N, K = _shapes(A, B, lay)
+    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _dev_bf16(C, "out")
+    _check(ng_rmsnorm_gemm_lazy(_ptr(A), _ptr(B), _ptr(C), M, N, K, lay, float(eps),
+                                _ptr(rstd_out), _stream(stream)), "ng_rmsnorm_gemm_lazy")
+    return C
+
+
+def gemm_rmsnorm(A, B, gamma=None, *, eps: float = 1e-6, b_layout="kn", out=None,
+                 rstd_out=None, workspace: Optional[Workspace] = None, stream=None):
+    """C = RMSNorm(A @ B) over each output row, optional per-column gamma."""
+    torch = _torch()
+    _dev_bf16(A, "A"); _dev_bf16(B, "B")
+    if gamma is not None:
+        _dev_bf16(gamma, "gamma")
+    lay = _layout(b_layout)
+    M, N, K = _shapes(A, B, lay)
+    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _dev_bf16(C, "out")
+    ws, wsb = _workspace(NG_OP_GEMM_RMSNORM, M, N, K, A.device, workspace)
+    _check(ng_gemm_rmsnorm(_ptr(A), _ptr(B), _ptr(gamma), _ptr(C), M, N, K, lay, float(eps),
+                           _ptr(rstd_out), ws, wsb, _stream(stream)), "ng_gemm_rmsnorm")
+    return C
+
+
+def gemm_layernorm(A, B, gamma=None, beta=None, *, eps: float = 1e-5, b_layout="kn", out=None,
+                   mean_out=None, rstd_out=None, workspace: Optional[Workspace] = None,
+                   stream=None):
+    """C = LayerNorm(A @ B) over each output row, optional per-column gamma/beta."""
+    torch = _torch()
+    _dev_bf16(A, "A"); _dev_bf16(B, "B")
+    if gamma is not None:
+        _dev_bf16(gamma, "gamma")
+    if beta is not None:
+        _dev_bf16(beta, "beta")
+    lay = _layout(b_layout)
+    M, N, K = _shapes(A, B, lay)
+    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _dev_bf16(C, "out")
+    ws, wsb = _workspace(NG_OP_GEMM_LAYERNORM, M, N, K, A.device, workspace)
+    _check(ng_gemm_layernorm(_ptr(A), _ptr(B), _ptr(gamma), _ptr(beta), _ptr(C), M, N, K, lay,
+                             float(eps), _ptr(mean_out), _ptr(rstd_out), ws, wsb,
+                             _stream(stream)), "ng_gemm_layernorm")
+    return C
+
+
+def gemm(A, B, *, b_layout="kn", out=None, stream=None):
+    """C = A @ B (bf16 out, fp32 accumulation): the unfused baseline GEMM."""
+    torch = _torch()
+    _dev_bf16(A, "A"); _dev_bf16(B, "B")
+    lay = _layout(b_layout)
+    M, N, K = _shapes(A, B, lay)
+    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _dev_bf16(C, "out")
+    _check(ng_gemm(_ptr(A), _ptr(B), _ptr(C), M, N, K, lay, _stream(stream)), "ng_gemm")
+    return C
+
+
+def norm(X, kind: str, gamma=None, beta=None, *, eps: float = 1e-5, out=None, mean_out=None,
+         rstd_out=None, stream=None):
+    """Standalone row norm ('rms' or 'layer'): the unfused baseline norm."""
+    torch = _torch()
+    _dev_bf16(X, "X")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    k = {"rms": NG_NORM_RMS, "layer": NG_NORM_LAYER}[kind]
+    if gamma is not None:
+        _dev_bf16(gamma, "gamma")
+    if beta is not None:
+        _dev_bf16(beta, "beta")
+    Y = out if out is not None else torch.empty_like(X)
+    _dev_bf16(Y, "out")
+    rows, cols = X.shape
+    _check(ng_norm(_ptr(X), _ptr(gamma), _ptr(beta), _ptr(Y), rows, cols, k, float(eps),
+                   _ptr(mean_out), _ptr(rstd_out), _stream(stream)), "ng_norm")
+    return Y

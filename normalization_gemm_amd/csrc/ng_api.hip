@@ -1,0 +1,358 @@
+// libnormgemm C ABI: argument checks, strategy choice and kernel launches.
+//
+// Every entry point validates its arguments on the host before any HIP call,
+// then enqueues on the caller's stream and returns; nothing here allocates,
+// frees or synchronizes (except ng_workspace_status, which exists to sync).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/normgemm.h"
+#include "ng_gemm_kernel.h"
+#include "ng_norm_kernel.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return NG_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+
+// Tile configurations.
+//   Large: 256x256 macro tile, 4 waves of 128x128 (MFMA-bound shapes).
+//   Row128: 128 x 128, 4 waves stacked along M, each owning whole rows (N <= 128).
+//   Row256: 128 x 256, 2x2 waves (128 < N <= 256).
+template <bool KN> using TLarge = ng::Tile<256, 256, 2, 2, KN>;
+template <bool KN> using TRow128 = ng::Tile<128, 128, 4, 1, KN>;
+template <bool KN> using TRow256 = ng::Tile<128, 256, 2, 2, KN>;
+
+int check_gemm(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
+               int b_layout) {
+  // A and C are empty when M == 0 and may then be NULL.
+  if (!B || (M != 0 && (!A || !C)))
+    return fail(NG_ERR_INVALID_ARG, "A, B and C must be non-NULL");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16))
+    return fail(NG_ERR_INVALID_ARG, "A, B and C must be 16-byte aligned");
+  if (M < 0 || N < 1 || K < 1)
+    return fail(NG_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1 (got M=%lld N=%lld K=%lld)",
+                (long long)M, (long long)N, (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(NG_ERR_INVALID_ARG, "M, N, K must be at most 2^24");
+  if (b_layout != NG_B_KN && b_layout != NG_B_NK)
+    return fail(NG_ERR_INVALID_ARG, "b_layout must be NG_B_KN or NG_B_NK (got %d)", b_layout);
+  if (N % 8 != 0 || K % 8 != 0)
+    return fail(NG_ERR_UNSUPPORTED, "N and K must be multiples of 8 (got N=%lld K=%lld)",
+                (long long)N, (long long)K);
+  if ((M * K) >= (int64_t(1) << 31) * 8 || (N * K) >= (int64_t(1) << 31) * 8 ||
+      (M * N) >= (int64_t(1) << 31) * 8)
+    return fail(NG_ERR_UNSUPPORTED, "a matrix has more than 2^34 elements");
+  return NG_OK;
+}
+
+int check_eps(float eps) {
+  if (!std::isfinite(eps) || eps < 0.f)
+    return fail(NG_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  return NG_OK;
+}
+
+int check_vec(const void* p, const char* name, size_t align) {
+  if (p && !aligned(p, align))
+    return fail(NG_ERR_INVALID_ARG, "%s must be %zu-byte aligned", name, align);
+  return NG_OK;
+}
+
+int launched(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(NG_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+ng::GemmParams make_params(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
+                           float eps) {
+  ng::GemmParams p{};
+  p.A = (const uint16_t*)A;
+  p.B = (const uint16_t*)B;
+  p.C = (uint16_t*)C;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.eps = eps;
+  p.spin_limit = 1 << 20;
+  return p;
+}
+
+template <class T, int EPI>
+int launch_grid(ng::GemmParams p, hipStream_t s, const char* what) {
+  p.tiles_m = (p.M + T::BM - 1) / T::BM;
+  p.tiles_n = (p.N + T::BN - 1) / T::BN;
+  const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
+  hipLaunchKernelGGL((ng::gemm_kernel<T, EPI>), dim3(grid), dim3(T::NT), 0, s, p);
+  return launched(what);
+}
+
+// Co-resident workgroups per device for the persistent cross-workgroup kernel.
+template <class T>
+int xwg_capacity(int* cap) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(NG_ERR_HIP, "hipGetDevice failed");
+  static std::mutex mu;
+  static int cached[64] = {0};
+  std::lock_guard<std::mutex> lk(mu);
+  if (dev < 64 && cached[dev] > 0) {
+    *cap = cached[dev];
+    return NG_OK;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ng::gemm_xwg_kernel<T>, T::NT, 0) !=
+      hipSuccess)
+    return fail(NG_ERR_HIP, "occupancy query failed");
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return fail(NG_ERR_HIP, "CU count query failed");
+  const int c = per_cu * cus;
+  if (c <= 0) return fail(NG_ERR_HIP, "cross-workgroup kernel cannot be resident");
+  if (dev < 64) cached[dev] = c;
+  *cap = c;
+  return NG_OK;
+}
+
+template <class T>
+int launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
+  p.tiles_m = (p.M + T::BM - 1) / T::BM;
+  p.tiles_n = (p.N + T::BN - 1) / T::BN;
+  int cap = 0;
+  int st = xwg_capacity<T>(&cap);
+  if (st) return st;
+  if (p.tiles_n > cap)
+    return fail(NG_ERR_UNSUPPORTED, "row of %d tiles exceeds %d co-resident workgroups",
+                p.tiles_n, cap);
+  int R = cap / p.tiles_n;  // row blocks per round
+  if (R > p.tiles_m) R = p.tiles_m;
+  p.iters = (p.tiles_m + R - 1) / R;
+  const unsigned grid = (unsigned)(R * p.tiles_n);
+  void* args[] = {&p};
+  hipError_t e = hipLaunchCooperativeKernel((const void*)ng::gemm_xwg_kernel<T>, dim3(grid),
+                                            dim3(T::NT), args, 0, s);
+  if (e != hipSuccess) return fail(NG_ERR_HIP, "%s cooperative launch failed: %s", what,
+                                   hipGetErrorString(e));
+  return launched(what);
+}
+
+size_t xwg_bytes(int64_t M, int64_t N) {
+  using T = TLarge<true>;
+  const int tm = (int)((M + T::BM - 1) / T::BM);
+  const int tn = (int)((N + T::BN - 1) / T::BN);
+  return ng::XwgLayout::bytes(tm, tn, T::BM);
+}
+
+// Shared by ng_gemm_rmsnorm / ng_gemm_layernorm.
+int gemm_norm(const void* A, const void* B, const void* gamma, const void* beta, void* C,
+              int64_t M, int64_t N, int64_t K, int b_layout, float eps, float* mean_out,
+              float* rstd_out, void* ws, size_t ws_bytes, hipStream_t s, int kind,
+              const char* what) {
+  int st = check_gemm(A, B, C, M, N, K, b_layout);
+  if (!st) st = check_eps(eps);
+  if (!st) st = check_vec(gamma, "gamma", 16);
+  if (!st) st = check_vec(beta, "beta", 16);
+  if (!st) st = check_vec(mean_out, "mean_out", 4);
+  if (!st) st = check_vec(rstd_out, "rstd_out", 4);
+  if (st) return st;
+  const bool local = N <= 256;
+  if (!local && M > 0) {
+    const size_t need = xwg_bytes(M, N);
+    if (!ws || ws_bytes < need || !aligned(ws, 256))
+      return fail(NG_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu",
+                  need, ws_bytes);
+  }
+  if (M == 0) return ok();
+  ng::GemmParams p = make_params(A, B, C, M, N, K, eps);
+  p.gamma = (const uint16_t*)gamma;
+  p.beta = (const uint16_t*)beta;
+  p.mean_out = mean_out;
+  p.rstd_out = rstd_out;
+  p.ws = (char*)ws;
+  p.norm_kind = kind;
+  const bool kn = b_layout == NG_B_KN;
+  if (N <= 128) {
+    return kn ? launch_grid<TRow128<true>, ng::EPI_ROW_LOCAL>(p, s, what)
+              : launch_grid<TRow128<false>, ng::EPI_ROW_LOCAL>(p, s, what);
+  }
+  if (local) {
+    return kn ? launch_grid<TRow256<true>, ng::EPI_ROW_LOCAL>(p, s, what)
+              : launch_grid<TRow256<false>, ng::EPI_ROW_LOCAL>(p, s, what);
+  }
+  return kn ? launch_xwg<TLarge<true>>(p, s, what) : launch_xwg<TLarge<false>>(p, s, what);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N,
+                         int64_t K, int b_layout, float eps, float* rstd_out, void* stream) {
+  int st = check_gemm(A, B, C, M, N, K, b_layout);
+  if (!st) st = check_eps(eps);
+  if (!st) st = check_vec(rstd_out, "rstd_out", 4);
+  if (st) return st;
+  if (M == 0) return ok();
+  ng::GemmParams p = make_params(A, B, C, M, N, K, eps);
+  p.rstd_out = rstd_out;
+  hipStream_t s = (hipStream_t)stream;
+  const bool kn = b_layout == NG_B_KN;
+  if (N <= 128)
+    return kn ? launch_grid<TRow128<true>, ng::EPI_LAZY>(p, s, "ng_rmsnorm_gemm_lazy")
+              : launch_grid<TRow128<false>, ng::EPI_LAZY>(p, s, "ng_rmsnorm_gemm_lazy");
+  return kn ? launch_grid<TLarge<true>, ng::EPI_LAZY>(p, s, "ng_rmsnorm_gemm_lazy")
+            : launch_grid<TLarge<false>, ng::EPI_LAZY>(p, s, "ng_rmsnorm_gemm_lazy");
+}
+
+int ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,
+                    int64_t M, int64_t N, int64_t K, int b_layout, float eps, float* rstd_out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_norm(A, B, gamma, nullptr, C, M, N, K, b_layout, eps, nullptr, rstd_out, workspace,
+                   workspace_bytes, (hipStream_t)stream, ng::NORM_RMS, "ng_gemm_rmsnorm");
+}
+
+int ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
+                      const ng_bf16* beta, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+                      int b_layout, float eps, float* mean_out, float* rstd_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return gemm_norm(A, B, gamma, beta, C, M, N, K, b_layout, eps, mean_out, rstd_out, workspace,
+                   workspace_bytes, (hipStream_t)stream, ng::NORM_LAYER, "ng_gemm_layernorm");
+}
+
+int ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+            int b_layout, void* stream) {
+  int st = check_gemm(A, B, C, M, N, K, b_layout);
+  if (st) return st;
+  if (M == 0) return ok();
+  ng::GemmParams p = make_params(A, B, C, M, N, K, 0.f);
+  hipStream_t s = (hipStream_t)stream;
+  const bool kn = b_layout == NG_B_KN;
+  if (N <= 128)
+    return kn ? launch_grid<TRow128<true>, ng::EPI_NONE>(p, s, "ng_gemm")
+              : launch_grid<TRow128<false>, ng::EPI_NONE>(p, s, "ng_gemm");
+  return kn ? launch_grid<TLarge<true>, ng::EPI_NONE>(p, s, "ng_gemm")
+            : launch_grid<TLarge<false>, ng::EPI_NONE>(p, s, "ng_gemm");
+}
+
+int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* Y,
+            int64_t rows, int64_t cols, int kind, float eps, float* mean_out, float* rstd_out,
+            void* stream) {
+  if (rows != 0 && (!X || !Y)) return fail(NG_ERR_INVALID_ARG, "X and Y must be non-NULL");
+  if (!aligned(X, 16) || !aligned(Y, 16))
+    return fail(NG_ERR_INVALID_ARG, "X and Y must be 16-byte aligned");
+  if (rows < 0 || cols < 1 || rows > kMaxDim * 64)
+    return fail(NG_ERR_INVALID_ARG, "need rows >= 0 and cols >= 1");
+  if (kind != NG_NORM_RMS && kind != NG_NORM_LAYER)
+    return fail(NG_ERR_INVALID_ARG, "kind must be NG_NORM_RMS or NG_NORM_LAYER");
+  if (kind == NG_NORM_RMS && (beta || mean_out))
+    return fail(NG_ERR_INVALID_ARG, "RMSNorm takes no beta and has no mean output");
+  int st = check_eps(eps);
+  if (!st) st = check_vec(gamma, "gamma", 16);
+  if (!st) st = check_vec(beta, "beta", 16);
+  if (!st) st = check_vec(mean_out, "mean_out", 4);
+  if (!st) st = check_vec(rstd_out, "rstd_out", 4);
+  if (st) return st;
+  if (cols % 8 != 0 || cols > 65536)
+    return fail(NG_ERR_UNSUPPORTED, "cols must be a multiple of 8 and at most 65536");
+  if (rows == 0) return ok();
+  ng::NormParams p{};
+  p.X = X;
+  p.gamma = gamma;
+  p.beta = beta;
+  p.Y = Y;
+  p.mean_out = mean_out;
+  p.rstd_out = rstd_out;
+  p.rows = (int)rows;
+  p.cols = (int)cols;
+  p.kind = kind;
+  p.eps = eps;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nch = cols / 8;
+#define NG_NORM_LAUNCH(LPR, CPL)                                                          \
+  do {                                                                                    \
+    const unsigned grid = (unsigned)((rows + (256 / LPR) - 1) / (256 / LPR));             \
+    hipLaunchKernelGGL((ng::norm_kernel<LPR, CPL>), dim3(grid), dim3(256), 0, s, p);      \
+    return launched("ng_norm");                                                           \
+  } while (0)
+  if (nch <= 16) NG_NORM_LAUNCH(16, 1);
+  if (nch <= 32) NG_NORM_LAUNCH(32, 1);
+  if (nch <= 64) NG_NORM_LAUNCH(64, 1);
+  if (nch <= 128) NG_NORM_LAUNCH(64, 2);
+  if (nch <= 256) NG_NORM_LAUNCH(64, 4);
+  if (nch <= 512) NG_NORM_LAUNCH(128, 4);
+  if (nch <= 1024) NG_NORM_LAUNCH(256, 4);
+  if (nch <= 2048) NG_NORM_LAUNCH(256, 8);
+  if (nch <= 4096) NG_NORM_LAUNCH(256, 16);
+  NG_NORM_LAUNCH(256, 32);
+#undef NG_NORM_LAUNCH
+}
+
+size_t ng_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  if (op != NG_OP_GEMM_RMSNORM && op != NG_OP_GEMM_LAYERNORM) return 0;
+  if (M <= 0 || N <= 256 || M > kMaxDim || N > kMaxDim) return 0;
+  return xwg_bytes(M, N);
+}
+
+int ng_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || !aligned(workspace, 256))
+    return fail(NG_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes % 4 != 0) return fail(NG_ERR_INVALID_ARG, "workspace size must be a multiple of 4");
+  if (workspace_bytes == 0) return ok();
+  const size_t n16 = workspace_bytes / 16;
+  const size_t ntail = (workspace_bytes % 16) / 4;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(ng::fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     (hipStream_t)stream, (ng::u32x4*)workspace, n16,
+                     (uint32_t*)((char*)workspace + n16 * 16), ntail);
+  return launched("ng_workspace_reset");
+}
+
+int ng_workspace_status(const void* workspace, void* stream) {
+  if (!workspace || !aligned(workspace, 256))
+    return fail(NG_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail(NG_ERR_HIP, "stream sync failed: %s", hipGetErrorString(e));
+  int word = 0;
+  e = hipMemcpy(&word, workspace, sizeof(int), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(NG_ERR_HIP, "reading the error word failed: %s", hipGetErrorString(e));
+  if (word != 0) return fail(NG_ERR_TIMEOUT, "a cross-workgroup wait timed out");
+  return ok();
+}
+
+const char* ng_status_string(int status) {
+  switch (status) {
+    case NG_OK: return "NG_OK";
+    case NG_ERR_INVALID_ARG: return "NG_ERR_INVALID_ARG";
+    case NG_ERR_UNSUPPORTED: return "NG_ERR_UNSUPPORTED";
+    case NG_ERR_WORKSPACE: return "NG_ERR_WORKSPACE";
+    case NG_ERR_HIP: return "NG_ERR_HIP";
+    case NG_ERR_TIMEOUT: return "NG_ERR_TIMEOUT";
+    default: return "NG_ERR_UNKNOWN";
+  }
+}
+
+const char* ng_last_error(void) { return g_err; }
+
+}  // extern "C"

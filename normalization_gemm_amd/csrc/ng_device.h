@@ -1,0 +1,105 @@
+// Device-side helpers shared by the libnormgemm kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ng {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) float lds_float;
+typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
+
+// bf16 <-> fp32.  bf16 is the upper half of an fp32 bit pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair (element 0 in the low half), round to nearest
+// even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// D(16x16, fp32) += Aop(16x32) * Bop(32x16), bf16 operands.
+// Lane l supplies Aop row (l % 16) and Bop column (l % 16), each with the 8
+// k-values 8*(l/16) .. 8*(l/16)+7; D element (4*(l/16) + r, l % 16) lands in
+// register r.  (Lane layout checked on the device against a host product.)
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Sum of squares of the 8 bf16 values in a 16-byte fragment, added to acc
+// (v_dot2_f32_bf16: each bf16 product is exact in fp32).  The pairs are taken
+// with shufflevector from the whole 8-vector: bit-casting single dwords of a
+// 4-vector to bf16x2 here made hipcc feed the first dword to all four dot2s.
+__device__ __forceinline__ float sumsq_bf16x8(u32x4 v, float acc) {
+  const bf16x8 a = __builtin_bit_cast(bf16x8, v);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1),
+                                        __builtin_shufflevector(a, a, 0, 1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3),
+                                        __builtin_shufflevector(a, a, 2, 3), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5),
+                                        __builtin_shufflevector(a, a, 4, 5), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7),
+                                        __builtin_shufflevector(a, a, 6, 7), acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ lds_char* lds_base(void* smem) { return (lds_char*)smem; }
+
+// 16-byte LDS access at a byte offset.
+__device__ __forceinline__ u32x4 lds_read16(lds_char* base, uint32_t off) {
+  return *(lds_u32x4*)(base + off);
+}
+__device__ __forceinline__ void lds_write16(lds_char* base, uint32_t off, u32x4 v) {
+  *(lds_u32x4*)(base + off) = v;
+}
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, let lane j point at four consecutive 16-bit elements e = 0..3; lane i
+// then receives, in slot q, element (i % 4) of lane (i / 4 + 4 * q).  (Mapping
+// checked on the device.)
+__device__ __forceinline__ u32x2 lds_read_tr16(lds_char* base, uint32_t off) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Agent-scope relaxed atomics: loads and stores bypass the per-XCD L2 so that
+// values written by a workgroup on another XCD are observed.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_agent(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int add_agent(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_all_mem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+}  // namespace ng

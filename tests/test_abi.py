@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments before making any HIP call."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "normgemm.h")
+
+from normalization_gemm_amd import _lib  # noqa: E402
+
+lib_missing = not os.path.exists(_lib.LIB_PATH)
+pytestmark = pytest.mark.skipif(lib_missing, reason="libnormgemm.so not built")
+
+# Fake but well-aligned device addresses: validation never dereferences them.
+P = 0x7F0000000000
+P2 = P + 0x100000
+P3 = P + 0x200000
+BAD = P + 2  # not 16-byte aligned
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ng_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    names = header_functions()
+    for n in ("ng_rmsnorm_gemm_lazy", "ng_gemm_layernorm", "ng_gemm_rmsnorm", "ng_gemm",
+              "ng_norm", "ng_workspace_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert sorted(_lib.exported_names()) == header_functions()
+
+
+def test_status_strings():
+    assert _lib.ng_status_string(0) == "NG_OK"
+    assert _lib.ng_status_string(1) == "NG_ERR_INVALID_ARG"
+    assert _lib.ng_status_string(5) == "NG_ERR_TIMEOUT"
+    assert _lib.ng_status_string(99) == "NG_ERR_UNKNOWN"
+
+
+def lazy(A=P, B=P2, C=P3, M=64, N=64, K=64, lay=0, eps=1e-6, rstd=None):
+    return _lib.ng_rmsnorm_gemm_lazy(A, B, C, M, N, K, lay, eps, rstd, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(A=None), 1), (dict(B=None), 1), (dict(C=None), 1),
+    (dict(A=BAD), 1), (dict(C=BAD), 1),
+    (dict(M=-1), 1), (dict(N=0), 1), (dict(K=0), 1), (dict(K=-8), 1),
+    (dict(N=1 << 25), 1),
+    (dict(lay=2), 1), (dict(lay=-1), 1),
+    (dict(eps=-1.0), 1), (dict(eps=math.nan), 1), (dict(eps=math.inf), 1),
+    (dict(N=60), 2), (dict(K=100), 2),
+    (dict(rstd=P + 2), 1),
+])
+def test_lazy_argument_checks(kw, code):
+    assert lazy(**kw) == code
+    assert _lib.ng_last_error() != ""
+
+
+def test_empty_M_is_a_noop():
+    assert lazy(M=0) == 0
+    assert lazy(M=0, A=None, C=None) == 0
+    assert lazy(M=0, B=None) == 1
+    assert _lib.ng_norm(None, None, None, None, 0, 64, 1, 1e-6, None, None, None) == 0
+    assert _lib.ng_gemm(P, P2, P3, 0, 64, 64, 0, None) == 0
+    assert _lib.ng_norm(P, None, None, P2, 0, 64, 0, 1e-6, None, None, None) == 0
+    assert _lib.ng_gemm_layernorm(P, P2, None, None, P3, 0, 4096, 64, 0, 1e-5, None, None,
+                                  None, 0, None) == 0
+
+
+def test_gemm_norm_workspace_checks():
+    need = _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 1000, 4096, 512)
+    assert need > 0
+    # no workspace for wide rows
+    assert _lib.ng_gemm_layernorm(P, P2, None, None, P3, 1000, 4096, 512, 0, 1e-5, None, None,
+                                  None, 0, None) == 3
+    # too small
+    assert _lib.ng_gemm_rmsnorm(P, P2, None, P3, 1000, 4096, 512, 0, 1e-6, None, P,
+                                need - 8, None) == 3
+    # misaligned workspace
+    assert _lib.ng_gemm_rmsnorm(P, P2, None, P3, 1000, 4096, 512, 0, 1e-6, None, P + 16,
+                                need, None) == 3
+    # narrow rows need none
+    assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 1000, 256, 512) == 0
+    assert _lib.ng_workspace_bytes(_lib.NG_OP_RMSNORM_GEMM_LAZY, 1000, 4096, 512) == 0
+    assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM, 1000, 4096, 512) == 0
+
+
+def test_workspace_size_formula():
+    # header 256 B + counters, then float2 partials per (row block, column tile, row)
+    M, N = 16384, 8192
+    rb, tn = M // 256, N // 256
+    counters = 256 + 8 * rb
+    part_off = (counters + 255) // 256 * 256
+    assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_RMSNORM, M, N, 4096) == part_off + rb * tn * 256 * 8
+
+
+def test_gemm_norm_argument_checks():
+    ok_ws = _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 64, 4096, 64)
+    # gamma/beta misaligned
+    assert _lib.ng_gemm_layernorm(P, P2, P + 8, None, P3, 64, 128, 64, 0, 1e-5, None, None,
+                                  None, 0, None) == 1
+    assert _lib.ng_gemm_layernorm(P, P2, None, P + 8, P3, 64, 128, 64, 0, 1e-5, None, None,
+                                  None, 0, None) == 1
+    assert _lib.ng_gemm_layernorm(P, P2, None, None, P3, 64, 128, 64, 0, -1.0, None, None,
+                                  None, 0, None) == 1
+    assert _lib.ng_gemm_layernorm(P, P2, None, None, P3, 64, 4096, 64, 5, 1e-5, None, None,
+                                  P, ok_ws, None) == 1
+    assert _lib.ng_gemm_rmsnorm(P, P2, None, P3, 64, 100, 64, 0, 1e-6, None, None, 0, None) == 2
+
+
+def test_norm_argument_checks():
+    f = _lib.ng_norm
+    assert f(None, None, None, P2, 4, 64, 0, 1e-6, None, None, None) == 1
+    assert f(P, None, None, BAD, 4, 64, 0, 1e-6, None, None, None) == 1
+    assert f(P, None, None, P2, 4, 64, 7, 1e-6, None, None, None) == 1
+    assert f(P, None, P3, P2, 4, 64, 0, 1e-6, None, None, None) == 1   # beta with RMS
+    assert f(P, None, None, P2, 4, 64, 0, 1e-6, P3, None, None) == 1   # mean_out with RMS
+    assert f(P, None, None, P2, 4, 60, 1, 1e-6, None, None, None) == 2
+    assert f(P, None, None, P2, 4, 65536 + 8, 1, 1e-6, None, None, None) == 2
+    assert f(P, None, None, P2, 4, 0, 1, 1e-6, None, None, None) == 1
+
+
+def test_workspace_helpers_argument_checks():
+    assert _lib.ng_workspace_reset(None, 256, None) == 1
+    assert _lib.ng_workspace_reset(P + 16, 256, None) == 1
+    assert _lib.ng_workspace_status(None, None) == 1
+
+
+def test_package_has_no_cpu_fallback():
+    import normalization_gemm_amd as ng
+    import torch
+    A = torch.zeros((8, 8), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ng.rmsnorm_gemm_lazy(A, A)
+    with pytest.raises(ValueError):
+        ng.norm(A, "rms")
