@@ -50,7 +50,22 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run 3 plain device copies of this many MiB (a known-size "
+                         "kernel for scaling profiler byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def algorithmic_bytes(w: workloads.Workload) -> int:
@@ -287,6 +302,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy_mib:
+        copy_calibration(args.calibrate_copy_mib)
     names = [w.name for w in workloads.WORKLOADS] if args.workload == "all" else [args.workload]
     for name in names:
         w = workloads.WORKLOAD_BY_NAME[name]

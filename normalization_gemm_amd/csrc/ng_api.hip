@@ -37,10 +37,12 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 constexpr int64_t kMaxDim = int64_t(1) << 24;
 
 // Tile configurations.
-//   Large: 256x256 macro tile, 4 waves of 128x128 (MFMA-bound shapes).
+//   Large: 256x256 macro tile, 8 waves (4 along M x 2 along N) of 64x128, two
+//          waves per SIMD so that one issues MFMAs while the other waits
+//          (MFMA-bound shapes; measured ahead of 4 waves of 128x128).
 //   Row128: 128 x 128, 4 waves stacked along M, each owning whole rows (N <= 128).
 //   Row256: 128 x 256, 2x2 waves (128 < N <= 256).
-template <bool KN> using TLarge = ng::Tile<256, 256, 2, 2, KN>;
+template <bool KN> using TLarge = ng::Tile<256, 256, 4, 2, KN>;
 template <bool KN> using TRow128 = ng::Tile<128, 128, 4, 1, KN>;
 template <bool KN> using TRow256 = ng::Tile<128, 256, 2, 2, KN>;
 

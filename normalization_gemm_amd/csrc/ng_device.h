@@ -19,6 +19,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) float lds_float;
 typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
 // bf16 <-> fp32.  bf16 is the upper half of an fp32 bit pattern.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -40,21 +41,23 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Sum of squares of the 8 bf16 values in a 16-byte fragment, added to acc
-// (v_dot2_f32_bf16: each bf16 product is exact in fp32).  The pairs are taken
-// with shufflevector from the whole 8-vector: bit-casting single dwords of a
-// 4-vector to bf16x2 here made hipcc feed the first dword to all four dot2s.
-__device__ __forceinline__ float sumsq_bf16x8(u32x4 v, float acc) {
+// Sum of squares of bf16 pair D (elements 2D, 2D+1) of a 16-byte fragment,
+// added to acc (v_dot2_f32_bf16: each bf16 product is exact in fp32).  The
+// pair is taken with shufflevector from the whole 8-vector: bit-casting one
+// dword of a 4-vector to bf16x2 made hipcc feed dword 0 to every call.
+template <int D>
+__device__ __forceinline__ float sumsq_pair(u32x4 v, float acc) {
   const bf16x8 a = __builtin_bit_cast(bf16x8, v);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1),
-                                        __builtin_shufflevector(a, a, 0, 1), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3),
-                                        __builtin_shufflevector(a, a, 2, 3), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5),
-                                        __builtin_shufflevector(a, a, 4, 5), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7),
-                                        __builtin_shufflevector(a, a, 6, 7), acc, false);
-  return acc;
+  const bf16x2 x = __builtin_shufflevector(a, a, 2 * D, 2 * D + 1);
+  return __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
+}
+__device__ __forceinline__ float sumsq_pair(u32x4 v, int d, float acc) {
+  switch (d) {
+    case 0: return sumsq_pair<0>(v, acc);
+    case 1: return sumsq_pair<1>(v, acc);
+    case 2: return sumsq_pair<2>(v, acc);
+    default: return sumsq_pair<3>(v, acc);
+  }
 }
 
 __device__ __forceinline__ lds_char* lds_base(void* smem) { return (lds_char*)smem; }
@@ -101,5 +104,42 @@ __device__ __forceinline__ void wait_all_mem() {
 }
 
 __device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Raw buffer resource over `bytes` bytes from `base`: loads at offsets at or
+// beyond the size return zero.  Sizes are clamped below 2^31 so that offset
+// kOOB is always out of range.
+constexpr uint32_t kOOB = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)n, 0x00020000);
+}
+
+// 16 bytes per lane from global memory straight into LDS (buffer_load_dwordx4
+// ... lds): lane l's data lands at LDS byte address lds_addr + 16*l; lds_addr
+// must be wave-uniform.  Issued through inline asm so that the compiler does
+// not add a full vmcnt wait before unrelated LDS reads; callers order the
+// transfer with wait_vmcnt() and a barrier.  M0 is saved and restored.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr, uint32_t voff,
+                                      uint32_t soff) {
+  uint32_t tmp;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(tmp)
+      : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff)
+      : "memory");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(lds_char* p) { return (uint32_t)(uintptr_t)p; }
 
 }  // namespace ng

@@ -4,8 +4,9 @@
 //   EPI_NONE      C = A @ B                               (unfused baseline GEMM)
 //   EPI_LAZY      C = (A @ B) * rstd(A)                   (Lazy Pre-Norm)
 //   EPI_ROW_LOCAL C = norm(A @ B), whole row in one workgroup (N <= BN)
-//   EPI_ROW_XWG   C = norm(A @ B), row split over workgroups; per-row fp32
-//                 partials merged through a workspace (persistent grid)
+//   cross-workgroup: C = norm(A @ B) for rows split over workgroups; per-row
+//                 fp32 partials merged through a workspace (persistent grid,
+//                 gemm_xwg_kernel below)
 //
 // Lazy Pre-Norm ("Free normalization fusion", section "Lazy Pre-Norm"): a
 // per-row scale commutes with the product, so the sum of squares of each row
@@ -23,8 +24,9 @@
 // Data layout in LDS per pipeline stage (BK = 64):
 //   A tile  [BM][64] bf16, 128-byte rows; 16-byte chunk c of row m is stored
 //           at chunk c ^ (m & 7) (conflict-free 16-byte fragment reads).
-//   B tile  KN: [64][BN] bf16 rows (N contiguous), read with the transposing
-//           LDS read; 32-byte pair p of row k stored at p ^ h(k).
+//   B tile  KN: blocked [64/4][BN/16][4][16] bf16 (128-byte blocks of 4 k-rows
+//           x 16 columns), read with the transposing LDS read: each 16-lane
+//           group reads one whole block.
 //           NK: [BN][64] bf16, same layout as A.
 // MFMA: v_mfma_f32_16x16x32_bf16 with B as the first operand and A as the
 // second, so each lane's accumulators hold four consecutive columns of one
@@ -37,23 +39,27 @@ namespace ng {
 
 constexpr int BK = 64;
 
-enum Epi { EPI_NONE = 0, EPI_LAZY = 1, EPI_ROW_LOCAL = 2, EPI_ROW_XWG = 3 };
+enum Epi { EPI_NONE = 0, EPI_LAZY = 1, EPI_ROW_LOCAL = 2 };
 enum NormKind { NORM_RMS = 0, NORM_LAYER = 1 };
 
-// Workspace layout for EPI_ROW_XWG (byte offsets).
+// Workspace layout of the cross-workgroup row norm (byte offsets).
 //   [0]            int error word (0 = ok, 1 = a wait timed out)
 //   [256 + 4 rb]   int arrive[row_blocks]
 //   [..]           int depart[row_blocks]
-//   [part_off]     float2 partial[row_blocks][tiles_n][BM]
+//   [part_off]     float2 partial[row_blocks][BM][tn_pad]: per row, the
+//                  (mean, M2) or (0, sum x^2) of each column tile, so that one
+//                  row's partials are contiguous (tn_pad = tiles_n rounded up
+//                  to even: 16-byte rows)
 struct XwgLayout {
   static constexpr size_t kErr = 0;
   static constexpr size_t kCnt = 256;
+  static __host__ __device__ int tn_pad(int tiles_n) { return (tiles_n + 1) & ~1; }
   static __host__ __device__ size_t part_off(int row_blocks) {
     size_t end = kCnt + 8u * (size_t)row_blocks;
     return (end + 255) & ~(size_t)255;
   }
   static __host__ __device__ size_t bytes(int row_blocks, int tiles_n, int bm) {
-    return part_off(row_blocks) + (size_t)row_blocks * tiles_n * bm * 8u;
+    return part_off(row_blocks) + (size_t)row_blocks * bm * tn_pad(tiles_n) * 8u;
   }
 };
 
@@ -87,7 +93,7 @@ struct Tile {
   static constexpr int A_PER = BM * BK / 8 / NT;  // 16-byte chunks per thread
   static constexpr int B_PER = BN * BK / 8 / NT;
   static constexpr int RED_BYTES = WN * BM * 4;   // cross-wave row partials
-  static constexpr int FIN_BYTES = BM * 8;        // per-row (mean, rstd)
+  static constexpr int FIN_BYTES = BM * 16;       // per-row (mean, rstd, tile mean)
   static constexpr int LDS = 2 * STAGE + RED_BYTES + FIN_BYTES;
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
   static_assert((BM * BK / 8) % NT == 0 && (BN * BK / 8) % NT == 0, "loader split");
@@ -95,140 +101,213 @@ struct Tile {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// Swizzle of the B (KN) tile: the 16 rows a transposing read touches at once
-// (k = 8g + i, g, i in 0..3) land on distinct 32-byte bank groups.
+// Byte offset of element (k, n) of the B (KN) tile in its blocked layout.
 template <int BN>
-__device__ __forceinline__ uint32_t b_row_swz(int k) {
-  return (uint32_t)(((k & 3) | (((k >> 3) & 3) << 2)) & (BN / 16 - 1));
+__host__ __device__ constexpr uint32_t b_blk_off(int k, int n) {
+  return (uint32_t)((((k >> 2) * (BN / 16) + (n >> 4)) << 7) + ((k & 3) << 5) + ((n & 15) << 1));
 }
 
+// Global -> LDS staging.  Each wave moves 1 KB per buffer_load ... lds
+// instruction (16 bytes per lane, landing at consecutive LDS addresses); the
+// swizzle is applied on the global side by choosing which 16-byte chunk each
+// lane fetches.  Chunks outside the matrices read as zero: rows past the end
+// fall outside the buffer resource, and chunks past K (A, B[N,K]) or past N
+// (B[K,N]) get an out-of-range offset.
 template <class T>
-struct Stage {
-  u32x4 a[T::A_PER];
-  u32x4 b[T::B_PER];
-};
+struct DmaPlan {
+  static constexpr int A_INS = T::A_BYTES / 1024 / (T::NT / 64);  // instructions per wave
+  static constexpr int B_INS = T::B_BYTES / 1024 / (T::NT / 64);
+  static constexpr int INS = A_INS + B_INS;
+  static_assert(A_INS * 1024 * (T::NT / 64) == T::A_BYTES, "A tile split");
+  static_assert(B_INS * 1024 * (T::NT / 64) == T::B_BYTES, "B tile split");
+  static_assert(INS < 32, "vmcnt budget");
+  int wave;
+  uint32_t a_voff;          // A (and B[N,K]): lane part of the offset, row 0 of the wave
+  uint32_t a_kc;            // k offset (elements) of this lane's chunk within the k-tile
+  uint32_t b_voff[B_INS];   // B[K,N]: lane part per instruction (N tail folded in)
+  uint32_t a_row_bytes;     // K * 2
 
-// Global -> registers for k-tile starting at k0.  Chunks outside the matrix
-// (row >= rows valid, k >= K, n >= N) read as zero.
-template <class T>
-__device__ __forceinline__ void load_tile(Stage<T>& st, const uint16_t* __restrict__ Ablk,
-                                          const uint16_t* __restrict__ Bblk, int m_valid,
-                                          int n_valid, int K, int N, int k0, int tid) {
+  __device__ __forceinline__ void init(const GemmParams& p, int n_base, int lane, int wave_) {
+    wave = wave_;
+    a_row_bytes = (uint32_t)p.K * 2u;
+    const uint32_t c = (uint32_t)((lane & 7) ^ ((lane >> 3) & 7));
+    a_kc = 8u * c;
+    a_voff = (uint32_t)(lane >> 3) * a_row_bytes + 16u * c;
+    if constexpr (T::KN) {
+      // LDS slot (16 bytes) -> (k, n) of the blocked layout -> global offset
 #pragma unroll
-  for (int i = 0; i < T::A_PER; ++i) {
-    int q = tid + i * T::NT;
-    int row = q >> 3, c = q & 7;
-    int k = k0 + 8 * c;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (row < m_valid && k < K) v = *(const u32x4*)(Ablk + (size_t)row * K + k);
-    st.a[i] = v;
-  }
-  if constexpr (T::KN) {
-    constexpr int CPR = T::BN / 8;
-#pragma unroll
-    for (int i = 0; i < T::B_PER; ++i) {
-      int q = tid + i * T::NT;
-      int kr = q / CPR, c = q % CPR;
-      int k = k0 + kr;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (k < K && 8 * c < n_valid) v = *(const u32x4*)(Bblk + (size_t)k * N + 8 * c);
-      st.b[i] = v;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < T::B_PER; ++i) {
-      int q = tid + i * T::NT;
-      int row = q >> 3, c = q & 7;
-      int k = k0 + 8 * c;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < n_valid && k < K) v = *(const u32x4*)(Bblk + (size_t)row * K + k);
-      st.b[i] = v;
-    }
-  }
-}
-
-template <class T>
-__device__ __forceinline__ void store_tile(const Stage<T>& st, lds_char* lds, uint32_t stage_off,
-                                           int tid) {
-#pragma unroll
-  for (int i = 0; i < T::A_PER; ++i) {
-    int q = tid + i * T::NT;
-    int row = q >> 3, c = q & 7;
-    lds_write16(lds, stage_off + row * 128 + ((c ^ (row & 7)) << 4), st.a[i]);
-  }
-  if constexpr (T::KN) {
-    constexpr int CPR = T::BN / 8;
-#pragma unroll
-    for (int i = 0; i < T::B_PER; ++i) {
-      int q = tid + i * T::NT;
-      int kr = q / CPR, c = q % CPR;
-      uint32_t pc = (uint32_t)c ^ (b_row_swz<T::BN>(kr) << 1);
-      lds_write16(lds, stage_off + T::A_BYTES + kr * (T::BN * 2) + (pc << 4), st.b[i]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < T::B_PER; ++i) {
-      int q = tid + i * T::NT;
-      int row = q >> 3, c = q & 7;
-      lds_write16(lds, stage_off + T::A_BYTES + row * 128 + ((c ^ (row & 7)) << 4), st.b[i]);
-    }
-  }
-}
-
-// MFMAs for one BK=64 stage: two k32 sub-steps.
-template <class T, bool LAZY>
-__device__ __forceinline__ void compute_stage(f32x4 (&acc)[T::FM][T::FN], float (&ss)[T::FM],
-                                              lds_char* lds, uint32_t stage_off, int wm, int wn,
-                                              int lane) {
-  const int l16 = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
-    u32x4 af[T::FM], bfr[T::FN];
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
-      int row = wm * T::WTM + 16 * i + l16;
-      int c = kk * 4 + g;
-      af[i] = lds_read16(lds, stage_off + row * 128 + ((c ^ (row & 7)) << 4));
-    }
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) {
-      if constexpr (T::KN) {
-        int ncol = wn * T::WTN + 16 * j + 4 * (l16 & 3);
-        uint32_t c = (uint32_t)(ncol >> 3);
-        uint32_t half = (uint32_t)(l16 & 1) << 3;
-        int kr0 = kk * 32 + 8 * g + (l16 >> 2);
-        int kr1 = kr0 + 4;
-        uint32_t o0 = stage_off + T::A_BYTES + kr0 * (T::BN * 2) +
-                      ((c ^ (b_row_swz<T::BN>(kr0) << 1)) << 4) + half;
-        uint32_t o1 = stage_off + T::A_BYTES + kr1 * (T::BN * 2) +
-                      ((c ^ (b_row_swz<T::BN>(kr1) << 1)) << 4) + half;
-        u32x2 lo = lds_read_tr16(lds, o0);
-        u32x2 hi = lds_read_tr16(lds, o1);
-        bfr[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      } else {
-        int row = wn * T::WTN + 16 * j + l16;
-        int c = kk * 4 + g;
-        bfr[j] = lds_read16(lds, stage_off + T::A_BYTES + row * 128 + ((c ^ (row & 7)) << 4));
+      for (int j = 0; j < B_INS; ++j) {
+        const int slot = (wave * B_INS + j) * 64 + lane;  // 16-byte slot in the B stage
+        const int blk = slot >> 3, in = slot & 7;
+        const int kr = 4 * (blk / (T::BN / 16)) + (in >> 1);
+        const int nc = 16 * (blk % (T::BN / 16)) + 8 * (in & 1);
+        const bool ok = n_base + nc < p.N;
+        b_voff[j] = ok ? (uint32_t)kr * (uint32_t)p.N * 2u + 2u * (uint32_t)nc : kOOB;
       }
     }
-    if constexpr (LAZY) {
+  }
+
+  // Issue the transfers of k-tile kt into the stage at LDS byte address `st`.
+  __device__ __forceinline__ void issue_a(const GemmParams& p, int m_base, int kt, uint32_t st,
+                                          int j) const {
+    const int k0 = kt * BK;
+    const uint64_t off = (uint64_t)m_base * p.K + k0;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(p.A + off, ((uint64_t)p.M * p.K - off) * 2u);
+    const uint32_t v = (k0 + (int)a_kc < p.K) ? a_voff : kOOB;
+    const uint32_t row0 = (uint32_t)((wave * A_INS + j) * 8);
+    dma16(rs, st + (uint32_t)(wave * A_INS + j) * 1024u, v, row0 * a_row_bytes);
+  }
+  __device__ __forceinline__ void issue_b(const GemmParams& p, int n_base, int kt, uint32_t st,
+                                          int j) const {
+    const int k0 = kt * BK;
+    if constexpr (T::KN) {
+      const uint64_t off = (uint64_t)k0 * p.N + n_base;
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(p.B + off, ((uint64_t)p.K * p.N - off) * 2u);
+      dma16(rs, st + T::A_BYTES + (uint32_t)(wave * B_INS + j) * 1024u, b_voff[j], 0u);
+    } else {
+      const uint64_t off = (uint64_t)n_base * p.K + k0;
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(p.B + off, ((uint64_t)p.N * p.K - off) * 2u);
+      const uint32_t v = (k0 + (int)a_kc < p.K) ? a_voff : kOOB;
+      const uint32_t row0 = (uint32_t)((wave * B_INS + j) * 8);
+      dma16(rs, st + T::A_BYTES + (uint32_t)(wave * B_INS + j) * 1024u, v, row0 * a_row_bytes);
+    }
+  }
+  // Transfer number d (0 .. INS-1) of k-tile kt.
+  __device__ __forceinline__ void issue(const GemmParams& p, int m_base, int n_base, int kt,
+                                        uint32_t st, int d) const {
+    if (d < A_INS) issue_a(p, m_base, kt, st, d);
+    else issue_b(p, n_base, kt, st, d - A_INS);
+  }
+};
+
+template <class T>
+struct Frags {
+  u32x4 a[T::FM];
+  u32x4 b[T::FN];
+};
+
+// LDS reads of one k32 sub-step's fragments, split into items so that they
+// can be spread between MFMAs: items 0..FM-1 read A fragments; the rest read
+// B fragments (two transposing 8-byte reads each for B[K,N], one 16-byte read
+// for B[N,K]).  Per lane only a base address per sub-step is computed; the
+// fragment index enters as a compile-time offset.
+template <class T>
+struct FragReader {
+  static constexpr int B_ITEMS = T::KN ? 2 * T::FN : T::FN;
+  static constexpr int ITEMS = T::FM + B_ITEMS;
+  uint32_t a_base[2];  // per kk: A fragment 0 of this lane (stage 0)
+  uint32_t b_base[2];  // per kk: B fragment 0 (half 0) of this lane (stage 0)
+
+  __device__ __forceinline__ void init(int wm, int wn, int lane) {
+    const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
-      for (int i = 0; i < T::FM; ++i) ss[i] = sumsq_bf16x8(af[i], ss[i]);
+    for (int kk = 0; kk < 2; ++kk) {
+      const int row = wm * T::WTM + l16;
+      a_base[kk] = (uint32_t)(row * 128 + (((kk * 4 + g) ^ (l16 & 7)) << 4));
+      if constexpr (T::KN) {
+        // k = kk*32 + 8g + (l16 >> 2) (+4 for the second half), n = wn*WTN + 4*(l16 & 3)
+        b_base[kk] = (uint32_t)T::A_BYTES +
+                     b_blk_off<T::BN>(kk * 32 + 8 * g + (l16 >> 2), wn * T::WTN + 4 * (l16 & 3));
+      } else {
+        const int brow = wn * T::WTN + l16;
+        b_base[kk] = (uint32_t)T::A_BYTES + (uint32_t)(brow * 128 + (((kk * 4 + g) ^ (l16 & 7)) << 4));
+      }
+    }
+  }
+  __device__ __forceinline__ void read(Frags<T>& f, int item, lds_char* lds, uint32_t st,
+                                       int kk) const {
+    if (item < T::FM) {
+      f.a[item] = lds_read16(lds, st + a_base[kk] + (uint32_t)item * 2048u);
+      return;
+    }
+    const int bi = item - T::FM;
+    if constexpr (T::KN) {
+      const int j = bi >> 1, h = bi & 1;
+      // +16 columns per fragment = next block; +4 k-rows per half = next block row
+      const uint32_t o = (uint32_t)j * 128u + (uint32_t)h * (uint32_t)(T::BN / 16) * 128u;
+      const u32x2 v = lds_read_tr16(lds, st + b_base[kk] + o);
+      if (h == 0) { f.b[j][0] = v[0]; f.b[j][1] = v[1]; }
+      else { f.b[j][2] = v[0]; f.b[j][3] = v[1]; }
+    } else {
+      f.b[bi] = lds_read16(lds, st + b_base[kk] + (uint32_t)bi * 2048u);
+    }
+  }
+};
+
+// One k32 sub-step: FM*FN MFMAs on `cur`, with the LDS reads of the next
+// sub-step's fragments (into `nxt`) and, when dma_on, the LDS transfers of a
+// later k-tile spread evenly between them.  (On the last sub-step the reads
+// fetch stale but in-bounds LDS data that is never used: one code path keeps
+// the accumulators in place.)  For Lazy Pre-Norm the sum of squares of each A
+// fragment is accumulated by four dot2s placed between that fragment's MFMAs.
+template <class T, bool LAZY>
+__device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN], float (&ss)[T::FM],
+                                        const Frags<T>& cur, Frags<T>& nxt, lds_char* lds,
+                                        const FragReader<T>& rd, uint32_t rd_st, int rd_kk,
+                                        const DmaPlan<T>& dma,
+                                        bool dma_on, const GemmParams& p, int m_base,
+                                        int n_base, int dma_kt, uint32_t dma_st) {
+  constexpr int NM = T::FM * T::FN;
+  constexpr int NR = FragReader<T>::ITEMS;
+  constexpr int ND = DmaPlan<T>::INS;
+#pragma unroll
+  for (int q = 0; q < NM; ++q) {
+    const int i = q / T::FN, j = q % T::FN;
+    acc[i][j] = mfma_16x16x32(cur.b[j], cur.a[i], acc[i][j]);
+    if constexpr (LAZY) {
+      // the four dot2s of fragment i, two MFMAs apart (a dependent chain)
+      constexpr int STEP = T::FN >= 8 ? T::FN / 4 : 1;
+      if (j % STEP == 0 && j / STEP < 4) ss[i] = sumsq_pair(cur.a[i], j / STEP, ss[i]);
+      if (T::FN < 4 && j == T::FN - 1)
+        for (int d = T::FN; d < 4; ++d) ss[i] = sumsq_pair(cur.a[i], d, ss[i]);
+      // pin the dot2 here: left alone, the compiler sinks all of them to the
+      // end of the sub-step, where they stall the MFMA issue
+      asm volatile("" : "+v"(ss[i]));
     }
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i)
+    for (int r = (q * NR) / NM; r < ((q + 1) * NR) / NM; ++r)
+      rd.read(nxt, r, lds, rd_st, rd_kk);
 #pragma unroll
-      for (int j = 0; j < T::FN; ++j) acc[i][j] = mfma_16x16x32(bfr[j], af[i], acc[i][j]);
+    for (int d = (q * ND) / NM; d < ((q + 1) * ND) / NM; ++d)
+      if (dma_on) dma.issue(p, m_base, n_base, dma_kt, dma_st, d);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Full k-loop for the tile at (m_base, n_base): two LDS stages, the next
-// k-tile's global loads in flight during the current stage's MFMAs.
+// Full k-loop for the tile at (m_base, n_base).  Two LDS stages; fragments
+// double-buffered in registers.  Per k-tile kt (stage s = kt & 1):
+//   sub-step 0: MFMAs on (kt, k 0..31) while reading (kt, k 32..63);
+//   wait for k-tile kt+1's transfers, barrier;
+//   sub-step 1: MFMAs on (kt, k 32..63) while reading (kt+1, k 0..31) and
+//               issuing k-tile kt+2's transfers into stage s (no wave reads
+//               stage s any more after the barrier).
+// LDS transfers of the first two k-tiles of the tile at (m_base, n_base).
+template <class T>
+__device__ __forceinline__ void issue_prologue(const GemmParams& p, uint32_t lds0, int m_base,
+                                               int n_base, int tid) {
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  DmaPlan<T> dma;
+  dma.init(p, n_base, lane, wave);
+  constexpr int ND = DmaPlan<T>::INS;
+#pragma unroll
+  for (int d = 0; d < ND; ++d) dma.issue(p, m_base, n_base, 0, lds0, d);
+  if (p.K > BK) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) dma.issue(p, m_base, n_base, 1, lds0 + T::STAGE, d);
+  }
+}
+
 template <class T, bool LAZY>
 __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM][T::FN],
-                                         float (&ss)[T::FM], lds_char* lds, int m_base,
-                                         int n_base) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                         float (&ss)[T::FM], lds_char* lds, uint32_t lds0,
+                                         int m_base, int n_base, int tid,
+                                         bool prologue_issued = false) {
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WN, wn = wave % T::WN;
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
@@ -236,27 +315,33 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int m_valid = min(T::BM, p.M - m_base);
-  const int n_valid = min(T::BN, p.N - n_base);
-  const uint16_t* Ablk = p.A + (size_t)m_base * p.K;
-  const uint16_t* Bblk = T::KN ? p.B + n_base : p.B + (size_t)n_base * p.K;
+  DmaPlan<T> dma;
+  dma.init(p, n_base, lane, wave);
+  FragReader<T> rd;
+  rd.init(wm, wn, lane);
+  constexpr int ND = DmaPlan<T>::INS;
+  constexpr int NR = FragReader<T>::ITEMS;
   const int nk = (p.K + BK - 1) / BK;
 
-  Stage<T> st;
-  load_tile<T>(st, Ablk, Bblk, m_valid, n_valid, p.K, p.N, 0, tid);
-  store_tile<T>(st, lds, 0, tid);
-  if (nk > 1) load_tile<T>(st, Ablk, Bblk, m_valid, n_valid, p.K, p.N, BK, tid);
+  if (!prologue_issued) issue_prologue<T>(p, lds0, m_base, n_base, tid);
+  if (nk > 1) wait_vmcnt<ND>();
+  else wait_vmcnt<0>();
   __syncthreads();
+  Frags<T> f0, f1;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) rd.read(f0, r, lds, 0, 0);
+
   for (int kt = 0; kt < nk; ++kt) {
     const uint32_t cur = (uint32_t)(kt & 1) * T::STAGE;
-    const uint32_t nxt = (uint32_t)((kt + 1) & 1) * T::STAGE;
-    compute_stage<T, LAZY>(acc, ss, lds, cur, wm, wn, lane);
-    if (kt + 1 < nk) {
-      store_tile<T>(st, lds, nxt, tid);
-      if (kt + 2 < nk) load_tile<T>(st, Ablk, Bblk, m_valid, n_valid, p.K, p.N, (kt + 2) * BK, tid);
-    }
+    const uint32_t nxt = (uint32_t)T::STAGE - cur;
+    substep<T, LAZY>(acc, ss, f0, f1, lds, rd, cur, 1, dma, false, p, m_base, n_base, 0, 0);
+    if (kt + 1 < nk) wait_vmcnt<0>();
     __syncthreads();
+    substep<T, LAZY>(acc, ss, f1, f0, lds, rd, nxt, 0, dma, kt + 2 < nk, p, m_base, n_base,
+                     kt + 2, lds0 + cur);
   }
+  // every wave is done with the stages before they are reused
+  __syncthreads();
 }
 
 // Sum over the 4 lane groups sharing (lane & 15): a row's partial over this
@@ -346,16 +431,48 @@ __device__ __forceinline__ void apply_store(const GemmParams& p, f32x4 (&acc)[T:
   }
 }
 
+// Row statistics of this tile's slice of each row, from the fp32
+// accumulators: LayerNorm (s1, s2) = (tile mean, tile M2 = sum (x - mean)^2),
+// two passes over registers; RMSNorm (0, sum x^2).
+template <class T>
+__device__ __forceinline__ void tile_stats(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
+                                           lds_char* lds, int n_base, int wm, int wn, int lane,
+                                           float (&s1)[T::FM], float (&s2)[T::FM]) {
+  const int g = lane >> 4;
+  bool colv[T::FN];
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) colv[j] = (n_base + wn * T::WTN + 16 * j + 4 * g) < p.N;
+  const int n_tile = min(T::BN, p.N - n_base);
+  float zero[T::FM];
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) zero[i] = 0.f;
+  if (p.norm_kind == NORM_LAYER) {
+    tile_row_sums<T>(acc, colv, 0, zero, s1, lds, wm, wn, lane);
+    const float inv = 1.0f / (float)n_tile;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) s1[i] *= inv;
+    tile_row_sums<T>(acc, colv, 1, s1, s2, lds, wm, wn, lane);
+  } else {
+    tile_row_sums<T>(acc, colv, 2, zero, s2, lds, wm, wn, lane);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) s1[i] = 0.f;
+  }
+}
+
 template <class T, int EPI>
 __device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds, int tm, int tn) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Opaque copy of the thread id: keeps lane-dependent addresses from being
+  // hoisted out of the persistent tile loop (where they would be spilled).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int l16 = lane & 15, g = lane >> 4;
   const int m_base = tm * T::BM, n_base = tn * T::BN;
 
   f32x4 acc[T::FM][T::FN];
   float ss[T::FM];
-  mainloop<T, EPI == EPI_LAZY>(p, acc, ss, lds, m_base, n_base);
+  mainloop<T, EPI == EPI_LAZY>(p, acc, ss, lds, lds_addr_of(lds), m_base, n_base, tid);
 
   float mean[T::FM], rstd[T::FM];
   if constexpr (EPI == EPI_NONE) {
@@ -381,102 +498,14 @@ __device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds,
     apply_store<T>(q, acc, mean, rstd, false, m_base, n_base, wm, wn, lane);
   } else {
     // Row statistics of this tile's slice of each row.
-    bool colv[T::FN];
-    int n_tile = 0;  // valid columns in this tile
-#pragma unroll
-    for (int j = 0; j < T::FN; ++j) colv[j] = (n_base + wn * T::WTN + 16 * j + 4 * g) < p.N;
-    n_tile = min(T::BN, p.N - n_base);
     const bool ln = p.norm_kind == NORM_LAYER;
-    float zero[T::FM], s1[T::FM], s2[T::FM];
+    float s1[T::FM], s2[T::FM];
+    tile_stats<T>(p, acc, lds, n_base, wm, wn, lane, s1, s2);
+    const float inv_n = 1.0f / (float)p.N;
 #pragma unroll
-    for (int i = 0; i < T::FM; ++i) zero[i] = 0.f;
-    if (ln) {
-      tile_row_sums<T>(acc, colv, 0, zero, s1, lds, wm, wn, lane);
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) s1[i] = s1[i] / (float)n_tile;  // tile mean
-      tile_row_sums<T>(acc, colv, 1, s1, s2, lds, wm, wn, lane);      // tile M2
-    } else {
-      tile_row_sums<T>(acc, colv, 2, zero, s2, lds, wm, wn, lane);    // tile sum x^2
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) s1[i] = 0.f;
-    }
-    if constexpr (EPI == EPI_ROW_LOCAL) {
-      const float inv_n = 1.0f / (float)p.N;
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) {
-        mean[i] = s1[i];
-        rstd[i] = 1.0f / __builtin_sqrtf(fmaf(s2[i], inv_n, p.eps));
-      }
-    } else {
-      // Cross-workgroup merge of per-row partials (persistent grid, all
-      // workgroups of a row block co-resident).
-      const uint32_t fin = 2 * T::STAGE + T::RED_BYTES;
-      const int row_blocks = p.tiles_m;
-      int* err = (int*)(p.ws + XwgLayout::kErr);
-      int* arrive = (int*)(p.ws + XwgLayout::kCnt);
-      int* depart = arrive + row_blocks;
-      float* part = (float*)(p.ws + XwgLayout::part_off(row_blocks));
-      float* mypart = part + ((size_t)tm * p.tiles_n + tn) * T::BM * 2;
-      if (wn == 0 && g == 0) {
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i) {
-          const int r = wm * T::WTM + 16 * i + l16;
-          store_agent(mypart + 2 * r, s1[i]);
-          store_agent(mypart + 2 * r + 1, s2[i]);
-        }
-      }
-      wait_all_mem();
-      __syncthreads();
-      if (tid == 0) {
-        add_agent(arrive + tm, 1);
-        int spins = 0;
-        while (load_agent(arrive + tm) < p.tiles_n) {
-          __builtin_amdgcn_s_sleep(4);
-          if (++spins > p.spin_limit) {
-            store_agent(err, 1);
-            break;
-          }
-        }
-      }
-      __syncthreads();
-      // Merge the tiles_n partials of each row in fixed tile order (all
-      // workgroups of the row block compute identical statistics).
-      for (int row = tid; row < T::BM; row += T::NT) {
-        const float* rowpart = part + (size_t)tm * p.tiles_n * T::BM * 2 + 2 * row;
-        float mu = 0.f, m2 = 0.f, cnt = 0.f;
-        for (int t = 0; t < p.tiles_n; ++t) {
-          const float a = load_agent(rowpart + (size_t)t * T::BM * 2);
-          const float b = load_agent(rowpart + (size_t)t * T::BM * 2 + 1);
-          const float nt = (float)min(T::BN, p.N - t * T::BN);
-          if (ln) {
-            const float nn = cnt + nt;
-            const float d = a - mu;
-            mu = fmaf(d, nt / nn, mu);
-            m2 = m2 + b + d * d * (cnt * nt / nn);
-            cnt = nn;
-          } else {
-            m2 += b;
-          }
-        }
-        const float r = 1.0f / __builtin_sqrtf(fmaf(m2, 1.0f / (float)p.N, p.eps));
-        *(lds_f32x2*)(lds + fin + row * 8) = f32x2{mu, r};
-      }
-      wait_all_mem();
-      __syncthreads();
-      if (tid == 0) {
-        // Last workgroup to leave resets the row block's counters for the
-        // next call (all have passed the wait by then).
-        if (add_agent(depart + tm, 1) == p.tiles_n - 1) {
-          store_agent(arrive + tm, 0);
-          store_agent(depart + tm, 0);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) {
-        f32x2 st = *(lds_f32x2*)(lds + fin + (wm * T::WTM + 16 * i + l16) * 8);
-        mean[i] = st[0];
-        rstd[i] = st[1];
-      }
+    for (int i = 0; i < T::FM; ++i) {
+      mean[i] = s1[i];
+      rstd[i] = 1.0f / __builtin_sqrtf(fmaf(s2[i], inv_n, p.eps));
     }
     if (p.mean_out || p.rstd_out) {
       if (tn == 0 && wn == 0 && g == 0) {
@@ -525,24 +554,226 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(GemmParams p) {
   process_tile<T, EPI>(p, lds, tm, tn);
 }
 
-// Persistent grid for EPI_ROW_XWG: gridDim.x = R * tiles_n workgroups, all
-// co-resident (cooperative launch).  Round `it` covers the complete row blocks
-// it*R .. it*R+R-1, so every workgroup a tile waits for is working on the
-// same round.
+// ---------------------------------------------------------------------------
+// Cross-workgroup row norm (rows wider than one tile).
+//
+// Persistent grid of R * tiles_n workgroups, all co-resident (cooperative
+// launch).  Round `it` covers the complete row blocks it*R .. it*R+R-1.  For
+// its tile of round `it` a workgroup
+//   1. runs the k-loop;
+//   2. reduces its slice of every row from the fp32 accumulators and
+//      publishes one (mean_t, M2_t) pair -- or (0, sum x^2) -- per row;
+//   3. writes its tile to C centred on the tile mean (LayerNorm) or as is
+//      (RMSNorm), rounded to bf16, and signals arrival for its row block;
+//   4. issues the LDS transfers that start its next tile;
+//   5. normalizes its tile of round it-1 in place: by now every workgroup of
+//      that row block has arrived (they did so one k-loop ago), so the wait
+//      is normally already over; the row statistics are merged from the
+//      partials in fixed tile order (Chan's update for mean/M2), identical in
+//      every workgroup of the row block.
+// The exchange latency thus hides behind the next tile's k-loop instead of
+// stalling every round.  Waits only ever point at earlier rounds, so the grid
+// cannot deadlock; the bounded spin is a guard, reported through the error
+// word.  Partials and counters use agent-scope (sc1) accesses that bypass the
+// per-XCD L2; a workgroup rereads only the C tile it wrote itself.
+// Storing the tile centred on its own mean keeps the bf16 intermediate small
+// relative to the row's spread, so the second rounding costs at most about
+// 2^-9 of the normalized value.
+
+// Byte offset of the row block's partials and an sc1 buffer view of them.
+template <class T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xwg_part_rsrc(const GemmParams& p, int tm) {
+  const int tnp = XwgLayout::tn_pad(p.tiles_n);
+  const size_t blk_bytes = (size_t)T::BM * tnp * 8u;
+  char* part = p.ws + XwgLayout::part_off(p.tiles_m);
+  return make_rsrc(part + (size_t)tm * blk_bytes, blk_bytes);
+}
+
+template <class T>
+__device__ __forceinline__ void xwg_publish(const GemmParams& p, f32x4 (&acc)[T::FM][T::FN],
+                                            lds_char* lds, int tm, int tn, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / T::WN, wn = wave % T::WN;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int m_base = tm * T::BM, n_base = tn * T::BN;
+  float s1[T::FM], s2[T::FM];
+  tile_stats<T>(p, acc, lds, n_base, wm, wn, lane, s1, s2);
+  const int tnp = XwgLayout::tn_pad(p.tiles_n);
+  const __amdgpu_buffer_rsrc_t prs = xwg_part_rsrc<T>(p, tm);
+  if (wn == 0 && g == 0) {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      const int r = wm * T::WTM + 16 * i + l16;
+      const u32x2 v = {__float_as_uint(s1[i]), __float_as_uint(s2[i])};
+      __builtin_amdgcn_raw_buffer_store_b64(v, prs, (uint32_t)(r * tnp + tn) * 8u, 0, 16);
+    }
+  }
+  // the tile, centred on its own row means (s1 is 0 for RMSNorm)
+  float one[T::FM];
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) one[i] = 1.f;
+  GemmParams q = p;
+  q.gamma = nullptr;
+  q.beta = nullptr;
+  apply_store<T>(q, acc, s1, one, true, m_base, n_base, wm, wn, lane);
+  wait_all_mem();
+  __syncthreads();
+  if (tid == 0) add_agent((int*)(p.ws + XwgLayout::kCnt) + tm, 1);
+}
+
+template <class T>
+__device__ __forceinline__ void xwg_apply(const GemmParams& p, lds_char* lds, int tm, int tn,
+                                          int tid) {
+  const uint32_t fin = 2 * T::STAGE + T::RED_BYTES;
+  int* err = (int*)(p.ws + XwgLayout::kErr);
+  int* arrive = (int*)(p.ws + XwgLayout::kCnt);
+  int* depart = arrive + p.tiles_m;
+  const bool ln = p.norm_kind == NORM_LAYER;
+  const int m_base = tm * T::BM, n_base = tn * T::BN;
+  if (tid == 0) {
+    int spins = 0;
+    while (load_agent(arrive + tm) < p.tiles_n) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > p.spin_limit) {
+        store_agent(err, 1);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+  // merge the row's partials in fixed tile order; batches of 8 x 16 bytes
+  const int tnp = XwgLayout::tn_pad(p.tiles_n);
+  const __amdgpu_buffer_rsrc_t prs = xwg_part_rsrc<T>(p, tm);
+  for (int row = tid; row < T::BM; row += T::NT) {
+    float mu = 0.f, m2 = 0.f, cnt = 0.f, mu_t = 0.f;
+    for (int t0 = 0; t0 < p.tiles_n; t0 += 16) {
+      u32x4 v[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        v[c] = __builtin_amdgcn_raw_buffer_load_b128(prs, (uint32_t)(row * tnp + t0 + 2 * c) * 8u,
+                                                     0, 16);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const int t = t0 + c;
+        if (t >= p.tiles_n) break;
+        const float a = __uint_as_float(v[c >> 1][(c & 1) * 2]);
+        const float b = __uint_as_float(v[c >> 1][(c & 1) * 2 + 1]);
+        if (t == tn) mu_t = a;
+        if (ln) {
+          const float nt = (float)min(T::BN, p.N - t * T::BN);
+          const float nn = cnt + nt;
+          const float d = a - mu;
+          mu = fmaf(d, nt / nn, mu);
+          m2 = m2 + b + d * d * (cnt * nt / nn);
+          cnt = nn;
+        } else {
+          m2 += b;
+        }
+      }
+    }
+    const float r = 1.0f / __builtin_sqrtf(fmaf(m2, 1.0f / (float)p.N, p.eps));
+    *(lds_f32x4*)(lds + fin + row * 16) = f32x4{mu, r, mu_t, 0.f};
+    const int m = m_base + row;
+    if (tn == 0 && m < p.M) {
+      if (p.mean_out) p.mean_out[m] = mu;
+      if (p.rstd_out) p.rstd_out[m] = r;
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // the last workgroup of the row block to get here resets its counters
+    // for the next call (all have passed the wait by then)
+    if (add_agent(depart + tm, 1) == p.tiles_n - 1) {
+      store_agent(arrive + tm, 0);
+      store_agent(depart + tm, 0);
+    }
+  }
+  // normalize the centred tile in place: y = (v + mu_t - mu) * rstd * gamma + beta.
+  // Thread t owns 8-column chunk t % (BN/8) of rows t / (BN/8) + k * NT/(BN/8).
+  constexpr int CPR = T::BN / 8;
+  constexpr int RSTEP = T::NT / CPR;
+  constexpr int NROW = T::BM / RSTEP;
+  static_assert(T::NT % CPR == 0 && T::BM % RSTEP == 0, "apply split");
+  const int c = tid % CPR;
+  const int n = n_base + 8 * c;
+  if (n >= p.N) return;
+  float gm[8], bt[8];
+  {
+    u32x4 gw = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
+    u32x4 bw = {0u, 0u, 0u, 0u};
+    if (p.gamma) gw = *(const u32x4*)(p.gamma + n);
+    if (p.beta) bw = *(const u32x4*)(p.beta + n);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      gm[2 * w] = bf16_lo(gw[w]); gm[2 * w + 1] = bf16_hi(gw[w]);
+      bt[2 * w] = bf16_lo(bw[w]); bt[2 * w + 1] = bf16_hi(bw[w]);
+    }
+  }
+  u32x4 v[NROW];
+#pragma unroll
+  for (int k = 0; k < NROW; ++k) {
+    const int m = m_base + tid / CPR + k * RSTEP;
+    v[k] = u32x4{0u, 0u, 0u, 0u};
+    if (m < p.M) v[k] = *(const u32x4*)(p.C + (size_t)m * p.N + n);
+  }
+#pragma unroll
+  for (int k = 0; k < NROW; ++k) {
+    const int row = tid / CPR + k * RSTEP;
+    const int m = m_base + row;
+    if (m >= p.M) continue;
+    const f32x4 st = *(lds_f32x4*)(lds + fin + row * 16);
+    const float r = st[1];
+    const float sh = (st[2] - st[0]) * r;
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = fmaf(fmaf(bf16_lo(v[k][w]), r, sh), gm[2 * w], bt[2 * w]);
+      const float b = fmaf(fmaf(bf16_hi(v[k][w]), r, sh), gm[2 * w + 1], bt[2 * w + 1]);
+      o[w] = pack_bf16x2(a, b);
+    }
+    *(u32x4*)(p.C + (size_t)m * p.N + n) = o;
+  }
+}
+
 template <class T>
 __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) char smem[T::LDS];
   lds_char* lds = lds_base(smem);
+  const uint32_t lds0 = lds_addr_of(lds);
   const int G = gridDim.x;
   const int R = G / p.tiles_n;
   const int j = (G % 8 == 0) ? xcd_contiguous(blockIdx.x, G) : (int)blockIdx.x;
   const int gh = (R % 4 == 0) ? 4 : ((R % 2 == 0) ? 2 : 1);
   int rb_in, tn;
   grouped_tile(j, R, p.tiles_n, gh, rb_in, tn);
+  int prev_tm = -1;
+  if (rb_in < p.tiles_m) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    issue_prologue<T>(p, lds0, rb_in * T::BM, tn * T::BN, tid);
+  }
   for (int it = 0; it < p.iters; ++it) {
     const int tm = it * R + rb_in;
     if (tm >= p.tiles_m) break;
-    process_tile<T, EPI_ROW_XWG>(p, lds, tm, tn);
+    // opaque thread id: keeps lane-dependent addresses from being hoisted
+    // out of the tile loop (where they would be spilled)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    {
+      f32x4 acc[T::FM][T::FN];
+      float ss[T::FM];
+      mainloop<T, false>(p, acc, ss, lds, lds0, tm * T::BM, tn * T::BN, tid, true);
+      xwg_publish<T>(p, acc, lds, tm, tn, tid);
+    }
+    const int next = tm + R;
+    if (next < p.tiles_m) issue_prologue<T>(p, lds0, next * T::BM, tn * T::BN, tid);
+    if (prev_tm >= 0) xwg_apply<T>(p, lds, prev_tm, tn, tid);
+    prev_tm = tm;
+  }
+  if (prev_tm >= 0) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    xwg_apply<T>(p, lds, prev_tm, tn, tid);
   }
 }
 
