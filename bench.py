@@ -53,7 +53,54 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run 3 plain device copies of this many MiB (a known-size "
                          "kernel for scaling profiler byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --calibrate-copy-mib 512` into profiles/traffic_<workload>.json")
     return ap.parse_args()
+
+
+def _pmc_rows(d, counter):
+    """(kernel name, value in KiB) per dispatch from a rocprofv3 --pmc csv."""
+    import csv
+    import glob
+    rows = []
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % d)
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return [(k, v) for _, k, v in rows]
+
+
+def summarize_pmc(fetch_dir, write_dir, w, copy_mib):
+    """HBM bytes per launch of the fused kernel, each counter scaled by what
+    it reads for a plain copy of known size (copy_mib read + written)."""
+    import statistics
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _pmc_rows(d, counter)
+        # the calibration copies are the first three runtime copy kernels
+        copies = [v for k, v in rows if "copybuffer" in k.lower()][:3]
+        fused = [v for k, v in rows if "gemm_kernel" in k or "gemm_xwg_kernel" in k]
+        if not copies or not fused:
+            raise SystemExit("missing copy or fused kernel rows for %s" % counter)
+        copy_kib = statistics.median(copies)
+        factor = (copy_mib * 1024.0) / copy_kib
+        out[counter] = {"copy_kib": copy_kib, "factor": factor,
+                        "fused_kib_median": statistics.median(fused),
+                        "fused_bytes": statistics.median(fused) * 1024.0 * factor}
+    rec = {"workload": w.name, "kernel_source_hash": kernel_source_hash(),
+           "copy_mib": copy_mib, "counters": out,
+           "bytes_per_launch": int(out["FETCH_SIZE"]["fused_bytes"] + out["WRITE_SIZE"]["fused_bytes"]),
+           "algorithmic_bytes": algorithmic_bytes(w)}
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % w.name)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
 
 
 def copy_calibration(mib: int):
@@ -127,9 +174,11 @@ class Bench:
         self.gamma = up(x.gamma) if x.gamma is not None else None
         self.beta = up(x.beta) if x.beta is not None else None
         self.C = [torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev) for _ in range(self.R)]
-        # unfused pair intermediates
+        # unfused pair intermediates: the normalized A of the lazy form's
+        # pair holds real values (the GEMM's speed depends on its data)
         if w.op == workloads.OP_LAZY:
-            self.An = [torch.empty_like(A0) for _ in range(self.R)]
+            An0 = ng.norm(A0, "rms", eps=w.eps)
+            self.An = [An0] + [An0.clone() for _ in range(self.R - 1)]
         self.ws = None
         op = {workloads.OP_LAZY: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_GEMM_RMSNORM: ng.NG_OP_GEMM_RMSNORM,
@@ -294,6 +343,10 @@ def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: f
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
+                      workloads.WORKLOAD_BY_NAME[args.workload], args.calibrate_copy_mib or 512)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(--gpus %d requested); run with --gpus 1" % args.gpus, file=sys.stderr)

@@ -42,22 +42,15 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // Sum of squares of bf16 pair D (elements 2D, 2D+1) of a 16-byte fragment,
-// added to acc (v_dot2_f32_bf16: each bf16 product is exact in fp32).  The
-// pair is taken with shufflevector from the whole 8-vector: bit-casting one
-// dword of a 4-vector to bf16x2 made hipcc feed dword 0 to every call.
-template <int D>
-__device__ __forceinline__ float sumsq_pair(u32x4 v, float acc) {
-  const bf16x8 a = __builtin_bit_cast(bf16x8, v);
-  const bf16x2 x = __builtin_shufflevector(a, a, 2 * D, 2 * D + 1);
-  return __builtin_amdgcn_fdot2_f32_bf16(x, x, acc, false);
-}
+// added to acc.  Widening to fp32 is exact (bf16 is the upper half of an
+// fp32), and so is each square in the fp32 FMA.  Plain VALU ops are used on
+// purpose: measured on gfx950, they co-issue with MFMAs at no cost, while
+// v_dot2_f32_bf16 competes with the MFMAs and slows the k-loop.
 __device__ __forceinline__ float sumsq_pair(u32x4 v, int d, float acc) {
-  switch (d) {
-    case 0: return sumsq_pair<0>(v, acc);
-    case 1: return sumsq_pair<1>(v, acc);
-    case 2: return sumsq_pair<2>(v, acc);
-    default: return sumsq_pair<3>(v, acc);
-  }
+  const uint32_t w = v[d];
+  const float lo = __uint_as_float(w << 16);
+  const float hi = __uint_as_float(w & 0xffff0000u);
+  return fmaf(lo, lo, fmaf(hi, hi, acc));
 }
 
 __device__ __forceinline__ lds_char* lds_base(void* smem) { return (lds_char*)smem; }

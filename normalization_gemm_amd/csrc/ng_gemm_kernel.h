@@ -80,9 +80,9 @@ struct GemmParams {
   int spin_limit;  // persistent grid: bounded wait (iterations of ~1 us)
 };
 
-template <int BM_, int BN_, int WM_, int WN_, bool KN_>
+template <int BM_, int BN_, int WM_, int WN_, bool KN_, int STAGES_ = 2>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
   static constexpr bool KN = KN_;
   static constexpr int NT = 64 * WM * WN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -94,17 +94,26 @@ struct Tile {
   static constexpr int B_PER = BN * BK / 8 / NT;
   static constexpr int RED_BYTES = WN * BM * 4;   // cross-wave row partials
   static constexpr int FIN_BYTES = BM * 16;       // per-row (mean, rstd, tile mean)
-  static constexpr int LDS = 2 * STAGE + RED_BYTES + FIN_BYTES;
+  static constexpr int RED_OFF = STAGES * STAGE;      // LDS byte offsets
+  static constexpr int FIN_OFF = RED_OFF + RED_BYTES;
+  static constexpr int LDS = FIN_OFF + FIN_BYTES;
+  static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
   static_assert((BM * BK / 8) % NT == 0 && (BN * BK / 8) % NT == 0, "loader split");
   static_assert((BN & (BN - 1)) == 0 && BN >= 16, "BN power of two");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// Byte offset of element (k, n) of the B (KN) tile in its blocked layout.
+// Byte offset of element (k, n) of the B (KN) tile in its blocked layout:
+// 128-byte blocks of 4 k-rows x 16 columns, block rows of BN/16 blocks.  The
+// column-block index is XORed with bit 3 of k so that the blocks that the
+// four 16-lane groups of one transposing read touch (k/8 = g) alternate
+// between the two 128-byte halves of the 64-bank LDS (measured: 1.5x faster
+// than the plain blocked layout).
 template <int BN>
 __host__ __device__ constexpr uint32_t b_blk_off(int k, int n) {
-  return (uint32_t)((((k >> 2) * (BN / 16) + (n >> 4)) << 7) + ((k & 3) << 5) + ((n & 15) << 1));
+  return (uint32_t)((((k >> 2) * (BN / 16) + ((n >> 4) ^ ((k >> 3) & 1))) << 7) +
+                    ((k & 3) << 5) + ((n & 15) << 1));
 }
 
 // Global -> LDS staging.  Each wave moves 1 KB per buffer_load ... lds
@@ -140,7 +149,7 @@ struct DmaPlan {
         const int slot = (wave * B_INS + j) * 64 + lane;  // 16-byte slot in the B stage
         const int blk = slot >> 3, in = slot & 7;
         const int kr = 4 * (blk / (T::BN / 16)) + (in >> 1);
-        const int nc = 16 * (blk % (T::BN / 16)) + 8 * (in & 1);
+        const int nc = 16 * ((blk % (T::BN / 16)) ^ ((kr >> 3) & 1)) + 8 * (in & 1);
         const bool ok = n_base + nc < p.N;
         b_voff[j] = ok ? (uint32_t)kr * (uint32_t)p.N * 2u + 2u * (uint32_t)nc : kOOB;
       }
@@ -200,6 +209,7 @@ struct FragReader {
   static constexpr int ITEMS = T::FM + B_ITEMS;
   uint32_t a_base[2];  // per kk: A fragment 0 of this lane (stage 0)
   uint32_t b_base[2];  // per kk: B fragment 0 (half 0) of this lane (stage 0)
+  uint32_t b_odd[2];   // KN: base for odd fragments (the XOR in b_blk_off)
 
   __device__ __forceinline__ void init(int wm, int wn, int lane) {
     const int l16 = lane & 15, g = lane >> 4;
@@ -208,9 +218,15 @@ struct FragReader {
       const int row = wm * T::WTM + l16;
       a_base[kk] = (uint32_t)(row * 128 + (((kk * 4 + g) ^ (l16 & 7)) << 4));
       if constexpr (T::KN) {
-        // k = kk*32 + 8g + (l16 >> 2) (+4 for the second half), n = wn*WTN + 4*(l16 & 3)
-        b_base[kk] = (uint32_t)T::A_BYTES +
-                     b_blk_off<T::BN>(kk * 32 + 8 * g + (l16 >> 2), wn * T::WTN + 4 * (l16 & 3));
+        // k = kk*32 + 8g + (l16 >> 2) (+4 for the second half), n = wn*WTN +
+        // 16j + 4*(l16 & 3).  Fragment j sits at block (j ^ p), p = g & 1,
+        // i.e. at +128 j from b_base (even j) or b_odd (odd j).
+        const int k = kk * 32 + 8 * g + (l16 >> 2);
+        const int n = wn * T::WTN + 4 * (l16 & 3);
+        const uint32_t p = (uint32_t)((k >> 3) & 1);
+        const uint32_t b0 = (uint32_t)T::A_BYTES + b_blk_off<T::BN>(k, n);  // fragment 0
+        b_base[kk] = b0;                       // even j: block j ^ p = j + p (p already in b0)
+        b_odd[kk] = b0 - 256u * p;             // odd j: block j ^ p = j - p
       } else {
         const int brow = wn * T::WTN + l16;
         b_base[kk] = (uint32_t)T::A_BYTES + (uint32_t)(brow * 128 + (((kk * 4 + g) ^ (l16 & 7)) << 4));
@@ -228,7 +244,7 @@ struct FragReader {
       const int j = bi >> 1, h = bi & 1;
       // +16 columns per fragment = next block; +4 k-rows per half = next block row
       const uint32_t o = (uint32_t)j * 128u + (uint32_t)h * (uint32_t)(T::BN / 16) * 128u;
-      const u32x2 v = lds_read_tr16(lds, st + b_base[kk] + o);
+      const u32x2 v = lds_read_tr16(lds, st + ((j & 1) ? b_odd[kk] : b_base[kk]) + o);
       if (h == 0) { f.b[j][0] = v[0]; f.b[j][1] = v[1]; }
       else { f.b[j][2] = v[0]; f.b[j][3] = v[1]; }
     } else {
@@ -241,15 +257,16 @@ struct FragReader {
 // sub-step's fragments (into `nxt`) and, when dma_on, the LDS transfers of a
 // later k-tile spread evenly between them.  (On the last sub-step the reads
 // fetch stale but in-bounds LDS data that is never used: one code path keeps
-// the accumulators in place.)  For Lazy Pre-Norm the sum of squares of each A
-// fragment is accumulated by four dot2s placed between that fragment's MFMAs.
+// the accumulators in place.)  For Lazy Pre-Norm the sum of squares of the A
+// fragments is accumulated by VALU ops placed between the MFMAs.
 template <class T, bool LAZY>
 __device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN], float (&ss)[T::FM],
+                                        float (&ss2)[T::FM],
                                         const Frags<T>& cur, Frags<T>& nxt, lds_char* lds,
                                         const FragReader<T>& rd, uint32_t rd_st, int rd_kk,
                                         const DmaPlan<T>& dma,
                                         bool dma_on, const GemmParams& p, int m_base,
-                                        int n_base, int dma_kt, uint32_t dma_st) {
+                                        int n_base, int dma_kt, uint32_t dma_st, int wn_) {
   constexpr int NM = T::FM * T::FN;
   constexpr int NR = FragReader<T>::ITEMS;
   constexpr int ND = DmaPlan<T>::INS;
@@ -258,14 +275,29 @@ __device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN], float (&ss)[
     const int i = q / T::FN, j = q % T::FN;
     acc[i][j] = mfma_16x16x32(cur.b[j], cur.a[i], acc[i][j]);
     if constexpr (LAZY) {
-      // the four dot2s of fragment i, two MFMAs apart (a dependent chain)
-      constexpr int STEP = T::FN >= 8 ? T::FN / 4 : 1;
-      if (j % STEP == 0 && j / STEP < 4) ss[i] = sumsq_pair(cur.a[i], j / STEP, ss[i]);
-      if (T::FN < 4 && j == T::FN - 1)
-        for (int d = T::FN; d < 4; ++d) ss[i] = sumsq_pair(cur.a[i], d, ss[i]);
-      // pin the dot2 here: left alone, the compiler sinks all of them to the
-      // end of the sub-step, where they stall the MFMA issue
-      asm volatile("" : "+v"(ss[i]));
+      // One dword (two bf16) of the sum of squares per MFMA: dword d of
+      // fragment ii, fragments interleaved so that consecutive updates of
+      // one accumulator are FM MFMAs apart, and the low and high halves
+      // going to two accumulators (no dependent VALU chain stalls the MFMA
+      // issue).
+      // The WN waves that share these rows split the dwords between them
+      // (wave wn takes dwords d with d % WN == wn); their sums are added in
+      // the epilogue.
+      constexpr int DPW = 4 / (T::WN < 4 ? T::WN : 4);  // dwords per wave per fragment
+      constexpr int NSQ = T::FM * DPW;
+      if (q < NSQ) {
+        const int ii = q % T::FM;
+        const int d = (q / T::FM) * (4 / DPW) + (wn_ % (4 / DPW));
+        const uint32_t w = cur.a[ii][d];
+        const float lo = __uint_as_float(w << 16);
+        const float hi = __uint_as_float(w & 0xffff0000u);
+        ss[ii] = fmaf(lo, lo, ss[ii]);
+        ss2[ii] = fmaf(hi, hi, ss2[ii]);
+        // pin the update here: left alone, the compiler sinks the squares to
+        // the end of the sub-step, where they wait for issue slots instead of
+        // sharing the MFMAs' shadow
+        asm volatile("" : "+v"(ss[ii]), "+v"(ss2[ii]));
+      }
     }
 #pragma unroll
     for (int r = (q * NR) / NM; r < ((q + 1) * NR) / NM; ++r)
@@ -277,13 +309,13 @@ __device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN], float (&ss)[
   }
 }
 
-// Full k-loop for the tile at (m_base, n_base).  Two LDS stages; fragments
-// double-buffered in registers.  Per k-tile kt (stage s = kt & 1):
+// Full k-loop for the tile at (m_base, n_base).  STAGES LDS stages used as a
+// ring; fragments double-buffered in registers.  Per k-tile kt (stage s):
 //   sub-step 0: MFMAs on (kt, k 0..31) while reading (kt, k 32..63);
 //   wait for k-tile kt+1's transfers, barrier;
 //   sub-step 1: MFMAs on (kt, k 32..63) while reading (kt+1, k 0..31) and
-//               issuing k-tile kt+2's transfers into stage s (no wave reads
-//               stage s any more after the barrier).
+//               issuing k-tile kt+STAGES's transfers into stage s (no wave
+//               reads stage s any more after the barrier).
 // LDS transfers of the first two k-tiles of the tile at (m_base, n_base).
 template <class T>
 __device__ __forceinline__ void issue_prologue(const GemmParams& p, uint32_t lds0, int m_base,
@@ -293,12 +325,25 @@ __device__ __forceinline__ void issue_prologue(const GemmParams& p, uint32_t lds
   DmaPlan<T> dma;
   dma.init(p, n_base, lane, wave);
   constexpr int ND = DmaPlan<T>::INS;
+  const int nk = (p.K + BK - 1) / BK;
 #pragma unroll
-  for (int d = 0; d < ND; ++d) dma.issue(p, m_base, n_base, 0, lds0, d);
-  if (p.K > BK) {
+  for (int st = 0; st < T::STAGES; ++st) {
+    if (st < nk) {
 #pragma unroll
-    for (int d = 0; d < ND; ++d) dma.issue(p, m_base, n_base, 1, lds0 + T::STAGE, d);
+      for (int d = 0; d < ND; ++d) dma.issue(p, m_base, n_base, st, lds0 + st * T::STAGE, d);
+    }
   }
+}
+
+// Wait until k-tile `t` has landed in LDS, given that k-tiles up to
+// min(nk-1, issued_last) were issued in order after it (ND transfers each).
+template <int ND, int STAGES>
+__device__ __forceinline__ void wait_ktile(int after) {
+  // `after` = number of later k-tiles already issued, 0 .. STAGES-1
+  if (STAGES > 3 && after >= 3) wait_vmcnt<(STAGES > 3 ? 3 * ND : 0)>();
+  else if (STAGES > 2 && after == 2) wait_vmcnt<(STAGES > 2 ? 2 * ND : 0)>();
+  else if (after == 1) wait_vmcnt<ND>();
+  else wait_vmcnt<0>();
 }
 
 template <class T, bool LAZY>
@@ -309,9 +354,11 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WN, wn = wave % T::WN;
+  float ss2[T::FM];
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
     ss[i] = 0.f;
+    ss2[i] = 0.f;
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -324,24 +371,33 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   const int nk = (p.K + BK - 1) / BK;
 
   if (!prologue_issued) issue_prologue<T>(p, lds0, m_base, n_base, tid);
-  if (nk > 1) wait_vmcnt<ND>();
-  else wait_vmcnt<0>();
+  wait_ktile<ND, T::STAGES>(min(nk, T::STAGES) - 1);
   __syncthreads();
   Frags<T> f0, f1;
 #pragma unroll
   for (int r = 0; r < NR; ++r) rd.read(f0, r, lds, 0, 0);
 
+  int cur_s = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const uint32_t cur = (uint32_t)(kt & 1) * T::STAGE;
-    const uint32_t nxt = (uint32_t)T::STAGE - cur;
-    substep<T, LAZY>(acc, ss, f0, f1, lds, rd, cur, 1, dma, false, p, m_base, n_base, 0, 0);
-    if (kt + 1 < nk) wait_vmcnt<0>();
+    const int nxt_s = cur_s + 1 == T::STAGES ? 0 : cur_s + 1;
+    const uint32_t cur = (uint32_t)cur_s * T::STAGE;
+    const uint32_t nxt = (uint32_t)nxt_s * T::STAGE;
+    substep<T, LAZY>(acc, ss, ss2, f0, f1, lds, rd, cur, 1, dma, false, p, m_base, n_base, 0, 0,
+                     wn);
+    // k-tile kt+1 must have landed; k-tiles kt+2 .. kt+STAGES-1 may still fly
+    if (kt + 1 < nk) wait_ktile<ND, T::STAGES>(min(nk - 1, kt + T::STAGES - 1) - (kt + 1));
     __syncthreads();
-    substep<T, LAZY>(acc, ss, f1, f0, lds, rd, nxt, 0, dma, kt + 2 < nk, p, m_base, n_base,
-                     kt + 2, lds0 + cur);
+    // stage cur is free now: refill it with k-tile kt+STAGES
+    substep<T, LAZY>(acc, ss, ss2, f1, f0, lds, rd, nxt, 0, dma, kt + T::STAGES < nk, p, m_base,
+                     n_base, kt + T::STAGES, lds0 + cur, wn);
+    cur_s = nxt_s;
   }
   // every wave is done with the stages before they are reused
   __syncthreads();
+  if constexpr (LAZY) {
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) ss[i] += ss2[i];
+  }
 }
 
 // Sum over the 4 lane groups sharing (lane & 15): a row's partial over this
@@ -361,7 +417,7 @@ __device__ __forceinline__ void tile_row_sums(const f32x4 (&acc)[T::FM][T::FN],
                                               const bool (&colv)[T::FN], int mode,
                                               const float (&center)[T::FM], float (&out)[T::FM],
                                               lds_char* lds, int wm, int wn, int lane) {
-  const uint32_t red = 2 * T::STAGE;
+  const uint32_t red = T::RED_OFF;
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
     float s = 0.f;
@@ -484,6 +540,26 @@ __device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds,
     apply_store<T>(q, acc, mean, rstd, false, m_base, n_base, wm, wn, lane);
   } else if constexpr (EPI == EPI_LAZY) {
     const float inv_k = 1.0f / (float)p.K;
+    if constexpr (T::WN > 1) {
+      // add the partial sums of squares of the WN waves that share rows
+      float part[T::FM];
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) part[i] = reduce_lane_groups(ss[i]);
+      const uint32_t red = T::RED_OFF;
+      if (lane < 16) {
+#pragma unroll
+        for (int i = 0; i < T::FM; ++i)
+          *(lds_float*)(lds + red + (wn * T::BM + wm * T::WTM + 16 * i + lane) * 4) = part[i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) {
+        float t = 0.f;
+        for (int w = 0; w < T::WN; ++w)
+          t += *(lds_float*)(lds + red + (w * T::BM + wm * T::WTM + 16 * i + l16) * 4);
+        ss[i] = (g == 0) ? t : 0.f;  // reduce_lane_groups below sums the 4 lane groups
+      }
+    }
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
       float s = reduce_lane_groups(ss[i]);
@@ -624,7 +700,7 @@ __device__ __forceinline__ void xwg_publish(const GemmParams& p, f32x4 (&acc)[T:
 template <class T>
 __device__ __forceinline__ void xwg_apply(const GemmParams& p, lds_char* lds, int tm, int tn,
                                           int tid) {
-  const uint32_t fin = 2 * T::STAGE + T::RED_BYTES;
+  const uint32_t fin = T::FIN_OFF;
   int* err = (int*)(p.ws + XwgLayout::kErr);
   int* arrive = (int*)(p.ws + XwgLayout::kCnt);
   int* depart = arrive + p.tiles_m;
