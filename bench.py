@@ -188,32 +188,54 @@ class Bench:
             self.ws = ng.Workspace(nb, dev)
         del x
         torch.cuda.synchronize()
+        self._bind()
 
-    # one fused call on rotation slot i
+    # The timed calls go straight to the C entry points with arguments
+    # marshalled once (the tensor helpers' checks cost more host time per call
+    # than the small kernels take on the GPU).
+    def _bind(self):
+        from normalization_gemm_amd import _lib
+        lib = _lib.load()  # the ctypes functions themselves
+        w, ng = self.w, self.ng
+        st = self.torch.cuda.current_stream().cuda_stream
+        ptr = lambda t: None if t is None else t.data_ptr()
+        ws, wsb = (self.ws.ptr(), self.ws.nbytes) if self.ws is not None else (None, 0)
+        M, N, K, eps = w.M, w.N, w.K, float(w.eps)
+        self._fused, self._gemm, self._norm = [], [], []
+        for r in range(self.R):
+            A, C = self.A[r].data_ptr(), self.C[r].data_ptr()
+            B, g, b = self.B.data_ptr(), ptr(self.gamma), ptr(self.beta)
+            if w.op == workloads.OP_LAZY:
+                An = self.An[r].data_ptr()
+                self._fused.append((lib.ng_rmsnorm_gemm_lazy,
+                                    (A, B, C, M, N, K, 0, eps, None, st)))
+                self._gemm.append((lib.ng_gemm, (An, B, C, M, N, K, 0, st)))
+                self._norm.append((lib.ng_norm, (A, None, None, An, M, K, 0, eps, None, None, st)))
+            elif w.op == workloads.OP_GEMM_RMSNORM:
+                self._fused.append((lib.ng_gemm_rmsnorm,
+                                    (A, B, g, C, M, N, K, 0, eps, None, ws, wsb, st)))
+                self._gemm.append((lib.ng_gemm, (A, B, C, M, N, K, 0, st)))
+                self._norm.append((lib.ng_norm, (C, g, None, C, M, N, 0, eps, None, None, st)))
+            else:
+                self._fused.append((lib.ng_gemm_layernorm,
+                                    (A, B, g, b, C, M, N, K, 0, eps, None, None, ws, wsb, st)))
+                self._gemm.append((lib.ng_gemm, (A, B, C, M, N, K, 0, st)))
+                self._norm.append((lib.ng_norm, (C, g, b, C, M, N, 1, eps, None, None, st)))
+
+    def _call(self, table, i):
+        fn, args = table[i % self.R]
+        status = fn(*args)
+        if status != 0:
+            raise self.ng.NormGemmError(status, fn.__name__)
+
     def fused(self, i):
-        w, ng, r = self.w, self.ng, i % self.R
-        if w.op == workloads.OP_LAZY:
-            ng.rmsnorm_gemm_lazy(self.A[r], self.B, eps=w.eps, out=self.C[r])
-        elif w.op == workloads.OP_GEMM_RMSNORM:
-            ng.gemm_rmsnorm(self.A[r], self.B, self.gamma, eps=w.eps, out=self.C[r],
-                            workspace=self.ws)
-        else:
-            ng.gemm_layernorm(self.A[r], self.B, self.gamma, self.beta, eps=w.eps,
-                              out=self.C[r], workspace=self.ws)
+        self._call(self._fused, i)
 
     def gemm_only(self, i):
-        r = i % self.R
-        src = self.An[r] if self.w.op == workloads.OP_LAZY else self.A[r]
-        self.ng.gemm(src, self.B, out=self.C[r])
+        self._call(self._gemm, i)
 
     def norm_only(self, i):
-        w, ng, r = self.w, self.ng, i % self.R
-        if w.op == workloads.OP_LAZY:
-            ng.norm(self.A[r], "rms", eps=w.eps, out=self.An[r])
-        elif w.op == workloads.OP_GEMM_RMSNORM:
-            ng.norm(self.C[r], "rms", self.gamma, eps=w.eps, out=self.C[r])
-        else:
-            ng.norm(self.C[r], "layer", self.gamma, self.beta, eps=w.eps, out=self.C[r])
+        self._call(self._norm, i)
 
     def pair(self, i):
         if self.w.op == workloads.OP_LAZY:
@@ -224,38 +246,50 @@ class Bench:
             self.norm_only(i)
 
     def time_launches(self, fn, steps, warmup):
-        """Per-launch durations (ms) from HIP events on the launch stream, and
-        the wall time of the whole timed loop (ms)."""
+        """Returns (per-launch durations in ms from events between launches,
+        wall time of the timed loop in ms, mean launch duration in ms from one
+        event pair around the loop).  The loop with only the outer event pair
+        is the one the wall time covers: events between launches add queue
+        packets of their own."""
         torch = self.torch
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3
+        mean = e0.elapsed_time(e1) / steps
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         ev[0].record()
         for i in range(steps):
             fn(i)
             ev[i + 1].record()
         torch.cuda.synchronize()
-        wall = (time.perf_counter() - t0) * 1e3
         per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-        return per, wall, ev[0].elapsed_time(ev[steps])
+        return per, wall, mean
 
 
 def cpu_baseline(w: workloads.Workload, target_s: float):
-    """The CPU oracle (untuned) on a row sample of the same workload."""
-    import numpy as np
+    """The CPU oracle (untuned) on a row sample of the same workload: passes
+    over a growing number of output rows (capped at M) until about target_s
+    seconds of CPU time are spent; throughput = GEMM flops of the rows done."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    rows = min(w.M, 256)
+    rows = min(w.M, 64)
     x = workloads.make_inputs(rows, w.N, w.K, seed=1, row_scale=w.row_scale, gamma=w.gamma,
                               beta=w.beta)
     done_rows, t_total = 0, 0.0
-    while True:
+    while t_total < target_s:
         t0 = time.perf_counter()
         if w.op == workloads.OP_LAZY:
             oracle.rmsnorm_gemm_lazy(x.A, x.B, w.eps)
@@ -263,19 +297,19 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
             oracle.gemm_rmsnorm(x.A, x.B, w.eps, x.gamma)
         else:
             oracle.gemm_layernorm(x.A, x.B, w.eps, x.gamma, x.beta)
-        t_total += time.perf_counter() - t0
+        dt = time.perf_counter() - t0
+        t_total += dt
         done_rows += rows
-        if t_total >= target_s or done_rows >= w.M:
-            break
-        if t_total < target_s / 8 and rows < w.M:
+        # grow the sample while one pass is short, up to the whole workload
+        if dt < target_s / 8 and rows < w.M:
             rows = min(w.M, rows * 4)
             x = workloads.make_inputs(rows, w.N, w.K, seed=1, row_scale=w.row_scale,
                                       gamma=w.gamma, beta=w.beta)
     flops = 2.0 * done_rows * w.N * w.K
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": "%d output rows of %s (fp64 NumPy GEMM + explicit norm, %.1f s)"
-                      % (done_rows, w.name, t_total)}
+            "sample": "%d output rows of %s in passes of up to %d rows (fp64 NumPy GEMM + "
+                      "explicit norm, %.1f s)" % (done_rows, w.name, rows, t_total)}
 
 
 def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: float):
@@ -283,14 +317,10 @@ def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: f
     torch_mod = __import__("torch")
     b = Bench(w)
     # headline: the fused kernel, steps timed with a sync on both sides
-    per, wall_ms, ev_ms = b.time_launches(b.fused, steps, warmup)
-    per_g, _, ev_g = b.time_launches(b.gemm_only, steps, warmup)
-    per_n, _, ev_n = b.time_launches(b.norm_only, steps, warmup)
-    per_p, _, ev_p = b.time_launches(b.pair, steps, warmup)
-    t_fused = ev_ms / steps
-    t_gemm = ev_g / steps
-    t_norm = ev_n / steps
-    t_pair = ev_p / steps
+    per, wall_ms, t_fused = b.time_launches(b.fused, steps, warmup)
+    _, _, t_gemm = b.time_launches(b.gemm_only, steps, warmup)
+    _, _, t_norm = b.time_launches(b.norm_only, steps, warmup)
+    _, _, t_pair = b.time_launches(b.pair, steps, warmup)
     flops = float(w.flops)
     tflops = flops * steps / (wall_ms * 1e-3) / 1e12
     kern_tflops = flops / (t_fused * 1e-3) / 1e12

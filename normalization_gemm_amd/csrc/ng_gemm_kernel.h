@@ -156,7 +156,7 @@ struct DmaPlan {
     }
   }
 
-  // Issue the transfers of k-tile kt into the stage at LDS byte address `st`.
+  // Transfer j of k-tile kt of A into the A region at LDS byte address `st`.
   __device__ __forceinline__ void issue_a(const GemmParams& p, int m_base, int kt, uint32_t st,
                                           int j) const {
     const int k0 = kt * BK;
@@ -167,6 +167,7 @@ struct DmaPlan {
     const uint32_t row0 = (uint32_t)((wave * A_INS + j) * 8);
     dma16(rs, st + (uint32_t)(wave * A_INS + j) * 1024u, v, row0 * a_row_bytes);
   }
+  // Transfer j of k-tile kt of B into the B region at LDS byte address `st`.
   __device__ __forceinline__ void issue_b(const GemmParams& p, int n_base, int kt, uint32_t st,
                                           int j) const {
     const int k0 = kt * BK;
@@ -174,21 +175,22 @@ struct DmaPlan {
       const uint64_t off = (uint64_t)k0 * p.N + n_base;
       const __amdgpu_buffer_rsrc_t rs =
           make_rsrc(p.B + off, ((uint64_t)p.K * p.N - off) * 2u);
-      dma16(rs, st + T::A_BYTES + (uint32_t)(wave * B_INS + j) * 1024u, b_voff[j], 0u);
+      dma16(rs, st + (uint32_t)(wave * B_INS + j) * 1024u, b_voff[j], 0u);
     } else {
       const uint64_t off = (uint64_t)n_base * p.K + k0;
       const __amdgpu_buffer_rsrc_t rs =
           make_rsrc(p.B + off, ((uint64_t)p.N * p.K - off) * 2u);
       const uint32_t v = (k0 + (int)a_kc < p.K) ? a_voff : kOOB;
       const uint32_t row0 = (uint32_t)((wave * B_INS + j) * 8);
-      dma16(rs, st + T::A_BYTES + (uint32_t)(wave * B_INS + j) * 1024u, v, row0 * a_row_bytes);
+      dma16(rs, st + (uint32_t)(wave * B_INS + j) * 1024u, v, row0 * a_row_bytes);
     }
   }
-  // Transfer number d (0 .. INS-1) of k-tile kt.
+  // Transfer number d (0 .. INS-1) of k-tile kt into the stage at `st` (A
+  // region first, then B).
   __device__ __forceinline__ void issue(const GemmParams& p, int m_base, int n_base, int kt,
                                         uint32_t st, int d) const {
     if (d < A_INS) issue_a(p, m_base, kt, st, d);
-    else issue_b(p, n_base, kt, st, d - A_INS);
+    else issue_b(p, n_base, kt, st + T::A_BYTES, d - A_INS);
   }
 };
 
@@ -207,8 +209,8 @@ template <class T>
 struct FragReader {
   static constexpr int B_ITEMS = T::KN ? 2 * T::FN : T::FN;
   static constexpr int ITEMS = T::FM + B_ITEMS;
-  uint32_t a_base[2];  // per kk: A fragment 0 of this lane (stage 0)
-  uint32_t b_base[2];  // per kk: B fragment 0 (half 0) of this lane (stage 0)
+  uint32_t a_base[2];  // per kk: A fragment 0 of this lane, from the A region
+  uint32_t b_base[2];  // per kk: B fragment 0 (half 0) of this lane, from the B region
   uint32_t b_odd[2];   // KN: base for odd fragments (the XOR in b_blk_off)
 
   __device__ __forceinline__ void init(int wm, int wn, int lane) {
@@ -224,19 +226,21 @@ struct FragReader {
         const int k = kk * 32 + 8 * g + (l16 >> 2);
         const int n = wn * T::WTN + 4 * (l16 & 3);
         const uint32_t p = (uint32_t)((k >> 3) & 1);
-        const uint32_t b0 = (uint32_t)T::A_BYTES + b_blk_off<T::BN>(k, n);  // fragment 0
+        const uint32_t b0 = b_blk_off<T::BN>(k, n) + 256u;  // fragment 0 (+256: see b_odd)
         b_base[kk] = b0;                       // even j: block j ^ p = j + p (p already in b0)
         b_odd[kk] = b0 - 256u * p;             // odd j: block j ^ p = j - p
+        // (both carry +256 so that b_odd stays non-negative; read() takes it off)
       } else {
         const int brow = wn * T::WTN + l16;
-        b_base[kk] = (uint32_t)T::A_BYTES + (uint32_t)(brow * 128 + (((kk * 4 + g) ^ (l16 & 7)) << 4));
+        b_base[kk] = (uint32_t)(brow * 128 + (((kk * 4 + g) ^ (l16 & 7)) << 4));
       }
     }
   }
-  __device__ __forceinline__ void read(Frags<T>& f, int item, lds_char* lds, uint32_t st,
-                                       int kk) const {
+  // a_st / b_st: LDS byte offsets of the A and B regions holding this k-tile.
+  __device__ __forceinline__ void read(Frags<T>& f, int item, lds_char* lds, uint32_t a_st,
+                                       uint32_t b_st, int kk) const {
     if (item < T::FM) {
-      f.a[item] = lds_read16(lds, st + a_base[kk] + (uint32_t)item * 2048u);
+      f.a[item] = lds_read16(lds, a_st + a_base[kk] + (uint32_t)item * 2048u);
       return;
     }
     const int bi = item - T::FM;
@@ -244,14 +248,46 @@ struct FragReader {
       const int j = bi >> 1, h = bi & 1;
       // +16 columns per fragment = next block; +4 k-rows per half = next block row
       const uint32_t o = (uint32_t)j * 128u + (uint32_t)h * (uint32_t)(T::BN / 16) * 128u;
-      const u32x2 v = lds_read_tr16(lds, st + ((j & 1) ? b_odd[kk] : b_base[kk]) + o);
+      const u32x2 v = lds_read_tr16(lds, b_st - 256u + ((j & 1) ? b_odd[kk] : b_base[kk]) + o);
       if (h == 0) { f.b[j][0] = v[0]; f.b[j][1] = v[1]; }
       else { f.b[j][2] = v[0]; f.b[j][3] = v[1]; }
     } else {
-      f.b[bi] = lds_read16(lds, st + b_base[kk] + (uint32_t)bi * 2048u);
+      f.b[bi] = lds_read16(lds, b_st + b_base[kk] + (uint32_t)bi * 2048u);
     }
   }
 };
+
+// Lazy Pre-Norm sum of squares, spread over the MFMAs of a sub-step: every
+// (fragment, dword) pair of the sub-step's A fragments is one dword (two
+// bf16) widened exactly to fp32 and squared with two FMAs into two
+// accumulators.  Pairs sit STEP MFMAs apart and consecutive pairs update
+// different fragments' sums, so no dependent VALU chain holds up the MFMA
+// issue.  (Plain VALU ops co-issue with MFMAs; v_dot2_f32_bf16 was measured
+// to compete with them.)  Waves that share rows compute the same sums.
+template <class T>
+__device__ __forceinline__ void lazy_square(int q, const Frags<T>& cur, float (&ss)[T::FM],
+                                            float (&ss2)[T::FM]) {
+  constexpr int NM = T::FM * T::FN;
+  constexpr int ITEMS = T::FM * 4;
+  constexpr int STEP = NM >= ITEMS ? NM / ITEMS : 1;
+  constexpr int PER = NM >= ITEMS ? 1 : (ITEMS + NM - 1) / NM;  // pairs per MFMA
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int t = (q / STEP) * PER + e;
+    if (q % STEP == 0 && t < ITEMS) {
+      const int ii = t % T::FM, d = t / T::FM;
+      const uint32_t w = cur.a[ii][d];
+      const float lo = __uint_as_float(w << 16);
+      const float hi = __uint_as_float(w & 0xffff0000u);
+      ss[ii] = fmaf(lo, lo, ss[ii]);
+      ss2[ii] = fmaf(hi, hi, ss2[ii]);
+      // pin the update here: left alone, the compiler sinks the squares to
+      // the end of the sub-step, where they wait for issue slots instead of
+      // sharing the MFMAs' shadow
+      asm volatile("" : "+v"(ss[ii]), "+v"(ss2[ii]));
+    }
+  }
+}
 
 // One k32 sub-step: FM*FN MFMAs on `cur`, with the LDS reads of the next
 // sub-step's fragments (into `nxt`) and, when dma_on, the LDS transfers of a
@@ -266,7 +302,7 @@ __device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN], float (&ss)[
                                         const FragReader<T>& rd, uint32_t rd_st, int rd_kk,
                                         const DmaPlan<T>& dma,
                                         bool dma_on, const GemmParams& p, int m_base,
-                                        int n_base, int dma_kt, uint32_t dma_st, int wn_) {
+                                        int n_base, int dma_kt, uint32_t dma_st) {
   constexpr int NM = T::FM * T::FN;
   constexpr int NR = FragReader<T>::ITEMS;
   constexpr int ND = DmaPlan<T>::INS;
@@ -274,34 +310,10 @@ __device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN], float (&ss)[
   for (int q = 0; q < NM; ++q) {
     const int i = q / T::FN, j = q % T::FN;
     acc[i][j] = mfma_16x16x32(cur.b[j], cur.a[i], acc[i][j]);
-    if constexpr (LAZY) {
-      // One dword (two bf16) of the sum of squares per MFMA: dword d of
-      // fragment ii, fragments interleaved so that consecutive updates of
-      // one accumulator are FM MFMAs apart, and the low and high halves
-      // going to two accumulators (no dependent VALU chain stalls the MFMA
-      // issue).
-      // The WN waves that share these rows split the dwords between them
-      // (wave wn takes dwords d with d % WN == wn); their sums are added in
-      // the epilogue.
-      constexpr int DPW = 4 / (T::WN < 4 ? T::WN : 4);  // dwords per wave per fragment
-      constexpr int NSQ = T::FM * DPW;
-      if (q < NSQ) {
-        const int ii = q % T::FM;
-        const int d = (q / T::FM) * (4 / DPW) + (wn_ % (4 / DPW));
-        const uint32_t w = cur.a[ii][d];
-        const float lo = __uint_as_float(w << 16);
-        const float hi = __uint_as_float(w & 0xffff0000u);
-        ss[ii] = fmaf(lo, lo, ss[ii]);
-        ss2[ii] = fmaf(hi, hi, ss2[ii]);
-        // pin the update here: left alone, the compiler sinks the squares to
-        // the end of the sub-step, where they wait for issue slots instead of
-        // sharing the MFMAs' shadow
-        asm volatile("" : "+v"(ss[ii]), "+v"(ss2[ii]));
-      }
-    }
+    if constexpr (LAZY) lazy_square<T>(q, cur, ss, ss2);
 #pragma unroll
     for (int r = (q * NR) / NM; r < ((q + 1) * NR) / NM; ++r)
-      rd.read(nxt, r, lds, rd_st, rd_kk);
+      rd.read(nxt, r, lds, rd_st, rd_st + T::A_BYTES, rd_kk);
 #pragma unroll
     for (int d = (q * ND) / NM; d < ((q + 1) * ND) / NM; ++d)
       if (dma_on) dma.issue(p, m_base, n_base, dma_kt, dma_st, d);
@@ -375,21 +387,20 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   __syncthreads();
   Frags<T> f0, f1;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) rd.read(f0, r, lds, 0, 0);
+  for (int r = 0; r < NR; ++r) rd.read(f0, r, lds, 0, T::A_BYTES, 0);
 
   int cur_s = 0;
   for (int kt = 0; kt < nk; ++kt) {
     const int nxt_s = cur_s + 1 == T::STAGES ? 0 : cur_s + 1;
     const uint32_t cur = (uint32_t)cur_s * T::STAGE;
     const uint32_t nxt = (uint32_t)nxt_s * T::STAGE;
-    substep<T, LAZY>(acc, ss, ss2, f0, f1, lds, rd, cur, 1, dma, false, p, m_base, n_base, 0, 0,
-                     wn);
+    substep<T, LAZY>(acc, ss, ss2, f0, f1, lds, rd, cur, 1, dma, false, p, m_base, n_base, 0, 0);
     // k-tile kt+1 must have landed; k-tiles kt+2 .. kt+STAGES-1 may still fly
     if (kt + 1 < nk) wait_ktile<ND, T::STAGES>(min(nk - 1, kt + T::STAGES - 1) - (kt + 1));
     __syncthreads();
     // stage cur is free now: refill it with k-tile kt+STAGES
     substep<T, LAZY>(acc, ss, ss2, f1, f0, lds, rd, nxt, 0, dma, kt + T::STAGES < nk, p, m_base,
-                     n_base, kt + T::STAGES, lds0 + cur, wn);
+                     n_base, kt + T::STAGES, lds0 + cur);
     cur_s = nxt_s;
   }
   // every wave is done with the stages before they are reused
@@ -540,26 +551,6 @@ __device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds,
     apply_store<T>(q, acc, mean, rstd, false, m_base, n_base, wm, wn, lane);
   } else if constexpr (EPI == EPI_LAZY) {
     const float inv_k = 1.0f / (float)p.K;
-    if constexpr (T::WN > 1) {
-      // add the partial sums of squares of the WN waves that share rows
-      float part[T::FM];
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) part[i] = reduce_lane_groups(ss[i]);
-      const uint32_t red = T::RED_OFF;
-      if (lane < 16) {
-#pragma unroll
-        for (int i = 0; i < T::FM; ++i)
-          *(lds_float*)(lds + red + (wn * T::BM + wm * T::WTM + 16 * i + lane) * 4) = part[i];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < T::FM; ++i) {
-        float t = 0.f;
-        for (int w = 0; w < T::WN; ++w)
-          t += *(lds_float*)(lds + red + (w * T::BM + wm * T::WTM + 16 * i + l16) * 4);
-        ss[i] = (g == 0) ? t : 0.f;  // reduce_lane_groups below sums the 4 lane groups
-      }
-    }
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
       float s = reduce_lane_groups(ss[i]);
