@@ -114,37 +114,57 @@ int launch_grid(ng::GemmParams p, hipStream_t s, const char* what) {
   return launched(what);
 }
 
-// Co-resident workgroups per device for the persistent cross-workgroup kernel.
-template <class T>
-int xwg_capacity(int* cap) {
+// Co-resident workgroups per device for a persistent kernel (cached per
+// kernel and device).
+int resident_capacity(const void* kernel, int threads, int slot, int* cap) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(NG_ERR_HIP, "hipGetDevice failed");
   static std::mutex mu;
-  static int cached[64] = {0};
+  static int cached[16][64] = {{0}};
   std::lock_guard<std::mutex> lk(mu);
-  if (dev < 64 && cached[dev] > 0) {
-    *cap = cached[dev];
+  if (dev < 64 && cached[slot][dev] > 0) {
+    *cap = cached[slot][dev];
     return NG_OK;
   }
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ng::gemm_xwg_kernel<T>, T::NT, 0) !=
-      hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
     return fail(NG_ERR_HIP, "occupancy query failed");
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return fail(NG_ERR_HIP, "CU count query failed");
   const int c = per_cu * cus;
-  if (c <= 0) return fail(NG_ERR_HIP, "cross-workgroup kernel cannot be resident");
-  if (dev < 64) cached[dev] = c;
+  if (c <= 0) return fail(NG_ERR_HIP, "persistent kernel cannot be resident");
+  if (dev < 64) cached[slot][dev] = c;
   *cap = c;
   return NG_OK;
 }
 
-template <class T>
+// Cache slots of resident_capacity, one per persistent kernel instance.
+template <class T, int EPI>
+constexpr int persistent_slot() {
+  return (T::KN ? 0 : 1) + (EPI == ng::EPI_LAZY ? 2 : 0);
+}
+
+template <class T, int EPI>
+int launch_persistent(ng::GemmParams p, hipStream_t s, const char* what) {
+  p.tiles_m = (p.M + T::BM - 1) / T::BM;
+  p.tiles_n = (p.N + T::BN - 1) / T::BN;
+  const long long total = (long long)p.tiles_m * p.tiles_n;
+  int cap = 0;
+  int st = resident_capacity((const void*)ng::gemm_persistent_kernel<T, EPI>, T::NT,
+                             persistent_slot<T, EPI>(), &cap);
+  if (st) return st;
+  const unsigned grid = (unsigned)(total < cap ? total : cap);
+  hipLaunchKernelGGL((ng::gemm_persistent_kernel<T, EPI>), dim3(grid), dim3(T::NT), 0, s, p);
+  return launched(what);
+}
+
+template <class T, bool LN>
 int launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   p.tiles_m = (p.M + T::BM - 1) / T::BM;
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
   int cap = 0;
-  int st = xwg_capacity<T>(&cap);
+  int st = resident_capacity((const void*)ng::gemm_xwg_kernel<T, LN>, T::NT,
+                             4 + (T::KN ? 0 : 1) + (LN ? 2 : 0), &cap);
   if (st) return st;
   if (p.tiles_n > cap)
     return fail(NG_ERR_UNSUPPORTED, "row of %d tiles exceeds %d co-resident workgroups",
@@ -154,7 +174,7 @@ int launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   p.iters = (p.tiles_m + R - 1) / R;
   const unsigned grid = (unsigned)(R * p.tiles_n);
   void* args[] = {&p};
-  hipError_t e = hipLaunchCooperativeKernel((const void*)ng::gemm_xwg_kernel<T>, dim3(grid),
+  hipError_t e = hipLaunchCooperativeKernel((const void*)ng::gemm_xwg_kernel<T, LN>, dim3(grid),
                                             dim3(T::NT), args, 0, s);
   if (e != hipSuccess) return fail(NG_ERR_HIP, "%s cooperative launch failed: %s", what,
                                    hipGetErrorString(e));
@@ -196,15 +216,26 @@ int gemm_norm(const void* A, const void* B, const void* gamma, const void* beta,
   p.ws = (char*)ws;
   p.norm_kind = kind;
   const bool kn = b_layout == NG_B_KN;
+  const bool ln = kind == ng::NORM_LAYER;
   if (N <= 128) {
-    return kn ? launch_grid<TRow128<true>, ng::EPI_ROW_LOCAL>(p, s, what)
-              : launch_grid<TRow128<false>, ng::EPI_ROW_LOCAL>(p, s, what);
+    if (ln)
+      return kn ? launch_grid<TRow128<true>, ng::EPI_ROW_LN>(p, s, what)
+                : launch_grid<TRow128<false>, ng::EPI_ROW_LN>(p, s, what);
+    return kn ? launch_grid<TRow128<true>, ng::EPI_ROW_RMS>(p, s, what)
+              : launch_grid<TRow128<false>, ng::EPI_ROW_RMS>(p, s, what);
   }
   if (local) {
-    return kn ? launch_grid<TRow256<true>, ng::EPI_ROW_LOCAL>(p, s, what)
-              : launch_grid<TRow256<false>, ng::EPI_ROW_LOCAL>(p, s, what);
+    if (ln)
+      return kn ? launch_grid<TRow256<true>, ng::EPI_ROW_LN>(p, s, what)
+                : launch_grid<TRow256<false>, ng::EPI_ROW_LN>(p, s, what);
+    return kn ? launch_grid<TRow256<true>, ng::EPI_ROW_RMS>(p, s, what)
+              : launch_grid<TRow256<false>, ng::EPI_ROW_RMS>(p, s, what);
   }
-  return kn ? launch_xwg<TLarge<true>>(p, s, what) : launch_xwg<TLarge<false>>(p, s, what);
+  if (ln)
+    return kn ? launch_xwg<TLarge<true>, true>(p, s, what)
+              : launch_xwg<TLarge<false>, true>(p, s, what);
+  return kn ? launch_xwg<TLarge<true>, false>(p, s, what)
+            : launch_xwg<TLarge<false>, false>(p, s, what);
 }
 
 }  // namespace
@@ -225,8 +256,8 @@ int ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t
   if (N <= 128)
     return kn ? launch_grid<TRow128<true>, ng::EPI_LAZY>(p, s, "ng_rmsnorm_gemm_lazy")
               : launch_grid<TRow128<false>, ng::EPI_LAZY>(p, s, "ng_rmsnorm_gemm_lazy");
-  return kn ? launch_grid<TLarge<true>, ng::EPI_LAZY>(p, s, "ng_rmsnorm_gemm_lazy")
-            : launch_grid<TLarge<false>, ng::EPI_LAZY>(p, s, "ng_rmsnorm_gemm_lazy");
+  return kn ? launch_persistent<TLarge<true>, ng::EPI_LAZY>(p, s, "ng_rmsnorm_gemm_lazy")
+            : launch_persistent<TLarge<false>, ng::EPI_LAZY>(p, s, "ng_rmsnorm_gemm_lazy");
 }
 
 int ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,
@@ -255,8 +286,8 @@ int ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N
   if (N <= 128)
     return kn ? launch_grid<TRow128<true>, ng::EPI_NONE>(p, s, "ng_gemm")
               : launch_grid<TRow128<false>, ng::EPI_NONE>(p, s, "ng_gemm");
-  return kn ? launch_grid<TLarge<true>, ng::EPI_NONE>(p, s, "ng_gemm")
-            : launch_grid<TLarge<false>, ng::EPI_NONE>(p, s, "ng_gemm");
+  return kn ? launch_persistent<TLarge<true>, ng::EPI_NONE>(p, s, "ng_gemm")
+            : launch_persistent<TLarge<false>, ng::EPI_NONE>(p, s, "ng_gemm");
 }
 
 int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* Y,

@@ -17,6 +17,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) float lds_float;
 typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;

@@ -3,7 +3,8 @@
 // One kernel template serves four epilogues:
 //   EPI_NONE      C = A @ B                               (unfused baseline GEMM)
 //   EPI_LAZY      C = (A @ B) * rstd(A)                   (Lazy Pre-Norm)
-//   EPI_ROW_LOCAL C = norm(A @ B), whole row in one workgroup (N <= BN)
+//   EPI_ROW_RMS / EPI_ROW_LN
+//                 C = norm(A @ B), whole row in one workgroup (N <= BN)
 //   cross-workgroup: C = norm(A @ B) for rows split over workgroups; per-row
 //                 fp32 partials merged through a workspace (persistent grid,
 //                 gemm_xwg_kernel below)
@@ -39,7 +40,7 @@ namespace ng {
 
 constexpr int BK = 64;
 
-enum Epi { EPI_NONE = 0, EPI_LAZY = 1, EPI_ROW_LOCAL = 2 };
+enum Epi { EPI_NONE = 0, EPI_LAZY = 1, EPI_ROW_RMS = 2, EPI_ROW_LN = 3 };
 enum NormKind { NORM_RMS = 0, NORM_LAYER = 1 };
 
 // Workspace layout of the cross-workgroup row norm (byte offsets).
@@ -96,7 +97,17 @@ struct Tile {
   static constexpr int FIN_BYTES = BM * 16;       // per-row (mean, rstd, tile mean)
   static constexpr int RED_OFF = STAGES * STAGE;      // LDS byte offsets
   static constexpr int FIN_OFF = RED_OFF + RED_BYTES;
-  static constexpr int LDS = FIN_OFF + FIN_BYTES;
+  // Output staging: 2 KB per wave (16 rows x 128 bytes).  In a region of its
+  // own when it fits (the next tile's transfers may then be in flight while
+  // the tile is stored), else on top of stage 0, which is free after the k-loop.
+  static constexpr int STG_BYTES = (NT / 64) * 2048;
+  static constexpr bool STG_OWN = FIN_OFF + FIN_BYTES + STG_BYTES <= 160 * 1024;
+  static constexpr int STG_OFF = STG_OWN ? FIN_OFF + FIN_BYTES : 0;
+  static constexpr int LDS = STG_OWN ? STG_OFF + STG_BYTES : FIN_OFF + FIN_BYTES;
+  // 16-byte output stores per thread per tile
+  static constexpr int C_STORES = FM * (FN / 4) * 2;
+  static_assert(STG_OWN || STG_BYTES <= STAGE, "output staging");
+  static_assert(FN % 4 == 0, "64-column output groups");
   static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
   static_assert((BM * BK / 8) % NT == 0 && (BN * BK / 8) % NT == 0, "loader split");
@@ -347,22 +358,28 @@ __device__ __forceinline__ void issue_prologue(const GemmParams& p, uint32_t lds
   }
 }
 
-// Wait until k-tile `t` has landed in LDS, given that k-tiles up to
-// min(nk-1, issued_last) were issued in order after it (ND transfers each).
-template <int ND, int STAGES>
+// Wait until a k-tile has landed in LDS, given that `after` later k-tiles
+// (ND transfers each, 0 .. STAGES-1 of them) and X other vector-memory
+// operations were issued after it.  Vector-memory operations of a wave
+// complete in issue order, so at most after*ND + X may remain outstanding;
+// X must not exceed the true count (more operations only make the wait
+// stricter).
+template <int ND, int STAGES, int X = 0>
 __device__ __forceinline__ void wait_ktile(int after) {
-  // `after` = number of later k-tiles already issued, 0 .. STAGES-1
-  if (STAGES > 3 && after >= 3) wait_vmcnt<(STAGES > 3 ? 3 * ND : 0)>();
-  else if (STAGES > 2 && after == 2) wait_vmcnt<(STAGES > 2 ? 2 * ND : 0)>();
-  else if (after == 1) wait_vmcnt<ND>();
-  else wait_vmcnt<0>();
+  if (STAGES > 3 && after >= 3) wait_vmcnt<(STAGES > 3 ? 3 * ND + X : 0)>();
+  else if (STAGES > 2 && after == 2) wait_vmcnt<(STAGES > 2 ? 2 * ND + X : 0)>();
+  else if (after == 1) wait_vmcnt<ND + X>();
+  else wait_vmcnt<X>();
 }
 
+// prologue_issued: the first STAGES k-tiles were issued by the caller.
+// stores_after: the caller then issued exactly T::C_STORES further
+// vector-memory operations (the previous tile's output) before this call.
 template <class T, bool LAZY>
 __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM][T::FN],
                                          float (&ss)[T::FM], lds_char* lds, uint32_t lds0,
                                          int m_base, int n_base, int tid,
-                                         bool prologue_issued = false) {
+                                         bool prologue_issued = false, bool stores_after = false) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WN, wn = wave % T::WN;
@@ -383,7 +400,8 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   const int nk = (p.K + BK - 1) / BK;
 
   if (!prologue_issued) issue_prologue<T>(p, lds0, m_base, n_base, tid);
-  wait_ktile<ND, T::STAGES>(min(nk, T::STAGES) - 1);
+  if (stores_after) wait_ktile<ND, T::STAGES, T::C_STORES>(min(nk, T::STAGES) - 1);
+  else wait_ktile<ND, T::STAGES>(min(nk, T::STAGES) - 1);
   __syncthreads();
   Frags<T> f0, f1;
 #pragma unroll
@@ -396,7 +414,12 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
     const uint32_t nxt = (uint32_t)nxt_s * T::STAGE;
     substep<T, LAZY>(acc, ss, ss2, f0, f1, lds, rd, cur, 1, dma, false, p, m_base, n_base, 0, 0);
     // k-tile kt+1 must have landed; k-tiles kt+2 .. kt+STAGES-1 may still fly
-    if (kt + 1 < nk) wait_ktile<ND, T::STAGES>(min(nk - 1, kt + T::STAGES - 1) - (kt + 1));
+    // (and, while kt+1 is a prologue k-tile, the caller's stores after them)
+    if (kt + 1 < nk) {
+      const int after = min(nk - 1, kt + T::STAGES - 1) - (kt + 1);
+      if (stores_after && kt + 1 < T::STAGES) wait_ktile<ND, T::STAGES, T::C_STORES>(after);
+      else wait_ktile<ND, T::STAGES>(after);
+    }
     __syncthreads();
     // stage cur is free now: refill it with k-tile kt+STAGES
     substep<T, LAZY>(acc, ss, ss2, f1, f0, lds, rd, nxt, 0, dma, kt + T::STAGES < nk, p, m_base,
@@ -463,37 +486,87 @@ __device__ __forceinline__ void tile_row_sums(const f32x4 (&acc)[T::FM][T::FN],
   }
 }
 
-// Scale/shift the accumulators by per-row (mean, rstd) and the per-column
-// affine, round to bf16 and store the valid part of the tile.
-template <class T>
-__device__ __forceinline__ void apply_store(const GemmParams& p, f32x4 (&acc)[T::FM][T::FN],
+// Byte offset of 16-byte chunk c (0..7) of row r (0..15) in a wave's 2 KB
+// output staging block.  XORing the chunk with (r >> 1) & 7 lets both the
+// 8-byte fragment writes (16 rows per 32 lanes) and the 16-byte row reads
+// touch every LDS bank once per pass.
+__device__ __forceinline__ uint32_t stg_chunk(int r, int c) {
+  return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+}
+
+// Scale/shift the accumulators by per-row (mean, rstd) and (AFFINE) the
+// per-column gamma/beta, round to bf16 and store the tile.  Each 16-row x
+// 64-column piece goes through the wave's LDS staging block so that every
+// global store writes whole 128-byte row segments (16 bytes per lane) instead
+// of 8-byte pieces of 16 rows.  Exactly T::C_STORES buffer stores per thread
+// are issued; rows past M and columns past N fall outside the buffer range
+// and are dropped.
+template <class T, bool AFFINE>
+__device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
                                             const float (&mean)[T::FM], const float (&rstd)[T::FM],
-                                            bool use_mean, int m_base, int n_base, int wm, int wn,
-                                            int lane) {
+                                            bool use_mean, lds_char* lds, int m_base, int n_base,
+                                            int wave, int wm, int wn, int lane) {
   const int l16 = lane & 15, g = lane >> 4;
+  const uint32_t stg = (uint32_t)T::STG_OFF + (uint32_t)wave * 2048u;
+  // fragment writes: lane (l16, g) of fragment jj holds 4 columns = 8 bytes
+  // at byte 32*jj + 8*g of row l16
+  const uint32_t w0 = stg + stg_chunk(l16, g >> 1) + 8u * (uint32_t)(g & 1);
+  const uint32_t w1 = stg + stg_chunk(l16, 2 + (g >> 1)) + 8u * (uint32_t)(g & 1);
+  const uint32_t w2 = stg + stg_chunk(l16, 4 + (g >> 1)) + 8u * (uint32_t)(g & 1);
+  const uint32_t w3 = stg + stg_chunk(l16, 6 + (g >> 1)) + 8u * (uint32_t)(g & 1);
+  // row reads: lane reads chunk (lane & 7) of rows (lane >> 3) and (lane >> 3) + 8
+  const int rr = lane >> 3, rc = lane & 7;
+  const uint32_t r0 = stg + stg_chunk(rr, rc), r1 = stg + stg_chunk(rr + 8, rc);
+  const uint32_t row_bytes = (uint32_t)p.N * 2u;
 #pragma unroll
-  for (int j = 0; j < T::FN; ++j) {
-    const int n = n_base + wn * T::WTN + 16 * j + 4 * g;
-    if (n >= p.N) continue;
-    float gm[4] = {1.f, 1.f, 1.f, 1.f}, bt[4] = {0.f, 0.f, 0.f, 0.f};
-    if (p.gamma) {
-      u32x2 w = *(const u32x2*)(p.gamma + n);
-      gm[0] = bf16_lo(w[0]); gm[1] = bf16_hi(w[0]); gm[2] = bf16_lo(w[1]); gm[3] = bf16_hi(w[1]);
+  for (int q = 0; q < T::FN / 4; ++q) {
+    u32x2 gw[4], bw[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      gw[jj] = u32x2{0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
+      bw[jj] = u32x2{0u, 0u};
+      if constexpr (AFFINE) {
+        const int n = n_base + wn * T::WTN + 16 * (4 * q + jj) + 4 * g;
+        if (n < p.N) {
+          if (p.gamma) gw[jj] = *(const u32x2*)(p.gamma + n);
+          if (p.beta) bw[jj] = *(const u32x2*)(p.beta + n);
+        }
+      }
     }
-    if (p.beta) {
-      u32x2 w = *(const u32x2*)(p.beta + n);
-      bt[0] = bf16_lo(w[0]); bt[1] = bf16_hi(w[0]); bt[2] = bf16_lo(w[1]); bt[3] = bf16_hi(w[1]);
-    }
+    const int n_st = n_base + wn * T::WTN + 64 * q + 8 * rc;
+    const uint32_t voff_c = n_st < p.N ? 2u * (uint32_t)n_st : kOOB;
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
-      const int m = m_base + wm * T::WTM + 16 * i + l16;
-      if (m >= p.M) continue;
       const float sh = use_mean ? -mean[i] * rstd[i] : 0.f;
-      float y[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y[r] = fmaf(fmaf(acc[i][j][r], rstd[i], sh), gm[r], bt[r]);
-      u32x2 o = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-      *(u32x2*)(p.C + (size_t)m * p.N + n) = o;
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 x = acc[i][4 * q + jj];
+        float y[4];
+        if constexpr (AFFINE) {
+          y[0] = fmaf(fmaf(x[0], rstd[i], sh), bf16_lo(gw[jj][0]), bf16_lo(bw[jj][0]));
+          y[1] = fmaf(fmaf(x[1], rstd[i], sh), bf16_hi(gw[jj][0]), bf16_hi(bw[jj][0]));
+          y[2] = fmaf(fmaf(x[2], rstd[i], sh), bf16_lo(gw[jj][1]), bf16_lo(bw[jj][1]));
+          y[3] = fmaf(fmaf(x[3], rstd[i], sh), bf16_hi(gw[jj][1]), bf16_hi(bw[jj][1]));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] = fmaf(x[r], rstd[i], sh);
+        }
+        const uint32_t w = jj == 0 ? w0 : jj == 1 ? w1 : jj == 2 ? w2 : w3;
+        *(lds_u32x2*)(lds + w) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      }
+      const u32x4 v0 = lds_read16(lds, r0);
+      const u32x4 v1 = lds_read16(lds, r1);
+      // rows m0 .. m0+15 of the output from a base at row m0 (32-bit offsets
+      // stay below 2^31 for any N <= 2^24)
+      const int m0 = m_base + wm * T::WTM + 16 * i;
+      const uint64_t base = (uint64_t)m0 * (uint64_t)p.N;
+      const uint64_t total = (uint64_t)p.M * (uint64_t)p.N;
+      const uint64_t left = total > base ? (total - base) * 2u : 0u;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.C + base, left);
+      const uint32_t o0 = voff_c == kOOB ? kOOB : voff_c + (uint32_t)rr * row_bytes;
+      const uint32_t o1 = voff_c == kOOB ? kOOB : voff_c + (uint32_t)(rr + 8) * row_bytes;
+      __builtin_amdgcn_raw_buffer_store_b128(v0, rs, o0, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v1, rs, o1, 0, 0);
     }
   }
 }
@@ -501,7 +574,7 @@ __device__ __forceinline__ void apply_store(const GemmParams& p, f32x4 (&acc)[T:
 // Row statistics of this tile's slice of each row, from the fp32
 // accumulators: LayerNorm (s1, s2) = (tile mean, tile M2 = sum (x - mean)^2),
 // two passes over registers; RMSNorm (0, sum x^2).
-template <class T>
+template <class T, bool LN>
 __device__ __forceinline__ void tile_stats(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
                                            lds_char* lds, int n_base, int wm, int wn, int lane,
                                            float (&s1)[T::FM], float (&s2)[T::FM]) {
@@ -513,7 +586,7 @@ __device__ __forceinline__ void tile_stats(const GemmParams& p, const f32x4 (&ac
   float zero[T::FM];
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) zero[i] = 0.f;
-  if (p.norm_kind == NORM_LAYER) {
+  if constexpr (LN) {
     tile_row_sums<T>(acc, colv, 0, zero, s1, lds, wm, wn, lane);
     const float inv = 1.0f / (float)n_tile;
 #pragma unroll
@@ -523,6 +596,24 @@ __device__ __forceinline__ void tile_stats(const GemmParams& p, const f32x4 (&ac
     tile_row_sums<T>(acc, colv, 2, zero, s2, lds, wm, wn, lane);
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) s1[i] = 0.f;
+  }
+}
+
+// Per-row scale of the Lazy Pre-Norm epilogue from the k-loop's sums of
+// squares: rstd = 1 / sqrt(sum_k a^2 / K + eps).  The workgroup holding
+// column tile 0 also writes rstd_out.
+template <class T>
+__device__ __forceinline__ void lazy_rstd(const GemmParams& p, const float (&ss)[T::FM],
+                                          float (&rstd)[T::FM], int m_base, int tn, int wm,
+                                          int wn, int lane) {
+  const float inv_k = 1.0f / (float)p.K;
+  const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    const float s = reduce_lane_groups(ss[i]);
+    rstd[i] = 1.0f / __builtin_sqrtf(fmaf(s, inv_k, p.eps));
+    const int m = m_base + wm * T::WTM + 16 * i + l16;
+    if (p.rstd_out && tn == 0 && wn == 0 && g == 0 && m < p.M) p.rstd_out[m] = rstd[i];
   }
 }
 
@@ -542,32 +633,18 @@ __device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds,
   mainloop<T, EPI == EPI_LAZY>(p, acc, ss, lds, lds_addr_of(lds), m_base, n_base, tid);
 
   float mean[T::FM], rstd[T::FM];
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) { mean[i] = 0.f; rstd[i] = 1.f; }
   if constexpr (EPI == EPI_NONE) {
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i) { mean[i] = 0.f; rstd[i] = 1.f; }
-    GemmParams q = p;
-    q.gamma = nullptr;
-    q.beta = nullptr;
-    apply_store<T>(q, acc, mean, rstd, false, m_base, n_base, wm, wn, lane);
+    apply_store<T, false>(p, acc, mean, rstd, false, lds, m_base, n_base, wave, wm, wn, lane);
   } else if constexpr (EPI == EPI_LAZY) {
-    const float inv_k = 1.0f / (float)p.K;
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i) {
-      float s = reduce_lane_groups(ss[i]);
-      rstd[i] = 1.0f / __builtin_sqrtf(fmaf(s, inv_k, p.eps));
-      mean[i] = 0.f;
-      const int m = m_base + wm * T::WTM + 16 * i + l16;
-      if (p.rstd_out && tn == 0 && wn == 0 && g == 0 && m < p.M) p.rstd_out[m] = rstd[i];
-    }
-    GemmParams q = p;
-    q.gamma = nullptr;
-    q.beta = nullptr;
-    apply_store<T>(q, acc, mean, rstd, false, m_base, n_base, wm, wn, lane);
+    lazy_rstd<T>(p, ss, rstd, m_base, tn, wm, wn, lane);
+    apply_store<T, false>(p, acc, mean, rstd, false, lds, m_base, n_base, wave, wm, wn, lane);
   } else {
     // Row statistics of this tile's slice of each row.
-    const bool ln = p.norm_kind == NORM_LAYER;
+    constexpr bool ln = EPI == EPI_ROW_LN;
     float s1[T::FM], s2[T::FM];
-    tile_stats<T>(p, acc, lds, n_base, wm, wn, lane, s1, s2);
+    tile_stats<T, ln>(p, acc, lds, n_base, wm, wn, lane, s1, s2);
     const float inv_n = 1.0f / (float)p.N;
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
@@ -586,11 +663,11 @@ __device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds,
         }
       }
     }
-    apply_store<T>(p, acc, mean, rstd, ln, m_base, n_base, wm, wn, lane);
+    apply_store<T, true>(p, acc, mean, rstd, ln, lds, m_base, n_base, wave, wm, wn, lane);
   }
 }
 
-// Tile order shared by both grids: tiles grouped 4 tile-rows high, column-major
+// Tile order shared by the grids: tiles grouped 4 tile-rows high, column-major
 // inside a group, and every XCD (workgroup id mod 8) handed a contiguous run
 // of that order so the workgroups resident on one XCD share A and B panels in
 // its L2.
@@ -610,6 +687,8 @@ __device__ __forceinline__ int xcd_contiguous(int b, int total) {
   return x * per + min(x, rem) + local;
 }
 
+// One workgroup per output tile (shapes with few tiles, and tiles whose
+// output staging shares LDS with the pipeline stages).
 template <class T, int EPI>
 __global__ void __launch_bounds__(T::NT) gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) char smem[T::LDS];
@@ -621,31 +700,73 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(GemmParams p) {
   process_tile<T, EPI>(p, lds, tm, tn);
 }
 
+// Persistent grid for the plain and Lazy Pre-Norm GEMMs: gridDim.x workgroups
+// (at most one round of resident workgroups) walk the tile order with stride
+// gridDim.x.  After a tile's k-loop a workgroup issues the LDS transfers that
+// start its next tile, then scales and stores the finished tile, so the
+// memory latency of the next tile's first k-tiles hides behind the output
+// stores.
+template <class T, int EPI>
+__global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
+  static_assert(T::STG_OWN, "persistent tiles need their own output staging");
+  __shared__ __attribute__((aligned(16))) char smem[T::LDS];
+  lds_char* lds = lds_base(smem);
+  const uint32_t lds0 = lds_addr_of(lds);
+  const int G = gridDim.x;
+  const int total = p.tiles_m * p.tiles_n;
+  const int first = (G % 8 == 0) ? xcd_contiguous(blockIdx.x, G) : (int)blockIdx.x;
+  if (first < total) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    int tm, tn;
+    grouped_tile(first, p.tiles_m, p.tiles_n, 4, tm, tn);
+    issue_prologue<T>(p, lds0, tm * T::BM, tn * T::BN, tid);
+  }
+  for (int t = first; t < total; t += G) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / T::WN, wn = wave % T::WN;
+    int tm, tn;
+    grouped_tile(t, p.tiles_m, p.tiles_n, 4, tm, tn);
+    const int m_base = tm * T::BM, n_base = tn * T::BN;
+    f32x4 acc[T::FM][T::FN];
+    float ss[T::FM];
+    mainloop<T, EPI == EPI_LAZY>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, t != first);
+    float mean[T::FM], rstd[T::FM];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) { mean[i] = 0.f; rstd[i] = 1.f; }
+    if constexpr (EPI == EPI_LAZY) lazy_rstd<T>(p, ss, rstd, m_base, tn, wm, wn, lane);
+    if (t + G < total) {
+      int tm2, tn2;
+      grouped_tile(t + G, p.tiles_m, p.tiles_n, 4, tm2, tn2);
+      issue_prologue<T>(p, lds0, tm2 * T::BM, tn2 * T::BN, tid);
+    }
+    apply_store<T, false>(p, acc, mean, rstd, false, lds, m_base, n_base, wave, wm, wn, lane);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Cross-workgroup row norm (rows wider than one tile).
 //
 // Persistent grid of R * tiles_n workgroups, all co-resident (cooperative
-// launch).  Round `it` covers the complete row blocks it*R .. it*R+R-1.  For
-// its tile of round `it` a workgroup
+// launch).  Round `it` covers the complete row blocks it*R .. it*R+R-1, one
+// column tile per workgroup.  For its tile a workgroup
 //   1. runs the k-loop;
 //   2. reduces its slice of every row from the fp32 accumulators and
-//      publishes one (mean_t, M2_t) pair -- or (0, sum x^2) -- per row;
-//   3. writes its tile to C centred on the tile mean (LayerNorm) or as is
-//      (RMSNorm), rounded to bf16, and signals arrival for its row block;
-//   4. issues the LDS transfers that start its next tile;
-//   5. normalizes its tile of round it-1 in place: by now every workgroup of
-//      that row block has arrived (they did so one k-loop ago), so the wait
-//      is normally already over; the row statistics are merged from the
-//      partials in fixed tile order (Chan's update for mean/M2), identical in
-//      every workgroup of the row block.
-// The exchange latency thus hides behind the next tile's k-loop instead of
-// stalling every round.  Waits only ever point at earlier rounds, so the grid
-// cannot deadlock; the bounded spin is a guard, reported through the error
-// word.  Partials and counters use agent-scope (sc1) accesses that bypass the
-// per-XCD L2; a workgroup rereads only the C tile it wrote itself.
-// Storing the tile centred on its own mean keeps the bf16 intermediate small
-// relative to the row's spread, so the second rounding costs at most about
-// 2^-9 of the normalized value.
+//      publishes one (mean_t, M2_t) pair -- or (0, sum x^2) -- per row, then
+//      signals arrival for its row block;
+//   3. issues the LDS transfers that start its next tile;
+//   4. waits until every workgroup of the row block has arrived (they run
+//      the same k-loop in the same round, so the wait is short), merges the
+//      row's partials in fixed tile order (Chan's update for mean/M2),
+//      identically in every workgroup of the row block;
+//   5. normalizes the accumulators still held in registers and stores the
+//      tile once.
+// Waits only ever point at workgroups of the same round, which are all
+// resident, so the grid cannot deadlock; the bounded spin is a guard,
+// reported through the error word.  Partials and counters use agent-scope
+// (sc1) accesses that bypass the per-XCD L2.
 
 // Byte offset of the row block's partials and an sc1 buffer view of them.
 template <class T>
@@ -656,15 +777,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t xwg_part_rsrc(const GemmParams
   return make_rsrc(part + (size_t)tm * blk_bytes, blk_bytes);
 }
 
-template <class T>
-__device__ __forceinline__ void xwg_publish(const GemmParams& p, f32x4 (&acc)[T::FM][T::FN],
+// Step 2: per-row partials of this tile, then the arrival signal.
+template <class T, bool LN>
+__device__ __forceinline__ void xwg_publish(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
                                             lds_char* lds, int tm, int tn, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int l16 = lane & 15, g = lane >> 4;
-  const int m_base = tm * T::BM, n_base = tn * T::BN;
   float s1[T::FM], s2[T::FM];
-  tile_stats<T>(p, acc, lds, n_base, wm, wn, lane, s1, s2);
+  tile_stats<T, LN>(p, acc, lds, tn * T::BN, wm, wn, lane, s1, s2);
   const int tnp = XwgLayout::tn_pad(p.tiles_n);
   const __amdgpu_buffer_rsrc_t prs = xwg_part_rsrc<T>(p, tm);
   if (wn == 0 && g == 0) {
@@ -675,32 +796,26 @@ __device__ __forceinline__ void xwg_publish(const GemmParams& p, f32x4 (&acc)[T:
       __builtin_amdgcn_raw_buffer_store_b64(v, prs, (uint32_t)(r * tnp + tn) * 8u, 0, 16);
     }
   }
-  // the tile, centred on its own row means (s1 is 0 for RMSNorm)
-  float one[T::FM];
-#pragma unroll
-  for (int i = 0; i < T::FM; ++i) one[i] = 1.f;
-  GemmParams q = p;
-  q.gamma = nullptr;
-  q.beta = nullptr;
-  apply_store<T>(q, acc, s1, one, true, m_base, n_base, wm, wn, lane);
   wait_all_mem();
   __syncthreads();
   if (tid == 0) add_agent((int*)(p.ws + XwgLayout::kCnt) + tm, 1);
 }
 
-template <class T>
-__device__ __forceinline__ void xwg_apply(const GemmParams& p, lds_char* lds, int tm, int tn,
+// Step 4: wait for the row block, then merge its partials into (mean, rstd)
+// per row in the FIN region of LDS.  Two threads per row, each merging half
+// of the row's column tiles in order; the halves are then combined (first
+// half first) identically in both threads.
+template <class T, bool LN>
+__device__ __forceinline__ void xwg_merge(const GemmParams& p, lds_char* lds, int tm, int tn,
                                           int tid) {
-  const uint32_t fin = T::FIN_OFF;
+  static_assert(T::NT == 2 * T::BM, "two threads per row");
   int* err = (int*)(p.ws + XwgLayout::kErr);
   int* arrive = (int*)(p.ws + XwgLayout::kCnt);
   int* depart = arrive + p.tiles_m;
-  const bool ln = p.norm_kind == NORM_LAYER;
-  const int m_base = tm * T::BM, n_base = tn * T::BN;
   if (tid == 0) {
     int spins = 0;
     while (load_agent(arrive + tm) < p.tiles_n) {
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
       if (++spins > p.spin_limit) {
         store_agent(err, 1);
         break;
@@ -708,41 +823,58 @@ __device__ __forceinline__ void xwg_apply(const GemmParams& p, lds_char* lds, in
     }
   }
   __syncthreads();
-  // merge the row's partials in fixed tile order; batches of 8 x 16 bytes
+  constexpr bool ln = LN;
+  const int row = tid >> 1, h = tid & 1;
   const int tnp = XwgLayout::tn_pad(p.tiles_n);
+  const int nch = tnp / 2;               // 16-byte chunks (two partials) per row
+  const int half = (nch + 1) / 2;
+  const int c_beg = h * half, c_end = min(nch, c_beg + half);
   const __amdgpu_buffer_rsrc_t prs = xwg_part_rsrc<T>(p, tm);
-  for (int row = tid; row < T::BM; row += T::NT) {
-    float mu = 0.f, m2 = 0.f, cnt = 0.f, mu_t = 0.f;
-    for (int t0 = 0; t0 < p.tiles_n; t0 += 16) {
-      u32x4 v[8];
+  float mu = 0.f, m2 = 0.f, cnt = 0.f;
+  for (int c0 = c_beg; c0 < c_end; c0 += 8) {
+    u32x4 v[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        v[c] = __builtin_amdgcn_raw_buffer_load_b128(prs, (uint32_t)(row * tnp + t0 + 2 * c) * 8u,
-                                                     0, 16);
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t off = c0 + c < c_end ? (uint32_t)(row * tnp + 2 * (c0 + c)) * 8u : kOOB;
+      v[c] = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 16);
+    }
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const int t = t0 + c;
-        if (t >= p.tiles_n) break;
-        const float a = __uint_as_float(v[c >> 1][(c & 1) * 2]);
-        const float b = __uint_as_float(v[c >> 1][(c & 1) * 2 + 1]);
-        if (t == tn) mu_t = a;
-        if (ln) {
-          const float nt = (float)min(T::BN, p.N - t * T::BN);
-          const float nn = cnt + nt;
-          const float d = a - mu;
-          mu = fmaf(d, nt / nn, mu);
-          m2 = m2 + b + d * d * (cnt * nt / nn);
-          cnt = nn;
-        } else {
-          m2 += b;
-        }
+    for (int e = 0; e < 16; ++e) {
+      const int t = 2 * c0 + e;
+      if (c0 + (e >> 1) >= c_end || t >= p.tiles_n) break;
+      const float a = __uint_as_float(v[e >> 1][(e & 1) * 2]);
+      const float b = __uint_as_float(v[e >> 1][(e & 1) * 2 + 1]);
+      if constexpr (ln) {
+        const float nt = (float)min(T::BN, p.N - t * T::BN);
+        const float nn = cnt + nt;
+        const float d = a - mu;
+        mu = fmaf(d, nt / nn, mu);
+        m2 = m2 + b + d * d * (cnt * nt / nn);
+        cnt = nn;
+      } else {
+        m2 += b;
       }
     }
-    const float r = 1.0f / __builtin_sqrtf(fmaf(m2, 1.0f / (float)p.N, p.eps));
-    *(lds_f32x4*)(lds + fin + row * 16) = f32x4{mu, r, mu_t, 0.f};
-    const int m = m_base + row;
+  }
+  // combine the halves: (first, second) = (h0, h1) in both threads
+  const float o_mu = xor_shfl(mu, 1), o_m2 = xor_shfl(m2, 1), o_cnt = xor_shfl(cnt, 1);
+  const float mu_a = h ? o_mu : mu, m2_a = h ? o_m2 : m2, n_a = h ? o_cnt : cnt;
+  const float mu_b = h ? mu : o_mu, m2_b = h ? m2 : o_m2, n_b = h ? cnt : o_cnt;
+  float mean = 0.f, tot;
+  if constexpr (ln) {
+    const float nn = n_a + n_b;
+    const float d = mu_b - mu_a;
+    mean = n_b > 0.f ? fmaf(d, n_b / nn, mu_a) : mu_a;
+    tot = n_b > 0.f ? m2_a + m2_b + d * d * (n_a * n_b / nn) : m2_a;
+  } else {
+    tot = m2_a + m2_b;
+  }
+  const float r = 1.0f / __builtin_sqrtf(fmaf(tot, 1.0f / (float)p.N, p.eps));
+  if (h == 0) {
+    *(lds_f32x2*)(lds + T::FIN_OFF + row * 16) = f32x2{mean, r};
+    const int m = tm * T::BM + row;
     if (tn == 0 && m < p.M) {
-      if (p.mean_out) p.mean_out[m] = mu;
+      if (p.mean_out) p.mean_out[m] = mean;
       if (p.rstd_out) p.rstd_out[m] = r;
     }
   }
@@ -755,55 +887,11 @@ __device__ __forceinline__ void xwg_apply(const GemmParams& p, lds_char* lds, in
       store_agent(depart + tm, 0);
     }
   }
-  // normalize the centred tile in place: y = (v + mu_t - mu) * rstd * gamma + beta.
-  // Thread t owns 8-column chunk t % (BN/8) of rows t / (BN/8) + k * NT/(BN/8).
-  constexpr int CPR = T::BN / 8;
-  constexpr int RSTEP = T::NT / CPR;
-  constexpr int NROW = T::BM / RSTEP;
-  static_assert(T::NT % CPR == 0 && T::BM % RSTEP == 0, "apply split");
-  const int c = tid % CPR;
-  const int n = n_base + 8 * c;
-  if (n >= p.N) return;
-  float gm[8], bt[8];
-  {
-    u32x4 gw = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
-    u32x4 bw = {0u, 0u, 0u, 0u};
-    if (p.gamma) gw = *(const u32x4*)(p.gamma + n);
-    if (p.beta) bw = *(const u32x4*)(p.beta + n);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      gm[2 * w] = bf16_lo(gw[w]); gm[2 * w + 1] = bf16_hi(gw[w]);
-      bt[2 * w] = bf16_lo(bw[w]); bt[2 * w + 1] = bf16_hi(bw[w]);
-    }
-  }
-  u32x4 v[NROW];
-#pragma unroll
-  for (int k = 0; k < NROW; ++k) {
-    const int m = m_base + tid / CPR + k * RSTEP;
-    v[k] = u32x4{0u, 0u, 0u, 0u};
-    if (m < p.M) v[k] = *(const u32x4*)(p.C + (size_t)m * p.N + n);
-  }
-#pragma unroll
-  for (int k = 0; k < NROW; ++k) {
-    const int row = tid / CPR + k * RSTEP;
-    const int m = m_base + row;
-    if (m >= p.M) continue;
-    const f32x4 st = *(lds_f32x4*)(lds + fin + row * 16);
-    const float r = st[1];
-    const float sh = (st[2] - st[0]) * r;
-    u32x4 o;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float a = fmaf(fmaf(bf16_lo(v[k][w]), r, sh), gm[2 * w], bt[2 * w]);
-      const float b = fmaf(fmaf(bf16_hi(v[k][w]), r, sh), gm[2 * w + 1], bt[2 * w + 1]);
-      o[w] = pack_bf16x2(a, b);
-    }
-    *(u32x4*)(p.C + (size_t)m * p.N + n) = o;
-  }
 }
 
-template <class T>
+template <class T, bool LN>
 __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
+  static_assert(T::STG_OWN, "persistent tiles need their own output staging");
   __shared__ __attribute__((aligned(16))) char smem[T::LDS];
   lds_char* lds = lds_base(smem);
   const uint32_t lds0 = lds_addr_of(lds);
@@ -813,7 +901,6 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
   const int gh = (R % 4 == 0) ? 4 : ((R % 2 == 0) ? 2 : 1);
   int rb_in, tn;
   grouped_tile(j, R, p.tiles_n, gh, rb_in, tn);
-  int prev_tm = -1;
   if (rb_in < p.tiles_m) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
@@ -826,21 +913,24 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
     // out of the tile loop (where they would be spilled)
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    {
-      f32x4 acc[T::FM][T::FN];
-      float ss[T::FM];
-      mainloop<T, false>(p, acc, ss, lds, lds0, tm * T::BM, tn * T::BN, tid, true);
-      xwg_publish<T>(p, acc, lds, tm, tn, tid);
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / T::WN, wn = wave % T::WN;
+    const int l16 = lane & 15;
+    const int m_base = tm * T::BM, n_base = tn * T::BN;
+    f32x4 acc[T::FM][T::FN];
+    float ss[T::FM];
+    mainloop<T, false>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, it > 0);
+    xwg_publish<T, LN>(p, acc, lds, tm, tn, tid);
+    if (tm + R < p.tiles_m) issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid);
+    xwg_merge<T, LN>(p, lds, tm, tn, tid);
+    float mean[T::FM], rstd[T::FM];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      const f32x2 st = *(lds_f32x2*)(lds + T::FIN_OFF + (wm * T::WTM + 16 * i + l16) * 16);
+      mean[i] = st[0];
+      rstd[i] = st[1];
     }
-    const int next = tm + R;
-    if (next < p.tiles_m) issue_prologue<T>(p, lds0, next * T::BM, tn * T::BN, tid);
-    if (prev_tm >= 0) xwg_apply<T>(p, lds, prev_tm, tn, tid);
-    prev_tm = tm;
-  }
-  if (prev_tm >= 0) {
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    xwg_apply<T>(p, lds, prev_tm, tn, tid);
+    apply_store<T, true>(p, acc, mean, rstd, LN, lds, m_base, n_base, wave, wm, wn, lane);
   }
 }
 
