@@ -98,8 +98,8 @@ def _shapes(A, B, lay):
 
 class Workspace:
     """Device scratch for the cross-workgroup epilogue (zeroed once here; the
-    kernels leave it zeroed).  One workspace must not serve two calls that
-    can run at the same time."""
+    kernels leave it ready for the next call).  One workspace must not serve
+    two calls that can run at the same time."""
 
     def __init__(self, nbytes: int, device=None):
         torch = _torch()

@@ -44,23 +44,28 @@ enum Epi { EPI_NONE = 0, EPI_LAZY = 1, EPI_ROW_RMS = 2, EPI_ROW_LN = 3 };
 enum NormKind { NORM_RMS = 0, NORM_LAYER = 1 };
 
 // Workspace layout of the cross-workgroup row norm (byte offsets).
-//   [0]            int error word (0 = ok, 1 = a wait timed out)
-//   [256 + 4 rb]   int arrive[row_blocks]
-//   [..]           int depart[row_blocks]
-//   [part_off]     float2 partial[row_blocks][BM][tn_pad]: per row, the
-//                  (mean, M2) or (0, sum x^2) of each column tile, so that one
-//                  row's partials are contiguous (tn_pad = tiles_n rounded up
-//                  to even: 16-byte rows)
+//   [0]        int error word (0 = ok, 1 = a wait timed out)
+//   [4]        uint call counter: a call's tag is its value + 1; the last
+//              workgroup of a call to finish stores the tag back
+//   [8]        uint number of workgroups of the running call that finished
+//   [256]      partial[row_blocks][BM][tiles_n], 16 bytes per (row, column
+//              tile): {mean_t, tag, M2_t, tag} (LayerNorm) or
+//              {0, tag, sum x^2, tag} (RMSNorm)
+//   [fin_off]  final[row_blocks][BM], 16 bytes per row: {mean, tag, rstd, tag}
+// Each 8-byte half of an entry carries the tag of the call that wrote it, and
+// 8-byte accesses are single transactions, so a reader that finds its own
+// call's tag in both halves holds the whole entry.  Entries of earlier calls
+// never match, so nothing needs resetting between calls.
 struct XwgLayout {
   static constexpr size_t kErr = 0;
-  static constexpr size_t kCnt = 256;
-  static __host__ __device__ int tn_pad(int tiles_n) { return (tiles_n + 1) & ~1; }
-  static __host__ __device__ size_t part_off(int row_blocks) {
-    size_t end = kCnt + 8u * (size_t)row_blocks;
-    return (end + 255) & ~(size_t)255;
+  static constexpr size_t kTag = 4;
+  static constexpr size_t kDone = 8;
+  static constexpr size_t kPart = 256;
+  static __host__ __device__ size_t fin_off(int row_blocks, int tiles_n, int bm) {
+    return kPart + (size_t)row_blocks * bm * tiles_n * 16u;
   }
   static __host__ __device__ size_t bytes(int row_blocks, int tiles_n, int bm) {
-    return part_off(row_blocks) + (size_t)row_blocks * bm * tn_pad(tiles_n) * 8u;
+    return fin_off(row_blocks, tiles_n, bm) + (size_t)row_blocks * bm * 16u;
   }
 };
 
@@ -754,137 +759,140 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
 // column tile per workgroup.  For its tile a workgroup
 //   1. runs the k-loop;
 //   2. reduces its slice of every row from the fp32 accumulators and
-//      publishes one (mean_t, M2_t) pair -- or (0, sum x^2) -- per row, then
-//      signals arrival for its row block;
+//      publishes one (mean_t, M2_t) pair -- or (0, sum x^2) -- per row;
 //   3. issues the LDS transfers that start its next tile;
-//   4. waits until every workgroup of the row block has arrived (they run
-//      the same k-loop in the same round, so the wait is short), merges the
-//      row's partials in fixed tile order (Chan's update for mean/M2),
-//      identically in every workgroup of the row block;
-//   5. normalizes the accumulators still held in registers and stores the
-//      tile once.
-// Waits only ever point at workgroups of the same round, which are all
-// resident, so the grid cannot deadlock; the bounded spin is a guard,
-// reported through the error word.  Partials and counters use agent-scope
-// (sc1) accesses that bypass the per-XCD L2.
+//   4. merges, for its own share of the row block's rows (BM / tiles_n of
+//      them), the partials of all column tiles (Chan's update for mean/M2, in
+//      a fixed order) and publishes each row's (mean, rstd);
+//   5. reads (mean, rstd) of all BM rows, normalizes the accumulators still
+//      held in registers and stores the tile once.
+// Steps 4 and 5 poll until the entries carry the call's tag.  Every wait
+// points at workgroups of the same round, which are all resident, so the
+// grid cannot deadlock; the bounded polls are a guard, reported through the
+// error word.  Entries are written and read with agent-scope (sc1) accesses,
+// which bypass the per-XCD L2.
 
-// Byte offset of the row block's partials and an sc1 buffer view of them.
+// sc1 buffer views of the row block's partials and final statistics.
 template <class T>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t xwg_part_rsrc(const GemmParams& p, int tm) {
-  const int tnp = XwgLayout::tn_pad(p.tiles_n);
-  const size_t blk_bytes = (size_t)T::BM * tnp * 8u;
-  char* part = p.ws + XwgLayout::part_off(p.tiles_m);
-  return make_rsrc(part + (size_t)tm * blk_bytes, blk_bytes);
+  const size_t blk = (size_t)T::BM * p.tiles_n * 16u;
+  return make_rsrc(p.ws + XwgLayout::kPart + (size_t)tm * blk, blk);
+}
+template <class T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xwg_fin_rsrc(const GemmParams& p, int tm) {
+  const size_t blk = (size_t)T::BM * 16u;
+  return make_rsrc(p.ws + XwgLayout::fin_off(p.tiles_m, p.tiles_n, T::BM) + (size_t)tm * blk, blk);
 }
 
-// Step 2: per-row partials of this tile, then the arrival signal.
+// 16-byte sc1 load of a tagged entry, repeated until both halves carry `tag`
+// (or the bounded wait gives up and raises the error word).
+__device__ __forceinline__ u32x4 xwg_poll(const GemmParams& p, __amdgpu_buffer_rsrc_t rs,
+                                          uint32_t off, uint32_t tag) {
+  u32x4 v;
+  int spins = 0;
+  while (true) {
+    v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16);
+    if (v[1] == tag && v[3] == tag) break;
+    if (++spins > p.spin_limit) {
+      store_agent((int*)(p.ws + XwgLayout::kErr), 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    asm volatile("" ::: "memory");  // reload on every pass
+  }
+  return v;
+}
+
+// Chan's combination of two (count, mean, M2) summaries, first one first.
+__device__ __forceinline__ void chan_combine(float& n_a, float& mu_a, float& m2_a, float n_b,
+                                             float mu_b, float m2_b) {
+  const float nn = n_a + n_b;
+  const float w = nn > 0.f ? n_b / nn : 0.f;
+  const float d = mu_b - mu_a;
+  mu_a = fmaf(d, w, mu_a);
+  m2_a = m2_a + m2_b + d * d * (n_a * w);
+  n_a = nn;
+}
+
+// Step 2.
 template <class T, bool LN>
 __device__ __forceinline__ void xwg_publish(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
-                                            lds_char* lds, int tm, int tn, int tid) {
+                                            lds_char* lds, int tm, int tn, int tid, uint32_t tag) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int l16 = lane & 15, g = lane >> 4;
   float s1[T::FM], s2[T::FM];
   tile_stats<T, LN>(p, acc, lds, tn * T::BN, wm, wn, lane, s1, s2);
-  const int tnp = XwgLayout::tn_pad(p.tiles_n);
   const __amdgpu_buffer_rsrc_t prs = xwg_part_rsrc<T>(p, tm);
   if (wn == 0 && g == 0) {
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
       const int r = wm * T::WTM + 16 * i + l16;
-      const u32x2 v = {__float_as_uint(s1[i]), __float_as_uint(s2[i])};
-      __builtin_amdgcn_raw_buffer_store_b64(v, prs, (uint32_t)(r * tnp + tn) * 8u, 0, 16);
+      const u32x4 v = {__float_as_uint(s1[i]), tag, __float_as_uint(s2[i]), tag};
+      __builtin_amdgcn_raw_buffer_store_b128(v, prs, (uint32_t)(r * p.tiles_n + tn) * 16u, 0, 16);
     }
   }
-  wait_all_mem();
-  __syncthreads();
-  if (tid == 0) add_agent((int*)(p.ws + XwgLayout::kCnt) + tm, 1);
 }
 
-// Step 4: wait for the row block, then merge its partials into (mean, rstd)
-// per row in the FIN region of LDS.  Two threads per row, each merging half
-// of the row's column tiles in order; the halves are then combined (first
-// half first) identically in both threads.
+// Step 4.  Rows r0 .. r1-1 of the row block belong to this workgroup.  A row
+// is merged by `cpl` lanes (a power of two, at most 64, at least tiles_n when
+// tiles_n <= 64): lane li takes column tiles li, li+cpl, ... in order, then
+// the lanes combine pairwise, lower lanes first.
 template <class T, bool LN>
-__device__ __forceinline__ void xwg_merge(const GemmParams& p, lds_char* lds, int tm, int tn,
-                                          int tid) {
-  static_assert(T::NT == 2 * T::BM, "two threads per row");
-  int* err = (int*)(p.ws + XwgLayout::kErr);
-  int* arrive = (int*)(p.ws + XwgLayout::kCnt);
-  int* depart = arrive + p.tiles_m;
-  if (tid == 0) {
-    int spins = 0;
-    while (load_agent(arrive + tm) < p.tiles_n) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > p.spin_limit) {
-        store_agent(err, 1);
-        break;
-      }
-    }
-  }
-  __syncthreads();
-  constexpr bool ln = LN;
-  const int row = tid >> 1, h = tid & 1;
-  const int tnp = XwgLayout::tn_pad(p.tiles_n);
-  const int nch = tnp / 2;               // 16-byte chunks (two partials) per row
-  const int half = (nch + 1) / 2;
-  const int c_beg = h * half, c_end = min(nch, c_beg + half);
+__device__ __forceinline__ void xwg_merge_rows(const GemmParams& p, int tm, int tn, int tid,
+                                               uint32_t tag) {
+  constexpr int NW = T::NT / 64;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tiles_n = p.tiles_n;
+  const int rpw = (T::BM + tiles_n - 1) / tiles_n;
+  const int r0 = tn * rpw, r1 = min(T::BM, r0 + rpw);
+  int cpl = 1;
+  while (cpl < tiles_n && cpl < 64) cpl <<= 1;
+  const int rows_per_pass = 64 / cpl;
+  const int sub = lane / cpl, li = lane % cpl;
   const __amdgpu_buffer_rsrc_t prs = xwg_part_rsrc<T>(p, tm);
-  float mu = 0.f, m2 = 0.f, cnt = 0.f;
-  for (int c0 = c_beg; c0 < c_end; c0 += 8) {
-    u32x4 v[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t off = c0 + c < c_end ? (uint32_t)(row * tnp + 2 * (c0 + c)) * 8u : kOOB;
-      v[c] = __builtin_amdgcn_raw_buffer_load_b128(prs, off, 0, 16);
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int t = 2 * c0 + e;
-      if (c0 + (e >> 1) >= c_end || t >= p.tiles_n) break;
-      const float a = __uint_as_float(v[e >> 1][(e & 1) * 2]);
-      const float b = __uint_as_float(v[e >> 1][(e & 1) * 2 + 1]);
-      if constexpr (ln) {
-        const float nt = (float)min(T::BN, p.N - t * T::BN);
-        const float nn = cnt + nt;
-        const float d = a - mu;
-        mu = fmaf(d, nt / nn, mu);
-        m2 = m2 + b + d * d * (cnt * nt / nn);
-        cnt = nn;
-      } else {
-        m2 += b;
+  const __amdgpu_buffer_rsrc_t frs = xwg_fin_rsrc<T>(p, tm);
+  const float inv_n = 1.0f / (float)p.N;
+  for (int rb = r0 + wave * rows_per_pass; rb < r1; rb += NW * rows_per_pass) {
+    const int row = rb + sub;
+    const bool active = row < r1;
+    float n = 0.f, mu = 0.f, m2 = 0.f;
+    if (active) {
+      for (int t = li; t < tiles_n; t += cpl) {
+        const u32x4 v = xwg_poll(p, prs, (uint32_t)(row * tiles_n + t) * 16u, tag);
+        if constexpr (LN) {
+          chan_combine(n, mu, m2, (float)min(T::BN, p.N - t * T::BN), __uint_as_float(v[0]),
+                       __uint_as_float(v[2]));
+        } else {
+          m2 += __uint_as_float(v[2]);
+        }
       }
     }
-  }
-  // combine the halves: (first, second) = (h0, h1) in both threads
-  const float o_mu = xor_shfl(mu, 1), o_m2 = xor_shfl(m2, 1), o_cnt = xor_shfl(cnt, 1);
-  const float mu_a = h ? o_mu : mu, m2_a = h ? o_m2 : m2, n_a = h ? o_cnt : cnt;
-  const float mu_b = h ? mu : o_mu, m2_b = h ? m2 : o_m2, n_b = h ? cnt : o_cnt;
-  float mean = 0.f, tot;
-  if constexpr (ln) {
-    const float nn = n_a + n_b;
-    const float d = mu_b - mu_a;
-    mean = n_b > 0.f ? fmaf(d, n_b / nn, mu_a) : mu_a;
-    tot = n_b > 0.f ? m2_a + m2_b + d * d * (n_a * n_b / nn) : m2_a;
-  } else {
-    tot = m2_a + m2_b;
-  }
-  const float r = 1.0f / __builtin_sqrtf(fmaf(tot, 1.0f / (float)p.N, p.eps));
-  if (h == 0) {
-    *(lds_f32x2*)(lds + T::FIN_OFF + row * 16) = f32x2{mean, r};
-    const int m = tm * T::BM + row;
-    if (tn == 0 && m < p.M) {
-      if (p.mean_out) p.mean_out[m] = mean;
-      if (p.rstd_out) p.rstd_out[m] = r;
+    for (int o = 1; o < cpl; o <<= 1) {
+      const float n_o = xor_shfl(n, o), mu_o = xor_shfl(mu, o), m2_o = xor_shfl(m2, o);
+      if constexpr (LN) {
+        if (li & o) {  // this lane holds the upper half: combine (partner, self)
+          float na = n_o, ma = mu_o, qa = m2_o;
+          chan_combine(na, ma, qa, n, mu, m2);
+          n = na; mu = ma; m2 = qa;
+        } else {
+          chan_combine(n, mu, m2, n_o, mu_o, m2_o);
+        }
+      } else {
+        m2 = (li & o) ? m2_o + m2 : m2 + m2_o;
+      }
     }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    // the last workgroup of the row block to get here resets its counters
-    // for the next call (all have passed the wait by then)
-    if (add_agent(depart + tm, 1) == p.tiles_n - 1) {
-      store_agent(arrive + tm, 0);
-      store_agent(depart + tm, 0);
+    if (active && li == 0) {
+      const float r = 1.0f / __builtin_sqrtf(fmaf(m2, inv_n, p.eps));
+      const float mean = LN ? mu : 0.f;
+      const u32x4 v = {__float_as_uint(mean), tag, __float_as_uint(r), tag};
+      __builtin_amdgcn_raw_buffer_store_b128(v, frs, (uint32_t)row * 16u, 0, 16);
+      const int m = tm * T::BM + row;
+      if (m < p.M) {
+        if (p.mean_out) p.mean_out[m] = mean;
+        if (p.rstd_out) p.rstd_out[m] = r;
+      }
     }
   }
 }
@@ -901,6 +909,9 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
   const int gh = (R % 4 == 0) ? 4 : ((R % 2 == 0) ? 2 : 1);
   int rb_in, tn;
   grouped_tile(j, R, p.tiles_n, gh, rb_in, tn);
+  const uint32_t tag =
+      __builtin_amdgcn_readfirstlane((uint32_t)load_agent((const int*)(p.ws + XwgLayout::kTag))) +
+      1u;
   if (rb_in < p.tiles_m) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
@@ -920,17 +931,28 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
     f32x4 acc[T::FM][T::FN];
     float ss[T::FM];
     mainloop<T, false>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, it > 0);
-    xwg_publish<T, LN>(p, acc, lds, tm, tn, tid);
+    xwg_publish<T, LN>(p, acc, lds, tm, tn, tid, tag);
     if (tm + R < p.tiles_m) issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid);
-    xwg_merge<T, LN>(p, lds, tm, tn, tid);
+    xwg_merge_rows<T, LN>(p, tm, tn, tid, tag);
+    // step 5: (mean, rstd) of this wave's rows
+    const __amdgpu_buffer_rsrc_t frs = xwg_fin_rsrc<T>(p, tm);
     float mean[T::FM], rstd[T::FM];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
-      const f32x2 st = *(lds_f32x2*)(lds + T::FIN_OFF + (wm * T::WTM + 16 * i + l16) * 16);
-      mean[i] = st[0];
-      rstd[i] = st[1];
+      const u32x4 v = xwg_poll(p, frs, (uint32_t)(wm * T::WTM + 16 * i + l16) * 16u, tag);
+      mean[i] = __uint_as_float(v[0]);
+      rstd[i] = __uint_as_float(v[2]);
     }
     apply_store<T, true>(p, acc, mean, rstd, LN, lds, m_base, n_base, wave, wm, wn, lane);
+  }
+  // the last workgroup to finish advances the call counter (every workgroup
+  // read it at its start)
+  if (threadIdx.x == 0) {
+    int* done = (int*)(p.ws + XwgLayout::kDone);
+    if (add_agent(done, 1) == G - 1) {
+      store_agent((int*)(p.ws + XwgLayout::kTag), (int)tag);
+      store_agent(done, 0);
+    }
   }
 }
 

@@ -98,12 +98,15 @@ def test_gemm_norm_workspace_checks():
 
 
 def test_workspace_size_formula():
-    # header 256 B + counters, then float2 partials per (row block, column tile, row)
+    # 256-byte header, then one 16-byte tagged partial per (row block, row,
+    # column tile) and one 16-byte tagged (mean, rstd) per row
     M, N = 16384, 8192
     rb, tn = M // 256, N // 256
-    counters = 256 + 8 * rb
-    part_off = (counters + 255) // 256 * 256
-    assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_RMSNORM, M, N, 4096) == part_off + rb * tn * 256 * 8
+    expect = 256 + rb * 256 * tn * 16 + rb * 256 * 16
+    assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_RMSNORM, M, N, 4096) == expect
+    # ragged: 1000 rows -> 4 row blocks, 4100 columns -> 17 column tiles
+    expect = 256 + 4 * 256 * 17 * 16 + 4 * 256 * 16
+    assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 1000, 4100, 64) == expect
 
 
 def test_gemm_norm_argument_checks():

@@ -169,7 +169,7 @@ def test_layernorm_constant_rows_give_beta(N):
     assert dev.max() <= 1e-2
 
 
-def test_cross_workgroup_path_is_deterministic_and_leaves_workspace_clean():
+def test_cross_workgroup_path_is_deterministic_and_leaves_workspace_ready():
     M, N, K = 1000, 4096, 256
     x = workloads.make_inputs(M, N, K, seed=99, gamma=True, beta=True)
     ws = ng.Workspace(ng.ng_workspace_bytes(ng.NG_OP_GEMM_LAYERNORM, M, N, K))
@@ -182,8 +182,10 @@ def test_cross_workgroup_path_is_deterministic_and_leaves_workspace_clean():
     assert ws.status() == 0
     torch.cuda.synchronize()
     assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
-    counters = ws.buf[256:256 + 8 * 4].cpu().numpy()
-    assert np.all(counters == 0)
+    # header: error word 0, call counter advanced once per call, no workgroup
+    # of a running call left over
+    header = ws.buf[0:12].view(torch.int32).cpu().numpy()
+    assert header[0] == 0 and header[1] == 3 and header[2] == 0
     ref, _ = oracle.gemm_rmsnorm(y.A, y.B, 1e-6, y.gamma)
     _check("xwg second shape", down(C3), ref)
 
