@@ -221,20 +221,29 @@ struct Frags {
 // B fragments (two transposing 8-byte reads each for B[K,N], one 16-byte read
 // for B[N,K]).  Per lane only a base address per sub-step is computed; the
 // fragment index enters as a compile-time offset.
+//
+// With a_xor = 1 the A fragment slots are permuted (slot i holds fragment
+// i ^ 1), so that two waves sharing rows hold different fragments in the
+// same slots; the Lazy Pre-Norm squares use this to split their work.
 template <class T>
 struct FragReader {
   static constexpr int B_ITEMS = T::KN ? 2 * T::FN : T::FN;
   static constexpr int ITEMS = T::FM + B_ITEMS;
-  uint32_t a_base[2];  // per kk: A fragment 0 of this lane, from the A region
+  uint32_t a_base[2];  // per kk: A slot 0 of this lane (even slots), from the A region
+  uint32_t a_odd[2];   // per kk: base for odd slots
   uint32_t b_base[2];  // per kk: B fragment 0 (half 0) of this lane, from the B region
   uint32_t b_odd[2];   // KN: base for odd fragments (the XOR in b_blk_off)
 
-  __device__ __forceinline__ void init(int wm, int wn, int lane) {
+  __device__ __forceinline__ void init(int wm, int wn, int lane, int a_xor = 0) {
     const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int row = wm * T::WTM + l16;
-      a_base[kk] = (uint32_t)(row * 128 + (((kk * 4 + g) ^ (l16 & 7)) << 4));
+      const uint32_t a0 = (uint32_t)(row * 128 + (((kk * 4 + g) ^ (l16 & 7)) << 4));
+      // slot i reads fragment i ^ a_xor: +2048 for even slots, -2048 for odd
+      // ones (odd slots are >= 1, so the sum never wraps below zero)
+      a_base[kk] = a0 + 2048u * (uint32_t)a_xor;
+      a_odd[kk] = a0 - 2048u * (uint32_t)a_xor;
       if constexpr (T::KN) {
         // k = kk*32 + 8g + (l16 >> 2) (+4 for the second half), n = wn*WTN +
         // 16j + 4*(l16 & 3).  Fragment j sits at block (j ^ p), p = g & 1,
@@ -256,7 +265,8 @@ struct FragReader {
   __device__ __forceinline__ void read(Frags<T>& f, int item, lds_char* lds, uint32_t a_st,
                                        uint32_t b_st, int kk) const {
     if (item < T::FM) {
-      f.a[item] = lds_read16(lds, a_st + a_base[kk] + (uint32_t)item * 2048u);
+      f.a[item] = lds_read16(lds, a_st + ((item & 1) ? a_odd[kk] : a_base[kk]) +
+                                      (uint32_t)item * 2048u);
       return;
     }
     const int bi = item - T::FM;
@@ -279,19 +289,25 @@ struct FragReader {
 // accumulators.  Pairs sit STEP MFMAs apart and consecutive pairs update
 // different fragments' sums, so no dependent VALU chain holds up the MFMA
 // issue.  (Plain VALU ops co-issue with MFMAs; v_dot2_f32_bf16 was measured
-// to compete with them.)  Waves that share rows compute the same sums.
+// to compete with them.)  With two waves per row set (lazy_split), each
+// squares only its even slots, which hold different fragments in the two
+// waves (FragReader's a_xor), and the halves are combined after the k-loop.
+template <class T>
+constexpr bool lazy_split() { return T::WN == 2 && T::FM % 2 == 0; }
+
 template <class T>
 __device__ __forceinline__ void lazy_square(int q, const Frags<T>& cur, float (&ss)[T::FM],
                                             float (&ss2)[T::FM]) {
   constexpr int NM = T::FM * T::FN;
-  constexpr int ITEMS = T::FM * 4;
+  constexpr int SLOTS = lazy_split<T>() ? T::FM / 2 : T::FM;
+  constexpr int ITEMS = SLOTS * 4;
   constexpr int STEP = NM >= ITEMS ? NM / ITEMS : 1;
   constexpr int PER = NM >= ITEMS ? 1 : (ITEMS + NM - 1) / NM;  // pairs per MFMA
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int t = (q / STEP) * PER + e;
     if (q % STEP == 0 && t < ITEMS) {
-      const int ii = t % T::FM, d = t / T::FM;
+      const int ii = lazy_split<T>() ? 2 * (t % SLOTS) : t % SLOTS, d = t / SLOTS;
       const uint32_t w = cur.a[ii][d];
       const float lo = __uint_as_float(w << 16);
       const float hi = __uint_as_float(w & 0xffff0000u);
@@ -399,7 +415,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   DmaPlan<T> dma;
   dma.init(p, n_base, lane, wave);
   FragReader<T> rd;
-  rd.init(wm, wn, lane);
+  rd.init(wm, wn, lane, (LAZY && lazy_split<T>()) ? wn : 0);
   constexpr int ND = DmaPlan<T>::INS;
   constexpr int NR = FragReader<T>::ITEMS;
   const int nk = (p.K + BK - 1) / BK;
@@ -505,12 +521,12 @@ __device__ __forceinline__ uint32_t stg_chunk(int r, int c) {
 // global store writes whole 128-byte row segments (16 bytes per lane) instead
 // of 8-byte pieces of 16 rows.  Exactly T::C_STORES buffer stores per thread
 // are issued; rows past M and columns past N fall outside the buffer range
-// and are dropped.
+// and are dropped.  Slot i of acc holds fragment i ^ a_xor.
 template <class T, bool AFFINE>
 __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
                                             const float (&mean)[T::FM], const float (&rstd)[T::FM],
                                             bool use_mean, lds_char* lds, int m_base, int n_base,
-                                            int wave, int wm, int wn, int lane) {
+                                            int wave, int wm, int wn, int lane, int a_xor = 0) {
   const int l16 = lane & 15, g = lane >> 4;
   const uint32_t stg = (uint32_t)T::STG_OFF + (uint32_t)wave * 2048u;
   // fragment writes: lane (l16, g) of fragment jj holds 4 columns = 8 bytes
@@ -563,7 +579,7 @@ __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&a
       const u32x4 v1 = lds_read16(lds, r1);
       // rows m0 .. m0+15 of the output from a base at row m0 (32-bit offsets
       // stay below 2^31 for any N <= 2^24)
-      const int m0 = m_base + wm * T::WTM + 16 * i;
+      const int m0 = m_base + wm * T::WTM + 16 * (i ^ a_xor);
       const uint64_t base = (uint64_t)m0 * (uint64_t)p.N;
       const uint64_t total = (uint64_t)p.M * (uint64_t)p.N;
       const uint64_t left = total > base ? (total - base) * 2u : 0u;
@@ -605,19 +621,35 @@ __device__ __forceinline__ void tile_stats(const GemmParams& p, const f32x4 (&ac
 }
 
 // Per-row scale of the Lazy Pre-Norm epilogue from the k-loop's sums of
-// squares: rstd = 1 / sqrt(sum_k a^2 / K + eps).  The workgroup holding
-// column tile 0 also writes rstd_out.
+// squares: rstd = 1 / sqrt(sum_k a^2 / K + eps).  Slot i of the wave holds
+// fragment i ^ a_xor.  With lazy_split the two waves of a row set each
+// summed half of the fragments; they swap their halves through LDS.  The
+// workgroup holding column tile 0 also writes rstd_out.
 template <class T>
 __device__ __forceinline__ void lazy_rstd(const GemmParams& p, const float (&ss)[T::FM],
-                                          float (&rstd)[T::FM], int m_base, int tn, int wm,
-                                          int wn, int lane) {
+                                          float (&rstd)[T::FM], lds_char* lds, int m_base,
+                                          int tn, int wm, int wn, int lane, int a_xor) {
   const float inv_k = 1.0f / (float)p.K;
   const int l16 = lane & 15, g = lane >> 4;
+  float s[T::FM];
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) s[i] = reduce_lane_groups(ss[i]);
+  if constexpr (lazy_split<T>()) {
+    const uint32_t red = T::RED_OFF;
+    if (g == 0) {
+#pragma unroll
+      for (int i = 0; i < T::FM; i += 2)
+        *(lds_float*)(lds + red + (wm * T::WTM + 16 * (i ^ a_xor) + l16) * 4) = s[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+      s[i] = *(lds_float*)(lds + red + (wm * T::WTM + 16 * (i ^ a_xor) + l16) * 4);
+  }
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
-    const float s = reduce_lane_groups(ss[i]);
-    rstd[i] = 1.0f / __builtin_sqrtf(fmaf(s, inv_k, p.eps));
-    const int m = m_base + wm * T::WTM + 16 * i + l16;
+    rstd[i] = 1.0f / __builtin_sqrtf(fmaf(s[i], inv_k, p.eps));
+    const int m = m_base + wm * T::WTM + 16 * (i ^ a_xor) + l16;
     if (p.rstd_out && tn == 0 && wn == 0 && g == 0 && m < p.M) p.rstd_out[m] = rstd[i];
   }
 }
@@ -643,8 +675,9 @@ __device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds,
   if constexpr (EPI == EPI_NONE) {
     apply_store<T, false>(p, acc, mean, rstd, false, lds, m_base, n_base, wave, wm, wn, lane);
   } else if constexpr (EPI == EPI_LAZY) {
-    lazy_rstd<T>(p, ss, rstd, m_base, tn, wm, wn, lane);
-    apply_store<T, false>(p, acc, mean, rstd, false, lds, m_base, n_base, wave, wm, wn, lane);
+    const int ax = lazy_split<T>() ? wn : 0;
+    lazy_rstd<T>(p, ss, rstd, lds, m_base, tn, wm, wn, lane, ax);
+    apply_store<T, false>(p, acc, mean, rstd, false, lds, m_base, n_base, wave, wm, wn, lane, ax);
   } else {
     // Row statistics of this tile's slice of each row.
     constexpr bool ln = EPI == EPI_ROW_LN;
@@ -741,13 +774,14 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     float mean[T::FM], rstd[T::FM];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) { mean[i] = 0.f; rstd[i] = 1.f; }
-    if constexpr (EPI == EPI_LAZY) lazy_rstd<T>(p, ss, rstd, m_base, tn, wm, wn, lane);
+    const int ax = (EPI == EPI_LAZY && lazy_split<T>()) ? wn : 0;
+    if constexpr (EPI == EPI_LAZY) lazy_rstd<T>(p, ss, rstd, lds, m_base, tn, wm, wn, lane, ax);
     if (t + G < total) {
       int tm2, tn2;
       grouped_tile(t + G, p.tiles_m, p.tiles_n, 4, tm2, tn2);
       issue_prologue<T>(p, lds0, tm2 * T::BM, tn2 * T::BN, tid);
     }
-    apply_store<T, false>(p, acc, mean, rstd, false, lds, m_base, n_base, wave, wm, wn, lane);
+    apply_store<T, false>(p, acc, mean, rstd, false, lds, m_base, n_base, wave, wm, wn, lane, ax);
   }
 }
 
