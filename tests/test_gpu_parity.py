@@ -122,6 +122,74 @@ def test_norm_small(rows, cols, kind):
     _check_stat("norm rstd", rstd, rref)
 
 
+# ------------------------------------------- persistent grids, several rounds
+# The 256x256-tile kernels run as persistent grids of one workgroup per
+# resident slot: these shapes give some workgroups two tiles (more tiles than
+# slots), ragged M, N and K tails, and, for the cross-workgroup norm, several
+# rounds of row blocks, more than 64 column tiles per row (several partials
+# per merging lane) and the widest row the grid holds (one row per merging
+# workgroup).
+
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+def test_persistent_gemm_and_lazy_multi_tile_ragged(layout):
+    M, N, K = 256 * 18 + 37, 256 * 16 + 72, 200
+    log("persistent gemm/lazy M=%d N=%d K=%d %s" % (M, N, K, layout))
+    x = workloads.make_inputs(M, N, K, seed=11, row_scale=True)
+    A, B = up(x.A), up(b_for_layout(x.B, layout))
+    C = ng.gemm(A, B, b_layout=layout)
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    L = ng.rmsnorm_gemm_lazy(A, B, eps=1e-6, b_layout=layout, rstd_out=rstd)
+    torch.cuda.synchronize()
+    _check("persistent gemm", down(C), oracle.gemm(x.A, x.B))
+    ref, rref = oracle.rmsnorm_gemm_lazy(x.A, x.B, 1e-6)
+    _check("persistent lazy", down(L), ref)
+    _check_stat("persistent lazy rstd", rstd, rref)
+
+
+@pytest.mark.parametrize("kind,layout", [("layer", "kn"), ("rms", "nk")])
+def test_cross_workgroup_several_rounds_ragged(kind, layout):
+    # 10 column tiles -> 25 row blocks per round; 31 row blocks -> 2 rounds
+    M, N, K = 256 * 30 + 100, 256 * 9 + 24, 136
+    log("xwg rounds %s M=%d N=%d K=%d %s" % (kind, M, N, K, layout))
+    x = workloads.make_inputs(M, N, K, seed=21, gamma=True, beta=kind == "layer")
+    A, B = up(x.A), up(b_for_layout(x.B, layout))
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    if kind == "layer":
+        mean = torch.empty(M, dtype=torch.float32, device="cuda")
+        C = ng.gemm_layernorm(A, B, up(x.gamma), up(x.beta), eps=1e-5, b_layout=layout,
+                              mean_out=mean, rstd_out=rstd)
+        torch.cuda.synchronize()
+        ref, mref, rref = oracle.gemm_layernorm(x.A, x.B, 1e-5, x.gamma, x.beta)
+        got_mean = mean.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(got_mean - mref) / (1.0 + np.abs(mref))) <= 1e-3
+    else:
+        C = ng.gemm_rmsnorm(A, B, up(x.gamma), eps=1e-6, b_layout=layout, rstd_out=rstd)
+        torch.cuda.synchronize()
+        ref, rref = oracle.gemm_rmsnorm(x.A, x.B, 1e-6, x.gamma)
+    _check("xwg rounds %s" % kind, down(C), ref)
+    _check_stat("xwg rounds rstd", rstd, rref)
+
+
+@pytest.mark.parametrize("kind", ["layer", "rms"])
+@pytest.mark.parametrize("M,N", [(300, 256 * 65 + 8), (100, 65536)])
+def test_cross_workgroup_many_column_tiles(M, N, kind):
+    K = 64
+    log("xwg wide %s M=%d N=%d K=%d" % (kind, M, N, K))
+    x = workloads.make_inputs(M, N, K, seed=N % 1000 + M, gamma=True, beta=kind == "layer")
+    A, B = up(x.A), up(x.B)
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    if kind == "layer":
+        C = ng.gemm_layernorm(A, B, up(x.gamma), up(x.beta), eps=1e-5, rstd_out=rstd)
+        torch.cuda.synchronize()
+        ref, _, rref = oracle.gemm_layernorm(x.A, x.B, 1e-5, x.gamma, x.beta)
+    else:
+        C = ng.gemm_rmsnorm(A, B, up(x.gamma), eps=1e-6, rstd_out=rstd)
+        torch.cuda.synchronize()
+        ref, rref = oracle.gemm_rmsnorm(x.A, x.B, 1e-6, x.gamma)
+    _check("xwg wide %s %dx%d" % (kind, M, N), down(C), ref)
+    _check_stat("xwg wide rstd", rstd, rref)
+
+
 # ------------------------------------------------------------ edge cases
 def test_empty_M_leaves_output_untouched():
     A = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
