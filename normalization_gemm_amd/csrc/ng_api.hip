@@ -116,15 +116,22 @@ int launch_grid(ng::GemmParams p, hipStream_t s, const char* what) {
 
 // Co-resident workgroups per device for a persistent kernel (cached per
 // kernel and device).
-int resident_capacity(const void* kernel, int threads, int slot, int* cap) {
+int resident_capacity(const void* kernel, int threads, int* cap) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(NG_ERR_HIP, "hipGetDevice failed");
+  struct Entry {
+    const void* kernel;
+    int dev, cap;
+  };
   static std::mutex mu;
-  static int cached[16][64] = {{0}};
+  static Entry cache[64];
+  static int n_cached = 0;
   std::lock_guard<std::mutex> lk(mu);
-  if (dev < 64 && cached[slot][dev] > 0) {
-    *cap = cached[slot][dev];
-    return NG_OK;
+  for (int i = 0; i < n_cached; ++i) {
+    if (cache[i].kernel == kernel && cache[i].dev == dev) {
+      *cap = cache[i].cap;
+      return NG_OK;
+    }
   }
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
@@ -133,15 +140,9 @@ int resident_capacity(const void* kernel, int threads, int slot, int* cap) {
     return fail(NG_ERR_HIP, "CU count query failed");
   const int c = per_cu * cus;
   if (c <= 0) return fail(NG_ERR_HIP, "persistent kernel cannot be resident");
-  if (dev < 64) cached[slot][dev] = c;
+  if (n_cached < 64) cache[n_cached++] = Entry{kernel, dev, c};
   *cap = c;
   return NG_OK;
-}
-
-// Cache slots of resident_capacity, one per persistent kernel instance.
-template <class T, int EPI>
-constexpr int persistent_slot() {
-  return (T::KN ? 0 : 1) + (EPI == ng::EPI_LAZY ? 2 : 0);
 }
 
 template <class T, int EPI>
@@ -150,8 +151,7 @@ int launch_persistent(ng::GemmParams p, hipStream_t s, const char* what) {
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
   const long long total = (long long)p.tiles_m * p.tiles_n;
   int cap = 0;
-  int st = resident_capacity((const void*)ng::gemm_persistent_kernel<T, EPI>, T::NT,
-                             persistent_slot<T, EPI>(), &cap);
+  int st = resident_capacity((const void*)ng::gemm_persistent_kernel<T, EPI>, T::NT, &cap);
   if (st) return st;
   const unsigned grid = (unsigned)(total < cap ? total : cap);
   hipLaunchKernelGGL((ng::gemm_persistent_kernel<T, EPI>), dim3(grid), dim3(T::NT), 0, s, p);
@@ -163,8 +163,7 @@ int launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   p.tiles_m = (p.M + T::BM - 1) / T::BM;
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
   int cap = 0;
-  int st = resident_capacity((const void*)ng::gemm_xwg_kernel<T, LN>, T::NT,
-                             4 + (T::KN ? 0 : 1) + (LN ? 2 : 0), &cap);
+  int st = resident_capacity((const void*)ng::gemm_xwg_kernel<T, LN>, T::NT, &cap);
   if (st) return st;
   if (p.tiles_n > cap)
     return fail(NG_ERR_UNSUPPORTED, "row of %d tiles exceeds %d co-resident workgroups",

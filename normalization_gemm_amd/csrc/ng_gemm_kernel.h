@@ -457,10 +457,16 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
 
 // Sum over the 4 lane groups sharing (lane & 15): a row's partial over this
 // wave's columns (or, for the lazy sum of squares, over this wave's k-groups).
+// v_permlane16_swap / v_permlane32_swap hand every lane both members of its
+// xor-16 (then xor-32) pair, lower lane first, so all four lanes add the same
+// operands in the same order: (x0 + x16) + (x32 + x48).
 __device__ __forceinline__ float reduce_lane_groups(float v) {
-  v += xor_shfl(v, 16);
-  v += xor_shfl(v, 32);
-  return v;
+  const uint32_t u = __float_as_uint(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float s16 = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  const uint32_t w = __float_as_uint(s16);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
 }
 
 // Per-row sums of this workgroup's accumulators over its valid columns,
@@ -515,6 +521,31 @@ __device__ __forceinline__ uint32_t stg_chunk(int r, int c) {
   return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
 }
 
+// Per-column gamma/beta of a wave's columns, as loaded bf16 pairs: g[j] and
+// b[j] hold the 4 columns 16j + 4(lane >> 4) .. +3 of the wave's slice
+// (1 and 0 where absent).  Loaded ahead of the row statistics so that their
+// latency overlaps them.
+template <class T>
+struct Affine {
+  u32x2 g[T::FN], b[T::FN];
+};
+
+template <class T>
+__device__ __forceinline__ void load_affine(const GemmParams& p, int n_base, int wn, int lane,
+                                            Affine<T>& aff) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) {
+    aff.g[j] = u32x2{0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
+    aff.b[j] = u32x2{0u, 0u};
+    const int n = n_base + wn * T::WTN + 16 * j + 4 * g;
+    if (n < p.N) {
+      if (p.gamma) aff.g[j] = *(const u32x2*)(p.gamma + n);
+      if (p.beta) aff.b[j] = *(const u32x2*)(p.beta + n);
+    }
+  }
+}
+
 // Scale/shift the accumulators by per-row (mean, rstd) and (AFFINE) the
 // per-column gamma/beta, round to bf16 and store the tile.  Each 16-row x
 // 64-column piece goes through the wave's LDS staging block so that every
@@ -525,8 +556,9 @@ __device__ __forceinline__ uint32_t stg_chunk(int r, int c) {
 template <class T, bool AFFINE>
 __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
                                             const float (&mean)[T::FM], const float (&rstd)[T::FM],
-                                            bool use_mean, lds_char* lds, int m_base, int n_base,
-                                            int wave, int wm, int wn, int lane, int a_xor = 0) {
+                                            bool use_mean, const Affine<T>& aff, lds_char* lds,
+                                            int m_base, int n_base, int wave, int wm, int wn,
+                                            int lane, int a_xor = 0) {
   const int l16 = lane & 15, g = lane >> 4;
   const uint32_t stg = (uint32_t)T::STG_OFF + (uint32_t)wave * 2048u;
   // fragment writes: lane (l16, g) of fragment jj holds 4 columns = 8 bytes
@@ -541,19 +573,8 @@ __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&a
   const uint32_t row_bytes = (uint32_t)p.N * 2u;
 #pragma unroll
   for (int q = 0; q < T::FN / 4; ++q) {
-    u32x2 gw[4], bw[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      gw[jj] = u32x2{0x3f803f80u, 0x3f803f80u};  // bf16 1.0 pairs
-      bw[jj] = u32x2{0u, 0u};
-      if constexpr (AFFINE) {
-        const int n = n_base + wn * T::WTN + 16 * (4 * q + jj) + 4 * g;
-        if (n < p.N) {
-          if (p.gamma) gw[jj] = *(const u32x2*)(p.gamma + n);
-          if (p.beta) bw[jj] = *(const u32x2*)(p.beta + n);
-        }
-      }
-    }
+    const u32x2* gw = &aff.g[4 * q];
+    const u32x2* bw = &aff.b[4 * q];
     const int n_st = n_base + wn * T::WTN + 64 * q + 8 * rc;
     const uint32_t voff_c = n_st < p.N ? 2u * (uint32_t)n_st : kOOB;
 #pragma unroll
@@ -654,35 +675,23 @@ __device__ __forceinline__ void lazy_rstd(const GemmParams& p, const float (&ss)
   }
 }
 
+// Per-row (mean, rstd) that the epilogue applies to a finished tile:
+// EPI_NONE (0, 1); EPI_LAZY (0, rstd of the row of A); EPI_ROW_* the row's
+// statistics over the tile (which holds whole rows).  Also writes the
+// statistic outputs.  ax: slot permutation of the accumulators (lazy_split).
 template <class T, int EPI>
-__device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds, int tm, int tn) {
-  // Opaque copy of the thread id: keeps lane-dependent addresses from being
-  // hoisted out of the persistent tile loop (where they would be spilled).
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / T::WN, wn = wave % T::WN;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int m_base = tm * T::BM, n_base = tn * T::BN;
-
-  f32x4 acc[T::FM][T::FN];
-  float ss[T::FM];
-  mainloop<T, EPI == EPI_LAZY>(p, acc, ss, lds, lds_addr_of(lds), m_base, n_base, tid);
-
-  float mean[T::FM], rstd[T::FM];
+__device__ __forceinline__ void tile_scale(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
+                                           const float (&ss)[T::FM], lds_char* lds, int m_base,
+                                           int n_base, int tn, int wm, int wn, int lane, int ax,
+                                           float (&mean)[T::FM], float (&rstd)[T::FM]) {
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) { mean[i] = 0.f; rstd[i] = 1.f; }
-  if constexpr (EPI == EPI_NONE) {
-    apply_store<T, false>(p, acc, mean, rstd, false, lds, m_base, n_base, wave, wm, wn, lane);
-  } else if constexpr (EPI == EPI_LAZY) {
-    const int ax = lazy_split<T>() ? wn : 0;
+  if constexpr (EPI == EPI_LAZY) {
     lazy_rstd<T>(p, ss, rstd, lds, m_base, tn, wm, wn, lane, ax);
-    apply_store<T, false>(p, acc, mean, rstd, false, lds, m_base, n_base, wave, wm, wn, lane, ax);
-  } else {
-    // Row statistics of this tile's slice of each row.
-    constexpr bool ln = EPI == EPI_ROW_LN;
+  } else if constexpr (EPI == EPI_ROW_RMS || EPI == EPI_ROW_LN) {
+    const int l16 = lane & 15, g = lane >> 4;
     float s1[T::FM], s2[T::FM];
-    tile_stats<T, ln>(p, acc, lds, n_base, wm, wn, lane, s1, s2);
+    tile_stats<T, EPI == EPI_ROW_LN>(p, acc, lds, n_base, wm, wn, lane, s1, s2);
     const float inv_n = 1.0f / (float)p.N;
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
@@ -701,8 +710,34 @@ __device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds,
         }
       }
     }
-    apply_store<T, true>(p, acc, mean, rstd, ln, lds, m_base, n_base, wave, wm, wn, lane);
   }
+}
+
+template <class T, int EPI>
+__device__ __forceinline__ void tile_store(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
+                                           const float (&mean)[T::FM], const float (&rstd)[T::FM],
+                                           const Affine<T>& aff, lds_char* lds, int m_base,
+                                           int n_base, int wave, int wm, int wn, int lane, int ax) {
+  constexpr bool ROW = EPI == EPI_ROW_RMS || EPI == EPI_ROW_LN;
+  apply_store<T, ROW>(p, acc, mean, rstd, EPI == EPI_ROW_LN, aff, lds, m_base, n_base, wave, wm,
+                      wn, lane, ax);
+}
+
+template <class T, int EPI>
+__device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds, int tm, int tn) {
+  int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / T::WN, wn = wave % T::WN;
+  const int m_base = tm * T::BM, n_base = tn * T::BN;
+  const int ax = (EPI == EPI_LAZY && lazy_split<T>()) ? wn : 0;
+  f32x4 acc[T::FM][T::FN];
+  float ss[T::FM];
+  mainloop<T, EPI == EPI_LAZY>(p, acc, ss, lds, lds_addr_of(lds), m_base, n_base, tid);
+  Affine<T> aff;
+  if constexpr (EPI == EPI_ROW_RMS || EPI == EPI_ROW_LN) load_affine<T>(p, n_base, wn, lane, aff);
+  float mean[T::FM], rstd[T::FM];
+  tile_scale<T, EPI>(p, acc, ss, lds, m_base, n_base, tn, wm, wn, lane, ax, mean, rstd);
+  tile_store<T, EPI>(p, acc, mean, rstd, aff, lds, m_base, n_base, wave, wm, wn, lane, ax);
 }
 
 // Tile order shared by the grids: tiles grouped 4 tile-rows high, column-major
@@ -738,12 +773,12 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(GemmParams p) {
   process_tile<T, EPI>(p, lds, tm, tn);
 }
 
-// Persistent grid for the plain and Lazy Pre-Norm GEMMs: gridDim.x workgroups
-// (at most one round of resident workgroups) walk the tile order with stride
-// gridDim.x.  After a tile's k-loop a workgroup issues the LDS transfers that
-// start its next tile, then scales and stores the finished tile, so the
-// memory latency of the next tile's first k-tiles hides behind the output
-// stores.
+// Persistent grid: gridDim.x workgroups (at most one round of resident
+// workgroups) walk the tile order with stride gridDim.x.  After a tile's
+// k-loop a workgroup computes the tile's row scales, issues the LDS transfers
+// that start its next tile, then scales and stores the finished tile, so the
+// next tile's first k-tiles stream in behind the epilogue.  All epilogues
+// whose tile holds what it needs (EPI_NONE, EPI_LAZY, EPI_ROW_*).
 template <class T, int EPI>
 __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
   static_assert(T::STG_OWN, "persistent tiles need their own output staging");
@@ -761,6 +796,8 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     issue_prologue<T>(p, lds0, tm * T::BM, tn * T::BN, tid);
   }
   for (int t = first; t < total; t += G) {
+    // opaque thread id: keeps lane-dependent addresses from being hoisted
+    // out of the tile loop (where they would be spilled)
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = tid >> 6;
@@ -768,20 +805,21 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     int tm, tn;
     grouped_tile(t, p.tiles_m, p.tiles_n, 4, tm, tn);
     const int m_base = tm * T::BM, n_base = tn * T::BN;
+    const int ax = (EPI == EPI_LAZY && lazy_split<T>()) ? wn : 0;
     f32x4 acc[T::FM][T::FN];
     float ss[T::FM];
     mainloop<T, EPI == EPI_LAZY>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, t != first);
+    Affine<T> aff;
+    if constexpr (EPI == EPI_ROW_RMS || EPI == EPI_ROW_LN)
+      load_affine<T>(p, n_base, wn, lane, aff);
     float mean[T::FM], rstd[T::FM];
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i) { mean[i] = 0.f; rstd[i] = 1.f; }
-    const int ax = (EPI == EPI_LAZY && lazy_split<T>()) ? wn : 0;
-    if constexpr (EPI == EPI_LAZY) lazy_rstd<T>(p, ss, rstd, lds, m_base, tn, wm, wn, lane, ax);
+    tile_scale<T, EPI>(p, acc, ss, lds, m_base, n_base, tn, wm, wn, lane, ax, mean, rstd);
     if (t + G < total) {
       int tm2, tn2;
       grouped_tile(t + G, p.tiles_m, p.tiles_n, 4, tm2, tn2);
       issue_prologue<T>(p, lds0, tm2 * T::BM, tn2 * T::BN, tid);
     }
-    apply_store<T, false>(p, acc, mean, rstd, false, lds, m_base, n_base, wave, wm, wn, lane, ax);
+    tile_store<T, EPI>(p, acc, mean, rstd, aff, lds, m_base, n_base, wave, wm, wn, lane, ax);
   }
 }
 
@@ -966,6 +1004,8 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
     float ss[T::FM];
     mainloop<T, false>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, it > 0);
     xwg_publish<T, LN>(p, acc, lds, tm, tn, tid, tag);
+    Affine<T> aff;
+    load_affine<T>(p, n_base, wn, lane, aff);
     if (tm + R < p.tiles_m) issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid);
     xwg_merge_rows<T, LN>(p, tm, tn, tid, tag);
     // step 5: (mean, rstd) of this wave's rows
@@ -977,7 +1017,7 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
       mean[i] = __uint_as_float(v[0]);
       rstd[i] = __uint_as_float(v[2]);
     }
-    apply_store<T, true>(p, acc, mean, rstd, LN, lds, m_base, n_base, wave, wm, wn, lane);
+    apply_store<T, true>(p, acc, mean, rstd, LN, aff, lds, m_base, n_base, wave, wm, wn, lane);
   }
   // the last workgroup to finish advances the call counter (every workgroup
   // read it at its start)
