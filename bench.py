@@ -8,7 +8,11 @@ synthetic bf16 inputs (seeded, see workloads/).  The default workload is the
 GEMM + LayerNorm epilogue case (A 65536x512 @ B 512x128, N = 128: the
 single-workgroup row tile).  Inputs sit in HBM before the timed region;
 several input/output copies are rotated so that the 256 MB Infinity Cache
-cannot serve a step from the previous step's data.
+cannot serve a step from the previous step's data.  The fused call and the
+unfused baseline (ng_gemm, ng_norm, and the pair) are timed round-robin over
+three rounds of W warm-up + K timed launches each, and each reports its
+median round, so that the cold start of a process is not charged to whichever
+callable happens to be timed first.
 
 Printed: one JSON line with the fused kernel's throughput (TFLOP/s of the GEMM,
 2*M*N*K per step), its share of the bf16 MFMA peak, the share of standalone
@@ -34,6 +38,7 @@ import workloads  # noqa: E402
 
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+ROUNDS = 3  # round-robin timing rounds per callable (median reported)
 RIDGE_FLOP_PER_BYTE = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 DEFAULT_WORKLOAD = workloads.WORKLOADS[1].name
 ROTATE_BYTES = 768 << 20     # input+output copies rotated per step exceed this
@@ -316,11 +321,25 @@ def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: f
     import numpy as np
     torch_mod = __import__("torch")
     b = Bench(w)
-    # headline: the fused kernel, steps timed with a sync on both sides
-    per, wall_ms, t_fused = b.time_launches(b.fused, steps, warmup)
-    _, _, t_gemm = b.time_launches(b.gemm_only, steps, warmup)
-    _, _, t_norm = b.time_launches(b.norm_only, steps, warmup)
-    _, _, t_pair = b.time_launches(b.pair, steps, warmup)
+    # The fused kernel and the unfused baseline are timed round-robin over
+    # ROUNDS rounds (each: `warmup` untimed launches, then `steps` timed ones
+    # with a sync on both sides); each callable reports its median round.  The
+    # first round of a process runs on a cold GPU (clocks, TLBs) and would
+    # otherwise penalize whichever callable is timed first.
+    rounds = {"fused": [], "gemm": [], "norm": [], "pair": []}
+    fns = {"fused": b.fused, "gemm": b.gemm_only, "norm": b.norm_only, "pair": b.pair}
+    for _ in range(ROUNDS):
+        for k, fn in fns.items():
+            rounds[k].append(b.time_launches(fn, steps, warmup))
+
+    def median_round(k):
+        rs = sorted(rounds[k], key=lambda r: r[2])
+        return rs[len(rs) // 2]
+
+    per, wall_ms, t_fused = median_round("fused")
+    t_gemm = median_round("gemm")[2]
+    t_norm = median_round("norm")[2]
+    t_pair = median_round("pair")[2]
     flops = float(w.flops)
     tflops = flops * steps / (wall_ms * 1e-3) / 1e12
     kern_tflops = flops / (t_fused * 1e-3) / 1e12
