@@ -83,7 +83,12 @@ int ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t
  * ng_workspace_bytes(NG_OP_GEMM_RMSNORM, M, N, K) bytes (0 means none needed),
  * be 256-byte aligned and be zero-filled before its first use (see
  * ng_workspace_reset); calls leave it ready for the next call.  One workspace
- * must not be used by two calls that may run concurrently.
+ * must not be used by two calls that may run concurrently.  Wide rows run a
+ * grid of at most as many workgroups as the device holds at once, whose
+ * workgroups wait for each other: two such calls must not run concurrently
+ * on one device (e.g. on two streams).  If they do, a wait may give up after
+ * about a second; ng_workspace_status then reports NG_ERR_TIMEOUT and the
+ * output of that call is undefined.
  * gamma: bf16 [N] or NULL.  rstd_out: float32 [M] or NULL.
  */
 int ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,

@@ -826,8 +826,8 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // Cross-workgroup row norm (rows wider than one tile).
 //
-// Persistent grid of R * tiles_n workgroups, all co-resident (cooperative
-// launch).  Round `it` covers the complete row blocks it*R .. it*R+R-1, one
+// Persistent grid of R * tiles_n workgroups, no more than the device holds
+// at once.  Round `it` covers the complete row blocks it*R .. it*R+R-1, one
 // column tile per workgroup.  For its tile a workgroup
 //   1. runs the k-loop;
 //   2. reduces its slice of every row from the fp32 accumulators and
@@ -839,10 +839,13 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
 //   5. reads (mean, rstd) of all BM rows, normalizes the accumulators still
 //      held in registers and stores the tile once.
 // Steps 4 and 5 poll until the entries carry the call's tag.  Every wait
-// points at workgroups of the same round, which are all resident, so the
-// grid cannot deadlock; the bounded polls are a guard, reported through the
-// error word.  Entries are written and read with agent-scope (sc1) accesses,
-// which bypass the per-XCD L2.
+// points at workgroups of the same round.  The grid fits the device, so once
+// other work on the device drains all of its workgroups are resident and
+// every wait ends; the polls are bounded (about a second) and a wait that
+// gives up raises the error word, so a call that overlaps another such grid
+// on the same device reports an error instead of hanging.  Entries are
+// written and read with agent-scope (sc1) accesses, which bypass the per-XCD
+// L2.
 
 // sc1 buffer views of the row block's partials and final statistics.
 template <class T>
