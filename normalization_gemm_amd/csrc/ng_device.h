@@ -42,18 +42,6 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Sum of squares of bf16 pair D (elements 2D, 2D+1) of a 16-byte fragment,
-// added to acc.  Widening to fp32 is exact (bf16 is the upper half of an
-// fp32), and so is each square in the fp32 FMA.  Plain VALU ops are used on
-// purpose: measured on gfx950, they co-issue with MFMAs at no cost, while
-// v_dot2_f32_bf16 competes with the MFMAs and slows the k-loop.
-__device__ __forceinline__ float sumsq_pair(u32x4 v, int d, float acc) {
-  const uint32_t w = v[d];
-  const float lo = __uint_as_float(w << 16);
-  const float hi = __uint_as_float(w & 0xffff0000u);
-  return fmaf(lo, lo, fmaf(hi, hi, acc));
-}
-
 __device__ __forceinline__ lds_char* lds_base(void* smem) { return (lds_char*)smem; }
 
 // 16-byte LDS access at a byte offset.
