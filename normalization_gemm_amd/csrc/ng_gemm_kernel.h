@@ -319,7 +319,9 @@ __device__ __forceinline__ void lazy_gram(int q, const Frags<T>& cur,
 // fetch stale but in-bounds LDS data that is never used: one code path keeps
 // the accumulators in place.)  For Lazy Pre-Norm the Gram MFMAs of the A
 // fragments join the sequence.
-template <class T, bool LAZY>
+// DM: 0 = issue the transfers when dma_on, 1 = always, 2 = never (the last
+// two make the choice at compile time, without a branch per transfer).
+template <class T, bool LAZY, int DM = 0>
 __device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN],
                                         f32x4 (&gram)[lazy_slots<T>()],
                                         const Frags<T>& cur, Frags<T>& nxt, lds_char* lds,
@@ -340,7 +342,7 @@ __device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN],
       rd.read(nxt, r, lds, rd_st, rd_st + T::A_BYTES, rd_kk);
 #pragma unroll
     for (int d = (q * ND) / NM; d < ((q + 1) * ND) / NM; ++d)
-      if (dma_on) dma.issue(p, m_base, n_base, dma_kt, dma_st, d);
+      if (DM == 1 || (DM == 0 && dma_on)) dma.issue(p, m_base, n_base, dma_kt, dma_st, d);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -425,18 +427,38 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   for (int r = 0; r < NR; ++r) rd.read(f0, r, lds, 0, T::A_BYTES, 0);
 
   int cur_s = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int nxt_s = cur_s + 1 == T::STAGES ? 0 : cur_s + 1;
-    const uint32_t cur = (uint32_t)cur_s * T::STAGE;
-    const uint32_t nxt = (uint32_t)nxt_s * T::STAGE;
-    substep<T, LAZY>(acc, gram, f0, f1, lds, rd, cur, 1, dma, false, p, m_base, n_base, 0, 0);
-    // k-tile kt+1 must have landed; k-tiles kt+2 .. kt+STAGES-1 may still fly
-    // (and, while kt+1 is a prologue k-tile, the caller's stores after them)
+  int kt = 0;
+  // k-tile kt+1 must have landed; k-tiles kt+2 .. kt+STAGES-1 may still fly
+  // (and, while kt+1 is a prologue k-tile, the caller's stores after them)
+  auto wait_next = [&](int kt) {
     if (kt + 1 < nk) {
       const int after = min(nk - 1, kt + T::STAGES - 1) - (kt + 1);
       if (stores_after && kt + 1 < T::STAGES) wait_ktile<ND, T::STAGES, T::C_STORES>(after);
       else wait_ktile<ND, T::STAGES>(after);
     }
+  };
+  if constexpr (!LAZY) {
+    // steady state, peeled: every k-tile refills its stage, with no branch per
+    // transfer (for Lazy Pre-Norm the second copy of the loop body costs
+    // registers that it does not have to spare)
+    for (; kt + T::STAGES < nk; ++kt) {
+      const int nxt_s = cur_s + 1 == T::STAGES ? 0 : cur_s + 1;
+      const uint32_t cur = (uint32_t)cur_s * T::STAGE;
+      const uint32_t nxt = (uint32_t)nxt_s * T::STAGE;
+      substep<T, LAZY, 2>(acc, gram, f0, f1, lds, rd, cur, 1, dma, false, p, m_base, n_base, 0, 0);
+      wait_next(kt);
+      __syncthreads();
+      substep<T, LAZY, 1>(acc, gram, f1, f0, lds, rd, nxt, 0, dma, true, p, m_base, n_base,
+                          kt + T::STAGES, lds0 + cur);
+      cur_s = nxt_s;
+    }
+  }
+  for (; kt < nk; ++kt) {
+    const int nxt_s = cur_s + 1 == T::STAGES ? 0 : cur_s + 1;
+    const uint32_t cur = (uint32_t)cur_s * T::STAGE;
+    const uint32_t nxt = (uint32_t)nxt_s * T::STAGE;
+    substep<T, LAZY, 2>(acc, gram, f0, f1, lds, rd, cur, 1, dma, false, p, m_base, n_base, 0, 0);
+    wait_next(kt);
     __syncthreads();
     // stage cur is free now: refill it with k-tile kt+STAGES
     substep<T, LAZY>(acc, gram, f1, f0, lds, rd, nxt, 0, dma, kt + T::STAGES < nk, p, m_base,
