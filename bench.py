@@ -10,7 +10,7 @@ single-workgroup row tile).  Inputs sit in HBM before the timed region;
 several input/output copies are rotated so that the 256 MB Infinity Cache
 cannot serve a step from the previous step's data.  The fused call and the
 unfused baseline (ng_gemm, ng_norm, and the pair) are timed round-robin over
-three rounds of W warm-up + K timed launches each, and each reports its
+five rounds of W warm-up + K timed launches each, and each reports its
 median round, so that the cold start of a process is not charged to whichever
 callable happens to be timed first.
 
@@ -38,7 +38,7 @@ import workloads  # noqa: E402
 
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
-ROUNDS = 3  # round-robin timing rounds per callable (median reported)
+ROUNDS = 5  # round-robin timing rounds per callable (median reported)
 RIDGE_FLOP_PER_BYTE = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 DEFAULT_WORKLOAD = workloads.WORKLOADS[1].name
 ROTATE_BYTES = 768 << 20     # input+output copies rotated per step exceed this
