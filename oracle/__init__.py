@@ -16,6 +16,7 @@ from .normgemm_oracle import (  # noqa: F401
     rms_norm_rows,
     layer_norm_rows,
     rmsnorm_gemm_lazy,
+    rmsnorm_gemm_lazy_affine,
     gemm_rmsnorm,
     gemm_layernorm,
     norm,

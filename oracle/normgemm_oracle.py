@@ -113,6 +113,25 @@ def rmsnorm_gemm_lazy(A, B, eps: float) -> Tuple[np.ndarray, np.ndarray]:
     return A_hat @ _f64(B), rstd
 
 
+def rmsnorm_gemm_lazy_affine(A, B, eps: float, gamma=None, beta=None
+                             ) -> Tuple[np.ndarray, np.ndarray]:
+    """C = (rmsnorm(A) * gamma + beta) @ B: pre-RMSNorm with per-column affine
+    (gamma, beta of length K), then the product.
+
+    The "Lazy Pre-Norm" section states that the row-scale trick does not hold
+    with an elementwise affine, which scales columns of A; "RMSNorm fusion on
+    Ascend", section 6.4, notes that for inference gamma is fixed and can be
+    merged into the following matmul's weights ahead of time.  The oracle
+    computes the definition as written: normalize each row of A over its K
+    elements, apply gamma and beta per column, then multiply by B (no
+    folding).  Returns (C, rstd) with rstd per row of A.
+    """
+    Y, rstd = rms_norm_rows(A, eps, gamma)
+    if beta is not None:
+        Y = Y + _f64(beta)[None, :]
+    return Y @ _f64(B), rstd
+
+
 def gemm_rmsnorm(A, B, eps: float, gamma=None) -> Tuple[np.ndarray, np.ndarray]:
     """Y = RMSNorm(A @ B) over each full output row (H = N), optional gamma.
 

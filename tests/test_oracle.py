@@ -71,6 +71,9 @@ def test_hand_worked_examples(case):
     if case["op"] == "rmsnorm_gemm_lazy":
         C, rstd = oracle.rmsnorm_gemm_lazy(A, B, eps)
         mean = None
+    elif case["op"] == "rmsnorm_gemm_lazy_affine":
+        C, rstd = oracle.rmsnorm_gemm_lazy_affine(A, B, eps, gamma, beta)
+        mean = None
     elif case["op"] == "gemm_rmsnorm":
         C, rstd = oracle.gemm_rmsnorm(A, B, eps, gamma)
         mean = None
@@ -215,6 +218,39 @@ def test_lazy_is_not_prenorm_with_columnwise_gamma():
     Yg, _, _ = oracle.norm(x.A, "rms", 1e-6, gamma=x.gamma)
     C_affine = oracle.gemm(Yg, x.B)
     assert oracle.rel_err(C_lazy, C_affine) > 0.05
+
+
+def test_lazy_affine_without_affine_is_lazy():
+    # gamma = 1, beta = 0 given explicitly: the affine path reduces to the
+    # plain Lazy Pre-Norm product
+    rng = np.random.default_rng(31)
+    A = rng.standard_normal((5, 7)) * 3.0
+    B = rng.standard_normal((7, 4))
+    C1, r1 = oracle.rmsnorm_gemm_lazy_affine(A, B, 1e-6, np.ones(7), np.zeros(7))
+    C0, r0 = oracle.rmsnorm_gemm_lazy(A, B, 1e-6)
+    np.testing.assert_allclose(C1, C0, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(r1, r0, rtol=1e-15)
+
+
+def test_lazy_affine_folds_into_weights():
+    # (rmsnorm(A) * gamma + beta) @ B == rstd * (A @ (diag(gamma) B)) + beta @ B:
+    # gamma scales the K rows of B, beta becomes a per-column bias (the
+    # folding the weight-merge passage describes); shapes with K != N so that
+    # a gamma applied along the wrong axis could not pass
+    rng = np.random.default_rng(32)
+    for (M, K, N) in [(3, 5, 7), (6, 4, 2)]:
+        A = rng.standard_normal((M, K)) * rng.uniform(0.1, 10.0, size=(M, 1))
+        B = rng.standard_normal((K, N))
+        g = rng.uniform(0.5, 2.0, size=K)
+        b = rng.standard_normal(K)
+        C, rstd = oracle.rmsnorm_gemm_lazy_affine(A, B, 1e-5, g, b)
+        ms = np.mean(A * A, axis=1)
+        r = 1.0 / np.sqrt(ms + 1e-5)
+        folded = r[:, None] * (A @ (g[:, None] * B)) + (b @ B)[None, :]
+        np.testing.assert_allclose(C, folded, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(rstd, r, rtol=1e-14)
+        wrong = r[:, None] * (A @ B) * np.resize(g, N)[None, :] + (b @ B)[None, :]
+        assert np.max(np.abs(C - wrong)) > 1e-2
 
 
 def test_lazy_is_not_layernorm_prenorm():
