@@ -17,6 +17,7 @@ from .normgemm_oracle import (  # noqa: F401
     layer_norm_rows,
     rmsnorm_gemm_lazy,
     rmsnorm_gemm_lazy_affine,
+    lazy_fold_affine,
     gemm_rmsnorm,
     gemm_layernorm,
     norm,

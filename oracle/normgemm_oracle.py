@@ -132,6 +132,20 @@ def rmsnorm_gemm_lazy_affine(A, B, eps: float, gamma=None, beta=None
     return Y @ _f64(B), rstd
 
 
+def lazy_fold_affine(B, gamma=None, beta=None) -> Tuple[np.ndarray, np.ndarray]:
+    """The weight fold of the Lazy Pre-Norm affine form, in float64:
+    B_folded = diag(gamma) B (row k of B scaled by gamma[k]) and
+    bias = beta^T B (one value per output column).  With these,
+    (rmsnorm(A) * gamma + beta) @ B = rstd(A) * (A @ B_folded) + bias
+    ("RMSNorm fusion on Ascend", section 6.4: gamma merged into the weights).
+    """
+    Bf = _f64(B)
+    K, N = Bf.shape
+    g = np.ones(K) if gamma is None else _f64(gamma)
+    b = np.zeros(K) if beta is None else _f64(beta)
+    return g[:, None] * Bf, b @ Bf
+
+
 def gemm_rmsnorm(A, B, eps: float, gamma=None) -> Tuple[np.ndarray, np.ndarray]:
     """Y = RMSNorm(A @ B) over each full output row (H = N), optional gamma.
 
@@ -153,12 +167,16 @@ def gemm_layernorm(A, B, eps: float, gamma=None, beta=None
 def norm(X, kind: str, eps: float, gamma=None, beta=None):
     """Standalone row norm of X: kind 'rms' or 'layer'.
 
+    For RMSNorm a beta, when given, is added after gamma as in the LayerNorm
+    affine ("RMSNorm fusion on Ascend", section 1.1: gamma * x_norm + beta); it
+    is the unfused form of a pre-norm with a full elementwise affine, the case
+    the "Lazy Pre-Norm" section names as outside the row-scale identity.
     Returns (Y, mean_or_None, rstd).
     """
     if kind == "rms":
-        if beta is not None:
-            raise ValueError("RMSNorm has no beta")
         Y, rstd = rms_norm_rows(X, eps, gamma)
+        if beta is not None:
+            Y = Y + _f64(beta)[None, :]
         return Y, None, rstd
     if kind == "layer":
         return layer_norm_rows(X, eps, gamma, beta)

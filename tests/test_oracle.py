@@ -248,9 +248,29 @@ def test_lazy_affine_folds_into_weights():
         r = 1.0 / np.sqrt(ms + 1e-5)
         folded = r[:, None] * (A @ (g[:, None] * B)) + (b @ B)[None, :]
         np.testing.assert_allclose(C, folded, rtol=1e-12, atol=1e-12)
+        # the oracle's fold helper gives the same B_folded and bias
+        Bf, bias = oracle.lazy_fold_affine(B, g, b)
+        np.testing.assert_allclose(r[:, None] * (A @ Bf) + bias[None, :], C, rtol=1e-12,
+                                   atol=1e-12)
         np.testing.assert_allclose(rstd, r, rtol=1e-14)
         wrong = r[:, None] * (A @ B) * np.resize(g, N)[None, :] + (b @ B)[None, :]
         assert np.max(np.abs(C - wrong)) > 1e-2
+
+
+def test_lazy_affine_is_affine_rmsnorm_then_matmul():
+    # the Lazy-affine definition agrees with the standalone RMSNorm (gamma,
+    # beta) followed by the product, and the RMSNorm beta is a plain column shift
+    rng = np.random.default_rng(33)
+    A = rng.standard_normal((4, 6)) * 2.0
+    B = rng.standard_normal((6, 3))
+    g = rng.uniform(0.5, 2.0, size=6)
+    b = rng.standard_normal(6)
+    Y, _, r = oracle.norm(A, "rms", 1e-6, g, b)
+    Y0, _, _ = oracle.norm(A, "rms", 1e-6, g)
+    np.testing.assert_allclose(Y - Y0, np.broadcast_to(b, Y.shape), rtol=0, atol=1e-14)
+    C, rstd = oracle.rmsnorm_gemm_lazy_affine(A, B, 1e-6, g, b)
+    np.testing.assert_allclose(C, Y @ B, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(rstd, r, rtol=1e-15)
 
 
 def test_lazy_is_not_layernorm_prenorm():
