@@ -72,6 +72,34 @@ int ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t
                          int64_t K, int b_layout, float eps, float* rstd_out, void* stream);
 
 /*
+ * Lazy Pre-Norm with a per-column affine on the normalized A (gamma, beta of
+ * length K):  C = (rmsnorm(A) * gamma + beta) @ B.
+ * ("Free normalization fusion", section "Lazy Pre-Norm": the affine scales
+ * columns of A, so the row-scale identity does not cover it directly; "RMSNorm
+ * fusion on Ascend", section 6.4: at inference gamma is fixed and can be
+ * merged into the next matmul's weights ahead of time.)  Two steps:
+ *
+ * ng_lazy_fold_affine, once per weight: B_folded = diag(gamma) B (row k of B,
+ * as [K, N], scaled by gamma[k], rounded to bf16) in B's layout, and
+ * bias[n] = sum_k beta[k] B[k,n] in fp32.  gamma NULL means 1; beta NULL means
+ * 0 (bias is then all zero); bias NULL skips it.  B_folded may equal B (the
+ * bias is computed from B first, on the same stream).  B, B_folded, gamma,
+ * beta 16-byte aligned; bias 4-byte aligned.  K and N multiples of 8.
+ *
+ * ng_rmsnorm_gemm_lazy_affine, per call: C = rstd(A) * (A @ B_folded) + bias,
+ * which equals the definition above (rstd from the row of A as in
+ * ng_rmsnorm_gemm_lazy).  bias: fp32 [N], 16-byte aligned, or NULL (no bias).
+ * rstd_out: float32 [M] or NULL.  Needs no workspace.
+ */
+int ng_lazy_fold_affine(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
+                        ng_bf16* B_folded, float* bias, int64_t K, int64_t N, int b_layout,
+                        void* stream);
+
+int ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded, const float* bias,
+                                ng_bf16* C, int64_t M, int64_t N, int64_t K, int b_layout,
+                                float eps, float* rstd_out, void* stream);
+
+/*
  * GEMM with an RMSNorm epilogue over each full output row (H = N):
  *   X = A @ B;  rstd[m] = 1 / sqrt((1/N) sum_n X[m,n]^2 + eps);
  *   C[m,n] = X[m,n] * rstd[m] * gamma[n]        (gamma NULL means 1)
@@ -121,10 +149,11 @@ int ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N
 /*
  * Standalone row norm, the other half of the unfused baseline.  X, Y: [rows,
  * cols] bf16 (Y may equal X for an in-place norm).  kind NG_NORM_RMS or
- * NG_NORM_LAYER with the formulas above (H = cols).  beta must be NULL for
- * RMS.  cols must be a multiple of 8 and at most 65536 (else
- * NG_ERR_UNSUPPORTED).  mean_out (LayerNorm only) and rstd_out: float32
- * [rows] or NULL.
+ * NG_NORM_LAYER with the formulas above (H = cols); for RMS a beta, when
+ * given, is added after gamma (y = x * rstd * gamma + beta, the unfused form
+ * of a pre-norm with a full affine).  cols must be a multiple of 8 and at
+ * most 65536 (else NG_ERR_UNSUPPORTED).  mean_out (LayerNorm only) and
+ * rstd_out: float32 [rows] or NULL.
  */
 int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* Y,
             int64_t rows, int64_t cols, int kind, float eps, float* mean_out, float* rstd_out,

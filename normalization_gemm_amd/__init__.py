@@ -18,13 +18,14 @@ from . import _lib
 from ._lib import (  # noqa: F401
     NG_B_KN, NG_B_NK, NG_NORM_LAYER, NG_NORM_RMS, NG_OK,
     NG_OP_GEMM, NG_OP_GEMM_LAYERNORM, NG_OP_GEMM_RMSNORM, NG_OP_NORM, NG_OP_RMSNORM_GEMM_LAZY,
-    ng_gemm, ng_gemm_layernorm, ng_gemm_rmsnorm, ng_last_error, ng_norm, ng_rmsnorm_gemm_lazy,
-    ng_status_string, ng_workspace_bytes, ng_workspace_reset, ng_workspace_status,
+    ng_gemm, ng_gemm_layernorm, ng_gemm_rmsnorm, ng_last_error, ng_lazy_fold_affine, ng_norm,
+    ng_rmsnorm_gemm_lazy, ng_rmsnorm_gemm_lazy_affine, ng_status_string, ng_workspace_bytes,
+    ng_workspace_reset, ng_workspace_status,
 )
 
 __all__ = [
-    "NormGemmError", "rmsnorm_gemm_lazy", "gemm_rmsnorm", "gemm_layernorm", "gemm", "norm",
-    "Workspace", "library_path",
+    "NormGemmError", "rmsnorm_gemm_lazy", "lazy_fold_affine", "rmsnorm_gemm_lazy_affine",
+    "gemm_rmsnorm", "gemm_layernorm", "gemm", "norm", "Workspace", "library_path",
 ]
 
 
@@ -142,6 +143,48 @@ def rmsnorm_gemm_lazy(A, B, *, eps: float = 1e-6, b_layout="kn", out=None, rstd_
     _dev_bf16(C, "out")
     _check(ng_rmsnorm_gemm_lazy(_ptr(A), _ptr(B), _ptr(C), M, N, K, lay, float(eps),
                                 _ptr(rstd_out), _stream(stream)), "ng_rmsnorm_gemm_lazy")
+    return C
+
+
+def lazy_fold_affine(B, gamma=None, beta=None, *, b_layout="kn", out=None, bias_out=None,
+                     stream=None):
+    """Fold a pre-norm affine into the weights: returns (B_folded, bias) with
+    B_folded = diag(gamma) B (bf16, B's layout) and bias = beta^T B (fp32 [N])."""
+    torch = _torch()
+    _dev_bf16(B, "B")
+    lay = _layout(b_layout)
+    if B.dim() != 2:
+        raise ValueError("B must be 2-D")
+    K, N = B.shape if lay == NG_B_KN else (B.shape[1], B.shape[0])
+    if gamma is not None:
+        _dev_bf16(gamma, "gamma")
+    if beta is not None:
+        _dev_bf16(beta, "beta")
+    Bf = out if out is not None else torch.empty_like(B)
+    _dev_bf16(Bf, "out")
+    bias = bias_out if bias_out is not None else torch.empty(N, dtype=torch.float32,
+                                                             device=B.device)
+    _check(ng_lazy_fold_affine(_ptr(B), _ptr(gamma), _ptr(beta), _ptr(Bf), _ptr(bias), K, N, lay,
+                               _stream(stream)), "ng_lazy_fold_affine")
+    return Bf, bias
+
+
+def rmsnorm_gemm_lazy_affine(A, B_folded, bias=None, *, eps: float = 1e-6, b_layout="kn",
+                             out=None, rstd_out=None, stream=None):
+    """C = (rmsnorm(A) * gamma + beta) @ B from the folded weights of
+    lazy_fold_affine: rstd(A) * (A @ B_folded) + bias."""
+    torch = _torch()
+    _dev_bf16(A, "A"); _dev_bf16(B_folded, "B_folded")
+    lay = _layout(b_layout)
+    M, N, K = _shapes(A, B_folded, lay)
+    if bias is not None and (bias.dtype != torch.float32 or bias.device.type != "cuda"
+                             or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous float32 GPU tensor")
+    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _dev_bf16(C, "out")
+    _check(ng_rmsnorm_gemm_lazy_affine(_ptr(A), _ptr(B_folded), _ptr(bias), _ptr(C), M, N, K, lay,
+                                       float(eps), _ptr(rstd_out), _stream(stream)),
+           "ng_rmsnorm_gemm_lazy_affine")
     return C
 
 

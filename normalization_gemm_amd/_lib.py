@@ -40,6 +40,8 @@ _SIGNATURES = {
     "ng_rmsnorm_gemm_lazy": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P]),
     "ng_gemm_rmsnorm": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _SZ, _P]),
     "ng_gemm_layernorm": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P, _SZ, _P]),
+    "ng_lazy_fold_affine": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _P]),
+    "ng_rmsnorm_gemm_lazy_affine": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P]),
     "ng_gemm": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "ng_norm": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _F, _P, _P, _P]),
     "ng_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64]),
@@ -79,6 +81,15 @@ def _call(name, *args):
 
 def ng_rmsnorm_gemm_lazy(A, B, C, M, N, K, b_layout, eps, rstd_out, stream):
     return _call("ng_rmsnorm_gemm_lazy", A, B, C, M, N, K, b_layout, eps, rstd_out, stream)
+
+
+def ng_lazy_fold_affine(B, gamma, beta, B_folded, bias, K, N, b_layout, stream):
+    return _call("ng_lazy_fold_affine", B, gamma, beta, B_folded, bias, K, N, b_layout, stream)
+
+
+def ng_rmsnorm_gemm_lazy_affine(A, B_folded, bias, C, M, N, K, b_layout, eps, rstd_out, stream):
+    return _call("ng_rmsnorm_gemm_lazy_affine", A, B_folded, bias, C, M, N, K, b_layout, eps,
+                 rstd_out, stream)
 
 
 def ng_gemm_rmsnorm(A, B, gamma, C, M, N, K, b_layout, eps, rstd_out, workspace,

@@ -14,6 +14,7 @@
 #include "../../include/normgemm.h"
 #include "ng_gemm_kernel.h"
 #include "ng_norm_kernel.h"
+#include "ng_fold_kernel.h"
 
 namespace {
 
@@ -259,6 +260,79 @@ int ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t
             : launch_persistent<TLarge<false>, ng::EPI_LAZY>(p, s, "ng_rmsnorm_gemm_lazy");
 }
 
+int ng_lazy_fold_affine(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
+                        ng_bf16* B_folded, float* bias, int64_t K, int64_t N, int b_layout,
+                        void* stream) {
+  if (!B || !B_folded) return fail(NG_ERR_INVALID_ARG, "B and B_folded must be non-NULL");
+  if (!aligned(B, 16) || !aligned(B_folded, 16))
+    return fail(NG_ERR_INVALID_ARG, "B and B_folded must be 16-byte aligned");
+  if (K < 1 || N < 1 || K > kMaxDim || N > kMaxDim)
+    return fail(NG_ERR_INVALID_ARG, "need 1 <= K, N <= 2^24 (got K=%lld N=%lld)", (long long)K,
+                (long long)N);
+  if (b_layout != NG_B_KN && b_layout != NG_B_NK)
+    return fail(NG_ERR_INVALID_ARG, "b_layout must be NG_B_KN or NG_B_NK (got %d)", b_layout);
+  int st = check_vec(gamma, "gamma", 16);
+  if (!st) st = check_vec(beta, "beta", 16);
+  if (!st) st = check_vec(bias, "bias", 4);
+  if (st) return st;
+  if (N % 8 != 0 || K % 8 != 0)
+    return fail(NG_ERR_UNSUPPORTED, "N and K must be multiples of 8 (got N=%lld K=%lld)",
+                (long long)N, (long long)K);
+  if (K * N >= (int64_t(1) << 31) * 8)
+    return fail(NG_ERR_UNSUPPORTED, "B has more than 2^34 elements");
+  ng::FoldParams p{};
+  p.B = B;
+  p.gamma = gamma;
+  p.beta = beta;
+  p.B_folded = B_folded;
+  p.bias = bias;
+  p.K = K;
+  p.N = N;
+  p.nk = b_layout == NG_B_NK;
+  hipStream_t s = (hipStream_t)stream;
+  // the bias reads B before B_folded may overwrite it (same stream, in order)
+  if (bias) {
+    const unsigned grid = (unsigned)(p.nk ? (N + 3) / 4 : (N + 63) / 64);
+    hipLaunchKernelGGL(ng::fold_bias_kernel, dim3(grid), dim3(256), 0, s, p);
+    st = launched("ng_lazy_fold_affine (bias)");
+    if (st) return st;
+  }
+  const int64_t chunks = K * N / 8;
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(ng::fold_gamma_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return launched("ng_lazy_fold_affine");
+}
+
+int ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded, const float* bias,
+                                ng_bf16* C, int64_t M, int64_t N, int64_t K, int b_layout,
+                                float eps, float* rstd_out, void* stream) {
+  int st = check_gemm(A, B_folded, C, M, N, K, b_layout);
+  if (!st) st = check_eps(eps);
+  if (!st) st = check_vec(bias, "bias", 16);
+  if (!st) st = check_vec(rstd_out, "rstd_out", 4);
+  if (st) return st;
+  if (M == 0) return ok();
+  ng::GemmParams p = make_params(A, B_folded, C, M, N, K, eps);
+  p.rstd_out = rstd_out;
+  p.bias = bias;
+  hipStream_t s = (hipStream_t)stream;
+  const bool kn = b_layout == NG_B_KN;
+  const char* what = "ng_rmsnorm_gemm_lazy_affine";
+  if (!bias) {
+    if (N <= 128)
+      return kn ? launch_grid<TRow128<true>, ng::EPI_LAZY>(p, s, what)
+                : launch_grid<TRow128<false>, ng::EPI_LAZY>(p, s, what);
+    return kn ? launch_persistent<TLarge<true>, ng::EPI_LAZY>(p, s, what)
+              : launch_persistent<TLarge<false>, ng::EPI_LAZY>(p, s, what);
+  }
+  if (N <= 128)
+    return kn ? launch_grid<TRow128<true>, ng::EPI_LAZY_BIAS>(p, s, what)
+              : launch_grid<TRow128<false>, ng::EPI_LAZY_BIAS>(p, s, what);
+  return kn ? launch_persistent<TLarge<true>, ng::EPI_LAZY_BIAS>(p, s, what)
+            : launch_persistent<TLarge<false>, ng::EPI_LAZY_BIAS>(p, s, what);
+}
+
 int ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,
                     int64_t M, int64_t N, int64_t K, int b_layout, float eps, float* rstd_out,
                     void* workspace, size_t workspace_bytes, void* stream) {
@@ -299,8 +373,8 @@ int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16
     return fail(NG_ERR_INVALID_ARG, "need rows >= 0 and cols >= 1");
   if (kind != NG_NORM_RMS && kind != NG_NORM_LAYER)
     return fail(NG_ERR_INVALID_ARG, "kind must be NG_NORM_RMS or NG_NORM_LAYER");
-  if (kind == NG_NORM_RMS && (beta || mean_out))
-    return fail(NG_ERR_INVALID_ARG, "RMSNorm takes no beta and has no mean output");
+  if (kind == NG_NORM_RMS && mean_out)
+    return fail(NG_ERR_INVALID_ARG, "RMSNorm has no mean output");
   int st = check_eps(eps);
   if (!st) st = check_vec(gamma, "gamma", 16);
   if (!st) st = check_vec(beta, "beta", 16);

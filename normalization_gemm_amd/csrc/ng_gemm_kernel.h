@@ -3,6 +3,8 @@
 // One kernel template serves four epilogues:
 //   EPI_NONE      C = A @ B                               (unfused baseline GEMM)
 //   EPI_LAZY      C = (A @ B) * rstd(A)                   (Lazy Pre-Norm)
+//   EPI_LAZY_BIAS C = (A @ B') * rstd(A) + bias            (Lazy Pre-Norm with the
+//                 affine folded into the weights: B' = diag(gamma) B, bias = beta^T B)
 //   EPI_ROW_RMS / EPI_ROW_LN
 //                 C = norm(A @ B), whole row in one workgroup (N <= BN)
 //   cross-workgroup: C = norm(A @ B) for rows split over workgroups; per-row
@@ -40,7 +42,8 @@ namespace ng {
 
 constexpr int BK = 64;
 
-enum Epi { EPI_NONE = 0, EPI_LAZY = 1, EPI_ROW_RMS = 2, EPI_ROW_LN = 3 };
+enum Epi { EPI_NONE = 0, EPI_LAZY = 1, EPI_ROW_RMS = 2, EPI_ROW_LN = 3, EPI_LAZY_BIAS = 4 };
+constexpr bool epi_lazy(int e) { return e == EPI_LAZY || e == EPI_LAZY_BIAS; }
 enum NormKind { NORM_RMS = 0, NORM_LAYER = 1 };
 
 // Workspace layout of the cross-workgroup row norm (byte offsets).
@@ -75,6 +78,7 @@ struct GemmParams {
   uint16_t* C;
   const uint16_t* gamma;
   const uint16_t* beta;
+  const float* bias;  // EPI_LAZY_BIAS: fp32 [N]
   float* mean_out;
   float* rstd_out;
   char* ws;
@@ -572,19 +576,39 @@ __device__ __forceinline__ void load_affine(const GemmParams& p, int n_base, int
   }
 }
 
+// Per-column fp32 bias of a wave's columns: v[j] holds the 4 columns
+// 16j + 4(lane >> 4) .. +3 of the wave's slice (0 past N).
+template <class T>
+struct Bias {
+  f32x4 v[T::FN];
+};
+
+template <class T>
+__device__ __forceinline__ void load_bias(const GemmParams& p, int n_base, int wn, int lane,
+                                          Bias<T>& bias) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j) {
+    const int n = n_base + wn * T::WTN + 16 * j + 4 * g;
+    bias.v[j] = n < p.N ? *(const f32x4*)(p.bias + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
 // Scale/shift the accumulators by per-row (mean, rstd) and (AFFINE) the
-// per-column gamma/beta, round to bf16 and store the tile.  Each 16-row x
+// per-column gamma/beta, or (BIAS) add a per-column fp32 bias after the row
+// scale, round to bf16 and store the tile.  Each 16-row x
 // 64-column piece goes through the wave's LDS staging block so that every
 // global store writes whole 128-byte row segments (16 bytes per lane) instead
 // of 8-byte pieces of 16 rows.  Exactly T::C_STORES buffer stores per thread
 // are issued; rows past M and columns past N fall outside the buffer range
 // and are dropped.  Slot i of acc holds fragment i ^ a_xor.
-template <class T, bool AFFINE>
+template <class T, bool AFFINE, bool BIAS = false>
 __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
                                             const float (&mean)[T::FM], const float (&rstd)[T::FM],
-                                            bool use_mean, const Affine<T>& aff, lds_char* lds,
-                                            int m_base, int n_base, int wave, int wm, int wn,
-                                            int lane, int a_xor = 0) {
+                                            bool use_mean, const Affine<T>& aff,
+                                            const Bias<T>& bias, lds_char* lds, int m_base,
+                                            int n_base, int wave, int wm, int wn, int lane,
+                                            int a_xor = 0) {
   const int l16 = lane & 15, g = lane >> 4;
   const uint32_t stg = (uint32_t)T::STG_OFF + (uint32_t)wave * 2048u;
   // fragment writes: lane (l16, g) of fragment jj holds 4 columns = 8 bytes
@@ -615,6 +639,9 @@ __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&a
           y[1] = fmaf(fmaf(x[1], rstd[i], sh), bf16_hi(gw[jj][0]), bf16_hi(bw[jj][0]));
           y[2] = fmaf(fmaf(x[2], rstd[i], sh), bf16_lo(gw[jj][1]), bf16_lo(bw[jj][1]));
           y[3] = fmaf(fmaf(x[3], rstd[i], sh), bf16_hi(gw[jj][1]), bf16_hi(bw[jj][1]));
+        } else if constexpr (BIAS) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] = fmaf(x[r], rstd[i], bias.v[4 * q + jj][r]);
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) y[r] = fmaf(x[r], rstd[i], sh);
@@ -702,7 +729,7 @@ __device__ __forceinline__ void lazy_rstd(const GemmParams& p, const float (&ss)
 }
 
 // Per-row (mean, rstd) that the epilogue applies to a finished tile:
-// EPI_NONE (0, 1); EPI_LAZY (0, rstd of the row of A); EPI_ROW_* the row's
+// EPI_NONE (0, 1); EPI_LAZY* (0, rstd of the row of A); EPI_ROW_* the row's
 // statistics over the tile (which holds whole rows).  Also writes the
 // statistic outputs.  ax: slot permutation of the accumulators (lazy_split).
 template <class T, int EPI>
@@ -712,7 +739,7 @@ __device__ __forceinline__ void tile_scale(const GemmParams& p, const f32x4 (&ac
                                            float (&mean)[T::FM], float (&rstd)[T::FM]) {
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) { mean[i] = 0.f; rstd[i] = 1.f; }
-  if constexpr (EPI == EPI_LAZY) {
+  if constexpr (epi_lazy(EPI)) {
     lazy_rstd<T>(p, ss, rstd, lds, m_base, tn, wm, wn, lane, ax);
   } else if constexpr (EPI == EPI_ROW_RMS || EPI == EPI_ROW_LN) {
     const int l16 = lane & 15, g = lane >> 4;
@@ -742,11 +769,21 @@ __device__ __forceinline__ void tile_scale(const GemmParams& p, const f32x4 (&ac
 template <class T, int EPI>
 __device__ __forceinline__ void tile_store(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
                                            const float (&mean)[T::FM], const float (&rstd)[T::FM],
-                                           const Affine<T>& aff, lds_char* lds, int m_base,
-                                           int n_base, int wave, int wm, int wn, int lane, int ax) {
+                                           const Affine<T>& aff, const Bias<T>& bias, lds_char* lds,
+                                           int m_base, int n_base, int wave, int wm, int wn,
+                                           int lane, int ax) {
   constexpr bool ROW = EPI == EPI_ROW_RMS || EPI == EPI_ROW_LN;
-  apply_store<T, ROW>(p, acc, mean, rstd, EPI == EPI_ROW_LN, aff, lds, m_base, n_base, wave, wm,
-                      wn, lane, ax);
+  apply_store<T, ROW, EPI == EPI_LAZY_BIAS>(p, acc, mean, rstd, EPI == EPI_ROW_LN, aff, bias, lds,
+                                            m_base, n_base, wave, wm, wn, lane, ax);
+}
+
+// Per-column data the epilogue needs, loaded before the row statistics so
+// that its latency overlaps them.
+template <class T, int EPI>
+__device__ __forceinline__ void load_columns(const GemmParams& p, int n_base, int wn, int lane,
+                                             Affine<T>& aff, Bias<T>& bias) {
+  if constexpr (EPI == EPI_ROW_RMS || EPI == EPI_ROW_LN) load_affine<T>(p, n_base, wn, lane, aff);
+  if constexpr (EPI == EPI_LAZY_BIAS) load_bias<T>(p, n_base, wn, lane, bias);
 }
 
 template <class T, int EPI>
@@ -755,15 +792,16 @@ __device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds,
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int m_base = tm * T::BM, n_base = tn * T::BN;
-  const int ax = (EPI == EPI_LAZY && lazy_split<T>()) ? wn : 0;
+  const int ax = (epi_lazy(EPI) && lazy_split<T>()) ? wn : 0;
   f32x4 acc[T::FM][T::FN];
   float ss[T::FM];
-  mainloop<T, EPI == EPI_LAZY>(p, acc, ss, lds, lds_addr_of(lds), m_base, n_base, tid);
+  mainloop<T, epi_lazy(EPI)>(p, acc, ss, lds, lds_addr_of(lds), m_base, n_base, tid);
   Affine<T> aff;
-  if constexpr (EPI == EPI_ROW_RMS || EPI == EPI_ROW_LN) load_affine<T>(p, n_base, wn, lane, aff);
+  Bias<T> bias;
+  load_columns<T, EPI>(p, n_base, wn, lane, aff, bias);
   float mean[T::FM], rstd[T::FM];
   tile_scale<T, EPI>(p, acc, ss, lds, m_base, n_base, tn, wm, wn, lane, ax, mean, rstd);
-  tile_store<T, EPI>(p, acc, mean, rstd, aff, lds, m_base, n_base, wave, wm, wn, lane, ax);
+  tile_store<T, EPI>(p, acc, mean, rstd, aff, bias, lds, m_base, n_base, wave, wm, wn, lane, ax);
 }
 
 // Tile order shared by the grids: tiles grouped 4 tile-rows high, column-major
@@ -804,7 +842,7 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(GemmParams p) {
 // k-loop a workgroup computes the tile's row scales, issues the LDS transfers
 // that start its next tile, then scales and stores the finished tile, so the
 // next tile's first k-tiles stream in behind the epilogue.  All epilogues
-// whose tile holds what it needs (EPI_NONE, EPI_LAZY, EPI_ROW_*).
+// whose tile holds what it needs (EPI_NONE, EPI_LAZY*, EPI_ROW_*).
 template <class T, int EPI>
 __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
   static_assert(T::STG_OWN, "persistent tiles need their own output staging");
@@ -831,13 +869,13 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     int tm, tn;
     grouped_tile(t, p.tiles_m, p.tiles_n, 4, tm, tn);
     const int m_base = tm * T::BM, n_base = tn * T::BN;
-    const int ax = (EPI == EPI_LAZY && lazy_split<T>()) ? wn : 0;
+    const int ax = (epi_lazy(EPI) && lazy_split<T>()) ? wn : 0;
     f32x4 acc[T::FM][T::FN];
     float ss[T::FM];
-    mainloop<T, EPI == EPI_LAZY>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, t != first);
+    mainloop<T, epi_lazy(EPI)>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, t != first);
     Affine<T> aff;
-    if constexpr (EPI == EPI_ROW_RMS || EPI == EPI_ROW_LN)
-      load_affine<T>(p, n_base, wn, lane, aff);
+    Bias<T> bias;
+    load_columns<T, EPI>(p, n_base, wn, lane, aff, bias);
     float mean[T::FM], rstd[T::FM];
     tile_scale<T, EPI>(p, acc, ss, lds, m_base, n_base, tn, wm, wn, lane, ax, mean, rstd);
     if (t + G < total) {
@@ -845,7 +883,8 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
       grouped_tile(t + G, p.tiles_m, p.tiles_n, 4, tm2, tn2);
       issue_prologue<T>(p, lds0, tm2 * T::BM, tn2 * T::BN, tid);
     }
-    tile_store<T, EPI>(p, acc, mean, rstd, aff, lds, m_base, n_base, wave, wm, wn, lane, ax);
+    tile_store<T, EPI>(p, acc, mean, rstd, aff, bias, lds, m_base, n_base, wave, wm, wn, lane,
+                       ax);
   }
 }
 
@@ -1046,7 +1085,9 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
       mean[i] = __uint_as_float(v[0]);
       rstd[i] = __uint_as_float(v[2]);
     }
-    apply_store<T, true>(p, acc, mean, rstd, LN, aff, lds, m_base, n_base, wave, wm, wn, lane);
+    Bias<T> no_bias;
+    apply_store<T, true>(p, acc, mean, rstd, LN, aff, no_bias, lds, m_base, n_base, wave, wm, wn,
+                         lane);
   }
   // the last workgroup to finish advances the call counter (every workgroup
   // read it at its start)

@@ -31,7 +31,8 @@ def header_functions():
 def test_header_declares_expected_entry_points():
     names = header_functions()
     for n in ("ng_rmsnorm_gemm_lazy", "ng_gemm_layernorm", "ng_gemm_rmsnorm", "ng_gemm",
-              "ng_norm", "ng_workspace_bytes"):
+              "ng_norm", "ng_workspace_bytes", "ng_lazy_fold_affine",
+              "ng_rmsnorm_gemm_lazy_affine"):
         assert n in names
 
 
@@ -128,11 +129,32 @@ def test_norm_argument_checks():
     assert f(None, None, None, P2, 4, 64, 0, 1e-6, None, None, None) == 1
     assert f(P, None, None, BAD, 4, 64, 0, 1e-6, None, None, None) == 1
     assert f(P, None, None, P2, 4, 64, 7, 1e-6, None, None, None) == 1
-    assert f(P, None, P3, P2, 4, 64, 0, 1e-6, None, None, None) == 1   # beta with RMS
+    assert f(P, None, None, P2, 4, 64, 0, 1e-6, P3, None, None) == 1   # mean_out with RMS
     assert f(P, None, None, P2, 4, 64, 0, 1e-6, P3, None, None) == 1   # mean_out with RMS
     assert f(P, None, None, P2, 4, 60, 1, 1e-6, None, None, None) == 2
     assert f(P, None, None, P2, 4, 65536 + 8, 1, 1e-6, None, None, None) == 2
     assert f(P, None, None, P2, 4, 0, 1, 1e-6, None, None, None) == 1
+
+
+def test_lazy_affine_argument_checks():
+    fold = _lib.ng_lazy_fold_affine
+    # NULL or misaligned B / B_folded, bad sizes or layout -> invalid argument
+    assert fold(None, None, None, P2, None, 64, 64, 0, None) == 1
+    assert fold(P, None, None, None, None, 64, 64, 0, None) == 1
+    assert fold(BAD, None, None, P2, None, 64, 64, 0, None) == 1
+    assert fold(P, None, None, P2, None, 0, 64, 0, None) == 1
+    assert fold(P, None, None, P2, None, 64, 64, 7, None) == 1
+    assert fold(P, BAD, None, P2, None, 64, 64, 0, None) == 1
+    assert fold(P, None, BAD, P2, None, 64, 64, 0, None) == 1
+    assert fold(P, None, None, P2, P3 + 2, 64, 64, 0, None) == 1
+    # K or N not a multiple of 8 -> unsupported
+    assert fold(P, None, None, P2, None, 60, 64, 0, None) == 2
+    lazy = _lib.ng_rmsnorm_gemm_lazy_affine
+    assert lazy(P, P2, P3 + 4, P3, 64, 64, 64, 0, 1e-6, None, None) == 1   # bias misaligned
+    assert lazy(P, None, None, P3, 64, 64, 64, 0, 1e-6, None, None) == 1   # B NULL
+    assert lazy(P, P2, None, P3, 64, 64, 64, 0, -1.0, None, None) == 1     # eps < 0
+    assert lazy(P, P2, None, P3, 64, 100, 64, 0, 1e-6, None, None) == 2    # N % 8
+    assert lazy(None, P2, None, None, 0, 64, 64, 0, 1e-6, None, None) == 0  # M = 0: no-op
 
 
 def test_workspace_helpers_argument_checks():

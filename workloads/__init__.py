@@ -34,6 +34,7 @@ import numpy as np
 OP_LAZY = "rmsnorm_gemm_lazy"
 OP_GEMM_RMSNORM = "gemm_rmsnorm"
 OP_GEMM_LAYERNORM = "gemm_layernorm"
+OP_LAZY_AFFINE = "rmsnorm_gemm_lazy_affine"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -72,7 +73,16 @@ WORKLOADS = [
              description="GEMM + LayerNorm epilogue with gamma and beta, large N, "
                          "A 8192x8192 @ B 8192x16384"),
 ]
-WORKLOAD_BY_NAME = {w.name: w for w in WORKLOADS}
+# Further forms beyond the five named workloads, on the same shapes: Lazy
+# Pre-Norm with a per-column affine (gamma, beta of length K) folded into the
+# weights.
+NEXT_WORKLOADS = [
+    Workload("lazy_rms_affine_32768x4096x4096", OP_LAZY_AFFINE, 32768, 4096, 4096, 1e-6,
+             row_scale=True, gamma=True, beta=True,
+             description="Lazy Pre-Norm RMSNorm with gamma and beta (length K) folded into B, "
+                         "A 32768x4096 @ B 4096x4096"),
+]
+WORKLOAD_BY_NAME = {w.name: w for w in WORKLOADS + NEXT_WORKLOADS}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -124,5 +134,7 @@ def make_inputs(M: int, N: int, K: int, *, seed: int = 0, row_scale: bool = Fals
 
 
 def workload_inputs(w: Workload, seed: int = 0) -> Inputs:
+    # the pre-norm affine of the Lazy form acts on rows of A (length K)
+    gl = w.K if w.op == OP_LAZY_AFFINE else None
     return make_inputs(w.M, w.N, w.K, seed=seed, row_scale=w.row_scale,
-                       gamma=w.gamma, beta=w.beta)
+                       gamma=w.gamma, beta=w.beta, gamma_len=gl)
