@@ -121,15 +121,19 @@ def copy_calibration(mib: int):
 
 
 def algorithmic_bytes(w: workloads.Workload) -> int:
-    """Compulsory HBM bytes of one fused call: A, B and C once, plus gamma/beta."""
+    """Compulsory HBM bytes of one fused call: A, B and C once, plus gamma/beta
+    (the Lazy affine form reads the folded B and an fp32 bias instead)."""
     b = 2 * (w.M * w.K + w.K * w.N + w.M * w.N)
+    if w.op == workloads.OP_LAZY_AFFINE:
+        return b + 4 * w.N
     b += 2 * w.N * (int(w.gamma) + int(w.beta))
     return b
 
 
 def norm_bytes(w: workloads.Workload) -> int:
     """Standalone norm of the unfused pair: read + write the normalized matrix."""
-    rows, cols = (w.M, w.K) if w.op == workloads.OP_LAZY else (w.M, w.N)
+    lazy = w.op in (workloads.OP_LAZY, workloads.OP_LAZY_AFFINE)
+    rows, cols = (w.M, w.K) if lazy else (w.M, w.N)
     return 4 * rows * cols
 
 
@@ -171,7 +175,8 @@ class Bench:
             return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
                 torch.bfloat16)
 
-        per_copy = 2 * (w.M * w.K + w.M * w.N) + (2 * w.M * w.K if w.op == workloads.OP_LAZY else 0)
+        lazy = w.op in (workloads.OP_LAZY, workloads.OP_LAZY_AFFINE)
+        per_copy = 2 * (w.M * w.K + w.M * w.N) + (2 * w.M * w.K if lazy else 0)
         self.R = max(1, min(8, math.ceil(ROTATE_BYTES / per_copy)))
         A0 = up(x.A)
         self.A = [A0] + [A0.clone() for _ in range(self.R - 1)]
@@ -181,11 +186,15 @@ class Bench:
         self.C = [torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev) for _ in range(self.R)]
         # unfused pair intermediates: the normalized A of the lazy form's
         # pair holds real values (the GEMM's speed depends on its data)
-        if w.op == workloads.OP_LAZY:
-            An0 = ng.norm(A0, "rms", eps=w.eps)
+        if lazy:
+            An0 = ng.norm(A0, "rms", self.gamma, self.beta, eps=w.eps)
             self.An = [An0] + [An0.clone() for _ in range(self.R - 1)]
+        if w.op == workloads.OP_LAZY_AFFINE:
+            # the weight fold is a one-off transform, outside the timed calls
+            self.Bf, self.bias = ng.lazy_fold_affine(self.B, self.gamma, self.beta)
         self.ws = None
         op = {workloads.OP_LAZY: ng.NG_OP_RMSNORM_GEMM_LAZY,
+              workloads.OP_LAZY_AFFINE: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_GEMM_RMSNORM: ng.NG_OP_GEMM_RMSNORM,
               workloads.OP_GEMM_LAYERNORM: ng.NG_OP_GEMM_LAYERNORM}[w.op]
         nb = ng.ng_workspace_bytes(op, w.M, w.N, w.K)
@@ -210,7 +219,14 @@ class Bench:
         for r in range(self.R):
             A, C = self.A[r].data_ptr(), self.C[r].data_ptr()
             B, g, b = self.B.data_ptr(), ptr(self.gamma), ptr(self.beta)
-            if w.op == workloads.OP_LAZY:
+            if w.op == workloads.OP_LAZY_AFFINE:
+                An = self.An[r].data_ptr()
+                self._fused.append((lib.ng_rmsnorm_gemm_lazy_affine,
+                                    (A, self.Bf.data_ptr(), self.bias.data_ptr(), C, M, N, K, 0,
+                                     eps, None, st)))
+                self._gemm.append((lib.ng_gemm, (An, B, C, M, N, K, 0, st)))
+                self._norm.append((lib.ng_norm, (A, g, b, An, M, K, 0, eps, None, None, st)))
+            elif w.op == workloads.OP_LAZY:
                 An = self.An[r].data_ptr()
                 self._fused.append((lib.ng_rmsnorm_gemm_lazy,
                                     (A, B, C, M, N, K, 0, eps, None, st)))
@@ -280,6 +296,20 @@ class Bench:
         return per, wall, mean
 
 
+def device_info():
+    """Name, CU count and maximum shader clock of the device, and the ROCm
+    version of the runtime (for the record; not used in any figure)."""
+    torch = __import__("torch")
+    prop = torch.cuda.get_device_properties(0)
+    info = {"name": prop.name, "arch": getattr(prop, "gcnArchName", ""),
+            "cus": prop.multi_processor_count,
+            "hip": getattr(torch.version, "hip", None)}
+    clk = getattr(prop, "clock_rate", None)
+    if clk:
+        info["max_sclk_mhz"] = round(clk / 1000.0)
+    return info
+
+
 def cpu_baseline(w: workloads.Workload, target_s: float):
     """The CPU oracle (untuned) on a row sample of the same workload: passes
     over a growing number of output rows (capped at M) until about target_s
@@ -292,12 +322,15 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
         cores = os.cpu_count() or 1
     rows = min(w.M, 64)
     x = workloads.make_inputs(rows, w.N, w.K, seed=1, row_scale=w.row_scale, gamma=w.gamma,
-                              beta=w.beta)
+                              beta=w.beta,
+                              gamma_len=w.K if w.op == workloads.OP_LAZY_AFFINE else None)
     done_rows, t_total = 0, 0.0
     while t_total < target_s:
         t0 = time.perf_counter()
         if w.op == workloads.OP_LAZY:
             oracle.rmsnorm_gemm_lazy(x.A, x.B, w.eps)
+        elif w.op == workloads.OP_LAZY_AFFINE:
+            oracle.rmsnorm_gemm_lazy_affine(x.A, x.B, w.eps, x.gamma, x.beta)
         elif w.op == workloads.OP_GEMM_RMSNORM:
             oracle.gemm_rmsnorm(x.A, x.B, w.eps, x.gamma)
         else:
@@ -354,6 +387,7 @@ def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: f
                 "unit": "TFLOP/s", "frac": round(kern_tflops / MFMA_PEAK_TFLOPS, 4)}
     roof["traffic"] = measured_traffic(w)
     roof["kernel"] = {workloads.OP_LAZY: "gemm_kernel<Lazy>",
+                      workloads.OP_LAZY_AFFINE: "gemm_kernel<LazyBias>",
                       workloads.OP_GEMM_RMSNORM: "gemm_kernel<RowNorm>",
                       workloads.OP_GEMM_LAYERNORM: "gemm_kernel<RowNorm>"}[w.op]
     roof["avg_launch_us"] = round(t_fused * 1e3, 2)
@@ -380,8 +414,11 @@ def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: f
         "unfused": {"gemm_us": round(t_gemm * 1e3, 2), "norm_us": round(t_norm * 1e3, 2),
                     "pair_us": round(t_pair * 1e3, 2), "fused_us": round(t_fused * 1e3, 2),
                     "norm_gbs": round(norm_bytes(w) / (t_norm * 1e-3) / 1e9, 1),
-                    "fused_median_us": round(float(np.median(per)) * 1e3, 2)},
+                    "fused_median_us": round(float(np.median(per)) * 1e3, 2),
+                    "fused_p10_us": round(float(np.percentile(per, 10)) * 1e3, 2),
+                    "fused_p90_us": round(float(np.percentile(per, 90)) * 1e3, 2)},
         "roofline": roof,
+        "device": device_info(),
     }
     del b
     torch_mod.cuda.empty_cache()
@@ -406,12 +443,15 @@ def main():
         sys.exit(1)
     if args.calibrate_copy_mib:
         copy_calibration(args.calibrate_copy_mib)
-    names = [w.name for w in workloads.WORKLOADS] if args.workload == "all" else [args.workload]
+    if args.workload == "all":
+        names = [w.name for w in workloads.WORKLOADS + workloads.NEXT_WORKLOADS]
+    else:
+        names = [args.workload]
     for name in names:
         w = workloads.WORKLOAD_BY_NAME[name]
         small = w.flops < 1e11
-        steps = args.steps if args.steps is not None else (200 if small else 20)
-        warmup = args.warmup if args.warmup is not None else (20 if small else 5)
+        steps = args.steps if args.steps is not None else (200 if small else 30)
+        warmup = args.warmup if args.warmup is not None else 20
         line = run(w, steps, warmup, not args.no_cpu_baseline, args.cpu_seconds)
         print(json.dumps(line), flush=True)
 

@@ -122,6 +122,72 @@ def test_norm_small(rows, cols, kind):
     _check_stat("norm rstd", rstd, rref)
 
 
+# -------------------------------------------- Lazy Pre-Norm with folded affine
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("M,N,K", [(256, 64, 128), (300, 136, 200), (77, 128, 72),
+                                   (513, 520, 264), (1, 8, 8)])
+def test_lazy_affine_small(M, N, K, layout):
+    log("lazy affine M=%d N=%d K=%d %s" % (M, N, K, layout))
+    x = workloads.make_inputs(M, N, K, seed=M + 2 * N + K, row_scale=True, gamma=True,
+                              beta=True, gamma_len=K)
+    B = up(b_for_layout(x.B, layout))
+    Bf, bias = ng.lazy_fold_affine(B, up(x.gamma), up(x.beta), b_layout=layout)
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    C = ng.rmsnorm_gemm_lazy_affine(up(x.A), Bf, bias, eps=1e-6, b_layout=layout,
+                                    rstd_out=rstd)
+    torch.cuda.synchronize()
+    # the fold: diag(gamma) B rounded once to bf16 (bit-exact), bias in fp32
+    Bf_ref, bias_ref = oracle.lazy_fold_affine(x.B, x.gamma, x.beta)
+    want = oracle.f64_to_bf16_bits(Bf_ref)
+    got = down(Bf)
+    if layout == "nk":
+        got = got.T
+    assert np.array_equal(got, want)
+    Bd = np.abs(oracle.bf16_to_f64(x.B))
+    bound = K * 6e-8 * (np.abs(oracle.bf16_to_f64(x.beta)) @ Bd) + 1e-30
+    assert np.all(np.abs(bias.cpu().numpy().astype(np.float64) - bias_ref) <= bound)
+    ref, rref = oracle.rmsnorm_gemm_lazy_affine(x.A, x.B, 1e-6, x.gamma, x.beta)
+    _check("lazy affine", down(C), ref)
+    _check_stat("lazy affine rstd", rstd, rref)
+
+
+def test_lazy_affine_without_bias_is_lazy_on_folded_weights():
+    M, N, K = 600, 512, 256
+    x = workloads.make_inputs(M, N, K, seed=5, row_scale=True, gamma=True, gamma_len=K)
+    Bf, _ = ng.lazy_fold_affine(up(x.B), up(x.gamma), None)
+    C1 = ng.rmsnorm_gemm_lazy_affine(up(x.A), Bf, None, eps=1e-6)
+    C0 = ng.rmsnorm_gemm_lazy(up(x.A), Bf, eps=1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int16), C0.view(torch.int16))
+    ref, _ = oracle.rmsnorm_gemm_lazy_affine(x.A, x.B, 1e-6, x.gamma)
+    _check("lazy affine gamma only", down(C1), ref)
+
+
+def test_lazy_affine_full_size_workload():
+    w = workloads.WORKLOAD_BY_NAME["lazy_rms_affine_32768x4096x4096"]
+    log("workload %s" % w.name)
+    x = workloads.workload_inputs(w)
+    rows = sample_rows(w.M, 24, seed=1)
+    Bf, bias = ng.lazy_fold_affine(up(x.B), up(x.gamma), up(x.beta))
+    C = ng.rmsnorm_gemm_lazy_affine(up(x.A), Bf, bias, eps=w.eps)
+    torch.cuda.synchronize()
+    got = down(C[torch.as_tensor(rows, device="cuda")])
+    ref, _ = oracle.rmsnorm_gemm_lazy_affine(x.A[rows], x.B, w.eps, x.gamma, x.beta)
+    _check(w.name, got, ref)
+
+
+@pytest.mark.parametrize("rows,cols", [(37, 128), (65, 1000), (9, 8200)])
+def test_norm_rms_with_beta(rows, cols):
+    x = workloads.make_inputs(1, cols, 8, seed=rows + 3 * cols, gamma=True, beta=True)
+    rng = np.random.default_rng(rows * cols + 1)
+    Xbits = workloads.f32_to_bf16_bits(
+        (rng.standard_normal((rows, cols)) * 2.0 + 0.5).astype(np.float32))
+    Y = ng.norm(up(Xbits), "rms", up(x.gamma), up(x.beta), eps=1e-6)
+    torch.cuda.synchronize()
+    ref, _, _ = oracle.norm(Xbits, "rms", 1e-6, x.gamma, x.beta)
+    _check("norm rms beta %dx%d" % (rows, cols), down(Y), ref)
+
+
 # ------------------------------------------- persistent grids, several rounds
 # The 256x256-tile kernels run as persistent grids of one workgroup per
 # resident slot: these shapes give some workgroups two tiles (more tiles than
