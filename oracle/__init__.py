@@ -20,6 +20,8 @@ from .normgemm_oracle import (  # noqa: F401
     lazy_fold_affine,
     gemm_rmsnorm,
     gemm_layernorm,
+    gemm_add_rmsnorm,
+    gemm_add_layernorm,
     norm,
     rel_err,
 )

@@ -164,6 +164,30 @@ def gemm_layernorm(A, B, eps: float, gamma=None, beta=None
     return layer_norm_rows(gemm(A, B), eps, gamma, beta)
 
 
+def gemm_add_rmsnorm(A, B, R, eps: float, gamma=None
+                     ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Y = RMSNorm(A @ B + R) over each full row (H = N), optional gamma:
+    a residual connection followed by a post-norm, the residual added before
+    the row statistics ("Free normalization fusion", section
+    "FlashNormAttention": residual connection, then post-RMSNorm, with the
+    residual added into the matrix-core accumulator).  Returns (Y, rstd, S)
+    with S = A @ B + R, the sum the norm is taken over.
+    """
+    S = gemm(A, B) + _f64(R)
+    Y, rstd = rms_norm_rows(S, eps, gamma)
+    return Y, rstd, S
+
+
+def gemm_add_layernorm(A, B, R, eps: float, gamma=None, beta=None
+                       ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Y = LayerNorm(A @ B + R) over each full row (H = N), optional affine.
+    Returns (Y, mean, rstd, S) with S = A @ B + R.
+    """
+    S = gemm(A, B) + _f64(R)
+    Y, mean, rstd = layer_norm_rows(S, eps, gamma, beta)
+    return Y, mean, rstd, S
+
+
 def norm(X, kind: str, eps: float, gamma=None, beta=None):
     """Standalone row norm of X: kind 'rms' or 'layer'.
 

@@ -77,6 +77,10 @@ def test_hand_worked_examples(case):
     elif case["op"] == "gemm_rmsnorm":
         C, rstd = oracle.gemm_rmsnorm(A, B, eps, gamma)
         mean = None
+    elif case["op"] == "gemm_add_layernorm":
+        R = np.array(case["R"], dtype=np.float64)
+        C, mean, rstd, S = oracle.gemm_add_layernorm(A, B, R, eps, gamma, beta)
+        np.testing.assert_allclose(S, [[float(v) for v in row] for row in case["S"]], rtol=0)
     else:
         C, mean, rstd = oracle.gemm_layernorm(A, B, eps, gamma, beta)
     want = np.array([[float(v) for v in row] for row in case["C"]])
@@ -271,6 +275,46 @@ def test_lazy_affine_is_affine_rmsnorm_then_matmul():
     C, rstd = oracle.rmsnorm_gemm_lazy_affine(A, B, 1e-6, g, b)
     np.testing.assert_allclose(C, Y @ B, rtol=1e-14, atol=1e-14)
     np.testing.assert_allclose(rstd, r, rtol=1e-15)
+
+
+def test_residual_norms_reduce_to_plain_forms():
+    # R = 0: the residual forms are the plain epilogue norms; A = 0: they are
+    # the standalone norm of R
+    rng = np.random.default_rng(34)
+    A = rng.standard_normal((5, 6))
+    B = rng.standard_normal((6, 9))
+    R = rng.standard_normal((5, 9)) * 2.0
+    g = rng.uniform(0.5, 2.0, size=9)
+    b = rng.standard_normal(9)
+    Z = np.zeros((5, 9))
+    Y, r, S = oracle.gemm_add_rmsnorm(A, B, Z, 1e-6, g)
+    Y0, r0 = oracle.gemm_rmsnorm(A, B, 1e-6, g)
+    np.testing.assert_allclose(Y, Y0, rtol=1e-14, atol=1e-14)
+    Y, m, r, S = oracle.gemm_add_layernorm(A, B, Z, 1e-5, g, b)
+    Y0, m0, r0 = oracle.gemm_layernorm(A, B, 1e-5, g, b)
+    np.testing.assert_allclose(Y, Y0, rtol=1e-14, atol=1e-14)
+    Y, r, S = oracle.gemm_add_rmsnorm(np.zeros((5, 6)), B, R, 1e-6, g)
+    Yn, _, rn = oracle.norm(R, "rms", 1e-6, g)
+    np.testing.assert_allclose(Y, Yn, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(S, R, rtol=0, atol=0)
+    Y, m, r, S = oracle.gemm_add_layernorm(np.zeros((5, 6)), B, R, 1e-5, g, b)
+    Yn, mn, rn = oracle.norm(R, "layer", 1e-5, g, b)
+    np.testing.assert_allclose(Y, Yn, rtol=1e-14, atol=1e-14)
+
+
+def test_residual_is_added_before_the_statistics():
+    # adding R after normalizing gives a different result (the residual
+    # shifts the row statistics)
+    rng = np.random.default_rng(35)
+    A = rng.standard_normal((4, 8))
+    B = rng.standard_normal((8, 16))
+    R = rng.standard_normal((4, 16)) * 3.0 + 1.0
+    Y, _, _, _ = oracle.gemm_add_layernorm(A, B, R, 1e-5)
+    Y_after, _, _ = oracle.gemm_layernorm(A, B, 1e-5)
+    assert np.max(np.abs(Y - (Y_after + R))) > 1e-1
+    # LayerNorm output rows of the sum are zero-mean, unit-variance
+    np.testing.assert_allclose(Y.mean(axis=1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(Y.var(axis=1), 1.0, rtol=1e-4)
 
 
 def test_lazy_is_not_layernorm_prenorm():
