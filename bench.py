@@ -122,19 +122,37 @@ def copy_calibration(mib: int):
 
 def algorithmic_bytes(w: workloads.Workload) -> int:
     """Compulsory HBM bytes of one fused call: A, B and C once, plus gamma/beta
-    (the Lazy affine form reads the folded B and an fp32 bias instead)."""
+    (the Lazy affine form reads the folded B and an fp32 bias instead) and
+    the residual R of the residual forms."""
     b = 2 * (w.M * w.K + w.K * w.N + w.M * w.N)
     if w.op == workloads.OP_LAZY_AFFINE:
         return b + 4 * w.N
     b += 2 * w.N * (int(w.gamma) + int(w.beta))
+    if w.residual:
+        b += 2 * w.M * w.N
     return b
 
 
 def norm_bytes(w: workloads.Workload) -> int:
-    """Standalone norm of the unfused pair: read + write the normalized matrix."""
+    """Standalone norm of the unfused pair: read + write the normalized matrix
+    (and read R for the residual forms)."""
     lazy = w.op in (workloads.OP_LAZY, workloads.OP_LAZY_AFFINE)
     rows, cols = (w.M, w.K) if lazy else (w.M, w.N)
-    return 4 * rows * cols
+    return (6 if w.residual else 4) * rows * cols
+
+
+def kernel_label(w: workloads.Workload) -> str:
+    """Name of the fused kernel the workload launches (the symbol's base name)
+    and its epilogue."""
+    epi = {workloads.OP_LAZY: "EPI_LAZY", workloads.OP_LAZY_AFFINE: "EPI_LAZY_BIAS",
+           workloads.OP_GEMM_RMSNORM: "EPI_ROW_RMS", workloads.OP_GEMM_LAYERNORM: "EPI_ROW_LN",
+           workloads.OP_GEMM_ADD_RMSNORM: "EPI_ROW_RMS_RES",
+           workloads.OP_GEMM_ADD_LAYERNORM: "EPI_ROW_LN_RES"}[w.op]
+    if w.op in (workloads.OP_LAZY, workloads.OP_LAZY_AFFINE):
+        base = "gemm_kernel" if w.N <= 128 else "gemm_persistent_kernel"
+    else:
+        base = "gemm_kernel" if w.N <= 256 else "gemm_xwg_kernel"
+    return "%s<%s>" % (base, epi)
 
 
 def kernel_source_hash() -> str:
@@ -177,6 +195,7 @@ class Bench:
 
         lazy = w.op in (workloads.OP_LAZY, workloads.OP_LAZY_AFFINE)
         per_copy = 2 * (w.M * w.K + w.M * w.N) + (2 * w.M * w.K if lazy else 0)
+        per_copy += 2 * w.M * w.N if w.residual else 0
         self.R = max(1, min(8, math.ceil(ROTATE_BYTES / per_copy)))
         A0 = up(x.A)
         self.A = [A0] + [A0.clone() for _ in range(self.R - 1)]
@@ -184,6 +203,9 @@ class Bench:
         self.gamma = up(x.gamma) if x.gamma is not None else None
         self.beta = up(x.beta) if x.beta is not None else None
         self.C = [torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev) for _ in range(self.R)]
+        if w.residual:
+            R0 = up(x.R)
+            self.res = [R0] + [R0.clone() for _ in range(self.R - 1)]
         # unfused pair intermediates: the normalized A of the lazy form's
         # pair holds real values (the GEMM's speed depends on its data)
         if lazy:
@@ -196,7 +218,9 @@ class Bench:
         op = {workloads.OP_LAZY: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_LAZY_AFFINE: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_GEMM_RMSNORM: ng.NG_OP_GEMM_RMSNORM,
-              workloads.OP_GEMM_LAYERNORM: ng.NG_OP_GEMM_LAYERNORM}[w.op]
+              workloads.OP_GEMM_LAYERNORM: ng.NG_OP_GEMM_LAYERNORM,
+              workloads.OP_GEMM_ADD_RMSNORM: ng.NG_OP_GEMM_ADD_RMSNORM,
+              workloads.OP_GEMM_ADD_LAYERNORM: ng.NG_OP_GEMM_ADD_LAYERNORM}[w.op]
         nb = ng.ng_workspace_bytes(op, w.M, w.N, w.K)
         if nb:
             self.ws = ng.Workspace(nb, dev)
@@ -232,6 +256,22 @@ class Bench:
                                     (A, B, C, M, N, K, 0, eps, None, st)))
                 self._gemm.append((lib.ng_gemm, (An, B, C, M, N, K, 0, st)))
                 self._norm.append((lib.ng_norm, (A, None, None, An, M, K, 0, eps, None, None, st)))
+            elif w.residual:
+                # post-norm with residual: the unfused pair is the GEMM, then
+                # one residual-add + norm kernel (no sum output in either)
+                Rr = self.res[r].data_ptr()
+                ln = w.op == workloads.OP_GEMM_ADD_LAYERNORM
+                if ln:
+                    self._fused.append((lib.ng_gemm_add_layernorm,
+                                        (A, B, Rr, g, b, C, None, M, N, K, 0, eps, None, None, ws,
+                                         wsb, st)))
+                else:
+                    self._fused.append((lib.ng_gemm_add_rmsnorm,
+                                        (A, B, Rr, g, C, None, M, N, K, 0, eps, None, ws, wsb,
+                                         st)))
+                self._gemm.append((lib.ng_gemm, (A, B, C, M, N, K, 0, st)))
+                self._norm.append((lib.ng_add_norm, (C, Rr, g, b, C, None, M, N, int(ln), eps,
+                                                     None, None, st)))
             elif w.op == workloads.OP_GEMM_RMSNORM:
                 self._fused.append((lib.ng_gemm_rmsnorm,
                                     (A, B, g, C, M, N, K, 0, eps, None, ws, wsb, st)))
@@ -320,10 +360,14 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
         cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
+    def sample(rows):
+        return workloads.make_inputs(rows, w.N, w.K, seed=1, row_scale=w.row_scale,
+                                     gamma=w.gamma, beta=w.beta,
+                                     gamma_len=w.K if w.op == workloads.OP_LAZY_AFFINE else None,
+                                     residual=w.residual)
+
     rows = min(w.M, 64)
-    x = workloads.make_inputs(rows, w.N, w.K, seed=1, row_scale=w.row_scale, gamma=w.gamma,
-                              beta=w.beta,
-                              gamma_len=w.K if w.op == workloads.OP_LAZY_AFFINE else None)
+    x = sample(rows)
     done_rows, t_total = 0, 0.0
     while t_total < target_s:
         t0 = time.perf_counter()
@@ -333,6 +377,10 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
             oracle.rmsnorm_gemm_lazy_affine(x.A, x.B, w.eps, x.gamma, x.beta)
         elif w.op == workloads.OP_GEMM_RMSNORM:
             oracle.gemm_rmsnorm(x.A, x.B, w.eps, x.gamma)
+        elif w.op == workloads.OP_GEMM_ADD_RMSNORM:
+            oracle.gemm_add_rmsnorm(x.A, x.B, x.R, w.eps, x.gamma)
+        elif w.op == workloads.OP_GEMM_ADD_LAYERNORM:
+            oracle.gemm_add_layernorm(x.A, x.B, x.R, w.eps, x.gamma, x.beta)
         else:
             oracle.gemm_layernorm(x.A, x.B, w.eps, x.gamma, x.beta)
         dt = time.perf_counter() - t0
@@ -341,8 +389,7 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
         # grow the sample while one pass is short, up to the whole workload
         if dt < target_s / 8 and rows < w.M:
             rows = min(w.M, rows * 4)
-            x = workloads.make_inputs(rows, w.N, w.K, seed=1, row_scale=w.row_scale,
-                                      gamma=w.gamma, beta=w.beta)
+            x = sample(rows)
     flops = 2.0 * done_rows * w.N * w.K
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
@@ -386,10 +433,7 @@ def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: f
         roof = {"bound": "mfma", "achieved": round(kern_tflops, 1), "peak": MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(kern_tflops / MFMA_PEAK_TFLOPS, 4)}
     roof["traffic"] = measured_traffic(w)
-    roof["kernel"] = {workloads.OP_LAZY: "gemm_kernel<Lazy>",
-                      workloads.OP_LAZY_AFFINE: "gemm_kernel<LazyBias>",
-                      workloads.OP_GEMM_RMSNORM: "gemm_kernel<RowNorm>",
-                      workloads.OP_GEMM_LAYERNORM: "gemm_kernel<RowNorm>"}[w.op]
+    roof["kernel"] = kernel_label(w)
     roof["avg_launch_us"] = round(t_fused * 1e3, 2)
     roof["algorithmic_bytes"] = algorithmic_bytes(w)
     hidden = (t_gemm + t_norm - t_fused) / t_norm * 100.0
@@ -407,7 +451,7 @@ def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: f
         "dtype": "bf16",
         "data": "synthetic (seeded bf16, shapes and distributions of the named workload)",
         "config": {"workload": w.name, "op": w.op, "M": w.M, "N": w.N, "K": w.K, "eps": w.eps,
-                   "gamma": w.gamma, "beta": w.beta, "b_layout": "kn",
+                   "gamma": w.gamma, "beta": w.beta, "residual": w.residual, "b_layout": "kn",
                    "rotated_copies": b.R},
         "mfma_peak_pct": round(kern_tflops / MFMA_PEAK_TFLOPS * 100.0, 2),
         "norm_hidden_pct": round(hidden, 1),

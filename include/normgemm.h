@@ -19,7 +19,8 @@
  *     aligned; the float32 statistic outputs 4-byte aligned;
  *   - b_layout is NG_B_KN (B stored [K, N], N contiguous) or NG_B_NK (B stored
  *     [N, K], K contiguous: a Linear layer's weight).
- * Outputs must not overlap inputs.
+ * Outputs must not overlap inputs (the residual forms below name the
+ * exceptions).
  *
  * Accuracy: bf16 inputs, fp32 accumulation and fp32 row statistics, outputs
  * rounded to bf16 (nearest, ties to even).  Against a float64 evaluation of
@@ -54,7 +55,9 @@ enum {
   NG_OP_GEMM_RMSNORM = 1,
   NG_OP_GEMM_LAYERNORM = 2,
   NG_OP_GEMM = 3,
-  NG_OP_NORM = 4
+  NG_OP_NORM = 4,
+  NG_OP_GEMM_ADD_RMSNORM = 5,
+  NG_OP_GEMM_ADD_LAYERNORM = 6
 };
 
 /*
@@ -140,6 +143,33 @@ int ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
                       size_t workspace_bytes, void* stream);
 
 /*
+ * Residual connection followed by a post-norm ("Free normalization fusion",
+ * section "FlashNormAttention": residual add, then the post-norm, the residual
+ * added to the product's accumulator; norm formulas as above):
+ *   S = A @ B + R          (fp32: the product's accumulators plus R)
+ *   C = RMSNorm(S) * gamma                     (ng_gemm_add_rmsnorm)
+ *   C = LayerNorm(S) * gamma + beta            (ng_gemm_add_layernorm)
+ *   S_out = bf16(S)        (when S_out is non-NULL: the new residual stream)
+ * with the statistics taken over each full row of S (H = N in the formulas
+ * above).  R: [M, N] bf16, required; S_out: [M, N] bf16 or NULL.  R may be
+ * the very buffer of C or of S_out (an in-place update: every element of R
+ * is read before the same element of C or S_out is written); S_out and C
+ * must differ, and no other overlap is allowed.  mean_out/rstd_out describe S.  Strategies and
+ * workspace rules as for ng_gemm_rmsnorm / ng_gemm_layernorm, with
+ * ng_workspace_bytes(NG_OP_GEMM_ADD_RMSNORM / NG_OP_GEMM_ADD_LAYERNORM, ...).
+ */
+int ng_gemm_add_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
+                        const ng_bf16* gamma, ng_bf16* C, ng_bf16* S_out, int64_t M, int64_t N,
+                        int64_t K, int b_layout, float eps, float* rstd_out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+int ng_gemm_add_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
+                          const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* C, ng_bf16* S_out,
+                          int64_t M, int64_t N, int64_t K, int b_layout, float eps,
+                          float* mean_out, float* rstd_out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * Plain GEMM, the matrix half of the unfused baseline: C = A @ B (bf16 out,
  * fp32 accumulation).
  */
@@ -158,6 +188,19 @@ int ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N
 int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* Y,
             int64_t rows, int64_t cols, int kind, float eps, float* mean_out, float* rstd_out,
             void* stream);
+
+/*
+ * Standalone residual add and row norm, the norm half of the unfused
+ * baseline of the residual forms: S = X + R, rounded to bf16 as it is formed
+ * (the residual stream's storage type); Y = norm(S) with kind, gamma, beta,
+ * eps and the statistic outputs as for ng_norm; S_out (bf16 [rows, cols] or
+ * NULL) receives S.  R: [rows, cols] bf16, required.  Y may equal X, and S_out
+ * may equal X or R (in-place updates: each element is read before the same
+ * element is written); S_out and Y must differ.  Limits as for ng_norm.
+ */
+int ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng_bf16* beta,
+                ng_bf16* Y, ng_bf16* S_out, int64_t rows, int64_t cols, int kind, float eps,
+                float* mean_out, float* rstd_out, void* stream);
 
 /* Workspace bytes `op` needs for this shape (0 when it needs none). */
 size_t ng_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);

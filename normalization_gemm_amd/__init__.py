@@ -17,15 +17,19 @@ from typing import Optional
 from . import _lib
 from ._lib import (  # noqa: F401
     NG_B_KN, NG_B_NK, NG_NORM_LAYER, NG_NORM_RMS, NG_OK,
-    NG_OP_GEMM, NG_OP_GEMM_LAYERNORM, NG_OP_GEMM_RMSNORM, NG_OP_NORM, NG_OP_RMSNORM_GEMM_LAZY,
-    ng_gemm, ng_gemm_layernorm, ng_gemm_rmsnorm, ng_last_error, ng_lazy_fold_affine, ng_norm,
+    NG_OP_GEMM, NG_OP_GEMM_ADD_LAYERNORM, NG_OP_GEMM_ADD_RMSNORM, NG_OP_GEMM_LAYERNORM,
+    NG_OP_GEMM_RMSNORM, NG_OP_NORM, NG_OP_RMSNORM_GEMM_LAZY,
+    ng_gemm, ng_gemm_add_layernorm, ng_gemm_add_rmsnorm, ng_gemm_layernorm, ng_gemm_rmsnorm,
+    ng_add_norm, ng_last_error, ng_lazy_fold_affine, ng_norm,
     ng_rmsnorm_gemm_lazy, ng_rmsnorm_gemm_lazy_affine, ng_status_string, ng_workspace_bytes,
     ng_workspace_reset, ng_workspace_status,
 )
 
 __all__ = [
     "NormGemmError", "rmsnorm_gemm_lazy", "lazy_fold_affine", "rmsnorm_gemm_lazy_affine",
-    "gemm_rmsnorm", "gemm_layernorm", "gemm", "norm", "Workspace", "library_path",
+    "gemm_rmsnorm", "gemm_layernorm", "gemm_add_rmsnorm", "gemm_add_layernorm", "gemm", "norm",
+    "add_norm",
+    "Workspace", "library_path",
 ]
 
 
@@ -226,6 +230,62 @@ def gemm_layernorm(A, B, gamma=None, beta=None, *, eps: float = 1e-5, b_layout="
     return C
 
 
+def _residual(R, S_out, M, N):
+    _dev_bf16(R, "R")
+    if tuple(R.shape) != (M, N):
+        raise ValueError("R must be [%d, %d] (got %s)" % (M, N, tuple(R.shape)))
+    if S_out is not None:
+        _dev_bf16(S_out, "s_out")
+        if tuple(S_out.shape) != (M, N):
+            raise ValueError("s_out must be [%d, %d]" % (M, N))
+
+
+def gemm_add_rmsnorm(A, B, R, gamma=None, *, eps: float = 1e-6, b_layout="kn", out=None,
+                     s_out=None, rstd_out=None, workspace: Optional[Workspace] = None,
+                     stream=None):
+    """C = RMSNorm(A @ B + R) over each output row, optional per-column gamma;
+    s_out, when given, receives A @ B + R in bf16 (R may be out or s_out for
+    an in-place update)."""
+    torch = _torch()
+    _dev_bf16(A, "A"); _dev_bf16(B, "B")
+    if gamma is not None:
+        _dev_bf16(gamma, "gamma")
+    lay = _layout(b_layout)
+    M, N, K = _shapes(A, B, lay)
+    _residual(R, s_out, M, N)
+    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _dev_bf16(C, "out")
+    ws, wsb = _workspace(NG_OP_GEMM_ADD_RMSNORM, M, N, K, A.device, workspace)
+    _check(ng_gemm_add_rmsnorm(_ptr(A), _ptr(B), _ptr(R), _ptr(gamma), _ptr(C), _ptr(s_out), M, N,
+                               K, lay, float(eps), _ptr(rstd_out), ws, wsb, _stream(stream)),
+           "ng_gemm_add_rmsnorm")
+    return C
+
+
+def gemm_add_layernorm(A, B, R, gamma=None, beta=None, *, eps: float = 1e-5, b_layout="kn",
+                       out=None, s_out=None, mean_out=None, rstd_out=None,
+                       workspace: Optional[Workspace] = None, stream=None):
+    """C = LayerNorm(A @ B + R) over each output row, optional per-column
+    gamma/beta; s_out as for gemm_add_rmsnorm."""
+    torch = _torch()
+    _dev_bf16(A, "A"); _dev_bf16(B, "B")
+    if gamma is not None:
+        _dev_bf16(gamma, "gamma")
+    if beta is not None:
+        _dev_bf16(beta, "beta")
+    lay = _layout(b_layout)
+    M, N, K = _shapes(A, B, lay)
+    _residual(R, s_out, M, N)
+    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _dev_bf16(C, "out")
+    ws, wsb = _workspace(NG_OP_GEMM_ADD_LAYERNORM, M, N, K, A.device, workspace)
+    _check(ng_gemm_add_layernorm(_ptr(A), _ptr(B), _ptr(R), _ptr(gamma), _ptr(beta), _ptr(C),
+                                 _ptr(s_out), M, N, K, lay, float(eps), _ptr(mean_out),
+                                 _ptr(rstd_out), ws, wsb, _stream(stream)),
+           "ng_gemm_add_layernorm")
+    return C
+
+
 def gemm(A, B, *, b_layout="kn", out=None, stream=None):
     """C = A @ B (bf16 out, fp32 accumulation): the unfused baseline GEMM."""
     torch = _torch()
@@ -255,4 +315,27 @@ def norm(X, kind: str, gamma=None, beta=None, *, eps: float = 1e-5, out=None, me
     rows, cols = X.shape
     _check(ng_norm(_ptr(X), _ptr(gamma), _ptr(beta), _ptr(Y), rows, cols, k, float(eps),
                    _ptr(mean_out), _ptr(rstd_out), _stream(stream)), "ng_norm")
+    return Y
+
+
+def add_norm(X, R, kind: str, gamma=None, beta=None, *, eps: float = 1e-5, out=None, s_out=None,
+             mean_out=None, rstd_out=None, stream=None):
+    """Standalone residual add + row norm: Y = norm(X + R) with X + R rounded
+    to bf16 (s_out, when given, receives it): the unfused baseline's norm."""
+    torch = _torch()
+    _dev_bf16(X, "X")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    rows, cols = X.shape
+    _residual(R, s_out, rows, cols)
+    k = {"rms": NG_NORM_RMS, "layer": NG_NORM_LAYER}[kind]
+    if gamma is not None:
+        _dev_bf16(gamma, "gamma")
+    if beta is not None:
+        _dev_bf16(beta, "beta")
+    Y = out if out is not None else torch.empty_like(X)
+    _dev_bf16(Y, "out")
+    _check(ng_add_norm(_ptr(X), _ptr(R), _ptr(gamma), _ptr(beta), _ptr(Y), _ptr(s_out), rows, cols,
+                       k, float(eps), _ptr(mean_out), _ptr(rstd_out), _stream(stream)),
+           "ng_add_norm")
     return Y

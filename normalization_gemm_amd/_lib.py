@@ -29,6 +29,8 @@ NG_OP_GEMM_RMSNORM = 1
 NG_OP_GEMM_LAYERNORM = 2
 NG_OP_GEMM = 3
 NG_OP_NORM = 4
+NG_OP_GEMM_ADD_RMSNORM = 5
+NG_OP_GEMM_ADD_LAYERNORM = 6
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -40,10 +42,15 @@ _SIGNATURES = {
     "ng_rmsnorm_gemm_lazy": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P]),
     "ng_gemm_rmsnorm": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _SZ, _P]),
     "ng_gemm_layernorm": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P, _SZ, _P]),
+    "ng_gemm_add_rmsnorm": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _SZ,
+                                 _P]),
+    "ng_gemm_add_layernorm": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P,
+                                   _P, _SZ, _P]),
     "ng_lazy_fold_affine": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _P]),
     "ng_rmsnorm_gemm_lazy_affine": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P]),
     "ng_gemm": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "ng_norm": (_I, [_P, _P, _P, _P, _I64, _I64, _I, _F, _P, _P, _P]),
+    "ng_add_norm": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I, _F, _P, _P, _P]),
     "ng_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64]),
     "ng_workspace_reset": (_I, [_P, _SZ, _P]),
     "ng_workspace_status": (_I, [_P, _P]),
@@ -104,12 +111,29 @@ def ng_gemm_layernorm(A, B, gamma, beta, C, M, N, K, b_layout, eps, mean_out, rs
                  rstd_out, workspace, workspace_bytes, stream)
 
 
+def ng_gemm_add_rmsnorm(A, B, R, gamma, C, S_out, M, N, K, b_layout, eps, rstd_out, workspace,
+                        workspace_bytes, stream):
+    return _call("ng_gemm_add_rmsnorm", A, B, R, gamma, C, S_out, M, N, K, b_layout, eps,
+                 rstd_out, workspace, workspace_bytes, stream)
+
+
+def ng_gemm_add_layernorm(A, B, R, gamma, beta, C, S_out, M, N, K, b_layout, eps, mean_out,
+                          rstd_out, workspace, workspace_bytes, stream):
+    return _call("ng_gemm_add_layernorm", A, B, R, gamma, beta, C, S_out, M, N, K, b_layout, eps,
+                 mean_out, rstd_out, workspace, workspace_bytes, stream)
+
+
 def ng_gemm(A, B, C, M, N, K, b_layout, stream):
     return _call("ng_gemm", A, B, C, M, N, K, b_layout, stream)
 
 
 def ng_norm(X, gamma, beta, Y, rows, cols, kind, eps, mean_out, rstd_out, stream):
     return _call("ng_norm", X, gamma, beta, Y, rows, cols, kind, eps, mean_out, rstd_out, stream)
+
+
+def ng_add_norm(X, R, gamma, beta, Y, S_out, rows, cols, kind, eps, mean_out, rstd_out, stream):
+    return _call("ng_add_norm", X, R, gamma, beta, Y, S_out, rows, cols, kind, eps, mean_out,
+                 rstd_out, stream)
 
 
 def ng_workspace_bytes(op, M, N, K):

@@ -159,12 +159,12 @@ int launch_persistent(ng::GemmParams p, hipStream_t s, const char* what) {
   return launched(what);
 }
 
-template <class T, bool LN>
+template <class T, bool LN, bool RES>
 int launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   p.tiles_m = (p.M + T::BM - 1) / T::BM;
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
   int cap = 0;
-  int st = resident_capacity((const void*)ng::gemm_xwg_kernel<T, LN>, T::NT, &cap);
+  int st = resident_capacity((const void*)ng::gemm_xwg_kernel<T, LN, RES>, T::NT, &cap);
   if (st) return st;
   if (p.tiles_n > cap)
     return fail(NG_ERR_UNSUPPORTED, "row of %d tiles exceeds %d co-resident workgroups",
@@ -177,7 +177,7 @@ int launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   // on a device not shared with another such grid all workgroups become
   // resident.  (A cooperative launch would guarantee it even then, but was
   // measured to add ~18 us per call.)
-  hipLaunchKernelGGL((ng::gemm_xwg_kernel<T, LN>), dim3(grid), dim3(T::NT), 0, s, p);
+  hipLaunchKernelGGL((ng::gemm_xwg_kernel<T, LN, RES>), dim3(grid), dim3(T::NT), 0, s, p);
   return launched(what);
 }
 
@@ -188,11 +188,29 @@ size_t xwg_bytes(int64_t M, int64_t N) {
   return ng::XwgLayout::bytes(tm, tn, T::BM);
 }
 
-// Shared by ng_gemm_rmsnorm / ng_gemm_layernorm.
-int gemm_norm(const void* A, const void* B, const void* gamma, const void* beta, void* C,
-              int64_t M, int64_t N, int64_t K, int b_layout, float eps, float* mean_out,
-              float* rstd_out, void* ws, size_t ws_bytes, hipStream_t s, int kind,
-              const char* what) {
+// Strategy choice of the epilogue norms: N <= 128 one 256 x 128 workgroup
+// per row block, N <= 256 one 128 x 256 workgroup, wider rows the
+// cross-workgroup grid.
+template <bool LN, bool RES>
+int launch_norm(ng::GemmParams p, bool kn, bool local, hipStream_t s, const char* what) {
+  constexpr int EPI = RES ? (LN ? ng::EPI_ROW_LN_RES : ng::EPI_ROW_RMS_RES)
+                          : (LN ? ng::EPI_ROW_LN : ng::EPI_ROW_RMS);
+  if (p.N <= 128)
+    return kn ? launch_grid<TRow128<true>, EPI>(p, s, what)
+              : launch_grid<TRow128<false>, EPI>(p, s, what);
+  if (local)
+    return kn ? launch_grid<TRow256<true>, EPI>(p, s, what)
+              : launch_grid<TRow256<false>, EPI>(p, s, what);
+  return kn ? launch_xwg<TLarge<true>, LN, RES>(p, s, what)
+            : launch_xwg<TLarge<false>, LN, RES>(p, s, what);
+}
+
+// Shared by ng_gemm_rmsnorm / ng_gemm_layernorm and the residual forms
+// (R non-NULL).
+int gemm_norm(const void* A, const void* B, const void* R, const void* gamma, const void* beta,
+              void* C, void* S_out, int64_t M, int64_t N, int64_t K, int b_layout, float eps,
+              float* mean_out, float* rstd_out, void* ws, size_t ws_bytes, hipStream_t s,
+              int kind, bool residual, const char* what) {
   int st = check_gemm(A, B, C, M, N, K, b_layout);
   if (!st) st = check_eps(eps);
   if (!st) st = check_vec(gamma, "gamma", 16);
@@ -200,6 +218,13 @@ int gemm_norm(const void* A, const void* B, const void* gamma, const void* beta,
   if (!st) st = check_vec(mean_out, "mean_out", 4);
   if (!st) st = check_vec(rstd_out, "rstd_out", 4);
   if (st) return st;
+  if (residual) {
+    if (M != 0 && !R) return fail(NG_ERR_INVALID_ARG, "R must be non-NULL");
+    if (!aligned(R, 16) || !aligned(S_out, 16))
+      return fail(NG_ERR_INVALID_ARG, "R and S_out must be 16-byte aligned");
+    if (S_out && M != 0 && S_out == C)
+      return fail(NG_ERR_INVALID_ARG, "S_out and C must be different buffers");
+  }
   const bool local = N <= 256;
   if (!local && M > 0) {
     const size_t need = xwg_bytes(M, N);
@@ -211,31 +236,19 @@ int gemm_norm(const void* A, const void* B, const void* gamma, const void* beta,
   ng::GemmParams p = make_params(A, B, C, M, N, K, eps);
   p.gamma = (const uint16_t*)gamma;
   p.beta = (const uint16_t*)beta;
+  p.R = (const uint16_t*)R;
+  p.S_out = (uint16_t*)S_out;
   p.mean_out = mean_out;
   p.rstd_out = rstd_out;
   p.ws = (char*)ws;
   p.norm_kind = kind;
   const bool kn = b_layout == NG_B_KN;
   const bool ln = kind == ng::NORM_LAYER;
-  if (N <= 128) {
-    if (ln)
-      return kn ? launch_grid<TRow128<true>, ng::EPI_ROW_LN>(p, s, what)
-                : launch_grid<TRow128<false>, ng::EPI_ROW_LN>(p, s, what);
-    return kn ? launch_grid<TRow128<true>, ng::EPI_ROW_RMS>(p, s, what)
-              : launch_grid<TRow128<false>, ng::EPI_ROW_RMS>(p, s, what);
-  }
-  if (local) {
-    if (ln)
-      return kn ? launch_grid<TRow256<true>, ng::EPI_ROW_LN>(p, s, what)
-                : launch_grid<TRow256<false>, ng::EPI_ROW_LN>(p, s, what);
-    return kn ? launch_grid<TRow256<true>, ng::EPI_ROW_RMS>(p, s, what)
-              : launch_grid<TRow256<false>, ng::EPI_ROW_RMS>(p, s, what);
-  }
-  if (ln)
-    return kn ? launch_xwg<TLarge<true>, true>(p, s, what)
-              : launch_xwg<TLarge<false>, true>(p, s, what);
-  return kn ? launch_xwg<TLarge<true>, false>(p, s, what)
-            : launch_xwg<TLarge<false>, false>(p, s, what);
+  if (residual)
+    return ln ? launch_norm<true, true>(p, kn, local, s, what)
+              : launch_norm<false, true>(p, kn, local, s, what);
+  return ln ? launch_norm<true, false>(p, kn, local, s, what)
+            : launch_norm<false, false>(p, kn, local, s, what);
 }
 
 }  // namespace
@@ -336,16 +349,37 @@ int ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded, const
 int ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,
                     int64_t M, int64_t N, int64_t K, int b_layout, float eps, float* rstd_out,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  return gemm_norm(A, B, gamma, nullptr, C, M, N, K, b_layout, eps, nullptr, rstd_out, workspace,
-                   workspace_bytes, (hipStream_t)stream, ng::NORM_RMS, "ng_gemm_rmsnorm");
+  return gemm_norm(A, B, nullptr, gamma, nullptr, C, nullptr, M, N, K, b_layout, eps, nullptr,
+                   rstd_out, workspace, workspace_bytes, (hipStream_t)stream, ng::NORM_RMS, false,
+                   "ng_gemm_rmsnorm");
 }
 
 int ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
                       const ng_bf16* beta, ng_bf16* C, int64_t M, int64_t N, int64_t K,
                       int b_layout, float eps, float* mean_out, float* rstd_out, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  return gemm_norm(A, B, gamma, beta, C, M, N, K, b_layout, eps, mean_out, rstd_out, workspace,
-                   workspace_bytes, (hipStream_t)stream, ng::NORM_LAYER, "ng_gemm_layernorm");
+  return gemm_norm(A, B, nullptr, gamma, beta, C, nullptr, M, N, K, b_layout, eps, mean_out,
+                   rstd_out, workspace, workspace_bytes, (hipStream_t)stream, ng::NORM_LAYER, false,
+                   "ng_gemm_layernorm");
+}
+
+int ng_gemm_add_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
+                        const ng_bf16* gamma, ng_bf16* C, ng_bf16* S_out, int64_t M, int64_t N,
+                        int64_t K, int b_layout, float eps, float* rstd_out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return gemm_norm(A, B, R, gamma, nullptr, C, S_out, M, N, K, b_layout, eps, nullptr, rstd_out,
+                   workspace, workspace_bytes, (hipStream_t)stream, ng::NORM_RMS, true,
+                   "ng_gemm_add_rmsnorm");
+}
+
+int ng_gemm_add_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
+                          const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* C, ng_bf16* S_out,
+                          int64_t M, int64_t N, int64_t K, int b_layout, float eps,
+                          float* mean_out, float* rstd_out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return gemm_norm(A, B, R, gamma, beta, C, S_out, M, N, K, b_layout, eps, mean_out, rstd_out,
+                   workspace, workspace_bytes, (hipStream_t)stream, ng::NORM_LAYER, true,
+                   "ng_gemm_add_layernorm");
 }
 
 int ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
@@ -363,12 +397,24 @@ int ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N
             : launch_persistent<TLarge<false>, ng::EPI_NONE>(p, s, "ng_gemm");
 }
 
-int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* Y,
-            int64_t rows, int64_t cols, int kind, float eps, float* mean_out, float* rstd_out,
-            void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by ng_norm and ng_add_norm (R non-NULL).
+int norm_rows(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng_bf16* beta,
+              ng_bf16* Y, ng_bf16* S_out, int64_t rows, int64_t cols, int kind, float eps,
+              float* mean_out, float* rstd_out, hipStream_t s, bool residual, const char* what) {
   if (rows != 0 && (!X || !Y)) return fail(NG_ERR_INVALID_ARG, "X and Y must be non-NULL");
   if (!aligned(X, 16) || !aligned(Y, 16))
     return fail(NG_ERR_INVALID_ARG, "X and Y must be 16-byte aligned");
+  if (residual) {
+    if (rows != 0 && !R) return fail(NG_ERR_INVALID_ARG, "R must be non-NULL");
+    if (!aligned(R, 16) || !aligned(S_out, 16))
+      return fail(NG_ERR_INVALID_ARG, "R and S_out must be 16-byte aligned");
+    if (S_out && rows != 0 && S_out == Y)
+      return fail(NG_ERR_INVALID_ARG, "S_out and Y must be different buffers");
+  }
   if (rows < 0 || cols < 1 || rows > kMaxDim * 64)
     return fail(NG_ERR_INVALID_ARG, "need rows >= 0 and cols >= 1");
   if (kind != NG_NORM_RMS && kind != NG_NORM_LAYER)
@@ -386,6 +432,8 @@ int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16
   if (rows == 0) return ok();
   ng::NormParams p{};
   p.X = X;
+  p.R = R;
+  p.S_out = S_out;
   p.gamma = gamma;
   p.beta = beta;
   p.Y = Y;
@@ -395,13 +443,15 @@ int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16
   p.cols = (int)cols;
   p.kind = kind;
   p.eps = eps;
-  hipStream_t s = (hipStream_t)stream;
   const int64_t nch = cols / 8;
-#define NG_NORM_LAUNCH(LPR, CPL)                                                          \
-  do {                                                                                    \
-    const unsigned grid = (unsigned)((rows + (256 / LPR) - 1) / (256 / LPR));             \
-    hipLaunchKernelGGL((ng::norm_kernel<LPR, CPL>), dim3(grid), dim3(256), 0, s, p);      \
-    return launched("ng_norm");                                                           \
+#define NG_NORM_LAUNCH(LPR, CPL)                                                              \
+  do {                                                                                        \
+    const unsigned grid = (unsigned)((rows + (256 / LPR) - 1) / (256 / LPR));                 \
+    if (residual)                                                                             \
+      hipLaunchKernelGGL((ng::norm_kernel<LPR, CPL, true>), dim3(grid), dim3(256), 0, s, p);  \
+    else                                                                                      \
+      hipLaunchKernelGGL((ng::norm_kernel<LPR, CPL, false>), dim3(grid), dim3(256), 0, s, p); \
+    return launched(what);                                                                    \
   } while (0)
   if (nch <= 16) NG_NORM_LAUNCH(16, 1);
   if (nch <= 32) NG_NORM_LAUNCH(32, 1);
@@ -416,9 +466,29 @@ int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16
 #undef NG_NORM_LAUNCH
 }
 
+}  // namespace
+
+extern "C" {
+
+int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* Y,
+            int64_t rows, int64_t cols, int kind, float eps, float* mean_out, float* rstd_out,
+            void* stream) {
+  return norm_rows(X, nullptr, gamma, beta, Y, nullptr, rows, cols, kind, eps, mean_out,
+                   rstd_out, (hipStream_t)stream, false, "ng_norm");
+}
+
+int ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng_bf16* beta,
+                ng_bf16* Y, ng_bf16* S_out, int64_t rows, int64_t cols, int kind, float eps,
+                float* mean_out, float* rstd_out, void* stream) {
+  return norm_rows(X, R, gamma, beta, Y, S_out, rows, cols, kind, eps, mean_out, rstd_out,
+                   (hipStream_t)stream, true, "ng_add_norm");
+}
+
 size_t ng_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
   (void)K;
-  if (op != NG_OP_GEMM_RMSNORM && op != NG_OP_GEMM_LAYERNORM) return 0;
+  if (op != NG_OP_GEMM_RMSNORM && op != NG_OP_GEMM_LAYERNORM && op != NG_OP_GEMM_ADD_RMSNORM &&
+      op != NG_OP_GEMM_ADD_LAYERNORM)
+    return 0;
   if (M <= 0 || N <= 256 || M > kMaxDim || N > kMaxDim) return 0;
   return xwg_bytes(M, N);
 }

@@ -7,9 +7,12 @@
 //                 affine folded into the weights: B' = diag(gamma) B, bias = beta^T B)
 //   EPI_ROW_RMS / EPI_ROW_LN
 //                 C = norm(A @ B), whole row in one workgroup (N <= BN)
-//   cross-workgroup: C = norm(A @ B) for rows split over workgroups; per-row
-//                 fp32 partials merged through a workspace (persistent grid,
-//                 gemm_xwg_kernel below)
+//   EPI_ROW_RMS_RES / EPI_ROW_LN_RES
+//                 C = norm(A @ B + R), S_out = A @ B + R (optional): a
+//                 residual connection followed by a post-norm
+//   cross-workgroup: C = norm(A @ B [+ R]) for rows split over workgroups;
+//                 per-row fp32 partials merged through a workspace
+//                 (persistent grid, gemm_xwg_kernel below)
 //
 // Lazy Pre-Norm ("Free normalization fusion", section "Lazy Pre-Norm"): a
 // per-row scale commutes with the product, so the sum of squares of each row
@@ -42,8 +45,21 @@ namespace ng {
 
 constexpr int BK = 64;
 
-enum Epi { EPI_NONE = 0, EPI_LAZY = 1, EPI_ROW_RMS = 2, EPI_ROW_LN = 3, EPI_LAZY_BIAS = 4 };
+enum Epi {
+  EPI_NONE = 0,
+  EPI_LAZY = 1,
+  EPI_ROW_RMS = 2,
+  EPI_ROW_LN = 3,
+  EPI_LAZY_BIAS = 4,
+  EPI_ROW_RMS_RES = 5,
+  EPI_ROW_LN_RES = 6
+};
 constexpr bool epi_lazy(int e) { return e == EPI_LAZY || e == EPI_LAZY_BIAS; }
+constexpr bool epi_row(int e) {
+  return e == EPI_ROW_RMS || e == EPI_ROW_LN || e == EPI_ROW_RMS_RES || e == EPI_ROW_LN_RES;
+}
+constexpr bool epi_ln(int e) { return e == EPI_ROW_LN || e == EPI_ROW_LN_RES; }
+constexpr bool epi_res(int e) { return e == EPI_ROW_RMS_RES || e == EPI_ROW_LN_RES; }
 enum NormKind { NORM_RMS = 0, NORM_LAYER = 1 };
 
 // Workspace layout of the cross-workgroup row norm (byte offsets).
@@ -79,6 +95,8 @@ struct GemmParams {
   const uint16_t* gamma;
   const uint16_t* beta;
   const float* bias;  // EPI_LAZY_BIAS: fp32 [N]
+  const uint16_t* R;  // residual epilogues: bf16 [M][N] added before the norm
+  uint16_t* S_out;    // residual epilogues: optional bf16 [M][N] output A @ B + R
   float* mean_out;
   float* rstd_out;
   char* ws;
@@ -728,6 +746,75 @@ __device__ __forceinline__ void lazy_rstd(const GemmParams& p, const float (&ss)
   }
 }
 
+// Residual connection of the post-norm epilogues: acc += R over the wave's
+// WTM x WTN slice, then (when S_out is given) S_out = bf16(acc).  The pipeline
+// stages are idle between a tile's k-loop and the next tile's first
+// transfers, so the slice moves from HBM into them with LDS transfers: 256-byte
+// rows (WTN = 128 columns), one 1 KB transfer per 4 rows, 16-byte chunk c of
+// row r at chunk position c ^ (r & 15) so that a fragment read (16 rows, one
+// chunk each) touches every bank once.  Each wave reads back only the rows it
+// moved, so its own transfer count is the only wait.  Rows past M and columns
+// past N read as zero (they are neither counted in the statistics nor
+// stored).  Ends with a barrier, after which the stages and any output
+// staging aliased on them may be reused.  A workgroup reads R only inside its
+// own tile and before it writes C or S_out there, so R may be the very
+// buffer that C or S_out is.
+template <class T>
+__device__ __forceinline__ void add_residual(const GemmParams& p, f32x4 (&acc)[T::FM][T::FN],
+                                             lds_char* lds, uint32_t lds0, int m_base, int n_base,
+                                             int wave, int wm, int wn, int lane) {
+  static_assert(T::WTN == 128, "residual rows of 16 chunks");
+  static_assert((T::NT / 64) * T::WTM * 256 <= T::STAGES * T::STAGE, "residual slices fit the stages");
+  static_assert(T::WTM % 4 == 0, "4 rows per transfer");
+  // wave-uniform copies (the transfer's LDS address and buffer are scalar)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int m_w = __builtin_amdgcn_readfirstlane(m_base + (wv / T::WN) * T::WTM);
+  const int n_w = n_base + wn * T::WTN;
+  const uint32_t region = (uint32_t)wv * (uint32_t)T::WTM * 256u;
+  const uint64_t total = (uint64_t)p.M * (uint64_t)p.N;
+  {
+    const int rq = lane >> 4, c = (lane & 15);
+#pragma unroll
+    for (int q = 0; q < T::WTM / 4; ++q) {
+      // rows m_w + 4q .. +3 from a base at row m_w + 4q (offsets below 2^28)
+      const uint64_t base = (uint64_t)(m_w + 4 * q) * (uint64_t)p.N;
+      const uint64_t left = total > base ? (total - base) * 2u : 0u;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.R + base, left);
+      const int r = 4 * q + rq;
+      const int n = n_w + 8 * (c ^ (r & 15));
+      const uint32_t voff = n < p.N ? ((uint32_t)rq * (uint32_t)p.N + (uint32_t)n) * 2u : kOOB;
+      dma16(rs, lds0 + region + (uint32_t)q * 1024u, voff, 0);
+    }
+  }
+  wait_vmcnt<0>();
+  const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const int pos = (2 * j + (g >> 1)) ^ l16;
+      const u32x2 v = *(lds_u32x2*)(lds + region + (uint32_t)(16 * i + l16) * 256u +
+                                    (uint32_t)pos * 16u + 8u * (uint32_t)(g & 1));
+      acc[i][j][0] += bf16_lo(v[0]);
+      acc[i][j][1] += bf16_hi(v[0]);
+      acc[i][j][2] += bf16_lo(v[1]);
+      acc[i][j][3] += bf16_hi(v[1]);
+    }
+  }
+  __syncthreads();
+  if (p.S_out) {
+    GemmParams ph = p;
+    ph.C = p.S_out;
+    float zero[T::FM], one[T::FM];
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) { zero[i] = 0.f; one[i] = 1.f; }
+    Affine<T> no_aff;
+    Bias<T> no_bias;
+    apply_store<T, false>(ph, acc, zero, one, false, no_aff, no_bias, lds, m_base, n_base, wave,
+                          wm, wn, lane);
+  }
+}
+
 // Per-row (mean, rstd) that the epilogue applies to a finished tile:
 // EPI_NONE (0, 1); EPI_LAZY* (0, rstd of the row of A); EPI_ROW_* the row's
 // statistics over the tile (which holds whole rows).  Also writes the
@@ -741,10 +828,10 @@ __device__ __forceinline__ void tile_scale(const GemmParams& p, const f32x4 (&ac
   for (int i = 0; i < T::FM; ++i) { mean[i] = 0.f; rstd[i] = 1.f; }
   if constexpr (epi_lazy(EPI)) {
     lazy_rstd<T>(p, ss, rstd, lds, m_base, tn, wm, wn, lane, ax);
-  } else if constexpr (EPI == EPI_ROW_RMS || EPI == EPI_ROW_LN) {
+  } else if constexpr (epi_row(EPI)) {
     const int l16 = lane & 15, g = lane >> 4;
     float s1[T::FM], s2[T::FM];
-    tile_stats<T, EPI == EPI_ROW_LN>(p, acc, lds, n_base, wm, wn, lane, s1, s2);
+    tile_stats<T, epi_ln(EPI)>(p, acc, lds, n_base, wm, wn, lane, s1, s2);
     const float inv_n = 1.0f / (float)p.N;
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
@@ -772,9 +859,8 @@ __device__ __forceinline__ void tile_store(const GemmParams& p, const f32x4 (&ac
                                            const Affine<T>& aff, const Bias<T>& bias, lds_char* lds,
                                            int m_base, int n_base, int wave, int wm, int wn,
                                            int lane, int ax) {
-  constexpr bool ROW = EPI == EPI_ROW_RMS || EPI == EPI_ROW_LN;
-  apply_store<T, ROW, EPI == EPI_LAZY_BIAS>(p, acc, mean, rstd, EPI == EPI_ROW_LN, aff, bias, lds,
-                                            m_base, n_base, wave, wm, wn, lane, ax);
+  apply_store<T, epi_row(EPI), EPI == EPI_LAZY_BIAS>(p, acc, mean, rstd, epi_ln(EPI), aff, bias,
+                                                    lds, m_base, n_base, wave, wm, wn, lane, ax);
 }
 
 // Per-column data the epilogue needs, loaded before the row statistics so
@@ -782,7 +868,7 @@ __device__ __forceinline__ void tile_store(const GemmParams& p, const f32x4 (&ac
 template <class T, int EPI>
 __device__ __forceinline__ void load_columns(const GemmParams& p, int n_base, int wn, int lane,
                                              Affine<T>& aff, Bias<T>& bias) {
-  if constexpr (EPI == EPI_ROW_RMS || EPI == EPI_ROW_LN) load_affine<T>(p, n_base, wn, lane, aff);
+  if constexpr (epi_row(EPI)) load_affine<T>(p, n_base, wn, lane, aff);
   if constexpr (EPI == EPI_LAZY_BIAS) load_bias<T>(p, n_base, wn, lane, bias);
 }
 
@@ -796,6 +882,8 @@ __device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds,
   f32x4 acc[T::FM][T::FN];
   float ss[T::FM];
   mainloop<T, epi_lazy(EPI)>(p, acc, ss, lds, lds_addr_of(lds), m_base, n_base, tid);
+  if constexpr (epi_res(EPI))
+    add_residual<T>(p, acc, lds, lds_addr_of(lds), m_base, n_base, wave, wm, wn, lane);
   Affine<T> aff;
   Bias<T> bias;
   load_columns<T, EPI>(p, n_base, wn, lane, aff, bias);
@@ -873,6 +961,8 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     f32x4 acc[T::FM][T::FN];
     float ss[T::FM];
     mainloop<T, epi_lazy(EPI)>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, t != first);
+    if constexpr (epi_res(EPI))
+      add_residual<T>(p, acc, lds, lds0, m_base, n_base, wave, wm, wn, lane);
     Affine<T> aff;
     Bias<T> bias;
     load_columns<T, EPI>(p, n_base, wn, lane, aff, bias);
@@ -1037,7 +1127,7 @@ __device__ __forceinline__ void xwg_merge_rows(const GemmParams& p, int tm, int 
   }
 }
 
-template <class T, bool LN>
+template <class T, bool LN, bool RES = false>
 __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
   static_assert(T::STG_OWN, "persistent tiles need their own output staging");
   __shared__ __attribute__((aligned(16))) char smem[T::LDS];
@@ -1071,6 +1161,7 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
     f32x4 acc[T::FM][T::FN];
     float ss[T::FM];
     mainloop<T, false>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, it > 0);
+    if constexpr (RES) add_residual<T>(p, acc, lds, lds0, m_base, n_base, wave, wm, wn, lane);
     xwg_publish<T, LN>(p, acc, lds, tm, tn, tid, tag);
     Affine<T> aff;
     load_affine<T>(p, n_base, wn, lane, aff);

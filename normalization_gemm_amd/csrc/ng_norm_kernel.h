@@ -6,6 +6,11 @@
 // variance, or mean of squares, over the row; eps inside the square root;
 // gamma/beta per column).  LayerNorm takes its variance in a second pass over
 // the registers, around the row mean.
+//
+// Residual form (RES): the row is S = X + R, a residual connection followed by
+// the norm ("Free normalization fusion", section "FlashNormAttention").  S is
+// rounded to bf16 as it is formed (the residual stream's storage type),
+// optionally stored to S_out, and normalized.
 #pragma once
 
 #include "ng_device.h"
@@ -16,6 +21,8 @@ struct NormParams {
   const uint16_t* X;
   const uint16_t* gamma;
   const uint16_t* beta;
+  const uint16_t* R;  // RES: bf16 [rows][cols]
+  uint16_t* S_out;    // RES: optional bf16 [rows][cols] output X + R
   uint16_t* Y;
   float* mean_out;
   float* rstd_out;
@@ -47,7 +54,7 @@ __device__ __forceinline__ float row_reduce(float v, float* red, int tid) {
 }
 
 // LPR lanes per row, CPL 16-byte chunks per lane; 256 threads per block.
-template <int LPR, int CPL>
+template <int LPR, int CPL, bool RES = false>
 __global__ void __launch_bounds__(256) norm_kernel(NormParams p) {
   constexpr int RPB = 256 / LPR;  // rows per block
   __shared__ float red[4];
@@ -63,6 +70,20 @@ __global__ void __launch_bounds__(256) norm_kernel(NormParams p) {
     const int idx = lr + c * LPR;
     v[c] = u32x4{0u, 0u, 0u, 0u};
     if (rv && idx < nch) v[c] = xr[idx];
+  }
+  if constexpr (RES) {
+    const u32x4* rr = (const u32x4*)(p.R + row * (long)p.cols);
+    u32x4* sr = (u32x4*)(p.S_out + row * (long)p.cols);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int idx = lr + c * LPR;
+      if (!rv || idx >= nch) continue;
+      const u32x4 r = rr[idx];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        v[c][w] = pack_bf16x2(bf16_lo(v[c][w]) + bf16_lo(r[w]), bf16_hi(v[c][w]) + bf16_hi(r[w]));
+      if (p.S_out) sr[idx] = v[c];
+    }
   }
   const bool ln = p.kind == 1;
   // pass 1: sum x (LayerNorm) or sum x^2 (RMSNorm)

@@ -32,7 +32,8 @@ def test_header_declares_expected_entry_points():
     names = header_functions()
     for n in ("ng_rmsnorm_gemm_lazy", "ng_gemm_layernorm", "ng_gemm_rmsnorm", "ng_gemm",
               "ng_norm", "ng_workspace_bytes", "ng_lazy_fold_affine",
-              "ng_rmsnorm_gemm_lazy_affine"):
+              "ng_rmsnorm_gemm_lazy_affine", "ng_gemm_add_rmsnorm", "ng_gemm_add_layernorm",
+              "ng_add_norm"):
         assert n in names
 
 
@@ -155,6 +156,51 @@ def test_lazy_affine_argument_checks():
     assert lazy(P, P2, None, P3, 64, 64, 64, 0, -1.0, None, None) == 1     # eps < 0
     assert lazy(P, P2, None, P3, 64, 100, 64, 0, 1e-6, None, None) == 2    # N % 8
     assert lazy(None, P2, None, None, 0, 64, 64, 0, 1e-6, None, None) == 0  # M = 0: no-op
+
+
+P4 = P + 0x300000
+P5 = P + 0x400000
+
+
+def test_residual_argument_checks():
+    rms, ln = _lib.ng_gemm_add_rmsnorm, _lib.ng_gemm_add_layernorm
+    ws = _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_ADD_LAYERNORM, 64, 4096, 64)
+    assert ws == _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 64, 4096, 64) > 0
+    assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_ADD_RMSNORM, 64, 4096, 64) == ws
+    assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_ADD_RMSNORM, 64, 256, 64) == 0
+    # R required, 16-byte aligned; S_out optional, aligned, not C
+    assert rms(P, P2, None, None, P3, None, 64, 128, 64, 0, 1e-6, None, None, 0, None) == 1
+    assert rms(P, P2, BAD, None, P3, None, 64, 128, 64, 0, 1e-6, None, None, 0, None) == 1
+    assert rms(P, P2, P4, None, P3, BAD, 64, 128, 64, 0, 1e-6, None, None, 0, None) == 1
+    assert rms(P, P2, P4, None, P3, P3, 64, 128, 64, 0, 1e-6, None, None, 0, None) == 1
+    assert ln(P, P2, P4, None, None, P3, P3, 64, 128, 64, 0, 1e-5, None, None, None, 0,
+              None) == 1
+    # gamma/beta misaligned, bad eps, N % 8
+    assert ln(P, P2, P4, P + 8, None, P3, None, 64, 128, 64, 0, 1e-5, None, None, None, 0,
+              None) == 1
+    assert ln(P, P2, P4, None, P + 8, P3, None, 64, 128, 64, 0, 1e-5, None, None, None, 0,
+              None) == 1
+    assert rms(P, P2, P4, None, P3, None, 64, 128, 64, 0, -1.0, None, None, 0, None) == 1
+    assert rms(P, P2, P4, None, P3, None, 64, 100, 64, 0, 1e-6, None, None, 0, None) == 2
+    # wide rows need the workspace
+    assert ln(P, P2, P4, None, None, P3, None, 64, 4096, 64, 0, 1e-5, None, None, None, 0,
+              None) == 3
+    assert rms(P, P2, P4, None, P3, P5, 64, 4096, 64, 0, 1e-6, None, P, ws - 16, None) == 3
+    # M = 0: a no-op, even with R NULL
+    assert rms(None, P2, None, None, None, None, 0, 4096, 64, 0, 1e-6, None, None, 0, None) == 0
+    assert ln(None, P2, None, None, None, None, None, 0, 128, 64, 0, 1e-5, None, None, None, 0,
+              None) == 0
+
+
+def test_add_norm_argument_checks():
+    f = _lib.ng_add_norm
+    assert f(P, None, None, None, P2, None, 4, 64, 0, 1e-6, None, None, None) == 1   # R NULL
+    assert f(P, BAD, None, None, P2, None, 4, 64, 0, 1e-6, None, None, None) == 1    # R misaligned
+    assert f(P, P3, None, None, P2, BAD, 4, 64, 0, 1e-6, None, None, None) == 1      # S_out misaligned
+    assert f(P, P3, None, None, P2, P2, 4, 64, 0, 1e-6, None, None, None) == 1       # S_out == Y
+    assert f(P, P3, None, None, P2, None, 4, 64, 0, 1e-6, P4, None, None) == 1       # RMS mean_out
+    assert f(P, P3, None, None, P2, None, 4, 60, 1, 1e-6, None, None, None) == 2
+    assert f(None, None, None, None, None, None, 0, 64, 1, 1e-6, None, None, None) == 0
 
 
 def test_workspace_helpers_argument_checks():

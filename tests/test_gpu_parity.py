@@ -256,6 +256,133 @@ def test_cross_workgroup_many_column_tiles(M, N, kind):
     _check_stat("xwg wide rstd", rstd, rref)
 
 
+# -------------------------------------- residual add before the post-norm
+def _residual_call(kind, x, layout, eps, s_out=None, out=None, R=None, stats=True):
+    """Run gemm_add_{layer,rms}norm on the inputs; return (C, mean, rstd)."""
+    M = x.A.shape[0]
+    A, B = up(x.A), up(b_for_layout(x.B, layout))
+    R = up(x.R) if R is None else R
+    g = up(x.gamma) if x.gamma is not None else None
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda") if stats else None
+    mean = None
+    if kind == "layer":
+        b = up(x.beta) if x.beta is not None else None
+        mean = torch.empty(M, dtype=torch.float32, device="cuda") if stats else None
+        C = ng.gemm_add_layernorm(A, B, R, g, b, eps=eps, b_layout=layout, out=out, s_out=s_out,
+                                  mean_out=mean, rstd_out=rstd)
+    else:
+        C = ng.gemm_add_rmsnorm(A, B, R, g, eps=eps, b_layout=layout, out=out, s_out=s_out,
+                                rstd_out=rstd)
+    return C, mean, rstd
+
+
+def _residual_ref(kind, x, eps, rows=None):
+    A = x.A if rows is None else x.A[rows]
+    R = x.R if rows is None else x.R[rows]
+    if kind == "layer":
+        Y, mean, rstd, S = oracle.gemm_add_layernorm(A, x.B, R, eps, x.gamma, x.beta)
+    else:
+        Y, rstd, S = oracle.gemm_add_rmsnorm(A, x.B, R, eps, x.gamma)
+        mean = None
+    return Y, mean, rstd, S
+
+
+# row-local (N <= 128, N <= 256) and cross-workgroup shapes, ragged in M, N, K
+SMALL_RES = [(300, 128, 96), (64, 64, 64), (1000, 256, 136), (129, 200, 520), (517, 1000, 200),
+             (33, 2048, 128), (260, 264, 64)]
+
+
+@pytest.mark.parametrize("kind", ["layer", "rms"])
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("M,N,K", SMALL_RES)
+def test_gemm_add_norm_small(M, N, K, layout, kind):
+    log("gemm_add_%snorm M=%d N=%d K=%d %s" % (kind, M, N, K, layout))
+    affine = (M + N) % 2 == 0
+    x = workloads.make_inputs(M, N, K, seed=5 * M + N + K, gamma=affine,
+                              beta=affine and kind == "layer", residual=True)
+    S_dev = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    eps = 1e-5 if kind == "layer" else 1e-6
+    C, mean, rstd = _residual_call(kind, x, layout, eps, s_out=S_dev)
+    torch.cuda.synchronize()
+    Y, mref, rref, S = _residual_ref(kind, x, eps)
+    _check("gemm_add_%snorm" % kind, down(C), Y)
+    _check("gemm_add s_out", down(S_dev), S)
+    _check_stat("gemm_add rstd", rstd, rref)
+    if mean is not None:
+        got_mean = mean.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(got_mean - mref) / (1.0 + np.abs(mref))) <= 1e-3
+
+
+@pytest.mark.parametrize("kind", ["layer", "rms"])
+@pytest.mark.parametrize("N", [128, 256, 1000])
+def test_gemm_add_norm_in_place(N, kind):
+    # R may be the buffer of the sum output or of the normalized output
+    M, K = 300, 72
+    x = workloads.make_inputs(M, N, K, seed=N + 7, gamma=True, beta=True, residual=True)
+    eps = 1e-5
+    Y, _, _, S = _residual_ref(kind, x, eps)
+    R1 = up(x.R)
+    C1, _, _ = _residual_call(kind, x, "kn", eps, s_out=R1, R=R1, stats=False)
+    R2 = up(x.R)
+    C2, _, _ = _residual_call(kind, x, "kn", eps, out=R2, R=R2, stats=False)
+    torch.cuda.synchronize()
+    _check("in place: s_out is R", down(R1), S)
+    _check("in place: s_out is R (C)", down(C1), Y)
+    _check("in place: out is R", down(R2), Y)
+    assert C2.data_ptr() == R2.data_ptr()
+
+
+def test_gemm_add_norm_cross_workgroup_rounds_ragged():
+    # 10 column tiles -> 25 row blocks per round; 31 row blocks -> 2 rounds
+    M, N, K = 256 * 30 + 100, 256 * 9 + 24, 136
+    for kind, layout in (("layer", "nk"), ("rms", "kn")):
+        log("xwg residual rounds %s M=%d N=%d K=%d %s" % (kind, M, N, K, layout))
+        x = workloads.make_inputs(M, N, K, seed=23, gamma=True, beta=kind == "layer",
+                                  residual=True)
+        eps = 1e-5 if kind == "layer" else 1e-6
+        C, _, rstd = _residual_call(kind, x, layout, eps)
+        torch.cuda.synchronize()
+        Y, _, rref, _ = _residual_ref(kind, x, eps)
+        _check("xwg residual rounds %s" % kind, down(C), Y)
+        _check_stat("xwg residual rstd", rstd, rref)
+
+
+def test_gemm_add_norm_zero_residual_matches_plain():
+    # R = 0: the residual forms give exactly the plain epilogue's result
+    for N in (128, 1000):
+        x = workloads.make_inputs(200, N, 64, seed=N, gamma=True, beta=True)
+        A, B, g, b = up(x.A), up(x.B), up(x.gamma), up(x.beta)
+        Z = torch.zeros((200, N), dtype=torch.bfloat16, device="cuda")
+        C0 = ng.gemm_layernorm(A, B, g, b, eps=1e-5)
+        C1 = ng.gemm_add_layernorm(A, B, Z, g, b, eps=1e-5)
+        R0 = ng.gemm_rmsnorm(A, B, g, eps=1e-6)
+        R1 = ng.gemm_add_rmsnorm(A, B, Z, g, eps=1e-6)
+        torch.cuda.synchronize()
+        assert torch.equal(C0.view(torch.int16), C1.view(torch.int16)), N
+        assert torch.equal(R0.view(torch.int16), R1.view(torch.int16)), N
+
+
+@pytest.mark.parametrize("kind", ["rms", "layer"])
+@pytest.mark.parametrize("rows,cols", [(1, 8), (37, 128), (300, 136), (65, 1000), (9, 8200)])
+def test_add_norm_small(rows, cols, kind):
+    log("add_norm %s rows=%d cols=%d" % (kind, rows, cols))
+    x = workloads.make_inputs(rows, cols, 8, seed=rows * 3 + cols, gamma=True, beta=True,
+                              residual=True)
+    X = workloads.f32_to_bf16_bits(np.random.default_rng(rows).standard_normal(
+        (rows, cols), dtype=np.float32))
+    Sd = torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda")
+    rstd = torch.empty(rows, dtype=torch.float32, device="cuda")
+    eps = 1e-5
+    Yd = ng.add_norm(up(X), up(x.R), kind, up(x.gamma), up(x.beta), eps=eps, s_out=Sd,
+                     rstd_out=rstd)
+    torch.cuda.synchronize()
+    S = oracle.bf16_to_f64(X) + oracle.bf16_to_f64(x.R)
+    Y, _, rref = oracle.norm(S, kind, eps, x.gamma, x.beta)
+    _check("add_norm %s" % kind, down(Yd), Y)
+    _check("add_norm s_out", down(Sd), S)
+    _check_stat("add_norm rstd", rstd, rref)
+
+
 # ------------------------------------------------------------ edge cases
 def test_empty_M_leaves_output_untouched():
     A = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
@@ -335,6 +462,10 @@ def _workload_case(w, layout="kn", n_rows=24):
     if w.op == workloads.OP_LAZY:
         C = ng.rmsnorm_gemm_lazy(A, B, eps=w.eps, b_layout=layout)
         ref = oracle.rmsnorm_gemm_lazy(x.A[rows], x.B, w.eps)[0]
+    elif w.op in (workloads.OP_GEMM_ADD_RMSNORM, workloads.OP_GEMM_ADD_LAYERNORM):
+        kind = "layer" if w.op == workloads.OP_GEMM_ADD_LAYERNORM else "rms"
+        C, _, _ = _residual_call(kind, x, layout, w.eps, stats=False)
+        ref = _residual_ref(kind, x, w.eps, rows)[0]
     elif w.op == workloads.OP_GEMM_RMSNORM:
         C = ng.gemm_rmsnorm(A, B, g, eps=w.eps, b_layout=layout)
         ref = oracle.gemm_rmsnorm(x.A[rows], x.B, w.eps, x.gamma)[0]
@@ -350,6 +481,24 @@ def _workload_case(w, layout="kn", n_rows=24):
 @pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS])
 def test_named_workload_full_size(name):
     _workload_case(workloads.WORKLOAD_BY_NAME[name])
+
+
+@pytest.mark.parametrize("name", [w.name for w in workloads.NEXT_WORKLOADS
+                                  if w.op != workloads.OP_LAZY_AFFINE])
+def test_residual_workload_full_size(name):
+    _workload_case(workloads.WORKLOAD_BY_NAME[name])
+
+
+def test_residual_unfused_pair_full_size():
+    # the unfused baseline of the residual form: ng_gemm, then ng_add_norm
+    w = workloads.WORKLOAD_BY_NAME["gemm_add_rms_16384x4096x8192"]
+    x = workloads.workload_inputs(w)
+    rows = sample_rows(w.M, 16, seed=4)
+    X = ng.gemm(up(x.A), up(x.B))
+    Y = ng.add_norm(X, up(x.R), "rms", up(x.gamma), eps=w.eps)
+    torch.cuda.synchronize()
+    ref = _residual_ref("rms", x, w.eps, rows)[0]
+    _check("unfused gemm->add_norm", down(Y[torch.as_tensor(rows, device="cuda")]), ref)
 
 
 def test_named_workload_nk_layout_large():

@@ -9,7 +9,8 @@ Input recipe (the same for every workload):
 * ``numpy.random.default_rng(seed)`` (PCG64), values drawn in float32 in a
   fixed order: A's standard normals ``[M, K]``, then the per-row scales of A
   (when the workload has them), then B's standard normals ``[K, N]`` times
-  ``sqrt(1/K)``, then gamma, then beta.
+  ``sqrt(1/K)``, then gamma, then beta, then (residual forms) the residual
+  R's standard normals ``[M, N]`` (unit variance, the scale of ``A @ B``).
 * ``N(mu, v)`` in a workload description is read with ``v`` as the variance,
   so ``B ~ N(0, 1/K)`` keeps ``A @ B`` at unit variance per element and
   ``gamma ~ N(1, 0.1)`` has standard deviation ``sqrt(0.1)``.
@@ -35,6 +36,8 @@ OP_LAZY = "rmsnorm_gemm_lazy"
 OP_GEMM_RMSNORM = "gemm_rmsnorm"
 OP_GEMM_LAYERNORM = "gemm_layernorm"
 OP_LAZY_AFFINE = "rmsnorm_gemm_lazy_affine"
+OP_GEMM_ADD_RMSNORM = "gemm_add_rmsnorm"
+OP_GEMM_ADD_LAYERNORM = "gemm_add_layernorm"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -48,6 +51,7 @@ class Workload:
     row_scale: bool = False
     gamma: bool = False
     beta: bool = False
+    residual: bool = False
     description: str = ""
 
     @property
@@ -75,12 +79,21 @@ WORKLOADS = [
 ]
 # Further forms beyond the five named workloads, on the same shapes: Lazy
 # Pre-Norm with a per-column affine (gamma, beta of length K) folded into the
-# weights.
+# weights, and the post-norm epilogues with a residual added to the product
+# first (one narrow-row and one wide-row case).
 NEXT_WORKLOADS = [
     Workload("lazy_rms_affine_32768x4096x4096", OP_LAZY_AFFINE, 32768, 4096, 4096, 1e-6,
              row_scale=True, gamma=True, beta=True,
              description="Lazy Pre-Norm RMSNorm with gamma and beta (length K) folded into B, "
                          "A 32768x4096 @ B 4096x4096"),
+    Workload("gemm_add_ln_65536x512x128", OP_GEMM_ADD_LAYERNORM, 65536, 128, 512, 1e-5,
+             residual=True,
+             description="GEMM + residual add + LayerNorm epilogue (no affine), "
+                         "A 65536x512 @ B 512x128 + R 65536x128"),
+    Workload("gemm_add_rms_16384x4096x8192", OP_GEMM_ADD_RMSNORM, 16384, 8192, 4096, 1e-6,
+             gamma=True, residual=True,
+             description="GEMM + residual add + RMSNorm epilogue with gamma over N=8192, "
+                         "A 16384x4096 @ B 4096x8192 + R 16384x8192"),
 ]
 WORKLOAD_BY_NAME = {w.name: w for w in WORKLOADS + NEXT_WORKLOADS}
 
@@ -104,11 +117,12 @@ class Inputs:
     B: np.ndarray                   # uint16 bits [K, N] (logical layout)
     gamma: Optional[np.ndarray]     # uint16 bits [N] or None
     beta: Optional[np.ndarray]      # uint16 bits [N] or None
+    R: Optional[np.ndarray] = None  # uint16 bits [M, N] or None (residual forms)
 
 
 def make_inputs(M: int, N: int, K: int, *, seed: int = 0, row_scale: bool = False,
                 gamma: bool = False, beta: bool = False,
-                gamma_len: Optional[int] = None) -> Inputs:
+                gamma_len: Optional[int] = None, residual: bool = False) -> Inputs:
     """Draw one seeded input set in the fixed order documented above.
 
     ``gamma_len`` overrides the length of gamma/beta (default N).
@@ -130,11 +144,14 @@ def make_inputs(M: int, N: int, K: int, *, seed: int = 0, row_scale: bool = Fals
         g = f32_to_bf16_bits(1.0 + math.sqrt(0.1) * rng.standard_normal(L, dtype=np.float32))
     if beta:
         bt = f32_to_bf16_bits(math.sqrt(0.1) * rng.standard_normal(L, dtype=np.float32))
-    return Inputs(A, B, g, bt)
+    R = None
+    if residual:
+        R = f32_to_bf16_bits(rng.standard_normal((M, N), dtype=np.float32))
+    return Inputs(A, B, g, bt, R)
 
 
 def workload_inputs(w: Workload, seed: int = 0) -> Inputs:
     # the pre-norm affine of the Lazy form acts on rows of A (length K)
     gl = w.K if w.op == OP_LAZY_AFFINE else None
     return make_inputs(w.M, w.N, w.K, seed=seed, row_scale=w.row_scale,
-                       gamma=w.gamma, beta=w.beta, gamma_len=gl)
+                       gamma=w.gamma, beta=w.beta, gamma_len=gl, residual=w.residual)
