@@ -21,6 +21,8 @@ from .normgemm_oracle import (  # noqa: F401
     gemm_rmsnorm,
     gemm_layernorm,
     gemm_add_rmsnorm,
+    layernorm_gemm_prenorm,
+    layernorm_gemm_fold,
     gemm_add_layernorm,
     norm,
     rel_err,

@@ -146,6 +146,35 @@ def lazy_fold_affine(B, gamma=None, beta=None) -> Tuple[np.ndarray, np.ndarray]:
     return g[:, None] * Bf, b @ Bf
 
 
+def layernorm_gemm_prenorm(A, B, eps: float, gamma=None, beta=None
+                           ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """C = LayerNorm(A) @ B: a pre-LayerNorm over each row of A (length K),
+    with per-column gamma/beta of length K, then the product.
+
+    The "Lazy Pre-Norm" section states that its row-scale identity does not
+    cover LayerNorm; "RMSNorm fusion on Ascend", section 2.2, fuses a norm
+    with the following matmul in two stages: row statistics first, then the
+    normalized tiles enter the product.  The oracle computes the definition
+    as written: normalize each row of A (section 1.1), apply gamma and beta,
+    then multiply by B.  Returns (C, mean, rstd) per row of A.
+    """
+    Y, mean, rstd = layer_norm_rows(A, eps, gamma, beta)
+    return Y @ _f64(B), mean, rstd
+
+
+def layernorm_gemm_fold(B, gamma=None, beta=None
+                        ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """The weight fold of the pre-LayerNorm product, in float64:
+    B_folded = diag(gamma) B, colsum = 1^T B_folded (column sums of the folded
+    weights) and bias = beta^T B.  Each row of LayerNorm(A) is
+    (a - mean) * rstd * gamma + beta, and the product is linear, so
+    LayerNorm(A) @ B = rstd * (A @ B_folded - mean * colsum) + bias, with
+    mean and rstd per row of A and colsum, bias per output column.
+    """
+    Bf, bias = lazy_fold_affine(B, gamma, beta)
+    return Bf, Bf.sum(axis=0), bias
+
+
 def gemm_rmsnorm(A, B, eps: float, gamma=None) -> Tuple[np.ndarray, np.ndarray]:
     """Y = RMSNorm(A @ B) over each full output row (H = N), optional gamma.
 

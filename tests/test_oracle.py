@@ -77,6 +77,8 @@ def test_hand_worked_examples(case):
     elif case["op"] == "gemm_rmsnorm":
         C, rstd = oracle.gemm_rmsnorm(A, B, eps, gamma)
         mean = None
+    elif case["op"] == "layernorm_gemm_prenorm":
+        C, mean, rstd = oracle.layernorm_gemm_prenorm(A, B, eps, gamma, beta)
     elif case["op"] == "gemm_add_layernorm":
         R = np.array(case["R"], dtype=np.float64)
         C, mean, rstd, S = oracle.gemm_add_layernorm(A, B, R, eps, gamma, beta)
@@ -315,6 +317,64 @@ def test_residual_is_added_before_the_statistics():
     # LayerNorm output rows of the sum are zero-mean, unit-variance
     np.testing.assert_allclose(Y.mean(axis=1), 0.0, atol=1e-12)
     np.testing.assert_allclose(Y.var(axis=1), 1.0, rtol=1e-4)
+
+
+def test_prenorm_layernorm_invariances():
+    # LayerNorm removes a per-row shift and (eps = 0) a positive per-row
+    # scale of A, so the product does not see them
+    rng = np.random.default_rng(41)
+    A = rng.standard_normal((6, 16))
+    B = rng.standard_normal((16, 5))
+    g = rng.uniform(0.5, 2.0, size=16)
+    b = rng.standard_normal(16)
+    C, mean, rstd = oracle.layernorm_gemm_prenorm(A, B, 0.0, g, b)
+    shift = rng.uniform(-50, 50, size=(6, 1))
+    C2, mean2, rstd2 = oracle.layernorm_gemm_prenorm(A + shift, B, 0.0, g, b)
+    np.testing.assert_allclose(C2, C, rtol=1e-9, atol=1e-9)
+    np.testing.assert_allclose(mean2, mean + shift[:, 0], rtol=1e-12)
+    scale = rng.uniform(0.1, 10, size=(6, 1))
+    C3, _, rstd3 = oracle.layernorm_gemm_prenorm(A * scale, B, 0.0, g, b)
+    np.testing.assert_allclose(C3, C, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(rstd3, rstd / scale[:, 0], rtol=1e-12)
+    # beta enters after the norm, as the row vector beta^T B on every row
+    C0, _, _ = oracle.layernorm_gemm_prenorm(A, B, 0.0, g, None)
+    np.testing.assert_allclose(C - C0, np.broadcast_to(b @ B, C.shape), rtol=1e-12, atol=1e-12)
+
+
+def test_prenorm_layernorm_of_zero_mean_rows_is_rmsnorm():
+    # rows with mean exactly 0: LayerNorm equals RMSNorm (the RMSNorm oracle
+    # is pinned on its own)
+    rng = np.random.default_rng(42)
+    X = rng.standard_normal((5, 12))
+    X = X - X.mean(axis=1, keepdims=True)
+    B = rng.standard_normal((12, 7))
+    g = rng.uniform(0.5, 2.0, size=12)
+    C, mean, rstd = oracle.layernorm_gemm_prenorm(X, B, 1e-5, g)
+    Yr, rr = oracle.rms_norm_rows(X, 1e-5, g)
+    np.testing.assert_allclose(C, Yr @ B, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(rstd, rr, rtol=1e-12)
+    np.testing.assert_allclose(mean, 0.0, atol=1e-15)
+
+
+def test_prenorm_layernorm_fold_identity():
+    # rstd * (A @ B_folded - mean * colsum) + bias reproduces the definition;
+    # leaving out the mean term, or taking colsum of B instead of B_folded,
+    # does not
+    rng = np.random.default_rng(43)
+    A = rng.standard_normal((4, 24)) + 3.0
+    B = rng.standard_normal((24, 6))
+    g = rng.uniform(0.5, 2.0, size=24)
+    b = rng.standard_normal(24)
+    C, mean, rstd = oracle.layernorm_gemm_prenorm(A, B, 1e-5, g, b)
+    Bf, colsum, bias = oracle.layernorm_gemm_fold(B, g, b)
+    np.testing.assert_allclose(Bf, g[:, None] * B, rtol=0)
+    np.testing.assert_allclose(bias, b @ B, rtol=1e-14)
+    got = rstd[:, None] * (A @ Bf - mean[:, None] * colsum[None, :]) + bias[None, :]
+    np.testing.assert_allclose(got, C, rtol=1e-10, atol=1e-10)
+    wrong = rstd[:, None] * (A @ Bf) + bias[None, :]
+    assert np.max(np.abs(wrong - C)) > 1e-1
+    wrong = rstd[:, None] * (A @ Bf - mean[:, None] * B.sum(axis=0)[None, :]) + bias[None, :]
+    assert np.max(np.abs(wrong - C)) > 1e-1
 
 
 def test_lazy_is_not_layernorm_prenorm():
