@@ -127,6 +127,8 @@ def algorithmic_bytes(w: workloads.Workload) -> int:
     b = 2 * (w.M * w.K + w.K * w.N + w.M * w.N)
     if w.op == workloads.OP_LAZY_AFFINE:
         return b + 4 * w.N
+    if w.op == workloads.OP_PRENORM_LN:
+        return b + 8 * w.N  # fp32 colsum and bias
     b += 2 * w.N * (int(w.gamma) + int(w.beta))
     if w.residual:
         b += 2 * w.M * w.N
@@ -136,9 +138,13 @@ def algorithmic_bytes(w: workloads.Workload) -> int:
 def norm_bytes(w: workloads.Workload) -> int:
     """Standalone norm of the unfused pair: read + write the normalized matrix
     (and read R for the residual forms)."""
-    lazy = w.op in (workloads.OP_LAZY, workloads.OP_LAZY_AFFINE)
-    rows, cols = (w.M, w.K) if lazy else (w.M, w.N)
+    rows, cols = (w.M, w.K) if prenorm(w) else (w.M, w.N)
     return (6 if w.residual else 4) * rows * cols
+
+
+def prenorm(w: workloads.Workload) -> bool:
+    """The norm acts on A before the product (the unfused pair runs it first)."""
+    return w.op in (workloads.OP_LAZY, workloads.OP_LAZY_AFFINE, workloads.OP_PRENORM_LN)
 
 
 def kernel_label(w: workloads.Workload) -> str:
@@ -147,8 +153,9 @@ def kernel_label(w: workloads.Workload) -> str:
     epi = {workloads.OP_LAZY: "EPI_LAZY", workloads.OP_LAZY_AFFINE: "EPI_LAZY_BIAS",
            workloads.OP_GEMM_RMSNORM: "EPI_ROW_RMS", workloads.OP_GEMM_LAYERNORM: "EPI_ROW_LN",
            workloads.OP_GEMM_ADD_RMSNORM: "EPI_ROW_RMS_RES",
-           workloads.OP_GEMM_ADD_LAYERNORM: "EPI_ROW_LN_RES"}[w.op]
-    if w.op in (workloads.OP_LAZY, workloads.OP_LAZY_AFFINE):
+           workloads.OP_GEMM_ADD_LAYERNORM: "EPI_ROW_LN_RES",
+           workloads.OP_PRENORM_LN: "EPI_PRE_LN"}[w.op]
+    if prenorm(w):
         base = "gemm_kernel" if w.N <= 128 else "gemm_persistent_kernel"
     else:
         base = "gemm_kernel" if w.N <= 256 else "gemm_xwg_kernel"
@@ -193,7 +200,7 @@ class Bench:
             return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(
                 torch.bfloat16)
 
-        lazy = w.op in (workloads.OP_LAZY, workloads.OP_LAZY_AFFINE)
+        lazy = prenorm(w)
         per_copy = 2 * (w.M * w.K + w.M * w.N) + (2 * w.M * w.K if lazy else 0)
         per_copy += 2 * w.M * w.N if w.residual else 0
         self.R = max(1, min(8, math.ceil(ROTATE_BYTES / per_copy)))
@@ -209,14 +216,20 @@ class Bench:
         # unfused pair intermediates: the normalized A of the lazy form's
         # pair holds real values (the GEMM's speed depends on its data)
         if lazy:
-            An0 = ng.norm(A0, "rms", self.gamma, self.beta, eps=w.eps)
+            kind = "layer" if w.op == workloads.OP_PRENORM_LN else "rms"
+            An0 = ng.norm(A0, kind, self.gamma, self.beta, eps=w.eps)
             self.An = [An0] + [An0.clone() for _ in range(self.R - 1)]
         if w.op == workloads.OP_LAZY_AFFINE:
             # the weight fold is a one-off transform, outside the timed calls
             self.Bf, self.bias = ng.lazy_fold_affine(self.B, self.gamma, self.beta)
+        if w.op == workloads.OP_PRENORM_LN:
+            self.Bf, self.colsum, self.bias = ng.layernorm_gemm_fold(self.B, self.gamma, self.beta)
+            self.mean = torch.empty(w.M, dtype=torch.float32, device=dev)
+            self.rstd = torch.empty(w.M, dtype=torch.float32, device=dev)
         self.ws = None
         op = {workloads.OP_LAZY: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_LAZY_AFFINE: ng.NG_OP_RMSNORM_GEMM_LAZY,
+              workloads.OP_PRENORM_LN: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_GEMM_RMSNORM: ng.NG_OP_GEMM_RMSNORM,
               workloads.OP_GEMM_LAYERNORM: ng.NG_OP_GEMM_LAYERNORM,
               workloads.OP_GEMM_ADD_RMSNORM: ng.NG_OP_GEMM_ADD_RMSNORM,
@@ -250,6 +263,14 @@ class Bench:
                                      eps, None, st)))
                 self._gemm.append((lib.ng_gemm, (An, B, C, M, N, K, 0, st)))
                 self._norm.append((lib.ng_norm, (A, g, b, An, M, K, 0, eps, None, None, st)))
+            elif w.op == workloads.OP_PRENORM_LN:
+                An = self.An[r].data_ptr()
+                self._fused.append((lib.ng_layernorm_gemm_prenorm,
+                                    (A, self.Bf.data_ptr(), self.colsum.data_ptr(),
+                                     self.bias.data_ptr(), C, M, N, K, 0, eps,
+                                     self.mean.data_ptr(), self.rstd.data_ptr(), st)))
+                self._gemm.append((lib.ng_gemm, (An, B, C, M, N, K, 0, st)))
+                self._norm.append((lib.ng_norm, (A, g, b, An, M, K, 1, eps, None, None, st)))
             elif w.op == workloads.OP_LAZY:
                 An = self.An[r].data_ptr()
                 self._fused.append((lib.ng_rmsnorm_gemm_lazy,
@@ -299,7 +320,7 @@ class Bench:
         self._call(self._norm, i)
 
     def pair(self, i):
-        if self.w.op == workloads.OP_LAZY:
+        if prenorm(self.w):
             self.norm_only(i)
             self.gemm_only(i)
         else:
@@ -363,8 +384,9 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
     def sample(rows):
         return workloads.make_inputs(rows, w.N, w.K, seed=1, row_scale=w.row_scale,
                                      gamma=w.gamma, beta=w.beta,
-                                     gamma_len=w.K if w.op == workloads.OP_LAZY_AFFINE else None,
-                                     residual=w.residual)
+                                     gamma_len=w.K if w.op in (workloads.OP_LAZY_AFFINE,
+                                                               workloads.OP_PRENORM_LN) else None,
+                                     residual=w.residual, row_shift=w.row_shift)
 
     rows = min(w.M, 64)
     x = sample(rows)
@@ -375,6 +397,8 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
             oracle.rmsnorm_gemm_lazy(x.A, x.B, w.eps)
         elif w.op == workloads.OP_LAZY_AFFINE:
             oracle.rmsnorm_gemm_lazy_affine(x.A, x.B, w.eps, x.gamma, x.beta)
+        elif w.op == workloads.OP_PRENORM_LN:
+            oracle.layernorm_gemm_prenorm(x.A, x.B, w.eps, x.gamma, x.beta)
         elif w.op == workloads.OP_GEMM_RMSNORM:
             oracle.gemm_rmsnorm(x.A, x.B, w.eps, x.gamma)
         elif w.op == workloads.OP_GEMM_ADD_RMSNORM:

@@ -103,6 +103,37 @@ int ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded, const
                                 float eps, float* rstd_out, void* stream);
 
 /*
+ * Pre-LayerNorm fused with the following product: C = LayerNorm(A) @ B with
+ * the norm over each row of A (H = K; "RMSNorm fusion on Ascend", section 1.1)
+ * and per-column gamma/beta of length K.  Two stages ("RMSNorm fusion on
+ * Ascend", section 2.2: row statistics first, then the product of the
+ * normalized tiles): a pre-pass writes mean[m] and rstd[m] of every row of A,
+ * then the product applies the norm through its linearity,
+ *   C = rstd * (A @ B' - mean * colsum) + bias,
+ * so A is read as stored and never rewritten.  ("Free normalization fusion",
+ * section "Lazy Pre-Norm", notes that the plain row-scale form does not cover
+ * LayerNorm; the mean term above is what it lacks.)
+ *
+ * ng_layernorm_gemm_fold (one-off weight transform): B_folded = bf16(diag(gamma)
+ * B) in B's layout (may be B itself), colsum[n] = sum_k B_folded[k][n] (fp32,
+ * over the rounded folded weights), bias[n] = sum_k beta[k] B[k][n] (fp32).
+ * gamma, beta: bf16 [K] or NULL (1 and 0); colsum required; bias may be NULL
+ * only when beta is NULL.  colsum/bias 16-byte aligned.
+ *
+ * ng_layernorm_gemm_prenorm: A [M, K] bf16, B_folded/colsum/bias from the
+ * fold (bias may be NULL), C [M, N] bf16; mean, rstd: float32 [M] outputs,
+ * required (the pre-pass writes them, the product reads them).  K at most
+ * 65536 (else NG_ERR_UNSUPPORTED).  Needs no workspace.
+ */
+int ng_layernorm_gemm_fold(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
+                           ng_bf16* B_folded, float* colsum, float* bias, int64_t K, int64_t N,
+                           int b_layout, void* stream);
+
+int ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, const float* colsum,
+                              const float* bias, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+                              int b_layout, float eps, float* mean, float* rstd, void* stream);
+
+/*
  * GEMM with an RMSNorm epilogue over each full output row (H = N):
  *   X = A @ B;  rstd[m] = 1 / sqrt((1/N) sum_n X[m,n]^2 + eps);
  *   C[m,n] = X[m,n] * rstd[m] * gamma[n]        (gamma NULL means 1)

@@ -20,7 +20,8 @@ from ._lib import (  # noqa: F401
     NG_OP_GEMM, NG_OP_GEMM_ADD_LAYERNORM, NG_OP_GEMM_ADD_RMSNORM, NG_OP_GEMM_LAYERNORM,
     NG_OP_GEMM_RMSNORM, NG_OP_NORM, NG_OP_RMSNORM_GEMM_LAZY,
     ng_gemm, ng_gemm_add_layernorm, ng_gemm_add_rmsnorm, ng_gemm_layernorm, ng_gemm_rmsnorm,
-    ng_add_norm, ng_last_error, ng_lazy_fold_affine, ng_norm,
+    ng_add_norm, ng_last_error, ng_layernorm_gemm_fold, ng_layernorm_gemm_prenorm,
+    ng_lazy_fold_affine, ng_norm,
     ng_rmsnorm_gemm_lazy, ng_rmsnorm_gemm_lazy_affine, ng_status_string, ng_workspace_bytes,
     ng_workspace_reset, ng_workspace_status,
 )
@@ -28,7 +29,7 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "NormGemmError", "rmsnorm_gemm_lazy", "lazy_fold_affine", "rmsnorm_gemm_lazy_affine",
     "gemm_rmsnorm", "gemm_layernorm", "gemm_add_rmsnorm", "gemm_add_layernorm", "gemm", "norm",
-    "add_norm",
+    "add_norm", "layernorm_gemm_fold", "layernorm_gemm_prenorm",
     "Workspace", "library_path",
 ]
 
@@ -189,6 +190,56 @@ def rmsnorm_gemm_lazy_affine(A, B_folded, bias=None, *, eps: float = 1e-6, b_lay
     _check(ng_rmsnorm_gemm_lazy_affine(_ptr(A), _ptr(B_folded), _ptr(bias), _ptr(C), M, N, K, lay,
                                        float(eps), _ptr(rstd_out), _stream(stream)),
            "ng_rmsnorm_gemm_lazy_affine")
+    return C
+
+
+def layernorm_gemm_fold(B, gamma=None, beta=None, *, b_layout="kn", out=None, stream=None):
+    """One-off weight fold of the pre-LayerNorm product: returns (B_folded,
+    colsum, bias) with B_folded = diag(gamma) B (bf16, B's layout), colsum the
+    fp32 column sums of B_folded and bias = beta^T B (fp32 [N])."""
+    torch = _torch()
+    _dev_bf16(B, "B")
+    lay = _layout(b_layout)
+    if B.dim() != 2:
+        raise ValueError("B must be 2-D")
+    K, N = B.shape if lay == NG_B_KN else (B.shape[1], B.shape[0])
+    if gamma is not None:
+        _dev_bf16(gamma, "gamma")
+    if beta is not None:
+        _dev_bf16(beta, "beta")
+    Bf = out if out is not None else torch.empty_like(B)
+    _dev_bf16(Bf, "out")
+    colsum = torch.empty(N, dtype=torch.float32, device=B.device)
+    bias = torch.empty(N, dtype=torch.float32, device=B.device)
+    _check(ng_layernorm_gemm_fold(_ptr(B), _ptr(gamma), _ptr(beta), _ptr(Bf), _ptr(colsum),
+                                  _ptr(bias), K, N, lay, _stream(stream)), "ng_layernorm_gemm_fold")
+    return Bf, colsum, bias
+
+
+def layernorm_gemm_prenorm(A, B_folded, colsum, bias=None, *, eps: float = 1e-5, b_layout="kn",
+                           out=None, mean_out=None, rstd_out=None, stream=None):
+    """C = (LayerNorm(A) * gamma + beta) @ B from the folded weights of
+    layernorm_gemm_fold: a row-statistics pre-pass, then
+    rstd * (A @ B_folded - mean * colsum) + bias."""
+    torch = _torch()
+    _dev_bf16(A, "A"); _dev_bf16(B_folded, "B_folded")
+    lay = _layout(b_layout)
+    M, N, K = _shapes(A, B_folded, lay)
+    for t, name in ((colsum, "colsum"), (bias, "bias")):
+        if t is not None and (t.dtype != torch.float32 or t.device.type != "cuda"
+                              or not t.is_contiguous() or t.numel() != N):
+            raise ValueError("%s must be a contiguous float32 GPU tensor of %d values" % (name, N))
+    if colsum is None:
+        raise ValueError("colsum is required")
+    mean = mean_out if mean_out is not None else torch.empty(M, dtype=torch.float32,
+                                                             device=A.device)
+    rstd = rstd_out if rstd_out is not None else torch.empty(M, dtype=torch.float32,
+                                                             device=A.device)
+    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _dev_bf16(C, "out")
+    _check(ng_layernorm_gemm_prenorm(_ptr(A), _ptr(B_folded), _ptr(colsum), _ptr(bias), _ptr(C),
+                                     M, N, K, lay, float(eps), _ptr(mean), _ptr(rstd),
+                                     _stream(stream)), "ng_layernorm_gemm_prenorm")
     return C
 
 

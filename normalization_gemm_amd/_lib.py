@@ -46,6 +46,8 @@ _SIGNATURES = {
                                  _P]),
     "ng_gemm_add_layernorm": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P,
                                    _P, _SZ, _P]),
+    "ng_layernorm_gemm_fold": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I, _P]),
+    "ng_layernorm_gemm_prenorm": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P]),
     "ng_lazy_fold_affine": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _P]),
     "ng_rmsnorm_gemm_lazy_affine": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P]),
     "ng_gemm": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _P]),
@@ -121,6 +123,17 @@ def ng_gemm_add_layernorm(A, B, R, gamma, beta, C, S_out, M, N, K, b_layout, eps
                           rstd_out, workspace, workspace_bytes, stream):
     return _call("ng_gemm_add_layernorm", A, B, R, gamma, beta, C, S_out, M, N, K, b_layout, eps,
                  mean_out, rstd_out, workspace, workspace_bytes, stream)
+
+
+def ng_layernorm_gemm_fold(B, gamma, beta, B_folded, colsum, bias, K, N, b_layout, stream):
+    return _call("ng_layernorm_gemm_fold", B, gamma, beta, B_folded, colsum, bias, K, N, b_layout,
+                 stream)
+
+
+def ng_layernorm_gemm_prenorm(A, B_folded, colsum, bias, C, M, N, K, b_layout, eps, mean, rstd,
+                              stream):
+    return _call("ng_layernorm_gemm_prenorm", A, B_folded, colsum, bias, C, M, N, K, b_layout, eps,
+                 mean, rstd, stream)
 
 
 def ng_gemm(A, B, C, M, N, K, b_layout, stream):

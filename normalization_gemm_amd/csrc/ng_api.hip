@@ -401,6 +401,32 @@ int ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N
 
 namespace {
 
+// Launch shape of the norm kernel for p.cols (rows of up to 65536 columns).
+int launch_norm_rows(const ng::NormParams& p, hipStream_t s, bool residual, const char* what) {
+  const int64_t rows = p.rows;
+  const int64_t nch = p.cols / 8;
+#define NG_NORM_LAUNCH(LPR, CPL)                                                              \
+  do {                                                                                        \
+    const unsigned grid = (unsigned)((rows + (256 / LPR) - 1) / (256 / LPR));                 \
+    if (residual)                                                                             \
+      hipLaunchKernelGGL((ng::norm_kernel<LPR, CPL, true>), dim3(grid), dim3(256), 0, s, p);  \
+    else                                                                                      \
+      hipLaunchKernelGGL((ng::norm_kernel<LPR, CPL, false>), dim3(grid), dim3(256), 0, s, p); \
+    return launched(what);                                                                    \
+  } while (0)
+  if (nch <= 16) NG_NORM_LAUNCH(16, 1);
+  if (nch <= 32) NG_NORM_LAUNCH(32, 1);
+  if (nch <= 64) NG_NORM_LAUNCH(64, 1);
+  if (nch <= 128) NG_NORM_LAUNCH(64, 2);
+  if (nch <= 256) NG_NORM_LAUNCH(64, 4);
+  if (nch <= 512) NG_NORM_LAUNCH(128, 4);
+  if (nch <= 1024) NG_NORM_LAUNCH(256, 4);
+  if (nch <= 2048) NG_NORM_LAUNCH(256, 8);
+  if (nch <= 4096) NG_NORM_LAUNCH(256, 16);
+  NG_NORM_LAUNCH(256, 32);
+#undef NG_NORM_LAUNCH
+}
+
 // Shared by ng_norm and ng_add_norm (R non-NULL).
 int norm_rows(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng_bf16* beta,
               ng_bf16* Y, ng_bf16* S_out, int64_t rows, int64_t cols, int kind, float eps,
@@ -443,27 +469,7 @@ int norm_rows(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng
   p.cols = (int)cols;
   p.kind = kind;
   p.eps = eps;
-  const int64_t nch = cols / 8;
-#define NG_NORM_LAUNCH(LPR, CPL)                                                              \
-  do {                                                                                        \
-    const unsigned grid = (unsigned)((rows + (256 / LPR) - 1) / (256 / LPR));                 \
-    if (residual)                                                                             \
-      hipLaunchKernelGGL((ng::norm_kernel<LPR, CPL, true>), dim3(grid), dim3(256), 0, s, p);  \
-    else                                                                                      \
-      hipLaunchKernelGGL((ng::norm_kernel<LPR, CPL, false>), dim3(grid), dim3(256), 0, s, p); \
-    return launched(what);                                                                    \
-  } while (0)
-  if (nch <= 16) NG_NORM_LAUNCH(16, 1);
-  if (nch <= 32) NG_NORM_LAUNCH(32, 1);
-  if (nch <= 64) NG_NORM_LAUNCH(64, 1);
-  if (nch <= 128) NG_NORM_LAUNCH(64, 2);
-  if (nch <= 256) NG_NORM_LAUNCH(64, 4);
-  if (nch <= 512) NG_NORM_LAUNCH(128, 4);
-  if (nch <= 1024) NG_NORM_LAUNCH(256, 4);
-  if (nch <= 2048) NG_NORM_LAUNCH(256, 8);
-  if (nch <= 4096) NG_NORM_LAUNCH(256, 16);
-  NG_NORM_LAUNCH(256, 32);
-#undef NG_NORM_LAUNCH
+  return launch_norm_rows(p, s, residual, what);
 }
 
 }  // namespace
@@ -482,6 +488,70 @@ int ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const 
                 float* mean_out, float* rstd_out, void* stream) {
   return norm_rows(X, R, gamma, beta, Y, S_out, rows, cols, kind, eps, mean_out, rstd_out,
                    (hipStream_t)stream, true, "ng_add_norm");
+}
+
+int ng_layernorm_gemm_fold(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
+                           ng_bf16* B_folded, float* colsum, float* bias, int64_t K, int64_t N,
+                           int b_layout, void* stream) {
+  if (!colsum) return fail(NG_ERR_INVALID_ARG, "colsum must be non-NULL");
+  if (!aligned(colsum, 16)) return fail(NG_ERR_INVALID_ARG, "colsum must be 16-byte aligned");
+  if (bias && !aligned(bias, 16)) return fail(NG_ERR_INVALID_ARG, "bias must be 16-byte aligned");
+  if (beta && !bias) return fail(NG_ERR_INVALID_ARG, "beta needs a bias output");
+  // bias = beta^T B (before B_folded may overwrite B), then B' = diag(gamma) B
+  int st = ng_lazy_fold_affine(B, gamma, beta, B_folded, bias, K, N, b_layout, stream);
+  if (st) return st;
+  // colsum = 1^T B' over the folded (bf16-rounded) weights the product uses
+  ng::FoldParams p{};
+  p.B = B_folded;
+  p.bias = colsum;
+  p.K = K;
+  p.N = N;
+  p.nk = b_layout == NG_B_NK;
+  p.ones = 1;
+  const unsigned grid = (unsigned)(p.nk ? (N + 3) / 4 : (N + 63) / 64);
+  hipLaunchKernelGGL(ng::fold_bias_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, p);
+  return launched("ng_layernorm_gemm_fold");
+}
+
+int ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, const float* colsum,
+                              const float* bias, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+                              int b_layout, float eps, float* mean, float* rstd, void* stream) {
+  int st = check_gemm(A, B_folded, C, M, N, K, b_layout);
+  if (!st) st = check_eps(eps);
+  if (st) return st;
+  if (!colsum || !aligned(colsum, 16))
+    return fail(NG_ERR_INVALID_ARG, "colsum must be non-NULL and 16-byte aligned");
+  if (bias && !aligned(bias, 16)) return fail(NG_ERR_INVALID_ARG, "bias must be 16-byte aligned");
+  if (M != 0 && (!mean || !rstd)) return fail(NG_ERR_INVALID_ARG, "mean and rstd must be non-NULL");
+  if (!aligned(mean, 4) || !aligned(rstd, 4))
+    return fail(NG_ERR_INVALID_ARG, "mean and rstd must be 4-byte aligned");
+  if (K > 65536) return fail(NG_ERR_UNSUPPORTED, "K must be at most 65536 (row statistics)");
+  if (M == 0) return ok();
+  hipStream_t s = (hipStream_t)stream;
+  // stage 1: mean and rstd of every row of A (no normalized output)
+  ng::NormParams q{};
+  q.X = A;
+  q.mean_out = mean;
+  q.rstd_out = rstd;
+  q.rows = (int)M;
+  q.cols = (int)K;
+  q.kind = ng::NORM_LAYER;
+  q.eps = eps;
+  const char* what = "ng_layernorm_gemm_prenorm";
+  st = launch_norm_rows(q, s, false, what);
+  if (st) return st;
+  // stage 2: the product with the norm applied through it
+  ng::GemmParams p = make_params(A, B_folded, C, M, N, K, eps);
+  p.colsum = colsum;
+  p.bias = bias;
+  p.row_mean = mean;
+  p.row_rstd = rstd;
+  const bool kn = b_layout == NG_B_KN;
+  if (N <= 128)
+    return kn ? launch_grid<TRow128<true>, ng::EPI_PRE_LN>(p, s, what)
+              : launch_grid<TRow128<false>, ng::EPI_PRE_LN>(p, s, what);
+  return kn ? launch_persistent<TLarge<true>, ng::EPI_PRE_LN>(p, s, what)
+            : launch_persistent<TLarge<false>, ng::EPI_PRE_LN>(p, s, what);
 }
 
 size_t ng_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {

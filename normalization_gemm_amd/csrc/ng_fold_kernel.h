@@ -7,7 +7,9 @@
 // is what keeps the plain row-scale identity from applying; "RMSNorm fusion on
 // Ascend", section 6.4: at inference gamma is fixed and can be merged into the
 // following matmul's weights ahead of time.)  Both are one-off weight
-// transforms.
+// transforms.  The pre-LayerNorm product also needs colsum = 1^T B' (the same
+// column sum with every beta[k] = 1, taken over the folded weights): the row
+// mean of A passes through the product as mean * colsum.
 #pragma once
 
 #include "ng_device.h"
@@ -22,6 +24,7 @@ struct FoldParams {
   float* bias;            // [N] or NULL (not computed)
   int64_t K, N;
   int nk;                 // 1: B stored [N, K]
+  int ones;               // fold_bias_kernel: every beta[k] = 1 (column sums)
 };
 
 // B' = diag(gamma) B, 8 elements (16 bytes) per thread and step, rounded to
@@ -56,7 +59,7 @@ __global__ void __launch_bounds__(256) fold_gamma_kernel(FoldParams p) {
 }
 
 // bias[n] = sum_k beta[k] * B[k][n] in fp32 (bf16 products are exact in
-// fp32).  [K, N]: 64 columns per workgroup, thread (slice s, column c) sums
+// fp32); with `ones`, the column sums sum_k B[k][n].  [K, N]: 64 columns per workgroup, thread (slice s, column c) sums
 // k = s, s+4, ... (coalesced across c); the four slices are added in order.
 // [N, K]: one column per wave, lane l sums k = l, l+64, ... (contiguous), then
 // the lanes combine pairwise in a fixed order.
@@ -67,10 +70,10 @@ __global__ void __launch_bounds__(256) fold_bias_kernel(FoldParams p) {
     const int c = t & 63, s = t >> 6;
     const int64_t n = (int64_t)blockIdx.x * 64 + c;
     float acc = 0.f;
-    if (n < p.N && p.beta) {
+    if (n < p.N && (p.beta || p.ones)) {
       for (int64_t k = s; k < p.K; k += 4) {
         const float b = __uint_as_float((uint32_t)p.B[k * p.N + n] << 16);
-        const float be = __uint_as_float((uint32_t)p.beta[k] << 16);
+        const float be = p.ones ? 1.f : __uint_as_float((uint32_t)p.beta[k] << 16);
         acc = fmaf(be, b, acc);
       }
     }
@@ -81,10 +84,10 @@ __global__ void __launch_bounds__(256) fold_bias_kernel(FoldParams p) {
     const int lane = t & 63, w = t >> 6;
     const int64_t n = (int64_t)blockIdx.x * 4 + w;
     float acc = 0.f;
-    if (n < p.N && p.beta) {
+    if (n < p.N && (p.beta || p.ones)) {
       for (int64_t k = lane; k < p.K; k += 64) {
         const float b = __uint_as_float((uint32_t)p.B[n * p.K + k] << 16);
-        const float be = __uint_as_float((uint32_t)p.beta[k] << 16);
+        const float be = p.ones ? 1.f : __uint_as_float((uint32_t)p.beta[k] << 16);
         acc = fmaf(be, b, acc);
       }
     }

@@ -10,6 +10,10 @@
 //   EPI_ROW_RMS_RES / EPI_ROW_LN_RES
 //                 C = norm(A @ B + R), S_out = A @ B + R (optional): a
 //                 residual connection followed by a post-norm
+//   EPI_PRE_LN    C = rstd(A) * (A @ B' - mean(A) * colsum) + bias: LayerNorm
+//                 of A's rows before the product, carried through it (B' =
+//                 diag(gamma) B, colsum = 1^T B', bias = beta^T B; row
+//                 statistics from a pre-pass)
 //   cross-workgroup: C = norm(A @ B [+ R]) for rows split over workgroups;
 //                 per-row fp32 partials merged through a workspace
 //                 (persistent grid, gemm_xwg_kernel below)
@@ -52,7 +56,8 @@ enum Epi {
   EPI_ROW_LN = 3,
   EPI_LAZY_BIAS = 4,
   EPI_ROW_RMS_RES = 5,
-  EPI_ROW_LN_RES = 6
+  EPI_ROW_LN_RES = 6,
+  EPI_PRE_LN = 7
 };
 constexpr bool epi_lazy(int e) { return e == EPI_LAZY || e == EPI_LAZY_BIAS; }
 constexpr bool epi_row(int e) {
@@ -97,6 +102,9 @@ struct GemmParams {
   const float* bias;  // EPI_LAZY_BIAS: fp32 [N]
   const uint16_t* R;  // residual epilogues: bf16 [M][N] added before the norm
   uint16_t* S_out;    // residual epilogues: optional bf16 [M][N] output A @ B + R
+  const float* colsum;    // EPI_PRE_LN: fp32 [N] column sums of the folded weights
+  const float* row_mean;  // EPI_PRE_LN: fp32 [M] mean of each row of A
+  const float* row_rstd;  // EPI_PRE_LN: fp32 [M] rstd of each row of A
   float* mean_out;
   float* rstd_out;
   char* ws;
@@ -614,13 +622,15 @@ __device__ __forceinline__ void load_bias(const GemmParams& p, int n_base, int w
 
 // Scale/shift the accumulators by per-row (mean, rstd) and (AFFINE) the
 // per-column gamma/beta, or (BIAS) add a per-column fp32 bias after the row
-// scale, round to bf16 and store the tile.  Each 16-row x
+// scale, or (PRELN) apply rstd * x - mean * rstd * colsum + bias with the
+// per-column fp32 colsum/bias loaded per 64-column group, round to bf16 and
+// store the tile.  Each 16-row x
 // 64-column piece goes through the wave's LDS staging block so that every
 // global store writes whole 128-byte row segments (16 bytes per lane) instead
 // of 8-byte pieces of 16 rows.  Exactly T::C_STORES buffer stores per thread
 // are issued; rows past M and columns past N fall outside the buffer range
 // and are dropped.  Slot i of acc holds fragment i ^ a_xor.
-template <class T, bool AFFINE, bool BIAS = false>
+template <class T, bool AFFINE, bool BIAS = false, bool PRELN = false>
 __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
                                             const float (&mean)[T::FM], const float (&rstd)[T::FM],
                                             bool use_mean, const Affine<T>& aff,
@@ -645,6 +655,16 @@ __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&a
     const u32x2* bw = &aff.b[4 * q];
     const int n_st = n_base + wn * T::WTN + 64 * q + 8 * rc;
     const uint32_t voff_c = n_st < p.N ? 2u * (uint32_t)n_st : kOOB;
+    f32x4 pc[PRELN ? 4 : 1], pb[PRELN ? 4 : 1];
+    if constexpr (PRELN) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int n = n_base + wn * T::WTN + 64 * q + 16 * jj + 4 * g;
+        const bool in = n < p.N;
+        pc[jj] = in ? *(const f32x4*)(p.colsum + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+        pb[jj] = (in && p.bias) ? *(const f32x4*)(p.bias + n) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
       const float sh = use_mean ? -mean[i] * rstd[i] : 0.f;
@@ -660,6 +680,9 @@ __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&a
         } else if constexpr (BIAS) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) y[r] = fmaf(x[r], rstd[i], bias.v[4 * q + jj][r]);
+        } else if constexpr (PRELN) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) y[r] = fmaf(x[r], rstd[i], fmaf(sh, pc[jj][r], pb[jj][r]));
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) y[r] = fmaf(x[r], rstd[i], sh);
@@ -816,8 +839,9 @@ __device__ __forceinline__ void add_residual(const GemmParams& p, f32x4 (&acc)[T
 }
 
 // Per-row (mean, rstd) that the epilogue applies to a finished tile:
-// EPI_NONE (0, 1); EPI_LAZY* (0, rstd of the row of A); EPI_ROW_* the row's
-// statistics over the tile (which holds whole rows).  Also writes the
+// EPI_NONE (0, 1); EPI_LAZY* (0, rstd of the row of A); EPI_PRE_LN the
+// pre-pass statistics of the row of A; EPI_ROW_* the row's statistics over
+// the tile (which holds whole rows).  Also writes the
 // statistic outputs.  ax: slot permutation of the accumulators (lazy_split).
 template <class T, int EPI>
 __device__ __forceinline__ void tile_scale(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
@@ -828,6 +852,16 @@ __device__ __forceinline__ void tile_scale(const GemmParams& p, const f32x4 (&ac
   for (int i = 0; i < T::FM; ++i) { mean[i] = 0.f; rstd[i] = 1.f; }
   if constexpr (epi_lazy(EPI)) {
     lazy_rstd<T>(p, ss, rstd, lds, m_base, tn, wm, wn, lane, ax);
+  } else if constexpr (EPI == EPI_PRE_LN) {
+    const int l16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      const int m = m_base + wm * T::WTM + 16 * i + l16;
+      if (m < p.M) {
+        mean[i] = p.row_mean[m];
+        rstd[i] = p.row_rstd[m];
+      }
+    }
   } else if constexpr (epi_row(EPI)) {
     const int l16 = lane & 15, g = lane >> 4;
     float s1[T::FM], s2[T::FM];
@@ -859,8 +893,9 @@ __device__ __forceinline__ void tile_store(const GemmParams& p, const f32x4 (&ac
                                            const Affine<T>& aff, const Bias<T>& bias, lds_char* lds,
                                            int m_base, int n_base, int wave, int wm, int wn,
                                            int lane, int ax) {
-  apply_store<T, epi_row(EPI), EPI == EPI_LAZY_BIAS>(p, acc, mean, rstd, epi_ln(EPI), aff, bias,
-                                                    lds, m_base, n_base, wave, wm, wn, lane, ax);
+  apply_store<T, epi_row(EPI), EPI == EPI_LAZY_BIAS, EPI == EPI_PRE_LN>(
+      p, acc, mean, rstd, epi_ln(EPI) || EPI == EPI_PRE_LN, aff, bias, lds, m_base, n_base, wave,
+      wm, wn, lane, ax);
 }
 
 // Per-column data the epilogue needs, loaded before the row statistics so
@@ -930,7 +965,7 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(GemmParams p) {
 // k-loop a workgroup computes the tile's row scales, issues the LDS transfers
 // that start its next tile, then scales and stores the finished tile, so the
 // next tile's first k-tiles stream in behind the epilogue.  All epilogues
-// whose tile holds what it needs (EPI_NONE, EPI_LAZY*, EPI_ROW_*).
+// whose tile holds what it needs (EPI_NONE, EPI_LAZY*, EPI_ROW_*, EPI_PRE_LN).
 template <class T, int EPI>
 __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
   static_assert(T::STG_OWN, "persistent tiles need their own output staging");

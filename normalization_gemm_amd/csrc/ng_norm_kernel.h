@@ -122,6 +122,7 @@ __global__ void __launch_bounds__(256) norm_kernel(NormParams p) {
     if (p.mean_out) p.mean_out[row] = mean;
     if (p.rstd_out) p.rstd_out[row] = rstd;
   }
+  if (!p.Y) return;  // statistics only (the pre-pass of the pre-LayerNorm product)
   u32x4* yr = (u32x4*)(p.Y + row * (long)p.cols);
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {

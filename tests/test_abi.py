@@ -33,7 +33,7 @@ def test_header_declares_expected_entry_points():
     for n in ("ng_rmsnorm_gemm_lazy", "ng_gemm_layernorm", "ng_gemm_rmsnorm", "ng_gemm",
               "ng_norm", "ng_workspace_bytes", "ng_lazy_fold_affine",
               "ng_rmsnorm_gemm_lazy_affine", "ng_gemm_add_rmsnorm", "ng_gemm_add_layernorm",
-              "ng_add_norm"):
+              "ng_add_norm", "ng_layernorm_gemm_fold", "ng_layernorm_gemm_prenorm"):
         assert n in names
 
 
@@ -201,6 +201,25 @@ def test_add_norm_argument_checks():
     assert f(P, P3, None, None, P2, None, 4, 64, 0, 1e-6, P4, None, None) == 1       # RMS mean_out
     assert f(P, P3, None, None, P2, None, 4, 60, 1, 1e-6, None, None, None) == 2
     assert f(None, None, None, None, None, None, 0, 64, 1, 1e-6, None, None, None) == 0
+
+
+def test_prenorm_layernorm_argument_checks():
+    fold = _lib.ng_layernorm_gemm_fold
+    assert fold(P, None, None, P2, None, P3, 64, 64, 0, None) == 1          # colsum NULL
+    assert fold(P, None, None, P2, P4 + 4, P3, 64, 64, 0, None) == 1        # colsum misaligned
+    assert fold(P, None, P5, P2, P4, None, 64, 64, 0, None) == 1            # beta without bias
+    assert fold(P, None, None, P2, P4, P3 + 8, 64, 64, 0, None) == 1        # bias misaligned
+    assert fold(P, None, None, P2, P4, None, 60, 64, 0, None) == 2          # K % 8
+    f = _lib.ng_layernorm_gemm_prenorm
+    assert f(P, P2, None, None, P3, 64, 64, 64, 0, 1e-5, P4, P5, None) == 1    # colsum NULL
+    assert f(P, P2, P4 + 4, None, P3, 64, 64, 64, 0, 1e-5, P4, P5, None) == 1  # colsum misaligned
+    assert f(P, P2, P4, P4 + 8, P3, 64, 64, 64, 0, 1e-5, P4, P5, None) == 1   # bias misaligned
+    assert f(P, P2, P4, None, P3, 64, 64, 64, 0, 1e-5, None, P5, None) == 1   # mean NULL
+    assert f(P, P2, P4, None, P3, 64, 64, 64, 0, 1e-5, P4, P5 + 2, None) == 1  # rstd misaligned
+    assert f(P, P2, P4, None, P3, 64, 64, 64, 0, -1.0, P4, P5, None) == 1     # eps < 0
+    assert f(P, P2, P4, None, P3, 64, 64, 65544, 0, 1e-5, P4, P5, None) == 2  # K > 65536
+    assert f(P, P2, P4, None, P3, 64, 100, 64, 0, 1e-5, P4, P5, None) == 2    # N % 8
+    assert f(None, P2, P4, None, None, 0, 64, 64, 0, 1e-5, None, None, None) == 0  # M = 0
 
 
 def test_workspace_helpers_argument_checks():

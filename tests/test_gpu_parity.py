@@ -383,6 +383,90 @@ def test_add_norm_small(rows, cols, kind):
     _check_stat("add_norm rstd", rstd, rref)
 
 
+# ------------------------------------------ pre-LayerNorm through the product
+def _prenorm_case(x, layout, eps, affine=True):
+    """Fold on the GPU, then the two-stage product; returns (C, mean, rstd,
+    B_folded, colsum, bias) as device tensors."""
+    K = x.A.shape[1]
+    g = up(x.gamma) if affine and x.gamma is not None else None
+    b = up(x.beta) if affine and x.beta is not None else None
+    Bf, colsum, bias = ng.layernorm_gemm_fold(up(b_for_layout(x.B, layout)), g, b,
+                                              b_layout=layout)
+    mean = torch.empty(x.A.shape[0], dtype=torch.float32, device="cuda")
+    rstd = torch.empty(x.A.shape[0], dtype=torch.float32, device="cuda")
+    C = ng.layernorm_gemm_prenorm(up(x.A), Bf, colsum, bias, eps=eps, b_layout=layout,
+                                  mean_out=mean, rstd_out=rstd)
+    assert K == x.A.shape[1]
+    return C, mean, rstd, Bf, colsum, bias
+
+
+def _check_fold(x, layout, Bf, colsum, bias, affine=True):
+    g = x.gamma if affine else None
+    bt = x.beta if affine else None
+    Bf_ref, _, bias_ref = oracle.layernorm_gemm_fold(x.B, g, bt)
+    # B_folded: gamma * B rounded to bf16 (nearest even), bit for bit
+    Bf_bits = oracle.f64_to_bf16_bits(Bf_ref)
+    assert np.array_equal(down(Bf), b_for_layout(Bf_bits, layout))
+    # colsum over the rounded folded weights; fp32 sums of exact products
+    Bfr = oracle.bf16_to_f64(Bf_bits)
+    bound = Bfr.shape[0] * 6e-8 * np.abs(Bfr).sum(axis=0) + 1e-30
+    got = colsum.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - Bfr.sum(axis=0)) <= bound)
+    got = bias.cpu().numpy().astype(np.float64)
+    if bt is None:
+        assert np.all(got == 0.0)
+    else:
+        bb = np.abs(oracle.bf16_to_f64(bt)) @ np.abs(oracle.bf16_to_f64(x.B))
+        assert np.all(np.abs(got - bias_ref) <= x.B.shape[0] * 6e-8 * bb + 1e-30)
+
+
+def _check_prenorm_stats(mean, rstd, mref, rref):
+    got_mean = mean.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got_mean - mref) / (1.0 + np.abs(mref))) <= 1e-3
+    _check_stat("prenorm rstd", rstd, rref)
+
+
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("M,N,K", [(256, 64, 128), (300, 136, 200), (77, 128, 72),
+                                   (513, 520, 264), (130, 256, 64), (1, 8, 8)])
+def test_prenorm_layernorm_small(M, N, K, layout):
+    log("prenorm layernorm M=%d N=%d K=%d %s" % (M, N, K, layout))
+    x = workloads.make_inputs(M, N, K, seed=7 * M + N + K, row_scale=True, row_shift=True,
+                              gamma=True, beta=True, gamma_len=K)
+    C, mean, rstd, Bf, colsum, bias = _prenorm_case(x, layout, 1e-5)
+    torch.cuda.synchronize()
+    _check_fold(x, layout, Bf, colsum, bias)
+    ref, mref, rref = oracle.layernorm_gemm_prenorm(x.A, x.B, 1e-5, x.gamma, x.beta)
+    _check("prenorm layernorm", down(C), ref)
+    _check_prenorm_stats(mean, rstd, mref, rref)
+
+
+def test_prenorm_layernorm_without_affine_and_large_mean():
+    # no gamma/beta: B_folded = B, colsum = column sums of B, bias = 0; rows
+    # whose mean is 30 standard deviations from zero exercise the mean term
+    M, N, K = 300, 520, 136
+    x = workloads.make_inputs(M, N, K, seed=77, gamma=True, beta=True, gamma_len=K)
+    a = oracle.bf16_to_f64(x.A) + 30.0
+    x.A = oracle.f64_to_bf16_bits(a)
+    C, mean, rstd, Bf, colsum, bias = _prenorm_case(x, "kn", 1e-5, affine=False)
+    torch.cuda.synchronize()
+    _check_fold(x, "kn", Bf, colsum, bias, affine=False)
+    ref, mref, rref = oracle.layernorm_gemm_prenorm(x.A, x.B, 1e-5)
+    _check("prenorm no affine, mean 30", down(C), ref)
+    _check_prenorm_stats(mean, rstd, mref, rref)
+
+
+def test_prenorm_layernorm_persistent_multi_tile_ragged():
+    M, N, K = 256 * 9 + 37, 256 * 5 + 72, 200
+    x = workloads.make_inputs(M, N, K, seed=12, row_scale=True, row_shift=True, gamma=True,
+                              beta=True, gamma_len=K)
+    C, mean, rstd, _, _, _ = _prenorm_case(x, "nk", 1e-5)
+    torch.cuda.synchronize()
+    ref, mref, rref = oracle.layernorm_gemm_prenorm(x.A, x.B, 1e-5, x.gamma, x.beta)
+    _check("prenorm persistent", down(C), ref)
+    _check_prenorm_stats(mean, rstd, mref, rref)
+
+
 # ------------------------------------------------------------ edge cases
 def test_empty_M_leaves_output_untouched():
     A = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
@@ -462,6 +546,9 @@ def _workload_case(w, layout="kn", n_rows=24):
     if w.op == workloads.OP_LAZY:
         C = ng.rmsnorm_gemm_lazy(A, B, eps=w.eps, b_layout=layout)
         ref = oracle.rmsnorm_gemm_lazy(x.A[rows], x.B, w.eps)[0]
+    elif w.op == workloads.OP_PRENORM_LN:
+        C = _prenorm_case(x, layout, w.eps)[0]
+        ref = oracle.layernorm_gemm_prenorm(x.A[rows], x.B, w.eps, x.gamma, x.beta)[0]
     elif w.op in (workloads.OP_GEMM_ADD_RMSNORM, workloads.OP_GEMM_ADD_LAYERNORM):
         kind = "layer" if w.op == workloads.OP_GEMM_ADD_LAYERNORM else "rms"
         C, _, _ = _residual_call(kind, x, layout, w.eps, stats=False)
@@ -485,7 +572,7 @@ def test_named_workload_full_size(name):
 
 @pytest.mark.parametrize("name", [w.name for w in workloads.NEXT_WORKLOADS
                                   if w.op != workloads.OP_LAZY_AFFINE])
-def test_residual_workload_full_size(name):
+def test_next_workload_full_size(name):
     _workload_case(workloads.WORKLOAD_BY_NAME[name])
 
 
@@ -499,6 +586,18 @@ def test_residual_unfused_pair_full_size():
     torch.cuda.synchronize()
     ref = _residual_ref("rms", x, w.eps, rows)[0]
     _check("unfused gemm->add_norm", down(Y[torch.as_tensor(rows, device="cuda")]), ref)
+
+
+def test_prenorm_unfused_pair_full_size():
+    # the unfused baseline of the pre-LayerNorm product: ng_norm, then ng_gemm
+    w = workloads.WORKLOAD_BY_NAME["prenorm_ln_32768x4096x4096"]
+    x = workloads.workload_inputs(w)
+    rows = sample_rows(w.M, 16, seed=5)
+    An = ng.norm(up(x.A), "layer", up(x.gamma), up(x.beta), eps=w.eps)
+    C = ng.gemm(An, up(x.B))
+    torch.cuda.synchronize()
+    ref = oracle.layernorm_gemm_prenorm(x.A[rows], x.B, w.eps, x.gamma, x.beta)[0]
+    _check("unfused layernorm->gemm", down(C[torch.as_tensor(rows, device="cuda")]), ref)
 
 
 def test_named_workload_nk_layout_large():

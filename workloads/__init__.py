@@ -8,14 +8,17 @@ Input recipe (the same for every workload):
 
 * ``numpy.random.default_rng(seed)`` (PCG64), values drawn in float32 in a
   fixed order: A's standard normals ``[M, K]``, then the per-row scales of A
-  (when the workload has them), then B's standard normals ``[K, N]`` times
+  (when the workload has them), then the per-row shifts of A (when it has
+  them), then B's standard normals ``[K, N]`` times
   ``sqrt(1/K)``, then gamma, then beta, then (residual forms) the residual
   R's standard normals ``[M, N]`` (unit variance, the scale of ``A @ B``).
 * ``N(mu, v)`` in a workload description is read with ``v`` as the variance,
   so ``B ~ N(0, 1/K)`` keeps ``A @ B`` at unit variance per element and
   ``gamma ~ N(1, 0.1)`` has standard deviation ``sqrt(0.1)``.
 * A per-row scale "log-uniform[0.1, 10]" is ``10 ** U(-1, 1)`` multiplied
-  into the float32 row before rounding.
+  into the float32 row before rounding; a per-row shift is ``U(-2, 2)``
+  added after the scale (rows whose mean is far from zero relative to their
+  spread, the case a LayerNorm's mean term exists for).
 * Every array is rounded from float32 to bfloat16 with round-to-nearest-even
   and returned as raw ``uint16`` bit patterns; the caller decodes them.
 
@@ -38,6 +41,7 @@ OP_GEMM_LAYERNORM = "gemm_layernorm"
 OP_LAZY_AFFINE = "rmsnorm_gemm_lazy_affine"
 OP_GEMM_ADD_RMSNORM = "gemm_add_rmsnorm"
 OP_GEMM_ADD_LAYERNORM = "gemm_add_layernorm"
+OP_PRENORM_LN = "layernorm_gemm_prenorm"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -49,6 +53,7 @@ class Workload:
     K: int
     eps: float
     row_scale: bool = False
+    row_shift: bool = False
     gamma: bool = False
     beta: bool = False
     residual: bool = False
@@ -86,6 +91,10 @@ NEXT_WORKLOADS = [
              row_scale=True, gamma=True, beta=True,
              description="Lazy Pre-Norm RMSNorm with gamma and beta (length K) folded into B, "
                          "A 32768x4096 @ B 4096x4096"),
+    Workload("prenorm_ln_32768x4096x4096", OP_PRENORM_LN, 32768, 4096, 4096, 1e-5,
+             row_scale=True, row_shift=True, gamma=True, beta=True,
+             description="pre-LayerNorm with gamma and beta (length K) fused with the product, "
+                         "A 32768x4096 (row scale and shift) @ B 4096x4096"),
     Workload("gemm_add_ln_65536x512x128", OP_GEMM_ADD_LAYERNORM, 65536, 128, 512, 1e-5,
              residual=True,
              description="GEMM + residual add + LayerNorm epilogue (no affine), "
@@ -122,7 +131,8 @@ class Inputs:
 
 def make_inputs(M: int, N: int, K: int, *, seed: int = 0, row_scale: bool = False,
                 gamma: bool = False, beta: bool = False,
-                gamma_len: Optional[int] = None, residual: bool = False) -> Inputs:
+                gamma_len: Optional[int] = None, residual: bool = False,
+                row_shift: bool = False) -> Inputs:
     """Draw one seeded input set in the fixed order documented above.
 
     ``gamma_len`` overrides the length of gamma/beta (default N).
@@ -132,6 +142,8 @@ def make_inputs(M: int, N: int, K: int, *, seed: int = 0, row_scale: bool = Fals
     if row_scale:
         s = (10.0 ** rng.uniform(-1.0, 1.0, size=M)).astype(np.float32)
         a *= s[:, None]
+    if row_shift:
+        a += rng.uniform(-2.0, 2.0, size=M).astype(np.float32)[:, None]
     A = f32_to_bf16_bits(a)
     del a
     b = rng.standard_normal((K, N), dtype=np.float32)
@@ -151,7 +163,8 @@ def make_inputs(M: int, N: int, K: int, *, seed: int = 0, row_scale: bool = Fals
 
 
 def workload_inputs(w: Workload, seed: int = 0) -> Inputs:
-    # the pre-norm affine of the Lazy form acts on rows of A (length K)
-    gl = w.K if w.op == OP_LAZY_AFFINE else None
+    # a pre-norm's affine acts on rows of A (length K)
+    gl = w.K if w.op in (OP_LAZY_AFFINE, OP_PRENORM_LN) else None
     return make_inputs(w.M, w.N, w.K, seed=seed, row_scale=w.row_scale,
-                       gamma=w.gamma, beta=w.beta, gamma_len=gl, residual=w.residual)
+                       gamma=w.gamma, beta=w.beta, gamma_len=gl, residual=w.residual,
+                       row_shift=w.row_shift)
