@@ -23,6 +23,7 @@ from .normgemm_oracle import (  # noqa: F401
     gemm_add_rmsnorm,
     layernorm_gemm_prenorm,
     layernorm_gemm_fold,
+    rmsnorm_gemm_lazy_backward,
     gemm_add_layernorm,
     norm,
     rel_err,

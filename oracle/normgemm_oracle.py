@@ -175,6 +175,34 @@ def layernorm_gemm_fold(B, gamma=None, beta=None
     return Bf, Bf.sum(axis=0), bias
 
 
+def rmsnorm_gemm_lazy_backward(A, B, dC, eps: float
+                               ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Gradients of C = rmsnorm(A) @ B (RMSNorm without affine, the Lazy
+    Pre-Norm product) for an upstream gradient dC.
+
+    "Free normalization fusion", section "Lazy Pre-Norm": the normalized A is
+    never stored, so the backward pass has to rebuild it from A and the saved
+    per-row rstd; the "fusion regrouping" remark (the norm's backward fused
+    into the epilogue of a different matmul) places the norm backward after
+    dA_hat = dC @ B^T.  The formulas are the chain rule of the forward
+    definition, written out:
+        A_hat = rstd * A                 (rstd per row of A, over its K entries)
+        dA_hat = dC @ B^T
+        dB = A_hat^T @ dC
+        dA = rstd * (dA_hat - A_hat * mean_k(dA_hat * A_hat))
+    (the last from rstd = (mean(a^2) + eps)^(-1/2): d rstd / d a_k =
+    -rstd^3 a_k / K).  Returns (dA, dB, rstd).
+    """
+    A_hat, rstd = rms_norm_rows(A, eps)
+    G = _f64(dC)
+    dA_hat = G @ _f64(B).T
+    dB = A_hat.T @ G
+    K = A_hat.shape[1]
+    dot = (dA_hat * A_hat).sum(axis=1, keepdims=True) / K
+    dA = rstd[:, None] * (dA_hat - A_hat * dot)
+    return dA, dB, rstd
+
+
 def gemm_rmsnorm(A, B, eps: float, gamma=None) -> Tuple[np.ndarray, np.ndarray]:
     """Y = RMSNorm(A @ B) over each full output row (H = N), optional gamma.
 

@@ -377,6 +377,53 @@ def test_prenorm_layernorm_fold_identity():
     assert np.max(np.abs(wrong - C)) > 1e-1
 
 
+def _lazy_loss(A, B, G, eps):
+    C, _ = oracle.rmsnorm_gemm_lazy(A, B, eps)
+    return float((C * G).sum())
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.3])
+def test_lazy_backward_matches_finite_differences(eps):
+    # central differences of the forward oracle's scalar loss sum(C * G),
+    # for every entry of dA and dB (truncation error O(h^2) ~ 1e-10 at
+    # h = 1e-5; the loss is linear in B, so dB's differences are exact up
+    # to rounding)
+    rng = np.random.default_rng(51)
+    M, K, N = 3, 5, 4
+    A = rng.standard_normal((M, K)) * np.array([[0.5], [2.0], [1.0]])
+    B = rng.standard_normal((K, N))
+    G = rng.standard_normal((M, N))
+    dA, dB, rstd = oracle.rmsnorm_gemm_lazy_backward(A, B, G, eps)
+    h = 1e-5
+    for m in range(M):
+        for k in range(K):
+            E = np.zeros_like(A)
+            E[m, k] = h
+            fd = (_lazy_loss(A + E, B, G, eps) - _lazy_loss(A - E, B, G, eps)) / (2 * h)
+            assert abs(dA[m, k] - fd) <= 1e-7 * (1 + abs(fd)), (m, k, dA[m, k], fd)
+    for k in range(K):
+        for n in range(N):
+            E = np.zeros_like(B)
+            E[k, n] = h
+            fd = (_lazy_loss(A, B + E, G, eps) - _lazy_loss(A, B - E, G, eps)) / (2 * h)
+            assert abs(dB[k, n] - fd) <= 1e-7 * (1 + abs(fd)), (k, n)
+    np.testing.assert_allclose(rstd, oracle.rms_norm_rows(A, eps)[1], rtol=1e-15)
+
+
+def test_lazy_backward_input_gradient_is_orthogonal_to_rows():
+    # with eps = 0 the forward output does not change when a row of A is
+    # scaled, so the input gradient has no component along the row itself
+    rng = np.random.default_rng(52)
+    A = rng.standard_normal((6, 32)) * rng.uniform(0.1, 10, size=(6, 1))
+    B = rng.standard_normal((32, 9))
+    G = rng.standard_normal((6, 9))
+    dA, dB, _ = oracle.rmsnorm_gemm_lazy_backward(A, B, G, 0.0)
+    np.testing.assert_allclose((dA * A).sum(axis=1), 0.0, atol=1e-12)
+    # and the weight gradient is the normalized A transposed times G
+    A_hat, _ = oracle.rms_norm_rows(A, 0.0)
+    np.testing.assert_allclose(dB, A_hat.T @ G, rtol=1e-13)
+
+
 def test_lazy_is_not_layernorm_prenorm():
     # LayerNorm subtracts the row mean, which breaks the commutation.
     rng = np.random.default_rng(12)
