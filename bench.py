@@ -129,6 +129,9 @@ def algorithmic_bytes(w: workloads.Workload) -> int:
         return b + 4 * w.N
     if w.op == workloads.OP_PRENORM_LN:
         return b + 8 * w.N  # fp32 colsum and bias
+    if w.op == workloads.OP_LAZY_BWD:
+        # dC [M, N], B, A [M, K] and dA [M, K], fp32 rstd [M]
+        return 2 * (w.M * w.N + w.K * w.N + 2 * w.M * w.K) + 4 * w.M
     b += 2 * w.N * (int(w.gamma) + int(w.beta))
     if w.residual:
         b += 2 * w.M * w.N
@@ -138,8 +141,8 @@ def algorithmic_bytes(w: workloads.Workload) -> int:
 def norm_bytes(w: workloads.Workload) -> int:
     """Standalone norm of the unfused pair: read + write the normalized matrix
     (and read R for the residual forms)."""
-    rows, cols = (w.M, w.K) if prenorm(w) else (w.M, w.N)
-    return (6 if w.residual else 4) * rows * cols
+    rows, cols = (w.M, w.K) if prenorm(w) or w.op == workloads.OP_LAZY_BWD else (w.M, w.N)
+    return (6 if w.residual or w.op == workloads.OP_LAZY_BWD else 4) * rows * cols
 
 
 def prenorm(w: workloads.Workload) -> bool:
@@ -154,7 +157,9 @@ def kernel_label(w: workloads.Workload) -> str:
            workloads.OP_GEMM_RMSNORM: "EPI_ROW_RMS", workloads.OP_GEMM_LAYERNORM: "EPI_ROW_LN",
            workloads.OP_GEMM_ADD_RMSNORM: "EPI_ROW_RMS_RES",
            workloads.OP_GEMM_ADD_LAYERNORM: "EPI_ROW_LN_RES",
-           workloads.OP_PRENORM_LN: "EPI_PRE_LN"}[w.op]
+           workloads.OP_PRENORM_LN: "EPI_PRE_LN", workloads.OP_LAZY_BWD: "EPI_LAZY_BWD"}[w.op]
+    if w.op == workloads.OP_LAZY_BWD:
+        return "%s<%s>" % ("gemm_kernel" if w.K <= 256 else "gemm_xwg_kernel", epi)
     if prenorm(w):
         base = "gemm_kernel" if w.N <= 128 else "gemm_persistent_kernel"
     else:
@@ -203,6 +208,8 @@ class Bench:
         lazy = prenorm(w)
         per_copy = 2 * (w.M * w.K + w.M * w.N) + (2 * w.M * w.K if lazy else 0)
         per_copy += 2 * w.M * w.N if w.residual else 0
+        if w.op == workloads.OP_LAZY_BWD:
+            per_copy = 2 * (w.M * w.N + 3 * w.M * w.K)  # dC, A, dA, dA_hat
         self.R = max(1, min(8, math.ceil(ROTATE_BYTES / per_copy)))
         A0 = up(x.A)
         self.A = [A0] + [A0.clone() for _ in range(self.R - 1)]
@@ -213,6 +220,16 @@ class Bench:
         if w.residual:
             R0 = up(x.R)
             self.res = [R0] + [R0.clone() for _ in range(self.R - 1)]
+        if w.op == workloads.OP_LAZY_BWD:
+            # the forward pass's saved rstd (untimed); outputs are [M, K]
+            self.rstd = torch.empty(w.M, dtype=torch.float32, device=dev)
+            ng.rmsnorm_gemm_lazy(A0, self.B, eps=w.eps, rstd_out=self.rstd)
+            G0 = up(x.dC)
+            self.dC = [G0] + [G0.clone() for _ in range(self.R - 1)]
+            self.C = [torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev)
+                      for _ in range(self.R)]
+            self.dAh = [torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev)
+                        for _ in range(self.R)]
         # unfused pair intermediates: the normalized A of the lazy form's
         # pair holds real values (the GEMM's speed depends on its data)
         if lazy:
@@ -230,6 +247,7 @@ class Bench:
         op = {workloads.OP_LAZY: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_LAZY_AFFINE: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_PRENORM_LN: ng.NG_OP_RMSNORM_GEMM_LAZY,
+              workloads.OP_LAZY_BWD: ng.NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT,
               workloads.OP_GEMM_RMSNORM: ng.NG_OP_GEMM_RMSNORM,
               workloads.OP_GEMM_LAYERNORM: ng.NG_OP_GEMM_LAYERNORM,
               workloads.OP_GEMM_ADD_RMSNORM: ng.NG_OP_GEMM_ADD_RMSNORM,
@@ -263,6 +281,13 @@ class Bench:
                                      eps, None, st)))
                 self._gemm.append((lib.ng_gemm, (An, B, C, M, N, K, 0, st)))
                 self._norm.append((lib.ng_norm, (A, g, b, An, M, K, 0, eps, None, None, st)))
+            elif w.op == workloads.OP_LAZY_BWD:
+                G, dAh, rs = self.dC[r].data_ptr(), self.dAh[r].data_ptr(), self.rstd.data_ptr()
+                self._fused.append((lib.ng_rmsnorm_gemm_lazy_backward_input,
+                                    (G, B, A, rs, C, M, N, K, 0, ws, wsb, st)))
+                # dA_hat = dC @ B^T: B [K, N] read in the [N', K'] layout
+                self._gemm.append((lib.ng_gemm, (G, B, dAh, M, K, N, 1, st)))
+                self._norm.append((lib.ng_rmsnorm_backward, (dAh, A, rs, C, M, K, st)))
             elif w.op == workloads.OP_PRENORM_LN:
                 An = self.An[r].data_ptr()
                 self._fused.append((lib.ng_layernorm_gemm_prenorm,
@@ -386,7 +411,8 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
                                      gamma=w.gamma, beta=w.beta,
                                      gamma_len=w.K if w.op in (workloads.OP_LAZY_AFFINE,
                                                                workloads.OP_PRENORM_LN) else None,
-                                     residual=w.residual, row_shift=w.row_shift)
+                                     residual=w.residual, row_shift=w.row_shift,
+                                     upstream=w.upstream)
 
     rows = min(w.M, 64)
     x = sample(rows)
@@ -399,6 +425,8 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
             oracle.rmsnorm_gemm_lazy_affine(x.A, x.B, w.eps, x.gamma, x.beta)
         elif w.op == workloads.OP_PRENORM_LN:
             oracle.layernorm_gemm_prenorm(x.A, x.B, w.eps, x.gamma, x.beta)
+        elif w.op == workloads.OP_LAZY_BWD:
+            oracle.rmsnorm_gemm_lazy_backward(x.A, x.B, x.dC, w.eps)
         elif w.op == workloads.OP_GEMM_RMSNORM:
             oracle.gemm_rmsnorm(x.A, x.B, w.eps, x.gamma)
         elif w.op == workloads.OP_GEMM_ADD_RMSNORM:
@@ -414,11 +442,14 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
         if dt < target_s / 8 and rows < w.M:
             rows = min(w.M, rows * 4)
             x = sample(rows)
-    flops = 2.0 * done_rows * w.N * w.K
+    # the backward oracle also forms the weight gradient: two products per row
+    products = 2 if w.op == workloads.OP_LAZY_BWD else 1
+    flops = 2.0 * products * done_rows * w.N * w.K
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": "%d output rows of %s in passes of up to %d rows (fp64 NumPy GEMM + "
-                      "explicit norm, %.1f s)" % (done_rows, w.name, rows, t_total)}
+            "sample": "%d output rows of %s in passes of up to %d rows (fp64 NumPy GEMM%s + "
+                      "explicit norm, %.1f s)" % (done_rows, w.name, rows,
+                                                  "s" if products == 2 else "", t_total)}
 
 
 def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: float):

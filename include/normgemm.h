@@ -57,7 +57,8 @@ enum {
   NG_OP_GEMM = 3,
   NG_OP_NORM = 4,
   NG_OP_GEMM_ADD_RMSNORM = 5,
-  NG_OP_GEMM_ADD_LAYERNORM = 6
+  NG_OP_GEMM_ADD_LAYERNORM = 6,
+  NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT = 7
 };
 
 /*
@@ -101,6 +102,28 @@ int ng_lazy_fold_affine(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* b
 int ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded, const float* bias,
                                 ng_bf16* C, int64_t M, int64_t N, int64_t K, int b_layout,
                                 float eps, float* rstd_out, void* stream);
+
+/*
+ * Input gradient of Lazy Pre-Norm (C = rmsnorm(A) @ B, RMSNorm without
+ * affine) for an upstream gradient dC, with the norm's backward fused into
+ * the epilogue of dA_hat = dC @ B^T ("Free normalization fusion", section
+ * "Lazy Pre-Norm": backward rebuilds the normalized A from A and the saved
+ * rstd, and the norm's backward fuses into a different matmul than in the
+ * forward pass):
+ *   dA_hat = dC @ B^T;  s[m] = sum_k dA_hat[m,k] * A[m,k];
+ *   dA[m,k] = rstd[m] * dA_hat[m,k] - rstd[m]^3 * s[m] / K * A[m,k]
+ * (= rstd * (dA_hat - A_hat * mean_k(dA_hat * A_hat)) with A_hat = rstd * A).
+ * M, N, K and b_layout are the forward product's: dC [M, N], B as in the
+ * forward call, A [M, K] the forward input, rstd float32 [M] the forward's
+ * rstd_out, dA [M, K] bf16 output.  Rows with K <= 256 are reduced inside a
+ * workgroup; longer rows exchange per-row partial sums through `workspace`
+ * (ng_workspace_bytes(NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT, M, N, K) bytes; the
+ * same rules as for ng_gemm_rmsnorm).  dA must not overlap the inputs.
+ */
+int ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
+                                         const float* rstd, ng_bf16* dA, int64_t M, int64_t N,
+                                         int64_t K, int b_layout, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 /*
  * Pre-LayerNorm fused with the following product: C = LayerNorm(A) @ B with
@@ -232,6 +255,17 @@ int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16
 int ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng_bf16* beta,
                 ng_bf16* Y, ng_bf16* S_out, int64_t rows, int64_t cols, int kind, float eps,
                 float* mean_out, float* rstd_out, void* stream);
+
+/*
+ * Standalone RMSNorm backward (no affine), the norm half of the unfused
+ * baseline of ng_rmsnorm_gemm_lazy_backward_input: for each row x of X
+ * [rows, cols] with saved rstd (float32 [rows]) and upstream gradient dY,
+ *   dX = rstd * dY - rstd^3 * (sum_k dY_k x_k) / cols * x
+ * (the chain rule of y = x * rstd).  bf16 in and out; cols a multiple of 8
+ * and at most 65536 (else NG_ERR_UNSUPPORTED).  dX may equal dY.
+ */
+int ng_rmsnorm_backward(const ng_bf16* dY, const ng_bf16* X, const float* rstd, ng_bf16* dX,
+                        int64_t rows, int64_t cols, void* stream);
 
 /* Workspace bytes `op` needs for this shape (0 when it needs none). */
 size_t ng_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);

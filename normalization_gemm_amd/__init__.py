@@ -18,10 +18,10 @@ from . import _lib
 from ._lib import (  # noqa: F401
     NG_B_KN, NG_B_NK, NG_NORM_LAYER, NG_NORM_RMS, NG_OK,
     NG_OP_GEMM, NG_OP_GEMM_ADD_LAYERNORM, NG_OP_GEMM_ADD_RMSNORM, NG_OP_GEMM_LAYERNORM,
-    NG_OP_GEMM_RMSNORM, NG_OP_NORM, NG_OP_RMSNORM_GEMM_LAZY,
+    NG_OP_GEMM_RMSNORM, NG_OP_NORM, NG_OP_RMSNORM_GEMM_LAZY, NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT,
     ng_gemm, ng_gemm_add_layernorm, ng_gemm_add_rmsnorm, ng_gemm_layernorm, ng_gemm_rmsnorm,
     ng_add_norm, ng_last_error, ng_layernorm_gemm_fold, ng_layernorm_gemm_prenorm,
-    ng_lazy_fold_affine, ng_norm,
+    ng_lazy_fold_affine, ng_norm, ng_rmsnorm_backward, ng_rmsnorm_gemm_lazy_backward_input,
     ng_rmsnorm_gemm_lazy, ng_rmsnorm_gemm_lazy_affine, ng_status_string, ng_workspace_bytes,
     ng_workspace_reset, ng_workspace_status,
 )
@@ -30,6 +30,7 @@ __all__ = [
     "NormGemmError", "rmsnorm_gemm_lazy", "lazy_fold_affine", "rmsnorm_gemm_lazy_affine",
     "gemm_rmsnorm", "gemm_layernorm", "gemm_add_rmsnorm", "gemm_add_layernorm", "gemm", "norm",
     "add_norm", "layernorm_gemm_fold", "layernorm_gemm_prenorm",
+    "rmsnorm_gemm_lazy_backward_input", "rmsnorm_backward",
     "Workspace", "library_path",
 ]
 
@@ -241,6 +242,48 @@ def layernorm_gemm_prenorm(A, B_folded, colsum, bias=None, *, eps: float = 1e-5,
                                      M, N, K, lay, float(eps), _ptr(mean), _ptr(rstd),
                                      _stream(stream)), "ng_layernorm_gemm_prenorm")
     return C
+
+
+def _f32_vec(t, n, name):
+    torch = _torch()
+    if (t.dtype != torch.float32 or t.device.type != "cuda" or not t.is_contiguous()
+            or t.numel() != n):
+        raise ValueError("%s must be a contiguous float32 GPU tensor of %d values" % (name, n))
+
+
+def rmsnorm_gemm_lazy_backward_input(dC, B, A, rstd, *, b_layout="kn", out=None,
+                                     workspace: Optional[Workspace] = None, stream=None):
+    """dA for C = rmsnorm(A) @ B (no affine) given dC: the norm's backward
+    fused into the epilogue of dC @ B^T, from A and the forward's rstd."""
+    torch = _torch()
+    _dev_bf16(dC, "dC"); _dev_bf16(B, "B"); _dev_bf16(A, "A")
+    lay = _layout(b_layout)
+    M, N, K = _shapes(A, B, lay)
+    if tuple(dC.shape) != (M, N):
+        raise ValueError("dC must be [%d, %d] (got %s)" % (M, N, tuple(dC.shape)))
+    _f32_vec(rstd, M, "rstd")
+    dA = out if out is not None else torch.empty((M, K), dtype=torch.bfloat16, device=A.device)
+    _dev_bf16(dA, "out")
+    ws, wsb = _workspace(NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT, M, N, K, A.device, workspace)
+    _check(ng_rmsnorm_gemm_lazy_backward_input(_ptr(dC), _ptr(B), _ptr(A), _ptr(rstd), _ptr(dA),
+                                               M, N, K, lay, ws, wsb, _stream(stream)),
+           "ng_rmsnorm_gemm_lazy_backward_input")
+    return dA
+
+
+def rmsnorm_backward(dY, X, rstd, *, out=None, stream=None):
+    """Standalone RMSNorm backward (no affine): dX from dY, X and the saved rstd."""
+    torch = _torch()
+    _dev_bf16(dY, "dY"); _dev_bf16(X, "X")
+    if X.dim() != 2 or tuple(dY.shape) != tuple(X.shape):
+        raise ValueError("dY and X must be 2-D of one shape")
+    rows, cols = X.shape
+    _f32_vec(rstd, rows, "rstd")
+    dX = out if out is not None else torch.empty_like(X)
+    _dev_bf16(dX, "out")
+    _check(ng_rmsnorm_backward(_ptr(dY), _ptr(X), _ptr(rstd), _ptr(dX), rows, cols,
+                               _stream(stream)), "ng_rmsnorm_backward")
+    return dX
 
 
 def gemm_rmsnorm(A, B, gamma=None, *, eps: float = 1e-6, b_layout="kn", out=None,

@@ -31,6 +31,7 @@ NG_OP_GEMM = 3
 NG_OP_NORM = 4
 NG_OP_GEMM_ADD_RMSNORM = 5
 NG_OP_GEMM_ADD_LAYERNORM = 6
+NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT = 7
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -48,6 +49,9 @@ _SIGNATURES = {
                                    _P, _SZ, _P]),
     "ng_layernorm_gemm_fold": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I, _P]),
     "ng_layernorm_gemm_prenorm": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P]),
+    "ng_rmsnorm_gemm_lazy_backward_input": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P,
+                                                 _SZ, _P]),
+    "ng_rmsnorm_backward": (_I, [_P, _P, _P, _P, _I64, _I64, _P]),
     "ng_lazy_fold_affine": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _P]),
     "ng_rmsnorm_gemm_lazy_affine": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P]),
     "ng_gemm": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _P]),
@@ -134,6 +138,16 @@ def ng_layernorm_gemm_prenorm(A, B_folded, colsum, bias, C, M, N, K, b_layout, e
                               stream):
     return _call("ng_layernorm_gemm_prenorm", A, B_folded, colsum, bias, C, M, N, K, b_layout, eps,
                  mean, rstd, stream)
+
+
+def ng_rmsnorm_gemm_lazy_backward_input(dC, B, A, rstd, dA, M, N, K, b_layout, workspace,
+                                         workspace_bytes, stream):
+    return _call("ng_rmsnorm_gemm_lazy_backward_input", dC, B, A, rstd, dA, M, N, K, b_layout,
+                 workspace, workspace_bytes, stream)
+
+
+def ng_rmsnorm_backward(dY, X, rstd, dX, rows, cols, stream):
+    return _call("ng_rmsnorm_backward", dY, X, rstd, dX, rows, cols, stream)
 
 
 def ng_gemm(A, B, C, M, N, K, b_layout, stream):

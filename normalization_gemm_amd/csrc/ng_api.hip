@@ -159,12 +159,12 @@ int launch_persistent(ng::GemmParams p, hipStream_t s, const char* what) {
   return launched(what);
 }
 
-template <class T, bool LN, bool RES>
+template <class T, bool LN, bool RES, bool BWD = false>
 int launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   p.tiles_m = (p.M + T::BM - 1) / T::BM;
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
   int cap = 0;
-  int st = resident_capacity((const void*)ng::gemm_xwg_kernel<T, LN, RES>, T::NT, &cap);
+  int st = resident_capacity((const void*)ng::gemm_xwg_kernel<T, LN, RES, BWD>, T::NT, &cap);
   if (st) return st;
   if (p.tiles_n > cap)
     return fail(NG_ERR_UNSUPPORTED, "row of %d tiles exceeds %d co-resident workgroups",
@@ -177,7 +177,7 @@ int launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   // on a device not shared with another such grid all workgroups become
   // resident.  (A cooperative launch would guarantee it even then, but was
   // measured to add ~18 us per call.)
-  hipLaunchKernelGGL((ng::gemm_xwg_kernel<T, LN, RES>), dim3(grid), dim3(T::NT), 0, s, p);
+  hipLaunchKernelGGL((ng::gemm_xwg_kernel<T, LN, RES, BWD>), dim3(grid), dim3(T::NT), 0, s, p);
   return launched(what);
 }
 
@@ -554,10 +554,91 @@ int ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, const f
             : launch_persistent<TLarge<false>, ng::EPI_PRE_LN>(p, s, what);
 }
 
+int ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
+                                         const float* rstd, ng_bf16* dA, int64_t M, int64_t N,
+                                         int64_t K, int b_layout, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  // dA_hat = dC [M, N] @ B^T [N, K]: the product's output width is the
+  // forward K and its reduction the forward N; B^T is B read in the other
+  // layout
+  if (b_layout != NG_B_KN && b_layout != NG_B_NK)
+    return fail(NG_ERR_INVALID_ARG, "b_layout must be NG_B_KN or NG_B_NK (got %d)", b_layout);
+  const int lay = b_layout == NG_B_KN ? NG_B_NK : NG_B_KN;
+  int st = check_gemm(dC, B, dA, M, K, N, lay);
+  if (st) return st;
+  if (M != 0 && (!A || !rstd)) return fail(NG_ERR_INVALID_ARG, "A and rstd must be non-NULL");
+  if (!aligned(A, 16)) return fail(NG_ERR_INVALID_ARG, "A must be 16-byte aligned");
+  if (!aligned(rstd, 4)) return fail(NG_ERR_INVALID_ARG, "rstd must be 4-byte aligned");
+  const bool local = K <= 256;
+  if (!local && M > 0) {
+    const size_t need = xwg_bytes(M, K);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+      return fail(NG_ERR_WORKSPACE, "workspace of %zu bytes (256-byte aligned) needed, got %zu",
+                  need, workspace_bytes);
+  }
+  if (M == 0) return ok();
+  ng::GemmParams p = make_params(dC, B, dA, M, K, N, 0.f);
+  p.Xin = A;
+  p.row_rstd = rstd;
+  p.ws = (char*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  const bool kn = lay == NG_B_KN;
+  const char* what = "ng_rmsnorm_gemm_lazy_backward_input";
+  if (K <= 128)
+    return kn ? launch_grid<TRow128<true>, ng::EPI_LAZY_BWD>(p, s, what)
+              : launch_grid<TRow128<false>, ng::EPI_LAZY_BWD>(p, s, what);
+  if (local)
+    return kn ? launch_grid<TRow256<true>, ng::EPI_LAZY_BWD>(p, s, what)
+              : launch_grid<TRow256<false>, ng::EPI_LAZY_BWD>(p, s, what);
+  return kn ? launch_xwg<TLarge<true>, false, false, true>(p, s, what)
+            : launch_xwg<TLarge<false>, false, false, true>(p, s, what);
+}
+
+int ng_rmsnorm_backward(const ng_bf16* dY, const ng_bf16* X, const float* rstd, ng_bf16* dX,
+                        int64_t rows, int64_t cols, void* stream) {
+  if (rows != 0 && (!dY || !X || !rstd || !dX))
+    return fail(NG_ERR_INVALID_ARG, "dY, X, rstd and dX must be non-NULL");
+  if (!aligned(dY, 16) || !aligned(X, 16) || !aligned(dX, 16))
+    return fail(NG_ERR_INVALID_ARG, "dY, X and dX must be 16-byte aligned");
+  if (!aligned(rstd, 4)) return fail(NG_ERR_INVALID_ARG, "rstd must be 4-byte aligned");
+  if (rows < 0 || cols < 1 || rows > kMaxDim * 64)
+    return fail(NG_ERR_INVALID_ARG, "need rows >= 0 and cols >= 1");
+  if (cols % 8 != 0 || cols > 65536)
+    return fail(NG_ERR_UNSUPPORTED, "cols must be a multiple of 8 and at most 65536");
+  if (rows == 0) return ok();
+  ng::NormBwdParams p{};
+  p.dY = dY;
+  p.X = X;
+  p.rstd = rstd;
+  p.dX = dX;
+  p.rows = (int)rows;
+  p.cols = (int)cols;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t nch = cols / 8;
+#define NG_NORM_BWD_LAUNCH(LPR, CPL)                                                      \
+  do {                                                                                    \
+    const unsigned grid = (unsigned)((rows + (256 / LPR) - 1) / (256 / LPR));             \
+    hipLaunchKernelGGL((ng::norm_bwd_kernel<LPR, CPL>), dim3(grid), dim3(256), 0, s, p);  \
+    return launched("ng_rmsnorm_backward");                                               \
+  } while (0)
+  if (nch <= 16) NG_NORM_BWD_LAUNCH(16, 1);
+  if (nch <= 32) NG_NORM_BWD_LAUNCH(32, 1);
+  if (nch <= 64) NG_NORM_BWD_LAUNCH(64, 1);
+  if (nch <= 128) NG_NORM_BWD_LAUNCH(64, 2);
+  if (nch <= 256) NG_NORM_BWD_LAUNCH(64, 4);
+  if (nch <= 512) NG_NORM_BWD_LAUNCH(128, 4);
+  if (nch <= 1024) NG_NORM_BWD_LAUNCH(256, 4);
+  if (nch <= 2048) NG_NORM_BWD_LAUNCH(256, 8);
+  if (nch <= 4096) NG_NORM_BWD_LAUNCH(256, 16);
+  NG_NORM_BWD_LAUNCH(256, 32);
+#undef NG_NORM_BWD_LAUNCH
+}
+
 size_t ng_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
-  (void)K;
+  // the Lazy backward normalizes rows of length K (the forward A's rows)
+  if (op == NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT) N = K;
   if (op != NG_OP_GEMM_RMSNORM && op != NG_OP_GEMM_LAYERNORM && op != NG_OP_GEMM_ADD_RMSNORM &&
-      op != NG_OP_GEMM_ADD_LAYERNORM)
+      op != NG_OP_GEMM_ADD_LAYERNORM && op != NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT)
     return 0;
   if (M <= 0 || N <= 256 || M > kMaxDim || N > kMaxDim) return 0;
   return xwg_bytes(M, N);

@@ -14,6 +14,10 @@
 //                 of A's rows before the product, carried through it (B' =
 //                 diag(gamma) B, colsum = 1^T B', bias = beta^T B; row
 //                 statistics from a pre-pass)
+//   EPI_LAZY_BWD  input gradient of Lazy Pre-Norm, the norm's backward in the
+//                 epilogue of dA_hat = dC @ B^T: C = rstd * acc - c * X with
+//                 c = rstd^3 * sum_n(acc * X) / N per row (X the forward A,
+//                 rstd saved by the forward pass)
 //   cross-workgroup: C = norm(A @ B [+ R]) for rows split over workgroups;
 //                 per-row fp32 partials merged through a workspace
 //                 (persistent grid, gemm_xwg_kernel below)
@@ -57,7 +61,8 @@ enum Epi {
   EPI_LAZY_BIAS = 4,
   EPI_ROW_RMS_RES = 5,
   EPI_ROW_LN_RES = 6,
-  EPI_PRE_LN = 7
+  EPI_PRE_LN = 7,
+  EPI_LAZY_BWD = 8
 };
 constexpr bool epi_lazy(int e) { return e == EPI_LAZY || e == EPI_LAZY_BIAS; }
 constexpr bool epi_row(int e) {
@@ -104,7 +109,8 @@ struct GemmParams {
   uint16_t* S_out;    // residual epilogues: optional bf16 [M][N] output A @ B + R
   const float* colsum;    // EPI_PRE_LN: fp32 [N] column sums of the folded weights
   const float* row_mean;  // EPI_PRE_LN: fp32 [M] mean of each row of A
-  const float* row_rstd;  // EPI_PRE_LN: fp32 [M] rstd of each row of A
+  const float* row_rstd;  // EPI_PRE_LN: fp32 [M] rstd of each row of A; EPI_LAZY_BWD: saved rstd
+  const uint16_t* Xin;    // EPI_LAZY_BWD: the forward input A, bf16 [M][N]
   float* mean_out;
   float* rstd_out;
   char* ws;
@@ -525,6 +531,10 @@ __device__ __forceinline__ float reduce_lane_groups(float v) {
   return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
 }
 
+template <class T>
+__device__ __forceinline__ void combine_waves(float (&out)[T::FM], lds_char* lds, int wm, int wn,
+                                              int lane);
+
 // Per-row sums of this workgroup's accumulators over its valid columns,
 // combined across the WN waves that share rows through LDS (fixed order).
 // mode 0: sum x;  mode 1: sum (x - center[i])^2;  mode 2: sum x^2.
@@ -534,7 +544,6 @@ __device__ __forceinline__ void tile_row_sums(const f32x4 (&acc)[T::FM][T::FN],
                                               const bool (&colv)[T::FN], int mode,
                                               const float (&center)[T::FM], float (&out)[T::FM],
                                               lds_char* lds, int wm, int wn, int lane) {
-  const uint32_t red = T::RED_OFF;
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
     float s = 0.f;
@@ -551,6 +560,15 @@ __device__ __forceinline__ void tile_row_sums(const f32x4 (&acc)[T::FM][T::FN],
     }
     out[i] = reduce_lane_groups(s);
   }
+  combine_waves<T>(out, lds, wm, wn, lane);
+}
+
+// Sum of per-wave row partials over the WN waves that share rows, through
+// LDS in a fixed order (no-op for WN = 1).  Two barriers when WN > 1.
+template <class T>
+__device__ __forceinline__ void combine_waves(float (&out)[T::FM], lds_char* lds, int wm, int wn,
+                                              int lane) {
+  const uint32_t red = T::RED_OFF;
   if constexpr (T::WN > 1) {
     if (lane < 16) {
 #pragma unroll
@@ -575,6 +593,88 @@ __device__ __forceinline__ void tile_row_sums(const f32x4 (&acc)[T::FM][T::FN],
 // touch every LDS bank once per pass.
 __device__ __forceinline__ uint32_t stg_chunk(int r, int c) {
   return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+}
+
+// A bf16 [M][N] matrix's tile, staged in the pipeline stages between a
+// tile's k-loop and the next tile's first transfers (the residual R, or the
+// forward input of the Lazy backward).  Each wave moves its WTM x WTN slice:
+// 256-byte rows (WTN = 128 columns), one 1 KB transfer per 4 rows, 16-byte
+// chunk c of row r at chunk position c ^ (r & 15) so that a fragment read
+// (16 rows, one chunk each) touches every bank once.  Each wave reads back
+// only the rows it moved, so its own transfer count is the only wait.  Rows
+// past M and columns past N read as zero.  The slices start after the output
+// staging when the staging lies on the stages.
+template <class T>
+constexpr uint32_t tile_lds_base() {
+  return T::STG_OWN ? 0u : (uint32_t)T::STG_BYTES;
+}
+
+template <class T>
+__device__ __forceinline__ uint32_t tile_lds_region(int wave) {
+  return tile_lds_base<T>() +
+         (uint32_t)__builtin_amdgcn_readfirstlane(wave) * (uint32_t)T::WTM * 256u;
+}
+
+template <class T>
+__device__ __forceinline__ void load_tile_lds(const GemmParams& p, const uint16_t* src,
+                                              uint32_t lds0, int m_base, int n_base, int wave,
+                                              int wn, int lane) {
+  static_assert(T::WTN == 128, "staged rows of 16 chunks");
+  static_assert(tile_lds_base<T>() + (T::NT / 64) * T::WTM * 256 <= T::STAGES * T::STAGE,
+                "staged slices fit the stages");
+  static_assert(T::WTM % 4 == 0, "4 rows per transfer");
+  // wave-uniform copies (the transfer's LDS address and buffer are scalar)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int m_w = __builtin_amdgcn_readfirstlane(m_base + (wv / T::WN) * T::WTM);
+  const int n_w = n_base + wn * T::WTN;
+  const uint32_t region = tile_lds_region<T>(wv);
+  const uint64_t total = (uint64_t)p.M * (uint64_t)p.N;
+  const int rq = lane >> 4, c = (lane & 15);
+#pragma unroll
+  for (int q = 0; q < T::WTM / 4; ++q) {
+    // rows m_w + 4q .. +3 from a base at row m_w + 4q (offsets below 2^28)
+    const uint64_t base = (uint64_t)(m_w + 4 * q) * (uint64_t)p.N;
+    const uint64_t left = total > base ? (total - base) * 2u : 0u;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + base, left);
+    const int r = 4 * q + rq;
+    const int n = n_w + 8 * (c ^ (r & 15));
+    const uint32_t voff = n < p.N ? ((uint32_t)rq * (uint32_t)p.N + (uint32_t)n) * 2u : kOOB;
+    dma16(rs, lds0 + region + (uint32_t)q * 1024u, voff, 0);
+  }
+  wait_vmcnt<0>();
+}
+
+// The 4 bf16 of the staged tile at this lane's accumulator acc[i][j].
+template <class T>
+__device__ __forceinline__ u32x2 tile_lds_frag(lds_char* lds, uint32_t region, int i, int j,
+                                               int lane) {
+  const int l16 = lane & 15, g = lane >> 4;
+  const int pos = (2 * j + (g >> 1)) ^ l16;
+  return *(lds_u32x2*)(lds + region + (uint32_t)(16 * i + l16) * 256u + (uint32_t)pos * 16u +
+                       8u * (uint32_t)(g & 1));
+}
+
+// Per-row sums of acc * X over the workgroup's columns, X the staged tile
+// (zero past N), combined across the waves sharing rows.
+template <class T>
+__device__ __forceinline__ void tile_dot_sums(const f32x4 (&acc)[T::FM][T::FN], lds_char* lds,
+                                              int wave, int wm, int wn, int lane,
+                                              float (&out)[T::FM]) {
+  const uint32_t region = tile_lds_region<T>(wave);
+#pragma unroll
+  for (int i = 0; i < T::FM; ++i) {
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < T::FN; ++j) {
+      const u32x2 x = tile_lds_frag<T>(lds, region, i, j, lane);
+      s = fmaf(acc[i][j][0], bf16_lo(x[0]), s);
+      s = fmaf(acc[i][j][1], bf16_hi(x[0]), s);
+      s = fmaf(acc[i][j][2], bf16_lo(x[1]), s);
+      s = fmaf(acc[i][j][3], bf16_hi(x[1]), s);
+    }
+    out[i] = reduce_lane_groups(s);
+  }
+  combine_waves<T>(out, lds, wm, wn, lane);
 }
 
 // Per-column gamma/beta of a wave's columns, as loaded bf16 pairs: g[j] and
@@ -623,14 +723,15 @@ __device__ __forceinline__ void load_bias(const GemmParams& p, int n_base, int w
 // Scale/shift the accumulators by per-row (mean, rstd) and (AFFINE) the
 // per-column gamma/beta, or (BIAS) add a per-column fp32 bias after the row
 // scale, or (PRELN) apply rstd * x - mean * rstd * colsum + bias with the
-// per-column fp32 colsum/bias loaded per 64-column group, round to bf16 and
-// store the tile.  Each 16-row x
+// per-column fp32 colsum/bias loaded per 64-column group, or (BWD) apply
+// rstd * x - mean * X with X the staged tile (mean holds the row's c), round
+// to bf16 and store the tile.  Each 16-row x
 // 64-column piece goes through the wave's LDS staging block so that every
 // global store writes whole 128-byte row segments (16 bytes per lane) instead
 // of 8-byte pieces of 16 rows.  Exactly T::C_STORES buffer stores per thread
 // are issued; rows past M and columns past N fall outside the buffer range
 // and are dropped.  Slot i of acc holds fragment i ^ a_xor.
-template <class T, bool AFFINE, bool BIAS = false, bool PRELN = false>
+template <class T, bool AFFINE, bool BIAS = false, bool PRELN = false, bool BWD = false>
 __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
                                             const float (&mean)[T::FM], const float (&rstd)[T::FM],
                                             bool use_mean, const Affine<T>& aff,
@@ -649,6 +750,7 @@ __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&a
   const int rr = lane >> 3, rc = lane & 7;
   const uint32_t r0 = stg + stg_chunk(rr, rc), r1 = stg + stg_chunk(rr + 8, rc);
   const uint32_t row_bytes = (uint32_t)p.N * 2u;
+  const uint32_t xreg = BWD ? tile_lds_region<T>(wave) : 0u;
 #pragma unroll
   for (int q = 0; q < T::FN / 4; ++q) {
     const u32x2* gw = &aff.g[4 * q];
@@ -683,6 +785,12 @@ __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&a
         } else if constexpr (PRELN) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) y[r] = fmaf(x[r], rstd[i], fmaf(sh, pc[jj][r], pb[jj][r]));
+        } else if constexpr (BWD) {
+          const u32x2 xv = tile_lds_frag<T>(lds, xreg, i, 4 * q + jj, lane);
+          y[0] = fmaf(x[0], rstd[i], -mean[i] * bf16_lo(xv[0]));
+          y[1] = fmaf(x[1], rstd[i], -mean[i] * bf16_hi(xv[0]));
+          y[2] = fmaf(x[2], rstd[i], -mean[i] * bf16_lo(xv[1]));
+          y[3] = fmaf(x[3], rstd[i], -mean[i] * bf16_hi(xv[1]));
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r) y[r] = fmaf(x[r], rstd[i], sh);
@@ -770,54 +878,22 @@ __device__ __forceinline__ void lazy_rstd(const GemmParams& p, const float (&ss)
 }
 
 // Residual connection of the post-norm epilogues: acc += R over the wave's
-// WTM x WTN slice, then (when S_out is given) S_out = bf16(acc).  The pipeline
-// stages are idle between a tile's k-loop and the next tile's first
-// transfers, so the slice moves from HBM into them with LDS transfers: 256-byte
-// rows (WTN = 128 columns), one 1 KB transfer per 4 rows, 16-byte chunk c of
-// row r at chunk position c ^ (r & 15) so that a fragment read (16 rows, one
-// chunk each) touches every bank once.  Each wave reads back only the rows it
-// moved, so its own transfer count is the only wait.  Rows past M and columns
-// past N read as zero (they are neither counted in the statistics nor
-// stored).  Ends with a barrier, after which the stages and any output
-// staging aliased on them may be reused.  A workgroup reads R only inside its
-// own tile and before it writes C or S_out there, so R may be the very
-// buffer that C or S_out is.
+// WTM x WTN slice (R staged through the pipeline stages, load_tile_lds),
+// then (when S_out is given) S_out = bf16(acc).  Ends with a barrier, after
+// which the stages may be reused.  A workgroup reads R only inside its own
+// tile and before it writes C or S_out there, so R may be the very buffer
+// that C or S_out is.
 template <class T>
 __device__ __forceinline__ void add_residual(const GemmParams& p, f32x4 (&acc)[T::FM][T::FN],
                                              lds_char* lds, uint32_t lds0, int m_base, int n_base,
                                              int wave, int wm, int wn, int lane) {
-  static_assert(T::WTN == 128, "residual rows of 16 chunks");
-  static_assert((T::NT / 64) * T::WTM * 256 <= T::STAGES * T::STAGE, "residual slices fit the stages");
-  static_assert(T::WTM % 4 == 0, "4 rows per transfer");
-  // wave-uniform copies (the transfer's LDS address and buffer are scalar)
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int m_w = __builtin_amdgcn_readfirstlane(m_base + (wv / T::WN) * T::WTM);
-  const int n_w = n_base + wn * T::WTN;
-  const uint32_t region = (uint32_t)wv * (uint32_t)T::WTM * 256u;
-  const uint64_t total = (uint64_t)p.M * (uint64_t)p.N;
-  {
-    const int rq = lane >> 4, c = (lane & 15);
-#pragma unroll
-    for (int q = 0; q < T::WTM / 4; ++q) {
-      // rows m_w + 4q .. +3 from a base at row m_w + 4q (offsets below 2^28)
-      const uint64_t base = (uint64_t)(m_w + 4 * q) * (uint64_t)p.N;
-      const uint64_t left = total > base ? (total - base) * 2u : 0u;
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.R + base, left);
-      const int r = 4 * q + rq;
-      const int n = n_w + 8 * (c ^ (r & 15));
-      const uint32_t voff = n < p.N ? ((uint32_t)rq * (uint32_t)p.N + (uint32_t)n) * 2u : kOOB;
-      dma16(rs, lds0 + region + (uint32_t)q * 1024u, voff, 0);
-    }
-  }
-  wait_vmcnt<0>();
-  const int l16 = lane & 15, g = lane >> 4;
+  load_tile_lds<T>(p, p.R, lds0, m_base, n_base, wave, wn, lane);
+  const uint32_t region = tile_lds_region<T>(wave);
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
 #pragma unroll
     for (int j = 0; j < T::FN; ++j) {
-      const int pos = (2 * j + (g >> 1)) ^ l16;
-      const u32x2 v = *(lds_u32x2*)(lds + region + (uint32_t)(16 * i + l16) * 256u +
-                                    (uint32_t)pos * 16u + 8u * (uint32_t)(g & 1));
+      const u32x2 v = tile_lds_frag<T>(lds, region, i, j, lane);
       acc[i][j][0] += bf16_lo(v[0]);
       acc[i][j][1] += bf16_hi(v[0]);
       acc[i][j][2] += bf16_lo(v[1]);
@@ -852,6 +928,19 @@ __device__ __forceinline__ void tile_scale(const GemmParams& p, const f32x4 (&ac
   for (int i = 0; i < T::FM; ++i) { mean[i] = 0.f; rstd[i] = 1.f; }
   if constexpr (epi_lazy(EPI)) {
     lazy_rstd<T>(p, ss, rstd, lds, m_base, tn, wm, wn, lane, ax);
+  } else if constexpr (EPI == EPI_LAZY_BWD) {
+    // c = rstd^3 * sum(acc * X) / N, carried in mean[]
+    const int l16 = lane & 15;
+    float s[T::FM];
+    tile_dot_sums<T>(acc, lds, wm * T::WN + wn, wm, wn, lane, s);
+    const float inv_n = 1.0f / (float)p.N;
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) {
+      const int m = m_base + wm * T::WTM + 16 * i + l16;
+      const float r = m < p.M ? p.row_rstd[m] : 0.f;
+      rstd[i] = r;
+      mean[i] = r * r * r * s[i] * inv_n;
+    }
   } else if constexpr (EPI == EPI_PRE_LN) {
     const int l16 = lane & 15;
 #pragma unroll
@@ -893,7 +982,7 @@ __device__ __forceinline__ void tile_store(const GemmParams& p, const f32x4 (&ac
                                            const Affine<T>& aff, const Bias<T>& bias, lds_char* lds,
                                            int m_base, int n_base, int wave, int wm, int wn,
                                            int lane, int ax) {
-  apply_store<T, epi_row(EPI), EPI == EPI_LAZY_BIAS, EPI == EPI_PRE_LN>(
+  apply_store<T, epi_row(EPI), EPI == EPI_LAZY_BIAS, EPI == EPI_PRE_LN, EPI == EPI_LAZY_BWD>(
       p, acc, mean, rstd, epi_ln(EPI) || EPI == EPI_PRE_LN, aff, bias, lds, m_base, n_base, wave,
       wm, wn, lane, ax);
 }
@@ -919,6 +1008,8 @@ __device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds,
   mainloop<T, epi_lazy(EPI)>(p, acc, ss, lds, lds_addr_of(lds), m_base, n_base, tid);
   if constexpr (epi_res(EPI))
     add_residual<T>(p, acc, lds, lds_addr_of(lds), m_base, n_base, wave, wm, wn, lane);
+  if constexpr (EPI == EPI_LAZY_BWD)
+    load_tile_lds<T>(p, p.Xin, lds_addr_of(lds), m_base, n_base, wave, wn, lane);
   Affine<T> aff;
   Bias<T> bias;
   load_columns<T, EPI>(p, n_base, wn, lane, aff, bias);
@@ -1079,15 +1170,21 @@ __device__ __forceinline__ void chan_combine(float& n_a, float& mu_a, float& m2_
   n_a = nn;
 }
 
-// Step 2.
-template <class T, bool LN>
+// Step 2.  BWD: (0, sum acc * X) per row, X the staged forward input.
+template <class T, bool LN, bool BWD = false>
 __device__ __forceinline__ void xwg_publish(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
                                             lds_char* lds, int tm, int tn, int tid, uint32_t tag) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int l16 = lane & 15, g = lane >> 4;
   float s1[T::FM], s2[T::FM];
-  tile_stats<T, LN>(p, acc, lds, tn * T::BN, wm, wn, lane, s1, s2);
+  if constexpr (BWD) {
+    tile_dot_sums<T>(acc, lds, wave, wm, wn, lane, s2);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i) s1[i] = 0.f;
+  } else {
+    tile_stats<T, LN>(p, acc, lds, tn * T::BN, wm, wn, lane, s1, s2);
+  }
   const __amdgpu_buffer_rsrc_t prs = xwg_part_rsrc<T>(p, tm);
   if (wn == 0 && g == 0) {
 #pragma unroll
@@ -1102,8 +1199,9 @@ __device__ __forceinline__ void xwg_publish(const GemmParams& p, const f32x4 (&a
 // Step 4.  Rows r0 .. r1-1 of the row block belong to this workgroup.  A row
 // is merged by `cpl` lanes (a power of two, at most 64, at least tiles_n when
 // tiles_n <= 64): lane li takes column tiles li, li+cpl, ... in order, then
-// the lanes combine pairwise, lower lanes first.
-template <class T, bool LN>
+// the lanes combine pairwise, lower lanes first.  BWD: the row's plain sum is
+// published as is (in the rstd slot).
+template <class T, bool LN, bool BWD = false>
 __device__ __forceinline__ void xwg_merge_rows(const GemmParams& p, int tm, int tn, int tid,
                                                uint32_t tag) {
   constexpr int NW = T::NT / 64;
@@ -1149,12 +1247,12 @@ __device__ __forceinline__ void xwg_merge_rows(const GemmParams& p, int tm, int 
       }
     }
     if (active && li == 0) {
-      const float r = 1.0f / __builtin_sqrtf(fmaf(m2, inv_n, p.eps));
+      const float r = BWD ? m2 : 1.0f / __builtin_sqrtf(fmaf(m2, inv_n, p.eps));
       const float mean = LN ? mu : 0.f;
       const u32x4 v = {__float_as_uint(mean), tag, __float_as_uint(r), tag};
       __builtin_amdgcn_raw_buffer_store_b128(v, frs, (uint32_t)row * 16u, 0, 16);
       const int m = tm * T::BM + row;
-      if (m < p.M) {
+      if (!BWD && m < p.M) {
         if (p.mean_out) p.mean_out[m] = mean;
         if (p.rstd_out) p.rstd_out[m] = r;
       }
@@ -1162,7 +1260,7 @@ __device__ __forceinline__ void xwg_merge_rows(const GemmParams& p, int tm, int 
   }
 }
 
-template <class T, bool LN, bool RES = false>
+template <class T, bool LN, bool RES = false, bool BWD = false>
 __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
   static_assert(T::STG_OWN, "persistent tiles need their own output staging");
   __shared__ __attribute__((aligned(16))) char smem[T::LDS];
@@ -1195,25 +1293,45 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
     const int m_base = tm * T::BM, n_base = tn * T::BN;
     f32x4 acc[T::FM][T::FN];
     float ss[T::FM];
-    mainloop<T, false>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, it > 0);
+    // (BWD: the previous tile's output stores precede this tile's first
+    // transfers, so they are not counted after them)
+    mainloop<T, false>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, !BWD && it > 0);
     if constexpr (RES) add_residual<T>(p, acc, lds, lds0, m_base, n_base, wave, wm, wn, lane);
-    xwg_publish<T, LN>(p, acc, lds, tm, tn, tid, tag);
+    if constexpr (BWD) load_tile_lds<T>(p, p.Xin, lds0, m_base, n_base, wave, wn, lane);
+    xwg_publish<T, LN, BWD>(p, acc, lds, tm, tn, tid, tag);
     Affine<T> aff;
-    load_affine<T>(p, n_base, wn, lane, aff);
-    if (tm + R < p.tiles_m) issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid);
-    xwg_merge_rows<T, LN>(p, tm, tn, tid, tag);
-    // step 5: (mean, rstd) of this wave's rows
+    if constexpr (!BWD) {
+      load_affine<T>(p, n_base, wn, lane, aff);
+      if (tm + R < p.tiles_m) issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid);
+    }
+    xwg_merge_rows<T, LN, BWD>(p, tm, tn, tid, tag);
+    // step 5: (mean, rstd) of this wave's rows; BWD: (c, rstd) from the row's
+    // sum of acc * X and the saved rstd
     const __amdgpu_buffer_rsrc_t frs = xwg_fin_rsrc<T>(p, tm);
     float mean[T::FM], rstd[T::FM];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
       const u32x4 v = xwg_poll(p, frs, (uint32_t)(wm * T::WTM + 16 * i + l16) * 16u, tag);
-      mean[i] = __uint_as_float(v[0]);
-      rstd[i] = __uint_as_float(v[2]);
+      if constexpr (BWD) {
+        const int m = m_base + wm * T::WTM + 16 * i + l16;
+        const float r = m < p.M ? p.row_rstd[m] : 0.f;
+        rstd[i] = r;
+        mean[i] = r * r * r * __uint_as_float(v[2]) * (1.0f / (float)p.N);
+      } else {
+        mean[i] = __uint_as_float(v[0]);
+        rstd[i] = __uint_as_float(v[2]);
+      }
     }
     Bias<T> no_bias;
-    apply_store<T, true>(p, acc, mean, rstd, LN, aff, no_bias, lds, m_base, n_base, wave, wm, wn,
-                         lane);
+    apply_store<T, !BWD, false, false, BWD>(p, acc, mean, rstd, LN, aff, no_bias, lds, m_base,
+                                            n_base, wave, wm, wn, lane);
+    if constexpr (BWD) {
+      // every wave has read its staged X: the stages may take the next tile
+      if (tm + R < p.tiles_m) {
+        __syncthreads();
+        issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid);
+      }
+    }
   }
   // the last workgroup to finish advances the call counter (every workgroup
   // read it at its start)

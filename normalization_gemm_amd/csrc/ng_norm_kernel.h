@@ -156,6 +156,69 @@ __global__ void __launch_bounds__(256) norm_kernel(NormParams p) {
   }
 }
 
+// Standalone RMSNorm backward (no affine), the norm half of the unfused
+// baseline of the Lazy backward: for a row x with saved rstd and upstream
+// gradient dy,  dx = rstd * dy - rstd^3 * (sum_k dy_k x_k) / cols * x  (the
+// chain rule of y = x * rstd, rstd = (mean(x^2) + eps)^(-1/2)).  Both rows
+// stay in registers; LPR lanes per row, CPL 16-byte chunks per lane.
+struct NormBwdParams {
+  const uint16_t* dY;
+  const uint16_t* X;
+  const float* rstd;
+  uint16_t* dX;
+  int rows, cols;
+};
+
+template <int LPR, int CPL>
+__global__ void __launch_bounds__(256) norm_bwd_kernel(NormBwdParams p) {
+  constexpr int RPB = 256 / LPR;
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int r_in = tid / LPR, lr = tid % LPR;
+  const long row = (long)blockIdx.x * RPB + r_in;
+  const bool rv = row < p.rows;
+  const int nch = p.cols >> 3;
+  const u32x4* dyr = (const u32x4*)(p.dY + row * (long)p.cols);
+  const u32x4* xr = (const u32x4*)(p.X + row * (long)p.cols);
+  u32x4 dy[CPL], x[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int idx = lr + c * LPR;
+    dy[c] = u32x4{0u, 0u, 0u, 0u};
+    x[c] = u32x4{0u, 0u, 0u, 0u};
+    if (rv && idx < nch) {
+      dy[c] = dyr[idx];
+      x[c] = xr[idx];
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      s = fmaf(bf16_lo(dy[c][w]), bf16_lo(x[c][w]), s);
+      s = fmaf(bf16_hi(dy[c][w]), bf16_hi(x[c][w]), s);
+    }
+  s = row_reduce<LPR>(s, red, tid);
+  if (!rv) return;
+  const float r = p.rstd[row];
+  const float cx = r * r * r * s / (float)p.cols;
+  u32x4* dxr = (u32x4*)(p.dX + row * (long)p.cols);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int idx = lr + c * LPR;
+    if (idx >= nch) continue;
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float a = fmaf(bf16_lo(dy[c][w]), r, -cx * bf16_lo(x[c][w]));
+      const float b = fmaf(bf16_hi(dy[c][w]), r, -cx * bf16_hi(x[c][w]));
+      o[w] = pack_bf16x2(a, b);
+    }
+    dxr[idx] = o;
+  }
+}
+
 // Zero-fill (workspace reset) without hipMemsetAsync, so it may be captured
 // in a HIP graph.
 __global__ void __launch_bounds__(256) fill_zero_kernel(u32x4* p, size_t n16, uint32_t* tail,

@@ -33,7 +33,8 @@ def test_header_declares_expected_entry_points():
     for n in ("ng_rmsnorm_gemm_lazy", "ng_gemm_layernorm", "ng_gemm_rmsnorm", "ng_gemm",
               "ng_norm", "ng_workspace_bytes", "ng_lazy_fold_affine",
               "ng_rmsnorm_gemm_lazy_affine", "ng_gemm_add_rmsnorm", "ng_gemm_add_layernorm",
-              "ng_add_norm", "ng_layernorm_gemm_fold", "ng_layernorm_gemm_prenorm"):
+              "ng_add_norm", "ng_layernorm_gemm_fold", "ng_layernorm_gemm_prenorm",
+              "ng_rmsnorm_gemm_lazy_backward_input", "ng_rmsnorm_backward"):
         assert n in names
 
 
@@ -220,6 +221,30 @@ def test_prenorm_layernorm_argument_checks():
     assert f(P, P2, P4, None, P3, 64, 64, 65544, 0, 1e-5, P4, P5, None) == 2  # K > 65536
     assert f(P, P2, P4, None, P3, 64, 100, 64, 0, 1e-5, P4, P5, None) == 2    # N % 8
     assert f(None, P2, P4, None, None, 0, 64, 64, 0, 1e-5, None, None, None) == 0  # M = 0
+
+
+def test_lazy_backward_argument_checks():
+    f = _lib.ng_rmsnorm_gemm_lazy_backward_input
+    op = _lib.NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT
+    # rows of the forward A (length K) decide the strategy and the workspace
+    assert _lib.ng_workspace_bytes(op, 64, 128, 256) == 0
+    ws = _lib.ng_workspace_bytes(op, 64, 128, 4096)
+    assert ws == _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_RMSNORM, 64, 4096, 128) > 0
+    assert f(P, P2, None, P4, P3, 64, 128, 64, 0, None, 0, None) == 1     # A NULL
+    assert f(P, P2, P5, None, P3, 64, 128, 64, 0, None, 0, None) == 1     # rstd NULL
+    assert f(P, P2, BAD, P4, P3, 64, 128, 64, 0, None, 0, None) == 1      # A misaligned
+    assert f(P, P2, P5, P4 + 2, P3, 64, 128, 64, 0, None, 0, None) == 1   # rstd misaligned
+    assert f(P, P2, P5, P4, P3, 64, 128, 64, 3, None, 0, None) == 1       # layout
+    assert f(P, P2, P5, P4, P3, 64, 128, 60, 0, None, 0, None) == 2       # K % 8
+    assert f(P, P2, P5, P4, P3, 64, 128, 4096, 0, None, 0, None) == 3     # workspace
+    assert f(P, P2, P5, P4, P3, 64, 128, 4096, 1, P, ws - 16, None) == 3
+    assert f(None, P2, None, None, None, 0, 128, 64, 0, None, 0, None) == 0  # M = 0
+    g = _lib.ng_rmsnorm_backward
+    assert g(None, P2, P3, P4, 4, 64, None) == 1
+    assert g(P, BAD, P3, P4, 4, 64, None) == 1
+    assert g(P, P2, P3 + 2, P4, 4, 64, None) == 1
+    assert g(P, P2, P3, P4, 4, 60, None) == 2
+    assert g(None, None, None, None, 0, 64, None) == 0
 
 
 def test_workspace_helpers_argument_checks():

@@ -467,6 +467,57 @@ def test_prenorm_layernorm_persistent_multi_tile_ragged():
     _check_prenorm_stats(mean, rstd, mref, rref)
 
 
+# ------------------------------------------------- Lazy Pre-Norm backward
+def _lazy_bwd(x, layout, eps, workspace=None):
+    """Forward (saves rstd), then the fused input gradient; returns (dA, rstd)."""
+    M = x.A.shape[0]
+    A, B = up(x.A), up(b_for_layout(x.B, layout))
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    ng.rmsnorm_gemm_lazy(A, B, eps=eps, b_layout=layout, rstd_out=rstd)
+    dA = ng.rmsnorm_gemm_lazy_backward_input(up(x.dC), B, A, rstd, b_layout=layout,
+                                             workspace=workspace)
+    return dA, rstd
+
+
+# forward (M, N, K): rows of A of length K <= 128, <= 256 and wider (cross-workgroup)
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("M,N,K", [(256, 64, 128), (300, 136, 200), (77, 72, 128), (513, 264, 520),
+                                   (130, 64, 256), (1, 8, 8), (260, 96, 1000)])
+def test_lazy_backward_input_small(M, N, K, layout):
+    log("lazy backward M=%d N=%d K=%d %s" % (M, N, K, layout))
+    x = workloads.make_inputs(M, N, K, seed=11 * M + N + K, row_scale=True, upstream=True)
+    dA, rstd = _lazy_bwd(x, layout, 1e-6)
+    torch.cuda.synchronize()
+    ref, _, rref = oracle.rmsnorm_gemm_lazy_backward(x.A, x.B, x.dC, 1e-6)
+    _check("lazy backward dA", down(dA), ref)
+    _check_stat("lazy backward rstd (forward)", rstd, rref)
+
+
+def test_lazy_backward_input_cross_workgroup_rounds_ragged():
+    # 10 column tiles of dA -> 25 row blocks per round; 31 row blocks -> 2 rounds
+    M, N, K = 256 * 30 + 100, 136, 256 * 9 + 24
+    for layout in ("kn", "nk"):
+        log("lazy backward xwg rounds M=%d N=%d K=%d %s" % (M, N, K, layout))
+        x = workloads.make_inputs(M, N, K, seed=31, row_scale=True, upstream=True)
+        dA, _ = _lazy_bwd(x, layout, 1e-6)
+        torch.cuda.synchronize()
+        ref = oracle.rmsnorm_gemm_lazy_backward(x.A, x.B, x.dC, 1e-6)[0]
+        _check("lazy backward xwg rounds", down(dA), ref)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 8), (37, 128), (300, 136), (65, 1000), (9, 8200)])
+def test_rmsnorm_backward_small(rows, cols):
+    # the standalone norm backward is the oracle's input gradient with B = I
+    x = workloads.make_inputs(rows, cols, cols, seed=rows + 5 * cols, row_scale=True,
+                              upstream=True)
+    eye = np.eye(cols)
+    ref, _, rref = oracle.rmsnorm_gemm_lazy_backward(x.A, eye, x.dC, 1e-6)
+    rstd = torch.as_tensor(rref.astype(np.float32), device="cuda")
+    dX = ng.rmsnorm_backward(up(x.dC), up(x.A), rstd)
+    torch.cuda.synchronize()
+    _check("rmsnorm backward %dx%d" % (rows, cols), down(dX), ref)
+
+
 # ------------------------------------------------------------ edge cases
 def test_empty_M_leaves_output_untouched():
     A = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
@@ -546,6 +597,9 @@ def _workload_case(w, layout="kn", n_rows=24):
     if w.op == workloads.OP_LAZY:
         C = ng.rmsnorm_gemm_lazy(A, B, eps=w.eps, b_layout=layout)
         ref = oracle.rmsnorm_gemm_lazy(x.A[rows], x.B, w.eps)[0]
+    elif w.op == workloads.OP_LAZY_BWD:
+        C = _lazy_bwd(x, layout, w.eps)[0]
+        ref = oracle.rmsnorm_gemm_lazy_backward(x.A[rows], x.B, x.dC[rows], w.eps)[0]
     elif w.op == workloads.OP_PRENORM_LN:
         C = _prenorm_case(x, layout, w.eps)[0]
         ref = oracle.layernorm_gemm_prenorm(x.A[rows], x.B, w.eps, x.gamma, x.beta)[0]
@@ -598,6 +652,22 @@ def test_prenorm_unfused_pair_full_size():
     torch.cuda.synchronize()
     ref = oracle.layernorm_gemm_prenorm(x.A[rows], x.B, w.eps, x.gamma, x.beta)[0]
     _check("unfused layernorm->gemm", down(C[torch.as_tensor(rows, device="cuda")]), ref)
+
+
+def test_lazy_backward_unfused_pair_full_size():
+    # the unfused baseline of the input gradient: ng_gemm (dC @ B^T), then
+    # ng_rmsnorm_backward
+    w = workloads.WORKLOAD_BY_NAME["lazy_rms_bwd_32768x4096x4096"]
+    x = workloads.workload_inputs(w)
+    rows = sample_rows(w.M, 16, seed=6)
+    A, B = up(x.A), up(x.B)
+    rstd = torch.empty(w.M, dtype=torch.float32, device="cuda")
+    ng.rmsnorm_gemm_lazy(A, B, eps=w.eps, rstd_out=rstd)
+    dAh = ng.gemm(up(x.dC), B, b_layout="nk")   # B [K, N] read as B^T's [N', K'] layout
+    dA = ng.rmsnorm_backward(dAh, A, rstd)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm_gemm_lazy_backward(x.A[rows], x.B, x.dC[rows], w.eps)[0]
+    _check("unfused gemm->rmsnorm backward", down(dA[torch.as_tensor(rows, device="cuda")]), ref)
 
 
 def test_named_workload_nk_layout_large():

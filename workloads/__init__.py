@@ -11,7 +11,9 @@ Input recipe (the same for every workload):
   (when the workload has them), then the per-row shifts of A (when it has
   them), then B's standard normals ``[K, N]`` times
   ``sqrt(1/K)``, then gamma, then beta, then (residual forms) the residual
-  R's standard normals ``[M, N]`` (unit variance, the scale of ``A @ B``).
+  R's standard normals ``[M, N]`` (unit variance, the scale of ``A @ B``),
+  then (backward forms) the upstream gradient dC's standard normals
+  ``[M, N]``.
 * ``N(mu, v)`` in a workload description is read with ``v`` as the variance,
   so ``B ~ N(0, 1/K)`` keeps ``A @ B`` at unit variance per element and
   ``gamma ~ N(1, 0.1)`` has standard deviation ``sqrt(0.1)``.
@@ -42,6 +44,7 @@ OP_LAZY_AFFINE = "rmsnorm_gemm_lazy_affine"
 OP_GEMM_ADD_RMSNORM = "gemm_add_rmsnorm"
 OP_GEMM_ADD_LAYERNORM = "gemm_add_layernorm"
 OP_PRENORM_LN = "layernorm_gemm_prenorm"
+OP_LAZY_BWD = "rmsnorm_gemm_lazy_backward_input"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -57,6 +60,7 @@ class Workload:
     gamma: bool = False
     beta: bool = False
     residual: bool = False
+    upstream: bool = False
     description: str = ""
 
     @property
@@ -95,6 +99,10 @@ NEXT_WORKLOADS = [
              row_scale=True, row_shift=True, gamma=True, beta=True,
              description="pre-LayerNorm with gamma and beta (length K) fused with the product, "
                          "A 32768x4096 (row scale and shift) @ B 4096x4096"),
+    Workload("lazy_rms_bwd_32768x4096x4096", OP_LAZY_BWD, 32768, 4096, 4096, 1e-6,
+             row_scale=True, upstream=True,
+             description="Lazy Pre-Norm input gradient: dC 32768x4096 @ B^T, the RMSNorm "
+                         "backward over rows of A (32768x4096) in the epilogue"),
     Workload("gemm_add_ln_65536x512x128", OP_GEMM_ADD_LAYERNORM, 65536, 128, 512, 1e-5,
              residual=True,
              description="GEMM + residual add + LayerNorm epilogue (no affine), "
@@ -127,12 +135,13 @@ class Inputs:
     gamma: Optional[np.ndarray]     # uint16 bits [N] or None
     beta: Optional[np.ndarray]      # uint16 bits [N] or None
     R: Optional[np.ndarray] = None  # uint16 bits [M, N] or None (residual forms)
+    dC: Optional[np.ndarray] = None  # uint16 bits [M, N] or None (backward forms)
 
 
 def make_inputs(M: int, N: int, K: int, *, seed: int = 0, row_scale: bool = False,
                 gamma: bool = False, beta: bool = False,
                 gamma_len: Optional[int] = None, residual: bool = False,
-                row_shift: bool = False) -> Inputs:
+                row_shift: bool = False, upstream: bool = False) -> Inputs:
     """Draw one seeded input set in the fixed order documented above.
 
     ``gamma_len`` overrides the length of gamma/beta (default N).
@@ -159,7 +168,10 @@ def make_inputs(M: int, N: int, K: int, *, seed: int = 0, row_scale: bool = Fals
     R = None
     if residual:
         R = f32_to_bf16_bits(rng.standard_normal((M, N), dtype=np.float32))
-    return Inputs(A, B, g, bt, R)
+    dC = None
+    if upstream:
+        dC = f32_to_bf16_bits(rng.standard_normal((M, N), dtype=np.float32))
+    return Inputs(A, B, g, bt, R, dC)
 
 
 def workload_inputs(w: Workload, seed: int = 0) -> Inputs:
@@ -167,4 +179,4 @@ def workload_inputs(w: Workload, seed: int = 0) -> Inputs:
     gl = w.K if w.op in (OP_LAZY_AFFINE, OP_PRENORM_LN) else None
     return make_inputs(w.M, w.N, w.K, seed=seed, row_scale=w.row_scale,
                        gamma=w.gamma, beta=w.beta, gamma_len=gl, residual=w.residual,
-                       row_shift=w.row_shift)
+                       row_shift=w.row_shift, upstream=w.upstream)
