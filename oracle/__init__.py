@@ -24,6 +24,7 @@ from .normgemm_oracle import (  # noqa: F401
     layernorm_gemm_prenorm,
     layernorm_gemm_fold,
     rmsnorm_gemm_lazy_backward,
+    lazy_backward_weight,
     gemm_add_layernorm,
     norm,
     rel_err,

@@ -196,11 +196,21 @@ def rmsnorm_gemm_lazy_backward(A, B, dC, eps: float
     A_hat, rstd = rms_norm_rows(A, eps)
     G = _f64(dC)
     dA_hat = G @ _f64(B).T
-    dB = A_hat.T @ G
+    dB = lazy_backward_weight(A, dC, eps)
     K = A_hat.shape[1]
     dot = (dA_hat * A_hat).sum(axis=1, keepdims=True) / K
     dA = rstd[:, None] * (dA_hat - A_hat * dot)
     return dA, dB, rstd
+
+
+def lazy_backward_weight(A, dC, eps: float, rows=None) -> np.ndarray:
+    """dB = A_hat^T @ dC, the weight gradient of C = rmsnorm(A) @ B, with
+    A_hat = rmsnorm(A) (no affine).  `rows` selects rows of dB (columns of A)
+    so that a few rows of a large dB can be formed alone."""
+    A_hat, _ = rms_norm_rows(A, eps)
+    if rows is not None:
+        A_hat = A_hat[:, rows]
+    return A_hat.T @ _f64(dC)
 
 
 def gemm_rmsnorm(A, B, eps: float, gamma=None) -> Tuple[np.ndarray, np.ndarray]:

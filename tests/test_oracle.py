@@ -424,6 +424,17 @@ def test_lazy_backward_input_gradient_is_orthogonal_to_rows():
     np.testing.assert_allclose(dB, A_hat.T @ G, rtol=1e-13)
 
 
+def test_lazy_backward_weight_rows_are_rows_of_the_full_gradient():
+    rng = np.random.default_rng(53)
+    A = rng.standard_normal((40, 12))
+    G = rng.standard_normal((40, 7))
+    full = oracle.lazy_backward_weight(A, G, 1e-6)
+    rows = np.array([0, 5, 11])
+    np.testing.assert_array_equal(oracle.lazy_backward_weight(A, G, 1e-6, rows), full[rows])
+    _, dB, _ = oracle.rmsnorm_gemm_lazy_backward(A, rng.standard_normal((12, 7)), G, 1e-6)
+    np.testing.assert_array_equal(dB, full)
+
+
 def test_lazy_is_not_layernorm_prenorm():
     # LayerNorm subtracts the row mean, which breaks the commutation.
     rng = np.random.default_rng(12)
