@@ -129,6 +129,9 @@ def algorithmic_bytes(w: workloads.Workload) -> int:
         return b + 4 * w.N
     if w.op == workloads.OP_PRENORM_LN:
         return b + 8 * w.N  # fp32 colsum and bias
+    if w.op == workloads.OP_LAZY_BWD_W:
+        # A [M, K], dC [M, N], dB [K, N], fp32 rstd [M]
+        return 2 * (w.M * w.K + w.M * w.N + w.K * w.N) + 4 * w.M
     if w.op == workloads.OP_LAZY_BWD:
         # dC [M, N], B, A [M, K] and dA [M, K], fp32 rstd [M]
         return 2 * (w.M * w.N + w.K * w.N + 2 * w.M * w.K) + 4 * w.M
@@ -147,7 +150,8 @@ def norm_bytes(w: workloads.Workload) -> int:
 
 def prenorm(w: workloads.Workload) -> bool:
     """The norm acts on A before the product (the unfused pair runs it first)."""
-    return w.op in (workloads.OP_LAZY, workloads.OP_LAZY_AFFINE, workloads.OP_PRENORM_LN)
+    return w.op in (workloads.OP_LAZY, workloads.OP_LAZY_AFFINE, workloads.OP_PRENORM_LN,
+                    workloads.OP_LAZY_BWD_W)
 
 
 def kernel_label(w: workloads.Workload) -> str:
@@ -157,7 +161,10 @@ def kernel_label(w: workloads.Workload) -> str:
            workloads.OP_GEMM_RMSNORM: "EPI_ROW_RMS", workloads.OP_GEMM_LAYERNORM: "EPI_ROW_LN",
            workloads.OP_GEMM_ADD_RMSNORM: "EPI_ROW_RMS_RES",
            workloads.OP_GEMM_ADD_LAYERNORM: "EPI_ROW_LN_RES",
-           workloads.OP_PRENORM_LN: "EPI_PRE_LN", workloads.OP_LAZY_BWD: "EPI_LAZY_BWD"}[w.op]
+           workloads.OP_PRENORM_LN: "EPI_PRE_LN", workloads.OP_LAZY_BWD: "EPI_LAZY_BWD",
+           workloads.OP_LAZY_BWD_W: "EPI_NONE"}[w.op]
+    if w.op == workloads.OP_LAZY_BWD_W:
+        return "gemm_persistent_kernel<Tile<..., A stored [K,M], RS 1>, EPI_NONE>"
     if w.op == workloads.OP_LAZY_BWD:
         return "%s<%s>" % ("gemm_kernel" if w.K <= 256 else "gemm_xwg_kernel", epi)
     if prenorm(w):
@@ -220,6 +227,14 @@ class Bench:
         if w.residual:
             R0 = up(x.R)
             self.res = [R0] + [R0.clone() for _ in range(self.R - 1)]
+        if w.op == workloads.OP_LAZY_BWD_W:
+            # the forward pass's saved rstd (untimed); the output dB is [K, N]
+            self.rstd = torch.empty(w.M, dtype=torch.float32, device=dev)
+            ng.rmsnorm_gemm_lazy(A0, self.B, eps=w.eps, rstd_out=self.rstd)
+            G0 = up(x.dC)
+            self.dC = [G0] + [G0.clone() for _ in range(self.R - 1)]
+            self.C = [torch.empty((w.K, w.N), dtype=torch.bfloat16, device=dev)
+                      for _ in range(self.R)]
         if w.op == workloads.OP_LAZY_BWD:
             # the forward pass's saved rstd (untimed); outputs are [M, K]
             self.rstd = torch.empty(w.M, dtype=torch.float32, device=dev)
@@ -248,6 +263,7 @@ class Bench:
               workloads.OP_LAZY_AFFINE: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_PRENORM_LN: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_LAZY_BWD: ng.NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT,
+              workloads.OP_LAZY_BWD_W: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_GEMM_RMSNORM: ng.NG_OP_GEMM_RMSNORM,
               workloads.OP_GEMM_LAYERNORM: ng.NG_OP_GEMM_LAYERNORM,
               workloads.OP_GEMM_ADD_RMSNORM: ng.NG_OP_GEMM_ADD_RMSNORM,
@@ -281,6 +297,13 @@ class Bench:
                                      eps, None, st)))
                 self._gemm.append((lib.ng_gemm, (An, B, C, M, N, K, 0, st)))
                 self._norm.append((lib.ng_norm, (A, g, b, An, M, K, 0, eps, None, None, st)))
+            elif w.op == workloads.OP_LAZY_BWD_W:
+                G, An, rs = self.dC[r].data_ptr(), self.An[r].data_ptr(), self.rstd.data_ptr()
+                self._fused.append((lib.ng_rmsnorm_gemm_lazy_backward_weight,
+                                    (A, G, rs, C, M, N, K, 0, st)))
+                # unfused: A_hat stored by ng_norm, then dB = A_hat^T @ dC
+                self._gemm.append((lib.ng_gemm_at, (An, G, C, K, N, M, st)))
+                self._norm.append((lib.ng_norm, (A, None, None, An, M, K, 0, eps, None, None, st)))
             elif w.op == workloads.OP_LAZY_BWD:
                 G, dAh, rs = self.dC[r].data_ptr(), self.dAh[r].data_ptr(), self.rstd.data_ptr()
                 self._fused.append((lib.ng_rmsnorm_gemm_lazy_backward_input,
@@ -427,6 +450,8 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
             oracle.layernorm_gemm_prenorm(x.A, x.B, w.eps, x.gamma, x.beta)
         elif w.op == workloads.OP_LAZY_BWD:
             oracle.rmsnorm_gemm_lazy_backward(x.A, x.B, x.dC, w.eps)
+        elif w.op == workloads.OP_LAZY_BWD_W:
+            oracle.lazy_backward_weight(x.A, x.dC, w.eps)
         elif w.op == workloads.OP_GEMM_RMSNORM:
             oracle.gemm_rmsnorm(x.A, x.B, w.eps, x.gamma)
         elif w.op == workloads.OP_GEMM_ADD_RMSNORM:

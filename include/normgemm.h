@@ -257,6 +257,32 @@ int ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const 
                 float* mean_out, float* rstd_out, void* stream);
 
 /*
+ * Weight gradient of Lazy Pre-Norm: dB = A_hat^T @ dC with A_hat = rstd * A
+ * rebuilt on the fly from A and the forward's saved rstd ("Free
+ * normalization fusion", section "Lazy Pre-Norm": the normalized A is never
+ * stored, so backward rebuilds it).  The product runs over the forward rows:
+ * each k-tile of A is read transposed, its elements scaled by their row's
+ * rstd and rounded to bf16 in registers (the rounding of a stored A_hat),
+ * then multiplied.  M, N, K and b_layout are the forward product's: A [M, K],
+ * dC [M, N], rstd float32 [M]; dB is written in B's layout ([K, N] for
+ * NG_B_KN, [N, K] for NG_B_NK), bf16.  M may be any size (M == 0 writes
+ * zeros).  dB must not overlap the inputs.
+ */
+int ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* dC, const float* rstd,
+                                          ng_bf16* dB, int64_t M, int64_t N, int64_t K,
+                                          int b_layout, void* stream);
+
+/*
+ * Plain GEMM with the first operand stored transposed, the product half of
+ * the weight gradient's unfused baseline: C [M, N] = A^T @ B with A stored
+ * [K, M] and B stored [K, N] (the reduction runs over both matrices' rows),
+ * bf16 out, fp32 accumulation.  M and N multiples of 8 (else
+ * NG_ERR_UNSUPPORTED); K any size >= 1.
+ */
+int ng_gemm_at(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+               void* stream);
+
+/*
  * Standalone RMSNorm backward (no affine), the norm half of the unfused
  * baseline of ng_rmsnorm_gemm_lazy_backward_input: for each row x of X
  * [rows, cols] with saved rstd (float32 [rows]) and upstream gradient dY,

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     ng_gemm, ng_gemm_add_layernorm, ng_gemm_add_rmsnorm, ng_gemm_layernorm, ng_gemm_rmsnorm,
     ng_add_norm, ng_last_error, ng_layernorm_gemm_fold, ng_layernorm_gemm_prenorm,
     ng_lazy_fold_affine, ng_norm, ng_rmsnorm_backward, ng_rmsnorm_gemm_lazy_backward_input,
+    ng_rmsnorm_gemm_lazy_backward_weight, ng_gemm_at,
     ng_rmsnorm_gemm_lazy, ng_rmsnorm_gemm_lazy_affine, ng_status_string, ng_workspace_bytes,
     ng_workspace_reset, ng_workspace_status,
 )
@@ -30,7 +31,8 @@ __all__ = [
     "NormGemmError", "rmsnorm_gemm_lazy", "lazy_fold_affine", "rmsnorm_gemm_lazy_affine",
     "gemm_rmsnorm", "gemm_layernorm", "gemm_add_rmsnorm", "gemm_add_layernorm", "gemm", "norm",
     "add_norm", "layernorm_gemm_fold", "layernorm_gemm_prenorm",
-    "rmsnorm_gemm_lazy_backward_input", "rmsnorm_backward",
+    "rmsnorm_gemm_lazy_backward_input", "rmsnorm_gemm_lazy_backward_weight", "rmsnorm_backward",
+    "gemm_at",
     "Workspace", "library_path",
 ]
 
@@ -269,6 +271,42 @@ def rmsnorm_gemm_lazy_backward_input(dC, B, A, rstd, *, b_layout="kn", out=None,
                                                M, N, K, lay, ws, wsb, _stream(stream)),
            "ng_rmsnorm_gemm_lazy_backward_input")
     return dA
+
+
+def rmsnorm_gemm_lazy_backward_weight(A, dC, rstd, *, b_layout="kn", out=None, stream=None):
+    """dB for C = rmsnorm(A) @ B (no affine) given dC: A_hat^T @ dC with the
+    normalized A rebuilt from A and the forward's rstd; dB in B's layout."""
+    torch = _torch()
+    _dev_bf16(A, "A"); _dev_bf16(dC, "dC")
+    lay = _layout(b_layout)
+    if A.dim() != 2 or dC.dim() != 2 or A.shape[0] != dC.shape[0]:
+        raise ValueError("A [M, K] and dC [M, N] must share M")
+    M, K = A.shape
+    N = dC.shape[1]
+    _f32_vec(rstd, M, "rstd")
+    shape = (K, N) if lay == NG_B_KN else (N, K)
+    dB = out if out is not None else torch.empty(shape, dtype=torch.bfloat16, device=A.device)
+    _dev_bf16(dB, "out")
+    if tuple(dB.shape) != shape:
+        raise ValueError("out must be %s" % (shape,))
+    _check(ng_rmsnorm_gemm_lazy_backward_weight(_ptr(A), _ptr(dC), _ptr(rstd), _ptr(dB), M, N, K,
+                                                lay, _stream(stream)),
+           "ng_rmsnorm_gemm_lazy_backward_weight")
+    return dB
+
+
+def gemm_at(A, B, *, out=None, stream=None):
+    """C = A^T @ B with A stored [K, M] and B stored [K, N]."""
+    torch = _torch()
+    _dev_bf16(A, "A"); _dev_bf16(B, "B")
+    if A.dim() != 2 or B.dim() != 2 or A.shape[0] != B.shape[0]:
+        raise ValueError("A [K, M] and B [K, N] must share K")
+    K, M = A.shape
+    N = B.shape[1]
+    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _dev_bf16(C, "out")
+    _check(ng_gemm_at(_ptr(A), _ptr(B), _ptr(C), M, N, K, _stream(stream)), "ng_gemm_at")
+    return C
 
 
 def rmsnorm_backward(dY, X, rstd, *, out=None, stream=None):

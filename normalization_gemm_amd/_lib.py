@@ -52,6 +52,8 @@ _SIGNATURES = {
     "ng_rmsnorm_gemm_lazy_backward_input": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P,
                                                  _SZ, _P]),
     "ng_rmsnorm_backward": (_I, [_P, _P, _P, _P, _I64, _I64, _P]),
+    "ng_rmsnorm_gemm_lazy_backward_weight": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
+    "ng_gemm_at": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),
     "ng_lazy_fold_affine": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _P]),
     "ng_rmsnorm_gemm_lazy_affine": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P]),
     "ng_gemm": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _P]),
@@ -144,6 +146,15 @@ def ng_rmsnorm_gemm_lazy_backward_input(dC, B, A, rstd, dA, M, N, K, b_layout, w
                                          workspace_bytes, stream):
     return _call("ng_rmsnorm_gemm_lazy_backward_input", dC, B, A, rstd, dA, M, N, K, b_layout,
                  workspace, workspace_bytes, stream)
+
+
+def ng_rmsnorm_gemm_lazy_backward_weight(A, dC, rstd, dB, M, N, K, b_layout, stream):
+    return _call("ng_rmsnorm_gemm_lazy_backward_weight", A, dC, rstd, dB, M, N, K, b_layout,
+                 stream)
+
+
+def ng_gemm_at(A, B, C, M, N, K, stream):
+    return _call("ng_gemm_at", A, B, C, M, N, K, stream)
 
 
 def ng_rmsnorm_backward(dY, X, rstd, dX, rows, cols, stream):

@@ -50,6 +50,10 @@ constexpr int64_t kMaxDim = int64_t(1) << 24;
 template <bool KN> using TLarge = ng::Tile<256, 256, 4, 2, KN>;
 template <bool KN> using TRow128 = ng::Tile<256, 128, 8, 1, KN, 3>;
 template <bool KN> using TRow256 = ng::Tile<128, 256, 2, 2, KN>;
+//   Wgrad: the 256x256 tile with A stored [K, M] (the reduction over the
+//          forward rows) and the normalized A rebuilt on the A (RS 1) or B
+//          (RS 2) side.
+template <int RS> using TWgrad = ng::Tile<256, 256, 4, 2, true, 2, true, RS>;
 
 int check_gemm(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
                int b_layout) {
@@ -592,6 +596,88 @@ int ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, con
               : launch_grid<TRow256<false>, ng::EPI_LAZY_BWD>(p, s, what);
   return kn ? launch_xwg<TLarge<true>, false, false, true>(p, s, what)
             : launch_xwg<TLarge<false>, false, false, true>(p, s, what);
+}
+
+int ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* dC, const float* rstd,
+                                          ng_bf16* dB, int64_t M, int64_t N, int64_t K,
+                                          int b_layout, void* stream) {
+  if (M != 0 && (!A || !dC || !rstd)) return fail(NG_ERR_INVALID_ARG, "A, dC and rstd must be non-NULL");
+  if (!dB) return fail(NG_ERR_INVALID_ARG, "dB must be non-NULL");
+  if (!aligned(A, 16) || !aligned(dC, 16) || !aligned(dB, 16))
+    return fail(NG_ERR_INVALID_ARG, "A, dC and dB must be 16-byte aligned");
+  if (!aligned(rstd, 4)) return fail(NG_ERR_INVALID_ARG, "rstd must be 4-byte aligned");
+  if (M < 0 || N < 1 || K < 1)
+    return fail(NG_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1 (got M=%lld N=%lld K=%lld)",
+                (long long)M, (long long)N, (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(NG_ERR_INVALID_ARG, "M, N, K must be at most 2^24");
+  if (b_layout != NG_B_KN && b_layout != NG_B_NK)
+    return fail(NG_ERR_INVALID_ARG, "b_layout must be NG_B_KN or NG_B_NK (got %d)", b_layout);
+  if (N % 8 != 0 || K % 8 != 0)
+    return fail(NG_ERR_UNSUPPORTED, "N and K must be multiples of 8 (got N=%lld K=%lld)",
+                (long long)N, (long long)K);
+  if (M * K >= (int64_t(1) << 31) * 8 || M * N >= (int64_t(1) << 31) * 8 ||
+      K * N >= (int64_t(1) << 31) * 8)
+    return fail(NG_ERR_UNSUPPORTED, "a matrix has more than 2^34 elements");
+  hipStream_t s = (hipStream_t)stream;
+  const char* what = "ng_rmsnorm_gemm_lazy_backward_weight";
+  if (M == 0) {
+    // an empty sum over rows: dB = 0
+    const size_t n16 = (size_t)(K * N) / 8;
+    size_t blocks = (n16 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(ng::fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (ng::u32x4*)dB, n16, (uint32_t*)nullptr, (size_t)0);
+    return launched(what);
+  }
+  // B [K, N]: dB = A_hat^T @ dC, the product over the forward rows with A read
+  // transposed and scaled.  B [N, K]: dB = dC^T @ A_hat, dC read transposed
+  // and A scaled on the other side.
+  ng::GemmParams p{};
+  p.row_rstd = rstd;
+  p.C = (uint16_t*)dB;
+  p.K = (int)M;
+  p.spin_limit = 1 << 20;
+  if (b_layout == NG_B_KN) {
+    p.A = (const uint16_t*)A;
+    p.B = (const uint16_t*)dC;
+    p.M = (int)K;
+    p.N = (int)N;
+    return launch_persistent<TWgrad<1>, ng::EPI_NONE>(p, s, what);
+  }
+  p.A = (const uint16_t*)dC;
+  p.B = (const uint16_t*)A;
+  p.M = (int)N;
+  p.N = (int)K;
+  return launch_persistent<TWgrad<2>, ng::EPI_NONE>(p, s, what);
+}
+
+int ng_gemm_at(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+               void* stream) {
+  if (M != 0 && N != 0 && (!A || !B || !C))
+    return fail(NG_ERR_INVALID_ARG, "A, B and C must be non-NULL");
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16))
+    return fail(NG_ERR_INVALID_ARG, "A, B and C must be 16-byte aligned");
+  if (M < 1 || N < 1 || K < 1)
+    return fail(NG_ERR_INVALID_ARG, "need M, N, K >= 1 (got M=%lld N=%lld K=%lld)",
+                (long long)M, (long long)N, (long long)K);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim)
+    return fail(NG_ERR_INVALID_ARG, "M, N, K must be at most 2^24");
+  if (M % 8 != 0 || N % 8 != 0)
+    return fail(NG_ERR_UNSUPPORTED, "M and N must be multiples of 8 (got M=%lld N=%lld)",
+                (long long)M, (long long)N);
+  if (M * K >= (int64_t(1) << 31) * 8 || N * K >= (int64_t(1) << 31) * 8 ||
+      M * N >= (int64_t(1) << 31) * 8)
+    return fail(NG_ERR_UNSUPPORTED, "a matrix has more than 2^34 elements");
+  ng::GemmParams p{};
+  p.A = (const uint16_t*)A;
+  p.B = (const uint16_t*)B;
+  p.C = (uint16_t*)C;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.spin_limit = 1 << 20;
+  return launch_persistent<TWgrad<0>, ng::EPI_NONE>(p, (hipStream_t)stream, "ng_gemm_at");
 }
 
 int ng_rmsnorm_backward(const ng_bf16* dY, const ng_bf16* X, const float* rstd, ng_bf16* dX,

@@ -122,16 +122,26 @@ struct GemmParams {
   int spin_limit;  // persistent grid: bounded wait (iterations of ~1 us)
 };
 
-template <int BM_, int BN_, int WM_, int WN_, bool KN_, int STAGES_ = 2>
+// KN: B stored [K, N] (else [N, K]).  AKM: A stored [K, M] (the reduction
+// index is A's storage row: the weight-gradient products), read like B[K, N].
+// RS: the A (1) or B (2) fragments are scaled per reduction index by
+// row_rstd and rounded to bf16 in registers before the MFMAs (the
+// normalized A of Lazy Pre-Norm rebuilt from A and its saved rstd).
+template <int BM_, int BN_, int WM_, int WN_, bool KN_, int STAGES_ = 2, bool AKM_ = false,
+          int RS_ = 0>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
   static constexpr bool KN = KN_;
+  static constexpr bool AKM = AKM_;
+  static constexpr int RS = RS_;
   static constexpr int NT = 64 * WM * WN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 16, FN = WTN / 16;
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int B_BYTES = BN * BK * 2;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
+  // RS: the k-tile's 64 fp32 scales, in a 1 KB slot after B
+  static constexpr int R_BYTES = RS ? 1024 : 0;
+  static constexpr int STAGE = A_BYTES + B_BYTES + R_BYTES;
   static constexpr int A_PER = BM * BK / 8 / NT;  // 16-byte chunks per thread
   static constexpr int B_PER = BN * BK / 8 / NT;
   static constexpr int RED_BYTES = WN * BM * 4;   // cross-wave row partials
@@ -153,6 +163,8 @@ struct Tile {
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
   static_assert((BM * BK / 8) % NT == 0 && (BN * BK / 8) % NT == 0, "loader split");
   static_assert((BN & (BN - 1)) == 0 && BN >= 16, "BN power of two");
+  static_assert(!AKM || ((BM & (BM - 1)) == 0 && BM >= 16), "BM power of two");
+  static_assert(RS >= 0 && RS <= 2, "scale side");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -178,7 +190,8 @@ template <class T>
 struct DmaPlan {
   static constexpr int A_INS = T::A_BYTES / 1024 / (T::NT / 64);  // instructions per wave
   static constexpr int B_INS = T::B_BYTES / 1024 / (T::NT / 64);
-  static constexpr int INS = A_INS + B_INS;
+  static constexpr int R_INS = T::RS ? 1 : 0;  // the scales: one transfer per wave
+  static constexpr int INS = A_INS + B_INS + R_INS;
   static_assert(A_INS * 1024 * (T::NT / 64) == T::A_BYTES, "A tile split");
   static_assert(B_INS * 1024 * (T::NT / 64) == T::B_BYTES, "B tile split");
   static_assert(INS < 32, "vmcnt budget");
@@ -186,22 +199,42 @@ struct DmaPlan {
   uint32_t a_voff;          // A (and B[N,K]): lane part of the offset, row 0 of the wave
   uint32_t a_kc;            // k offset (elements) of this lane's chunk within the k-tile
   uint32_t b_voff[B_INS];   // B[K,N]: lane part per instruction (N tail folded in)
+  uint32_t a_km[T::AKM ? A_INS : 1];  // A[K,M]: lane part per instruction (M tail folded in)
+  uint32_t r_voff;          // RS: this lane's 16 bytes of the scales (lanes 0..15)
   uint32_t a_row_bytes;     // K * 2
 
-  __device__ __forceinline__ void init(const GemmParams& p, int n_base, int lane, int wave_) {
+  // Blocked-layout slot (16 bytes) -> (k row, column) of a [K, X] tile of
+  // width W (B[K,N], or A[K,M]).
+  template <int W>
+  static __device__ __forceinline__ void blk_slot(int slot, int& kr, int& xc) {
+    const int blk = slot >> 3, in = slot & 7;
+    kr = 4 * (blk / (W / 16)) + (in >> 1);
+    xc = 16 * ((blk % (W / 16)) ^ ((kr >> 3) & 1)) + 8 * (in & 1);
+  }
+
+  __device__ __forceinline__ void init(const GemmParams& p, int m_base, int n_base, int lane,
+                                       int wave_) {
     wave = wave_;
     a_row_bytes = (uint32_t)p.K * 2u;
     const uint32_t c = (uint32_t)((lane & 7) ^ ((lane >> 3) & 7));
     a_kc = 8u * c;
     a_voff = (uint32_t)(lane >> 3) * a_row_bytes + 16u * c;
+    r_voff = lane < 16 ? 16u * (uint32_t)lane : kOOB;
+    if constexpr (T::AKM) {
+#pragma unroll
+      for (int j = 0; j < A_INS; ++j) {
+        int kr, mc;
+        blk_slot<T::BM>((wave * A_INS + j) * 64 + lane, kr, mc);
+        const bool ok = m_base + mc < p.M;
+        a_km[j] = ok ? (uint32_t)kr * (uint32_t)p.M * 2u + 2u * (uint32_t)mc : kOOB;
+      }
+    }
     if constexpr (T::KN) {
       // LDS slot (16 bytes) -> (k, n) of the blocked layout -> global offset
 #pragma unroll
       for (int j = 0; j < B_INS; ++j) {
-        const int slot = (wave * B_INS + j) * 64 + lane;  // 16-byte slot in the B stage
-        const int blk = slot >> 3, in = slot & 7;
-        const int kr = 4 * (blk / (T::BN / 16)) + (in >> 1);
-        const int nc = 16 * ((blk % (T::BN / 16)) ^ ((kr >> 3) & 1)) + 8 * (in & 1);
+        int kr, nc;
+        blk_slot<T::BN>((wave * B_INS + j) * 64 + lane, kr, nc);  // 16-byte slot in the B stage
         const bool ok = n_base + nc < p.N;
         b_voff[j] = ok ? (uint32_t)kr * (uint32_t)p.N * 2u + 2u * (uint32_t)nc : kOOB;
       }
@@ -212,6 +245,13 @@ struct DmaPlan {
   __device__ __forceinline__ void issue_a(const GemmParams& p, int m_base, int kt, uint32_t st,
                                           int j) const {
     const int k0 = kt * BK;
+    if constexpr (T::AKM) {
+      const uint64_t off = (uint64_t)k0 * p.M + m_base;
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(p.A + off, ((uint64_t)p.K * p.M - off) * 2u);
+      dma16(rs, st + (uint32_t)(wave * A_INS + j) * 1024u, a_km[j], 0u);
+      return;
+    }
     const uint64_t off = (uint64_t)m_base * p.K + k0;
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(p.A + off, ((uint64_t)p.M * p.K - off) * 2u);
@@ -237,12 +277,22 @@ struct DmaPlan {
       dma16(rs, st + (uint32_t)(wave * B_INS + j) * 1024u, v, row0 * a_row_bytes);
     }
   }
+  // RS: the k-tile's 64 scales (lanes 0..15, 16 bytes each; the other lanes
+  // write zeros into the rest of the 1 KB slot).  Every wave moves the same
+  // bytes, so that each wave issues the same number of transfers per k-tile.
+  __device__ __forceinline__ void issue_r(const GemmParams& p, int kt, uint32_t st) const {
+    const int k0 = kt * BK;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(p.row_rstd + k0, k0 < p.K ? (uint64_t)(p.K - k0) * 4u : 0u);
+    dma16(rs, st, r_voff, 0u);
+  }
   // Transfer number d (0 .. INS-1) of k-tile kt into the stage at `st` (A
-  // region first, then B).
+  // region first, then B, then the scales).
   __device__ __forceinline__ void issue(const GemmParams& p, int m_base, int n_base, int kt,
                                         uint32_t st, int d) const {
     if (d < A_INS) issue_a(p, m_base, kt, st, d);
-    else issue_b(p, n_base, kt, st + T::A_BYTES, d - A_INS);
+    else if (d < A_INS + B_INS) issue_b(p, n_base, kt, st + T::A_BYTES, d - A_INS);
+    else issue_r(p, kt, st + T::A_BYTES + T::B_BYTES);
   }
 };
 
@@ -263,23 +313,35 @@ struct Frags {
 // same slots; the Lazy Pre-Norm squares use this to split their work.
 template <class T>
 struct FragReader {
+  static constexpr int A_ITEMS = T::AKM ? 2 * T::FM : T::FM;
   static constexpr int B_ITEMS = T::KN ? 2 * T::FN : T::FN;
-  static constexpr int ITEMS = T::FM + B_ITEMS;
+  static constexpr int ITEMS = A_ITEMS + B_ITEMS;
   uint32_t a_base[2];  // per kk: A slot 0 of this lane (even slots), from the A region
   uint32_t a_odd[2];   // per kk: base for odd slots
   uint32_t b_base[2];  // per kk: B fragment 0 (half 0) of this lane, from the B region
   uint32_t b_odd[2];   // KN: base for odd fragments (the XOR in b_blk_off)
+  uint32_t r_off[2];   // RS: per kk, this lane's 8 scales in the stage's scale slot
 
   __device__ __forceinline__ void init(int wm, int wn, int lane, int a_xor = 0) {
     const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      r_off[kk] = (uint32_t)(T::A_BYTES + T::B_BYTES + (kk * 32 + 8 * g) * 4);
       const int row = wm * T::WTM + l16;
       const uint32_t a0 = (uint32_t)(row * 128 + (((kk * 4 + g) ^ (l16 & 7)) << 4));
       // slot i reads fragment i ^ a_xor: +2048 for even slots, -2048 for odd
       // ones (odd slots are >= 1, so the sum never wraps below zero)
       a_base[kk] = a0 + 2048u * (uint32_t)a_xor;
       a_odd[kk] = a0 - 2048u * (uint32_t)a_xor;
+      if constexpr (T::AKM) {
+        // as B[K,N] below, with rows of A in place of columns of B
+        const int k = kk * 32 + 8 * g + (l16 >> 2);
+        const int m = wm * T::WTM + 4 * (l16 & 3);
+        const uint32_t p = (uint32_t)((k >> 3) & 1);
+        const uint32_t b0 = b_blk_off<T::BM>(k, m) + 256u;
+        a_base[kk] = b0;
+        a_odd[kk] = b0 - 256u * p;
+      }
       if constexpr (T::KN) {
         // k = kk*32 + 8g + (l16 >> 2) (+4 for the second half), n = wn*WTN +
         // 16j + 4*(l16 & 3).  Fragment j sits at block (j ^ p), p = g & 1,
@@ -300,12 +362,23 @@ struct FragReader {
   // a_st / b_st: LDS byte offsets of the A and B regions holding this k-tile.
   __device__ __forceinline__ void read(Frags<T>& f, int item, lds_char* lds, uint32_t a_st,
                                        uint32_t b_st, int kk) const {
-    if (item < T::FM) {
-      f.a[item] = lds_read16(lds, a_st + ((item & 1) ? a_odd[kk] : a_base[kk]) +
-                                      (uint32_t)item * 2048u);
-      return;
+    if constexpr (T::AKM) {
+      if (item < A_ITEMS) {
+        const int i = item >> 1, h = item & 1;
+        const uint32_t o = (uint32_t)i * 128u + (uint32_t)h * (uint32_t)(T::BM / 16) * 128u;
+        const u32x2 v = lds_read_tr16(lds, a_st - 256u + ((i & 1) ? a_odd[kk] : a_base[kk]) + o);
+        if (h == 0) { f.a[i][0] = v[0]; f.a[i][1] = v[1]; }
+        else { f.a[i][2] = v[0]; f.a[i][3] = v[1]; }
+        return;
+      }
+    } else {
+      if (item < T::FM) {
+        f.a[item] = lds_read16(lds, a_st + ((item & 1) ? a_odd[kk] : a_base[kk]) +
+                                        (uint32_t)item * 2048u);
+        return;
+      }
     }
-    const int bi = item - T::FM;
+    const int bi = item - A_ITEMS;
     if constexpr (T::KN) {
       const int j = bi >> 1, h = bi & 1;
       // +16 columns per fragment = next block; +4 k-rows per half = next block row
@@ -318,6 +391,48 @@ struct FragReader {
     }
   }
 };
+
+// RS: the fragments on the scaled side (A for RS 1, B for RS 2) are
+// multiplied by their reduction index's scale and rounded to bf16 in
+// registers after their LDS reads.  Element e of a fragment is reduction
+// index kk*32 + 8*(lane >> 4) + e (the MFMA operand layout), whatever LDS
+// read produced it; the k-tile's 64 scales sit in its stage's scale slot.
+template <class T>
+__device__ __forceinline__ void load_scales(lds_char* lds, uint32_t st, int kk,
+                                            const FragReader<T>& rd, float (&r)[8]) {
+  const uint32_t o = st + rd.r_off[kk];
+  const f32x4 r0 = *(lds_f32x4*)(lds + o);
+  const f32x4 r1 = *(lds_f32x4*)(lds + o + 16);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { r[e] = r0[e]; r[4 + e] = r1[e]; }
+}
+
+__device__ __forceinline__ uint32_t scale_pair(uint32_t w, float r_lo, float r_hi) {
+  return pack_bf16x2(bf16_lo(w) * r_lo, bf16_hi(w) * r_hi);
+}
+
+// RS 2 (B side): all fragments read in a sub-step, scaled at its end.
+template <class T>
+__device__ __forceinline__ void scale_frags_b(Frags<T>& f, lds_char* lds, uint32_t st, int kk,
+                                              const FragReader<T>& rd) {
+  float r[8];
+  load_scales<T>(lds, st, kk, rd, r);
+#pragma unroll
+  for (int j = 0; j < T::FN; ++j)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) f.b[j][w] = scale_pair(f.b[j][w], r[2 * w], r[2 * w + 1]);
+}
+
+// RS 1 (A side): one packed pair (dword) of the next sub-step's A fragments
+// per MFMA slot over the last 4*FM slots of the sequence, so that each
+// slot's few VALU operations sit under an MFMA in flight.  By then the A
+// reads (the first items) have been issued and the first rows of the
+// current fragments are dead, which leaves registers for the scales (loaded
+// one slot before the first use).
+template <class T>
+constexpr int scale_first_slot() {
+  return T::FM * T::FN - 4 * T::FM;
+}
 
 // Lazy Pre-Norm sum of squares on the matrix cores.  For an A fragment F
 // (16 rows x 32 k of the sub-step), one MFMA of F with itself gives the 16x16
@@ -368,10 +483,22 @@ __device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN],
   constexpr int NM = T::FM * T::FN;
   constexpr int NR = FragReader<T>::ITEMS;
   constexpr int ND = DmaPlan<T>::INS;
+  float rsc[8];
+  static_assert(T::RS != 1 || (scale_first_slot<T>() >= NM / 2 &&
+                               FragReader<T>::A_ITEMS * NM / NR < scale_first_slot<T>() - 1),
+                "scale slots");
 #pragma unroll
   for (int q = 0; q < NM; ++q) {
     const int i = q / T::FN, j = q % T::FN;
     acc[i][j] = mfma_16x16x32(cur.b[j], cur.a[i], acc[i][j]);
+    if constexpr (T::RS == 1) {
+      constexpr int S0 = scale_first_slot<T>();
+      if (q == S0 - 1) load_scales<T>(lds, rd_st, rd_kk, rd, rsc);
+      if (q >= S0) {
+        const int f = (q - S0) >> 2, w = (q - S0) & 3;
+        nxt.a[f][w] = scale_pair(nxt.a[f][w], rsc[2 * w], rsc[2 * w + 1]);
+      }
+    }
     if constexpr (LAZY) lazy_gram<T>(q, cur, gram);
 #pragma unroll
     for (int r = (q * NR) / NM; r < ((q + 1) * NR) / NM; ++r)
@@ -381,6 +508,7 @@ __device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN],
       if (DM == 1 || (DM == 0 && dma_on)) dma.issue(p, m_base, n_base, dma_kt, dma_st, d);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (T::RS == 2) scale_frags_b<T>(nxt, lds, rd_st, rd_kk, rd);
 }
 
 // Full k-loop for the tile at (m_base, n_base).  STAGES LDS stages used as a
@@ -397,7 +525,7 @@ __device__ __forceinline__ void issue_prologue(const GemmParams& p, uint32_t lds
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   DmaPlan<T> dma;
-  dma.init(p, n_base, lane, wave);
+  dma.init(p, m_base, n_base, lane, wave);
   constexpr int ND = DmaPlan<T>::INS;
   const int nk = (p.K + BK - 1) / BK;
 #pragma unroll
@@ -447,7 +575,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
     for (int j = 0; j < T::FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   DmaPlan<T> dma;
-  dma.init(p, n_base, lane, wave);
+  dma.init(p, m_base, n_base, lane, wave);
   FragReader<T> rd;
   rd.init(wm, wn, lane, (LAZY && lazy_split<T>()) ? wn : 0);
   constexpr int ND = DmaPlan<T>::INS;
@@ -461,6 +589,15 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   Frags<T> f0, f1;
 #pragma unroll
   for (int r = 0; r < NR; ++r) rd.read(f0, r, lds, 0, T::A_BYTES, 0);
+  if constexpr (T::RS == 1) {
+    float r0s[8];
+    load_scales<T>(lds, 0, 0, rd, r0s);
+#pragma unroll
+    for (int i = 0; i < T::FM; ++i)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) f0.a[i][w] = scale_pair(f0.a[i][w], r0s[2 * w], r0s[2 * w + 1]);
+  }
+  if constexpr (T::RS == 2) scale_frags_b<T>(f0, lds, 0, 0, rd);
 
   int cur_s = 0;
   int kt = 0;

@@ -34,7 +34,8 @@ def test_header_declares_expected_entry_points():
               "ng_norm", "ng_workspace_bytes", "ng_lazy_fold_affine",
               "ng_rmsnorm_gemm_lazy_affine", "ng_gemm_add_rmsnorm", "ng_gemm_add_layernorm",
               "ng_add_norm", "ng_layernorm_gemm_fold", "ng_layernorm_gemm_prenorm",
-              "ng_rmsnorm_gemm_lazy_backward_input", "ng_rmsnorm_backward"):
+              "ng_rmsnorm_gemm_lazy_backward_input", "ng_rmsnorm_backward",
+              "ng_rmsnorm_gemm_lazy_backward_weight", "ng_gemm_at"):
         assert n in names
 
 
@@ -239,6 +240,17 @@ def test_lazy_backward_argument_checks():
     assert f(P, P2, P5, P4, P3, 64, 128, 4096, 0, None, 0, None) == 3     # workspace
     assert f(P, P2, P5, P4, P3, 64, 128, 4096, 1, P, ws - 16, None) == 3
     assert f(None, P2, None, None, None, 0, 128, 64, 0, None, 0, None) == 0  # M = 0
+    w = _lib.ng_rmsnorm_gemm_lazy_backward_weight
+    assert w(None, P2, P3, P4, 64, 128, 64, 0, None) == 1        # A NULL
+    assert w(P, P2, P3, None, 64, 128, 64, 0, None) == 1         # dB NULL
+    assert w(P, BAD, P3, P4, 64, 128, 64, 0, None) == 1          # dC misaligned
+    assert w(P, P2, P3 + 2, P4, 64, 128, 64, 0, None) == 1       # rstd misaligned
+    assert w(P, P2, P3, P4, 64, 128, 64, 2, None) == 1           # layout
+    assert w(P, P2, P3, P4, 64, 100, 64, 0, None) == 2           # N % 8
+    at = _lib.ng_gemm_at
+    assert at(None, P2, P3, 64, 64, 8, None) == 1
+    assert at(P, P2, P3, 60, 64, 8, None) == 2                   # M % 8
+    assert at(P, P2, P3, 64, 64, 0, None) == 1                   # K = 0
     g = _lib.ng_rmsnorm_backward
     assert g(None, P2, P3, P4, 4, 64, None) == 1
     assert g(P, BAD, P3, P4, 4, 64, None) == 1

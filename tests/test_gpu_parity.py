@@ -30,6 +30,24 @@ def _check(name, got_bits, ref):
     assert err <= TOL, (name, err)
 
 
+def _check_wgrad(name, got_bits, ref, A_bits, dC_bits, eps, rows=None):
+    # The weight gradient multiplies the normalized A rounded to bf16 (as a
+    # stored A_hat would be) and sums over the forward rows: each product
+    # carries a relative rounding error of at most 2^-9 (nearest even), so on
+    # top of the usual bar the sum may differ by 2^-8 * sum_m |A_hat||dC|
+    # (2^-9 with a factor 2 for the fp32 rstd).
+    A_hat, _ = oracle.rms_norm_rows(A_bits, eps)
+    if rows is not None:
+        A_hat = A_hat[:, rows]
+    bound = 2.0 ** -8 * (np.abs(A_hat).T @ np.abs(oracle.bf16_to_f64(dC_bits)))
+    got = oracle.bf16_to_f64(got_bits)
+    excess = np.abs(got - ref) - TOL * (1.0 + np.abs(ref)) - bound
+    log("%s: max rel err %.3e, worst excess over the bound %.3e" % (
+        name, oracle.rel_err(got_bits, ref), excess.max()))
+    assert np.all(np.isfinite(got)), name
+    assert np.all(excess <= 0), (name, excess.max())
+
+
 def _check_stat(name, got, ref):
     got = got.cpu().numpy().astype(np.float64)
     rel = np.max(np.abs(got - ref) / np.abs(ref))
@@ -505,6 +523,46 @@ def test_lazy_backward_input_cross_workgroup_rounds_ragged():
         _check("lazy backward xwg rounds", down(dA), ref)
 
 
+# forward (M, N, K): M (the reduction here) ragged and short; N, K over tiles
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("M,N,K", [(300, 136, 200), (77, 264, 520), (1000, 64, 128), (1, 8, 8),
+                                   (513, 520, 264)])
+def test_lazy_backward_weight_small(M, N, K, layout):
+    log("lazy backward weight M=%d N=%d K=%d %s" % (M, N, K, layout))
+    x = workloads.make_inputs(M, N, K, seed=13 * M + N + K, row_scale=True, upstream=True)
+    A = up(x.A)
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    ng.rmsnorm_gemm_lazy(A, up(b_for_layout(x.B, layout)), eps=1e-6, b_layout=layout,
+                         rstd_out=rstd)
+    dB = ng.rmsnorm_gemm_lazy_backward_weight(A, up(x.dC), rstd, b_layout=layout)
+    torch.cuda.synchronize()
+    ref = oracle.lazy_backward_weight(x.A, x.dC, 1e-6)
+    got = down(dB) if layout == "kn" else np.ascontiguousarray(down(dB).T)
+    _check_wgrad("lazy backward dB %s" % layout, got, ref, x.A, x.dC, 1e-6)
+
+
+def test_lazy_backward_weight_empty_rows_give_zero():
+    dC = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    rstd = torch.zeros(0, dtype=torch.float32, device="cuda")
+    dB = torch.full((128, 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    ng.rmsnorm_gemm_lazy_backward_weight(A, dC, rstd, out=dB)
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(dB)) == 0
+
+
+@pytest.mark.parametrize("M,N,K", [(256, 64, 128), (264, 520, 77), (8, 8, 1), (1000, 136, 300)])
+def test_gemm_at_small(M, N, K):
+    # C = A^T @ B with A stored [K, M], B stored [K, N]
+    rng = np.random.default_rng(M + N + K)
+    At = workloads.f32_to_bf16_bits(rng.standard_normal((K, M), dtype=np.float32))
+    Bk = workloads.f32_to_bf16_bits(rng.standard_normal((K, N), dtype=np.float32)
+                                    / np.float32(np.sqrt(K)))
+    C = ng.gemm_at(up(At), up(Bk))
+    torch.cuda.synchronize()
+    _check("gemm_at %dx%dx%d" % (M, N, K), down(C), oracle.gemm(np.ascontiguousarray(At.T), Bk))
+
+
 @pytest.mark.parametrize("rows,cols", [(1, 8), (37, 128), (300, 136), (65, 1000), (9, 8200)])
 def test_rmsnorm_backward_small(rows, cols):
     # the standalone norm backward is the oracle's input gradient with B = I
@@ -600,6 +658,19 @@ def _workload_case(w, layout="kn", n_rows=24):
     elif w.op == workloads.OP_LAZY_BWD:
         C = _lazy_bwd(x, layout, w.eps)[0]
         ref = oracle.rmsnorm_gemm_lazy_backward(x.A[rows], x.B, x.dC[rows], w.eps)[0]
+    elif w.op == workloads.OP_LAZY_BWD_W:
+        # rows of dB (B [K, N]) = columns of A
+        rows = sample_rows(w.K, n_rows, seed=1)
+        rstd = torch.empty(w.M, dtype=torch.float32, device="cuda")
+        ng.rmsnorm_gemm_lazy(A, B, eps=w.eps, b_layout=layout, rstd_out=rstd)
+        C = ng.rmsnorm_gemm_lazy_backward_weight(A, up(x.dC), rstd, b_layout=layout)
+        if layout == "nk":
+            C = C.t().contiguous()
+        ref = oracle.lazy_backward_weight(x.A, x.dC, w.eps, rows)
+        torch.cuda.synchronize()
+        got = down(C[torch.as_tensor(rows, device="cuda")])
+        _check_wgrad(w.name, got, ref, x.A, x.dC, w.eps, rows)
+        return x, rows, C
     elif w.op == workloads.OP_PRENORM_LN:
         C = _prenorm_case(x, layout, w.eps)[0]
         ref = oracle.layernorm_gemm_prenorm(x.A[rows], x.B, w.eps, x.gamma, x.beta)[0]
@@ -668,6 +739,20 @@ def test_lazy_backward_unfused_pair_full_size():
     torch.cuda.synchronize()
     ref = oracle.rmsnorm_gemm_lazy_backward(x.A[rows], x.B, x.dC[rows], w.eps)[0]
     _check("unfused gemm->rmsnorm backward", down(dA[torch.as_tensor(rows, device="cuda")]), ref)
+
+
+def test_lazy_backward_weight_unfused_pair_full_size():
+    # the unfused baseline of the weight gradient: ng_norm (A_hat stored),
+    # then ng_gemm_at (A_hat^T @ dC)
+    w = workloads.WORKLOAD_BY_NAME["lazy_rms_bwd_weight_32768x4096x4096"]
+    x = workloads.workload_inputs(w)
+    rows = sample_rows(w.K, 16, seed=7)
+    An = ng.norm(up(x.A), "rms", eps=w.eps)
+    dB = ng.gemm_at(An, up(x.dC))
+    torch.cuda.synchronize()
+    ref = oracle.lazy_backward_weight(x.A, x.dC, w.eps, rows)
+    _check_wgrad("unfused rmsnorm->gemm_at", down(dB[torch.as_tensor(rows, device="cuda")]), ref,
+                 x.A, x.dC, w.eps, rows)
 
 
 def test_named_workload_nk_layout_large():

@@ -45,6 +45,7 @@ OP_GEMM_ADD_RMSNORM = "gemm_add_rmsnorm"
 OP_GEMM_ADD_LAYERNORM = "gemm_add_layernorm"
 OP_PRENORM_LN = "layernorm_gemm_prenorm"
 OP_LAZY_BWD = "rmsnorm_gemm_lazy_backward_input"
+OP_LAZY_BWD_W = "rmsnorm_gemm_lazy_backward_weight"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -103,6 +104,10 @@ NEXT_WORKLOADS = [
              row_scale=True, upstream=True,
              description="Lazy Pre-Norm input gradient: dC 32768x4096 @ B^T, the RMSNorm "
                          "backward over rows of A (32768x4096) in the epilogue"),
+    Workload("lazy_rms_bwd_weight_32768x4096x4096", OP_LAZY_BWD_W, 32768, 4096, 4096, 1e-6,
+             row_scale=True, upstream=True,
+             description="Lazy Pre-Norm weight gradient: A_hat^T @ dC over 32768 rows, A_hat "
+                         "rebuilt from A (32768x4096) and rstd"),
     Workload("gemm_add_ln_65536x512x128", OP_GEMM_ADD_LAYERNORM, 65536, 128, 512, 1e-5,
              residual=True,
              description="GEMM + residual add + LayerNorm epilogue (no affine), "
