@@ -41,14 +41,16 @@ constexpr int64_t kMaxDim = int64_t(1) << 24;
 //   Large: 256x256 macro tile, 8 waves (4 along M x 2 along N) of 64x128, two
 //          waves per SIMD so that one issues MFMAs while the other waits
 //          (MFMA-bound shapes; measured ahead of 4 waves of 128x128).
-//   Row128: 256 x 128, 8 waves stacked along M (each owns 32 whole rows, so
-//           row statistics need no cross-wave exchange), three LDS stages so
-//           that two k-tiles of A (64 KB) are in flight per CU: the N <= 128
-//           shapes are HBM-bound and need the bytes in flight more than MFMA
-//           throughput.
+//   Row128: 128 x 128, 4 waves stacked along M (each owns 32 whole rows, so
+//           row statistics need no cross-wave exchange), two LDS stages
+//           (75 KB), so that two workgroups share a CU and one's loads overlap
+//           the other's epilogue: the N <= 128 shapes are HBM-bound.
+//           (Measured on 65536x512x128 against 256 x 128 tiles of 8 waves
+//           with three stages, one workgroup per CU: 3 % faster; 128 x 128
+//           with three stages, 64 x 128 and 8-wave 128 x 128 were slower.)
 //   Row256: 128 x 256, 2x2 waves (128 < N <= 256).
 template <bool KN> using TLarge = ng::Tile<256, 256, 4, 2, KN>;
-template <bool KN> using TRow128 = ng::Tile<256, 128, 8, 1, KN, 3>;
+template <bool KN> using TRow128 = ng::Tile<128, 128, 4, 1, KN, 2>;
 template <bool KN> using TRow256 = ng::Tile<128, 256, 2, 2, KN>;
 //   Wgrad: the 256x256 tile with A stored [K, M] (the reduction over the
 //          forward rows) and the normalized A rebuilt on the A (RS 1) or B
