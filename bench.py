@@ -558,7 +558,7 @@ def main():
                       workloads.WORKLOAD_BY_NAME[args.workload], args.calibrate_copy_mib or 512)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus %d requested); run with --gpus 1" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch

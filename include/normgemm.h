@@ -42,7 +42,7 @@ typedef uint16_t ng_bf16; /* raw bfloat16 bits */
 typedef enum {
   NG_OK = 0,
   NG_ERR_INVALID_ARG = 1, /* NULL/misaligned pointer, bad size, bad eps or enum */
-  NG_ERR_UNSUPPORTED = 2, /* valid request this build does not tile (N or K not a multiple of 8, ...) */
+  NG_ERR_UNSUPPORTED = 2, /* valid request the library does not tile (N or K not a multiple of 8, ...) */
   NG_ERR_WORKSPACE = 3,   /* workspace NULL, too small or misaligned */
   NG_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
   NG_ERR_TIMEOUT = 5      /* a cross-workgroup wait gave up (reported by ng_workspace_status) */
