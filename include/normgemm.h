@@ -173,7 +173,8 @@ int ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, const f
  * workgroups wait for each other: two such calls must not run concurrently
  * on one device (e.g. on two streams).  If they do, a wait may give up after
  * about a second; ng_workspace_status then reports NG_ERR_TIMEOUT and the
- * output of that call is undefined.
+ * output of that call is undefined.  (The environment variable NG_WAIT_SPINS,
+ * read on every call, replaces the bound of 2^20 polls of ~1 us.)
  * gamma: bf16 [N] or NULL.  rstd_out: float32 [M] or NULL.
  */
 int ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -98,6 +99,19 @@ int launched(const char* what) {
   return ok();
 }
 
+// Bound of the cross-workgroup waits, in polls of ~1 us: 2^20 (about a
+// second) unless NG_WAIT_SPINS holds a non-negative integer (read on every
+// call, so a process can lower it to exercise the timeout report).
+int wait_spins() {
+  const char* e = getenv("NG_WAIT_SPINS");
+  if (e && *e) {
+    char* end = nullptr;
+    const long v = strtol(e, &end, 10);
+    if (end && *end == '\0' && v >= 0 && v <= (1L << 30)) return (int)v;
+  }
+  return 1 << 20;
+}
+
 ng::GemmParams make_params(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                            float eps) {
   ng::GemmParams p{};
@@ -108,7 +122,7 @@ ng::GemmParams make_params(const void* A, const void* B, void* C, int64_t M, int
   p.N = (int)N;
   p.K = (int)K;
   p.eps = eps;
-  p.spin_limit = 1 << 20;
+  p.spin_limit = wait_spins();
   return p;
 }
 

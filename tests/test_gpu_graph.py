@@ -101,3 +101,28 @@ def test_graph_replays_a_chain_of_forms():
         _check("chain replay %d: lazy" % rep, down(C), ref_c)
         _check("chain replay %d: lazy input gradient" % rep, down(dA), ref_da)
     assert ws.status() == 0
+
+
+def test_bounded_wait_reports_timeout_and_recovers(monkeypatch):
+    # A wait bound of zero polls makes every cross-workgroup wait that does
+    # not find its entry at once give up: the kernel still runs to its end,
+    # the workspace's error word reports it, and after a reset the next call
+    # is correct again.  (Forced from the host; no wave is left waiting.)
+    M, N, K = 2048, 8192, 2048
+    x = workloads.make_inputs(M, N, K, seed=63, gamma=True)
+    A, B, g = up(x.A), up(x.B), up(x.gamma)
+    ws = ng.Workspace(ng.ng_workspace_bytes(ng.NG_OP_GEMM_RMSNORM, M, N, K))
+    monkeypatch.setenv("NG_WAIT_SPINS", "0")
+    ng.gemm_rmsnorm(A, B, g, eps=1e-6, workspace=ws)
+    torch.cuda.synchronize()
+    status = ws.status()
+    log("status after zero-poll waits: %s" % ng.ng_status_string(status))
+    assert status == ng._lib.NG_ERR_TIMEOUT
+    monkeypatch.delenv("NG_WAIT_SPINS")
+    assert ng.ng_workspace_reset(ws.ptr(), ws.nbytes, torch.cuda.current_stream().cuda_stream) == 0
+    C = ng.gemm_rmsnorm(A, B, g, eps=1e-6, workspace=ws)
+    torch.cuda.synchronize()
+    assert ws.status() == 0
+    rows = np.array([0, 1, 777, M - 1])
+    ref = oracle.gemm_rmsnorm(x.A[rows], x.B, 1e-6, x.gamma)[0]
+    _check("after reset", down(C[torch.as_tensor(rows, device="cuda")]), ref)
