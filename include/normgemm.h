@@ -262,9 +262,8 @@ int ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const 
  * rebuilt on the fly from A and the forward's saved rstd ("Free
  * normalization fusion", section "Lazy Pre-Norm": the normalized A is never
  * stored, so backward rebuilds it).  The product runs over the forward rows:
- * each k-tile of A is read transposed, its elements scaled by their row's
- * rstd and rounded to bf16 in registers (the rounding of a stored A_hat),
- * then multiplied.  M, N, K and b_layout are the forward product's: A [M, K],
+ * each k-tile of A is read on chip, its elements scaled by their row's rstd
+ * and rounded to bf16 (the rounding of a stored A_hat), then multiplied.  M, N, K and b_layout are the forward product's: A [M, K],
  * dC [M, N], rstd float32 [M]; dB is written in B's layout ([K, N] for
  * NG_B_KN, [N, K] for NG_B_NK), bf16.  M may be any size (M == 0 writes
  * zeros).  dB must not overlap the inputs.

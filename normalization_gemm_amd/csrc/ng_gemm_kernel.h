@@ -392,9 +392,8 @@ struct FragReader {
   }
 };
 
-// RS: the fragments on the scaled side (A for RS 1, B for RS 2) are
-// multiplied by their reduction index's scale and rounded to bf16 in
-// registers after their LDS reads.  Element e of a fragment is reduction
+// RS 1: the A fragments are multiplied by their reduction index's scale and
+// rounded to bf16 in registers after their LDS reads.  Element e of a fragment is reduction
 // index kk*32 + 8*(lane >> 4) + e (the MFMA operand layout), whatever LDS
 // read produced it; the k-tile's 64 scales sit in its stage's scale slot.
 template <class T>
@@ -411,16 +410,35 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t w, float r_lo, float r_h
   return pack_bf16x2(bf16_lo(w) * r_lo, bf16_hi(w) * r_hi);
 }
 
-// RS 2 (B side): all fragments read in a sub-step, scaled at its end.
+// RS 2 (B side): a B fragment is held by the WM waves of a column, so the
+// k-tile is scaled in LDS instead, once per workgroup: each wave scales the
+// 16-byte chunks that its own transfers wrote, right after its own wait for
+// the k-tile and before the barrier that publishes it.  In the blocked
+// [K, N] layout a chunk holds 8 elements of one k row, which share one scale.
+// (Measured on 32768x4096x4096: 1030 us against 1216 us for scaling the
+// fragments in registers; on the A side, held by only WN waves, registers
+// win.)  The per-lane offsets are recomputed from an opaque lane index so
+// that they are not kept live across the k-loop.
 template <class T>
-__device__ __forceinline__ void scale_frags_b(Frags<T>& f, lds_char* lds, uint32_t st, int kk,
-                                              const FragReader<T>& rd) {
-  float r[8];
-  load_scales<T>(lds, st, kk, rd, r);
+__device__ __forceinline__ void scale_own_chunks(lds_char* lds, uint32_t st, int wave, int lane) {
+  static_assert(T::RS == 2 && T::KN, "B stored [K, N] scaled in LDS");
+  constexpr int INS = DmaPlan<T>::B_INS;
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const uint32_t region = st + (uint32_t)T::A_BYTES;
+  const uint32_t rslot = st + (uint32_t)(T::A_BYTES + T::B_BYTES);
 #pragma unroll
-  for (int j = 0; j < T::FN; ++j)
+  for (int j = 0; j < INS; ++j) {
+    const int slot = (wave * INS + j) * 64 + ln;
+    int kr, xc;
+    DmaPlan<T>::template blk_slot<T::BN>(slot, kr, xc);
+    const float r = *(lds_float*)(lds + rslot + (uint32_t)kr * 4u);
+    const uint32_t o = region + (uint32_t)slot * 16u;
+    u32x4 v = lds_read16(lds, o);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) f.b[j][w] = scale_pair(f.b[j][w], r[2 * w], r[2 * w + 1]);
+    for (int w = 0; w < 4; ++w) v[w] = scale_pair(v[w], r, r);
+    lds_write16(lds, o, v);
+  }
 }
 
 // RS 1 (A side): one packed pair (dword) of the next sub-step's A fragments
@@ -508,7 +526,6 @@ __device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN],
       if (DM == 1 || (DM == 0 && dma_on)) dma.issue(p, m_base, n_base, dma_kt, dma_st, d);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if constexpr (T::RS == 2) scale_frags_b<T>(nxt, lds, rd_st, rd_kk, rd);
 }
 
 // Full k-loop for the tile at (m_base, n_base).  STAGES LDS stages used as a
@@ -585,6 +602,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   if (!prologue_issued) issue_prologue<T>(p, lds0, m_base, n_base, tid);
   if (stores_after) wait_ktile<ND, T::STAGES, T::C_STORES>(min(nk, T::STAGES) - 1);
   else wait_ktile<ND, T::STAGES>(min(nk, T::STAGES) - 1);
+  if constexpr (T::RS == 2) scale_own_chunks<T>(lds, 0, wave, lane);
   __syncthreads();
   Frags<T> f0, f1;
 #pragma unroll
@@ -597,7 +615,6 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
 #pragma unroll
       for (int w = 0; w < 4; ++w) f0.a[i][w] = scale_pair(f0.a[i][w], r0s[2 * w], r0s[2 * w + 1]);
   }
-  if constexpr (T::RS == 2) scale_frags_b<T>(f0, lds, 0, 0, rd);
 
   int cur_s = 0;
   int kt = 0;
@@ -608,6 +625,8 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
       const int after = min(nk - 1, kt + T::STAGES - 1) - (kt + 1);
       if (stores_after && kt + 1 < T::STAGES) wait_ktile<ND, T::STAGES, T::C_STORES>(after);
       else wait_ktile<ND, T::STAGES>(after);
+      if constexpr (T::RS == 2)
+        scale_own_chunks<T>(lds, (uint32_t)((kt + 1) % T::STAGES) * T::STAGE, wave, lane);
     }
   };
   if constexpr (!LAZY) {
