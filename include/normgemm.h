@@ -174,7 +174,10 @@ int ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, const f
  * on one device (e.g. on two streams).  If they do, a wait may give up after
  * about a second; ng_workspace_status then reports NG_ERR_TIMEOUT and the
  * output of that call is undefined.  (The environment variable NG_WAIT_SPINS,
- * read on every call, replaces the bound of 2^20 polls of ~1 us.)
+ * read on every call, replaces the bound of 2^20 polls of ~1 us;
+ * NG_ROW_LOCAL_MAX, also read on every call and by ng_workspace_bytes,
+ * lowers the widest row reduced inside one workgroup from 256, so that the
+ * cross-workgroup path can be run on narrow rows for comparison.)
  * gamma: bf16 [N] or NULL.  rstd_out: float32 [M] or NULL.
  */
 int ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,

@@ -112,6 +112,20 @@ int wait_spins() {
   return 1 << 20;
 }
 
+// Widest row reduced inside one workgroup: 256 unless NG_ROW_LOCAL_MAX holds
+// a smaller non-negative integer (read on every call; a diagnostic that puts
+// narrow rows on the cross-workgroup path, so that both strategies can be
+// compared on one shape).
+int64_t row_local_max() {
+  const char* e = getenv("NG_ROW_LOCAL_MAX");
+  if (e && *e) {
+    char* end = nullptr;
+    const long v = strtol(e, &end, 10);
+    if (end && *end == '\0' && v >= 0 && v < 256) return v;
+  }
+  return 256;
+}
+
 ng::GemmParams make_params(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
                            float eps) {
   ng::GemmParams p{};
@@ -215,7 +229,7 @@ template <bool LN, bool RES>
 int launch_norm(ng::GemmParams p, bool kn, bool local, hipStream_t s, const char* what) {
   constexpr int EPI = RES ? (LN ? ng::EPI_ROW_LN_RES : ng::EPI_ROW_RMS_RES)
                           : (LN ? ng::EPI_ROW_LN : ng::EPI_ROW_RMS);
-  if (p.N <= 128)
+  if (local && p.N <= 128)
     return kn ? launch_grid<TRow128<true>, EPI>(p, s, what)
               : launch_grid<TRow128<false>, EPI>(p, s, what);
   if (local)
@@ -245,7 +259,7 @@ int gemm_norm(const void* A, const void* B, const void* R, const void* gamma, co
     if (S_out && M != 0 && S_out == C)
       return fail(NG_ERR_INVALID_ARG, "S_out and C must be different buffers");
   }
-  const bool local = N <= 256;
+  const bool local = N <= row_local_max();
   if (!local && M > 0) {
     const size_t need = xwg_bytes(M, N);
     if (!ws || ws_bytes < need || !aligned(ws, 256))
@@ -589,7 +603,7 @@ int ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, con
   if (M != 0 && (!A || !rstd)) return fail(NG_ERR_INVALID_ARG, "A and rstd must be non-NULL");
   if (!aligned(A, 16)) return fail(NG_ERR_INVALID_ARG, "A must be 16-byte aligned");
   if (!aligned(rstd, 4)) return fail(NG_ERR_INVALID_ARG, "rstd must be 4-byte aligned");
-  const bool local = K <= 256;
+  const bool local = K <= row_local_max();
   if (!local && M > 0) {
     const size_t need = xwg_bytes(M, K);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
@@ -604,7 +618,7 @@ int ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, con
   hipStream_t s = (hipStream_t)stream;
   const bool kn = lay == NG_B_KN;
   const char* what = "ng_rmsnorm_gemm_lazy_backward_input";
-  if (K <= 128)
+  if (local && K <= 128)
     return kn ? launch_grid<TRow128<true>, ng::EPI_LAZY_BWD>(p, s, what)
               : launch_grid<TRow128<false>, ng::EPI_LAZY_BWD>(p, s, what);
   if (local)
@@ -742,7 +756,7 @@ size_t ng_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
   if (op != NG_OP_GEMM_RMSNORM && op != NG_OP_GEMM_LAYERNORM && op != NG_OP_GEMM_ADD_RMSNORM &&
       op != NG_OP_GEMM_ADD_LAYERNORM && op != NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT)
     return 0;
-  if (M <= 0 || N <= 256 || M > kMaxDim || N > kMaxDim) return 0;
+  if (M <= 0 || N <= row_local_max() || M > kMaxDim || N > kMaxDim) return 0;
   return xwg_bytes(M, N);
 }
 

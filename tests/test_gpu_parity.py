@@ -576,6 +576,56 @@ def test_rmsnorm_backward_small(rows, cols):
     _check("rmsnorm backward %dx%d" % (rows, cols), down(dX), ref)
 
 
+# ------------------------------------------ strategy consistency on one shape
+def _ulp_distance(a_bits, b_bits):
+    """Distance in bf16 units in the last place (sign-magnitude bit patterns
+    mapped onto one ordered integer line)."""
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x & 0x7FFF)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+@pytest.mark.parametrize("N", [128, 256])
+@pytest.mark.parametrize("form", ["layer", "rms", "residual_rms", "lazy_backward"])
+def test_row_local_and_cross_workgroup_paths_agree(N, form, monkeypatch):
+    # The same shape through the workgroup-local reduction and, with
+    # NG_ROW_LOCAL_MAX=0, through the cross-workgroup exchange: both meet
+    # the oracle bar and differ by at most 2 bf16 ulp.
+    M, K = 700, 200
+    if form == "lazy_backward":
+        # the backward normalizes rows of length K (here N plays that role)
+        x = workloads.make_inputs(M, 136, N, seed=N + 71, row_scale=True, upstream=True)
+        A, B = up(x.A), up(x.B)
+        rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+        ng.rmsnorm_gemm_lazy(A, B, eps=1e-6, rstd_out=rstd)
+        run = lambda: ng.rmsnorm_gemm_lazy_backward_input(up(x.dC), B, A, rstd)
+        ref = oracle.rmsnorm_gemm_lazy_backward(x.A, x.B, x.dC, 1e-6)[0]
+    else:
+        x = workloads.make_inputs(M, N, K, seed=N + 72, gamma=True, beta=True, residual=True)
+        A, B, g, b, R = up(x.A), up(x.B), up(x.gamma), up(x.beta), up(x.R)
+        if form == "layer":
+            run = lambda: ng.gemm_layernorm(A, B, g, b, eps=1e-5)
+            ref = oracle.gemm_layernorm(x.A, x.B, 1e-5, x.gamma, x.beta)[0]
+        elif form == "rms":
+            run = lambda: ng.gemm_rmsnorm(A, B, g, eps=1e-6)
+            ref = oracle.gemm_rmsnorm(x.A, x.B, 1e-6, x.gamma)[0]
+        else:
+            run = lambda: ng.gemm_add_rmsnorm(A, B, R, g, eps=1e-6)
+            ref = oracle.gemm_add_rmsnorm(x.A, x.B, x.R, 1e-6, x.gamma)[0]
+    local = run()
+    torch.cuda.synchronize()
+    monkeypatch.setenv("NG_ROW_LOCAL_MAX", "0")
+    cross = run()
+    torch.cuda.synchronize()
+    monkeypatch.delenv("NG_ROW_LOCAL_MAX")
+    _check("%s N=%d row-local" % (form, N), down(local), ref)
+    _check("%s N=%d cross-workgroup" % (form, N), down(cross), ref)
+    d = _ulp_distance(down(local), down(cross))
+    log("%s N=%d: max ulp distance between the paths %d" % (form, N, d.max()))
+    assert d.max() <= 2
+
+
 # ------------------------------------------------------------ edge cases
 def test_empty_M_leaves_output_untouched():
     A = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
