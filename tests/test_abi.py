@@ -46,6 +46,17 @@ def test_library_exports_every_declared_symbol():
     assert sorted(_lib.exported_names()) == header_functions()
 
 
+def test_binding_signatures_match_the_header():
+    # argument counts of every prototype in the header against the ctypes
+    # table (a mismatch would pass arguments in the wrong slots)
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = dict(re.findall(r"\b(ng_\w+)\s*\(([^)]*)\)\s*;", text))
+    assert set(protos) == set(_lib.exported_names())
+    for name, args in protos.items():
+        n = 0 if args.strip() in ("", "void") else len(args.split(","))
+        assert len(_lib._SIGNATURES[name][1]) == n, name
+
+
 def test_status_strings():
     assert _lib.ng_status_string(0) == "NG_OK"
     assert _lib.ng_status_string(1) == "NG_ERR_INVALID_ARG"
