@@ -41,7 +41,11 @@ constexpr int64_t kMaxDim = int64_t(1) << 24;
 // Tile configurations.
 //   Large: 256x256 macro tile, 8 waves (4 along M x 2 along N) of 64x128, two
 //          waves per SIMD so that one issues MFMAs while the other waits
-//          (MFMA-bound shapes; measured ahead of 4 waves of 128x128).
+//          (MFMA-bound shapes; measured ahead of 4 waves of 128x128).  With B
+//          stored [K, N] the k-tiles are 32 deep in 4 stages (128 KB), which
+//          keeps 1.5 k64-steps of transfers in flight instead of one: 1-3 %
+//          faster on the large shapes than 2 stages of 64.  With B stored
+//          [N, K] 2 stages of 64 stay ahead (the deeper loop spills there).
 //   Row128: 128 x 128, 4 waves stacked along M (each owns 32 whole rows, so
 //           row statistics need no cross-wave exchange), two LDS stages
 //           (75 KB), so that two workgroups share a CU and one's loads overlap
@@ -50,7 +54,13 @@ constexpr int64_t kMaxDim = int64_t(1) << 24;
 //           with three stages, one workgroup per CU: 3 % faster; 128 x 128
 //           with three stages, 64 x 128 and 8-wave 128 x 128 were slower.)
 //   Row256: 128 x 256, 2x2 waves (128 < N <= 256).
-template <bool KN> using TLarge = ng::Tile<256, 256, 4, 2, KN>;
+template <bool KN> struct TLargeSel {
+  using type = ng::Tile<256, 256, 4, 2, false, 2>;
+};
+template <> struct TLargeSel<true> {
+  using type = ng::Tile<256, 256, 4, 2, true, 4, false, 0, 32>;
+};
+template <bool KN> using TLarge = typename TLargeSel<KN>::type;
 template <bool KN> using TRow128 = ng::Tile<128, 128, 4, 1, KN, 2>;
 template <bool KN> using TRow256 = ng::Tile<128, 256, 2, 2, KN>;
 //   Wgrad: the 256x256 tile with A stored [K, M] (the reduction over the

@@ -35,13 +35,14 @@
 // row and each applies the norm to its own slice.  Norm formulas: "RMSNorm
 // fusion on Ascend", sections 1.1 (LayerNorm) and 1.2 (RMSNorm).
 //
-// Data layout in LDS per pipeline stage (BK = 64):
-//   A tile  [BM][64] bf16, 128-byte rows; 16-byte chunk c of row m is stored
-//           at chunk c ^ (m & 7) (conflict-free 16-byte fragment reads).
-//   B tile  KN: blocked [64/4][BN/16][4][16] bf16 (128-byte blocks of 4 k-rows
+// Data layout in LDS per pipeline stage (k-tile depth BK = 64, or 32):
+//   A tile  [BM][BK] bf16, rows of 2*BK bytes; 16-byte chunk c of row m is
+//           stored at chunk c ^ (m & 7) for BK = 64, c ^ ((m >> 2) & 3) for
+//           BK = 32 (conflict-free 16-byte fragment reads of 16 rows).
+//   B tile  KN: blocked [BK/4][BN/16][4][16] bf16 (128-byte blocks of 4 k-rows
 //           x 16 columns), read with the transposing LDS read: each 16-lane
 //           group reads one whole block.
-//           NK: [BN][64] bf16, same layout as A.
+//           NK: [BN][BK] bf16, same layout as A.
 // MFMA: v_mfma_f32_16x16x32_bf16 with B as the first operand and A as the
 // second, so each lane's accumulators hold four consecutive columns of one
 // output row: acc[i][j][r] = C[m0 + 16i + (lane & 15)][n0 + 16j + 4(lane >> 4) + r].
@@ -51,7 +52,6 @@
 
 namespace ng {
 
-constexpr int BK = 64;
 
 enum Epi {
   EPI_NONE = 0,
@@ -127,13 +127,18 @@ struct GemmParams {
 // RS: the A (1) or B (2) fragments are scaled per reduction index by
 // row_rstd and rounded to bf16 in registers before the MFMAs (the
 // normalized A of Lazy Pre-Norm rebuilt from A and its saved rstd).
+// BK: k-tile depth (64, or 32 for deeper pipelines within the LDS budget).
 template <int BM_, int BN_, int WM_, int WN_, bool KN_, int STAGES_ = 2, bool AKM_ = false,
-          int RS_ = 0>
+          int RS_ = 0, int BK_ = 64>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
   static constexpr bool KN = KN_;
   static constexpr bool AKM = AKM_;
   static constexpr int RS = RS_;
+  static constexpr int BK = BK_;
+  static constexpr int KK = BK / 32;   // k32 sub-steps per k-tile
+  static constexpr int CPR = BK / 8;   // 16-byte chunks per row of A (and B[N,K])
+  static constexpr int RB = BK * 2;    // bytes per row of A (and B[N,K])
   static constexpr int NT = 64 * WM * WN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 16, FN = WTN / 16;
@@ -160,6 +165,8 @@ struct Tile {
   static_assert(STG_OWN || STG_BYTES <= STAGE, "output staging");
   static_assert(FN % 4 == 0, "64-column output groups");
   static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
+  static_assert(BK == 64 || BK == 32, "k-tile depth");
+  static_assert(RS == 0 || BK == 64, "scaled operands use 64-deep k-tiles");
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
   static_assert((BM * BK / 8) % NT == 0 && (BN * BK / 8) % NT == 0, "loader split");
   static_assert((BN & (BN - 1)) == 0 && BN >= 16, "BN power of two");
@@ -178,6 +185,13 @@ template <int BN>
 __host__ __device__ constexpr uint32_t b_blk_off(int k, int n) {
   return (uint32_t)((((k >> 2) * (BN / 16) + ((n >> 4) ^ ((k >> 3) & 1))) << 7) +
                     ((k & 3) << 5) + ((n & 15) << 1));
+}
+
+// Chunk swizzle of the A (and B[N,K]) rows: position of chunk c of row r is
+// c ^ a_swz(r).
+template <class T>
+__host__ __device__ constexpr int a_swz(int r) {
+  return T::CPR == 8 ? (r & 7) : ((r >> 2) & 3);
 }
 
 // Global -> LDS staging.  Each wave moves 1 KB per buffer_load ... lds
@@ -216,9 +230,12 @@ struct DmaPlan {
                                        int wave_) {
     wave = wave_;
     a_row_bytes = (uint32_t)p.K * 2u;
-    const uint32_t c = (uint32_t)((lane & 7) ^ ((lane >> 3) & 7));
+    // one transfer moves 64/CPR whole rows; lane: row lane / CPR, position
+    // lane % CPR, which holds chunk position ^ swizzle(row)
+    const int row_in = lane / T::CPR, pos = lane % T::CPR;
+    const uint32_t c = (uint32_t)(pos ^ a_swz<T>(row_in));
     a_kc = 8u * c;
-    a_voff = (uint32_t)(lane >> 3) * a_row_bytes + 16u * c;
+    a_voff = (uint32_t)row_in * a_row_bytes + 16u * c;
     r_voff = lane < 16 ? 16u * (uint32_t)lane : kOOB;
     if constexpr (T::AKM) {
 #pragma unroll
@@ -244,7 +261,7 @@ struct DmaPlan {
   // Transfer j of k-tile kt of A into the A region at LDS byte address `st`.
   __device__ __forceinline__ void issue_a(const GemmParams& p, int m_base, int kt, uint32_t st,
                                           int j) const {
-    const int k0 = kt * BK;
+    const int k0 = kt * T::BK;
     if constexpr (T::AKM) {
       const uint64_t off = (uint64_t)k0 * p.M + m_base;
       const __amdgpu_buffer_rsrc_t rs =
@@ -256,13 +273,13 @@ struct DmaPlan {
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(p.A + off, ((uint64_t)p.M * p.K - off) * 2u);
     const uint32_t v = (k0 + (int)a_kc < p.K) ? a_voff : kOOB;
-    const uint32_t row0 = (uint32_t)((wave * A_INS + j) * 8);
+    const uint32_t row0 = (uint32_t)((wave * A_INS + j) * (64 / T::CPR));
     dma16(rs, st + (uint32_t)(wave * A_INS + j) * 1024u, v, row0 * a_row_bytes);
   }
   // Transfer j of k-tile kt of B into the B region at LDS byte address `st`.
   __device__ __forceinline__ void issue_b(const GemmParams& p, int n_base, int kt, uint32_t st,
                                           int j) const {
-    const int k0 = kt * BK;
+    const int k0 = kt * T::BK;
     if constexpr (T::KN) {
       const uint64_t off = (uint64_t)k0 * p.N + n_base;
       const __amdgpu_buffer_rsrc_t rs =
@@ -273,7 +290,7 @@ struct DmaPlan {
       const __amdgpu_buffer_rsrc_t rs =
           make_rsrc(p.B + off, ((uint64_t)p.N * p.K - off) * 2u);
       const uint32_t v = (k0 + (int)a_kc < p.K) ? a_voff : kOOB;
-      const uint32_t row0 = (uint32_t)((wave * B_INS + j) * 8);
+      const uint32_t row0 = (uint32_t)((wave * B_INS + j) * (64 / T::CPR));
       dma16(rs, st + (uint32_t)(wave * B_INS + j) * 1024u, v, row0 * a_row_bytes);
     }
   }
@@ -281,7 +298,7 @@ struct DmaPlan {
   // write zeros into the rest of the 1 KB slot).  Every wave moves the same
   // bytes, so that each wave issues the same number of transfers per k-tile.
   __device__ __forceinline__ void issue_r(const GemmParams& p, int kt, uint32_t st) const {
-    const int k0 = kt * BK;
+    const int k0 = kt * T::BK;
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(p.row_rstd + k0, k0 < p.K ? (uint64_t)(p.K - k0) * 4u : 0u);
     dma16(rs, st, r_voff, 0u);
@@ -316,23 +333,25 @@ struct FragReader {
   static constexpr int A_ITEMS = T::AKM ? 2 * T::FM : T::FM;
   static constexpr int B_ITEMS = T::KN ? 2 * T::FN : T::FN;
   static constexpr int ITEMS = A_ITEMS + B_ITEMS;
-  uint32_t a_base[2];  // per kk: A slot 0 of this lane (even slots), from the A region
-  uint32_t a_odd[2];   // per kk: base for odd slots
-  uint32_t b_base[2];  // per kk: B fragment 0 (half 0) of this lane, from the B region
-  uint32_t b_odd[2];   // KN: base for odd fragments (the XOR in b_blk_off)
-  uint32_t r_off[2];   // RS: per kk, this lane's 8 scales in the stage's scale slot
+  static constexpr uint32_t FSTRIDE = 16u * T::RB;  // bytes per 16-row fragment of A / B[N,K]
+  uint32_t a_base[T::KK];  // per kk: A slot 0 of this lane (even slots), from the A region
+  uint32_t a_odd[T::KK];   // per kk: base for odd slots
+  uint32_t b_base[T::KK];  // per kk: B fragment 0 (half 0) of this lane, from the B region
+  uint32_t b_odd[T::KK];   // KN: base for odd fragments (the XOR in b_blk_off)
+  uint32_t r_off[T::KK];   // RS: per kk, this lane's 8 scales in the stage's scale slot
 
   __device__ __forceinline__ void init(int wm, int wn, int lane, int a_xor = 0) {
     const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < T::KK; ++kk) {
       r_off[kk] = (uint32_t)(T::A_BYTES + T::B_BYTES + (kk * 32 + 8 * g) * 4);
       const int row = wm * T::WTM + l16;
-      const uint32_t a0 = (uint32_t)(row * 128 + (((kk * 4 + g) ^ (l16 & 7)) << 4));
-      // slot i reads fragment i ^ a_xor: +2048 for even slots, -2048 for odd
-      // ones (odd slots are >= 1, so the sum never wraps below zero)
-      a_base[kk] = a0 + 2048u * (uint32_t)a_xor;
-      a_odd[kk] = a0 - 2048u * (uint32_t)a_xor;
+      // (row = l16 modulo 16, which is all the swizzle looks at)
+      const uint32_t a0 = (uint32_t)(row * T::RB + (((kk * 4 + g) ^ a_swz<T>(l16)) << 4));
+      // slot i reads fragment i ^ a_xor: +FSTRIDE for even slots, -FSTRIDE for
+      // odd ones (odd slots are >= 1, so the sum never wraps below zero)
+      a_base[kk] = a0 + FSTRIDE * (uint32_t)a_xor;
+      a_odd[kk] = a0 - FSTRIDE * (uint32_t)a_xor;
       if constexpr (T::AKM) {
         // as B[K,N] below, with rows of A in place of columns of B
         const int k = kk * 32 + 8 * g + (l16 >> 2);
@@ -355,7 +374,7 @@ struct FragReader {
         // (both carry +256 so that b_odd stays non-negative; read() takes it off)
       } else {
         const int brow = wn * T::WTN + l16;
-        b_base[kk] = (uint32_t)(brow * 128 + (((kk * 4 + g) ^ (l16 & 7)) << 4));
+        b_base[kk] = (uint32_t)(brow * T::RB + (((kk * 4 + g) ^ a_swz<T>(l16)) << 4));
       }
     }
   }
@@ -374,7 +393,7 @@ struct FragReader {
     } else {
       if (item < T::FM) {
         f.a[item] = lds_read16(lds, a_st + ((item & 1) ? a_odd[kk] : a_base[kk]) +
-                                        (uint32_t)item * 2048u);
+                                        (uint32_t)item * FSTRIDE);
         return;
       }
     }
@@ -387,7 +406,7 @@ struct FragReader {
       if (h == 0) { f.b[j][0] = v[0]; f.b[j][1] = v[1]; }
       else { f.b[j][2] = v[0]; f.b[j][3] = v[1]; }
     } else {
-      f.b[bi] = lds_read16(lds, b_st + b_base[kk] + (uint32_t)bi * 2048u);
+      f.b[bi] = lds_read16(lds, b_st + b_base[kk] + (uint32_t)bi * FSTRIDE);
     }
   }
 };
@@ -544,7 +563,7 @@ __device__ __forceinline__ void issue_prologue(const GemmParams& p, uint32_t lds
   DmaPlan<T> dma;
   dma.init(p, m_base, n_base, lane, wave);
   constexpr int ND = DmaPlan<T>::INS;
-  const int nk = (p.K + BK - 1) / BK;
+  const int nk = (p.K + T::BK - 1) / T::BK;
 #pragma unroll
   for (int st = 0; st < T::STAGES; ++st) {
     if (st < nk) {
@@ -597,7 +616,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   rd.init(wm, wn, lane, (LAZY && lazy_split<T>()) ? wn : 0);
   constexpr int ND = DmaPlan<T>::INS;
   constexpr int NR = FragReader<T>::ITEMS;
-  const int nk = (p.K + BK - 1) / BK;
+  const int nk = (p.K + T::BK - 1) / T::BK;
 
   if (!prologue_issued) issue_prologue<T>(p, lds0, m_base, n_base, tid);
   if (stores_after) wait_ktile<ND, T::STAGES, T::C_STORES>(min(nk, T::STAGES) - 1);
@@ -629,33 +648,67 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
         scale_own_chunks<T>(lds, (uint32_t)((kt + 1) % T::STAGES) * T::STAGE, wave, lane);
     }
   };
-  if constexpr (!LAZY) {
-    // steady state, peeled: every k-tile refills its stage, with no branch per
-    // transfer (for Lazy Pre-Norm the second copy of the loop body costs
-    // registers that it does not have to spare)
-    for (; kt + T::STAGES < nk; ++kt) {
+  if constexpr (T::KK == 1) {
+    // One k32 sub-step per k-tile.  Before k-tile kt is computed (its
+    // fragments are in registers), k-tile kt+1 must have landed; the sub-step
+    // reads kt+1's fragments and refills kt's stage, whose reads all completed
+    // before the barrier, with k-tile kt+STAGES.  Two k-tiles per trip keep
+    // the two fragment sets in fixed registers.
+    // steady state, peeled: both k-tiles of a trip refill a stage
+    for (; kt + 1 + T::STAGES < nk; kt += 2) {
+      const uint32_t s0 = (uint32_t)(kt % T::STAGES) * T::STAGE;
+      const uint32_t s1 = (uint32_t)((kt + 1) % T::STAGES) * T::STAGE;
+      const uint32_t s2 = (uint32_t)((kt + 2) % T::STAGES) * T::STAGE;
+      wait_next(kt);
+      __syncthreads();
+      substep<T, LAZY, 1>(acc, gram, f0, f1, lds, rd, s1, 0, dma, true, p, m_base, n_base,
+                          kt + T::STAGES, lds0 + s0);
+      wait_next(kt + 1);
+      __syncthreads();
+      substep<T, LAZY, 1>(acc, gram, f1, f0, lds, rd, s2, 0, dma, true, p, m_base, n_base,
+                          kt + 1 + T::STAGES, lds0 + s1);
+    }
+    for (; kt < nk; kt += 2) {
+      wait_next(kt);
+      __syncthreads();
+      substep<T, LAZY>(acc, gram, f0, f1, lds, rd, (uint32_t)((kt + 1) % T::STAGES) * T::STAGE, 0,
+                       dma, kt + T::STAGES < nk, p, m_base, n_base, kt + T::STAGES,
+                       lds0 + (uint32_t)(kt % T::STAGES) * T::STAGE);
+      if (kt + 1 >= nk) break;
+      wait_next(kt + 1);
+      __syncthreads();
+      substep<T, LAZY, 2>(acc, gram, f1, f0, lds, rd, (uint32_t)((kt + 2) % T::STAGES) * T::STAGE,
+                          0, dma, false, p, m_base, n_base, 0, 0);
+    }
+  } else {
+    if constexpr (!LAZY) {
+      // steady state, peeled: every k-tile refills its stage, with no branch per
+      // transfer (for Lazy Pre-Norm the second copy of the loop body costs
+      // registers that it does not have to spare)
+      for (; kt + T::STAGES < nk; ++kt) {
+        const int nxt_s = cur_s + 1 == T::STAGES ? 0 : cur_s + 1;
+        const uint32_t cur = (uint32_t)cur_s * T::STAGE;
+        const uint32_t nxt = (uint32_t)nxt_s * T::STAGE;
+        substep<T, LAZY, 2>(acc, gram, f0, f1, lds, rd, cur, 1, dma, false, p, m_base, n_base, 0, 0);
+        wait_next(kt);
+        __syncthreads();
+        substep<T, LAZY, 1>(acc, gram, f1, f0, lds, rd, nxt, 0, dma, true, p, m_base, n_base,
+                            kt + T::STAGES, lds0 + cur);
+        cur_s = nxt_s;
+      }
+    }
+    for (; kt < nk; ++kt) {
       const int nxt_s = cur_s + 1 == T::STAGES ? 0 : cur_s + 1;
       const uint32_t cur = (uint32_t)cur_s * T::STAGE;
       const uint32_t nxt = (uint32_t)nxt_s * T::STAGE;
       substep<T, LAZY, 2>(acc, gram, f0, f1, lds, rd, cur, 1, dma, false, p, m_base, n_base, 0, 0);
       wait_next(kt);
       __syncthreads();
-      substep<T, LAZY, 1>(acc, gram, f1, f0, lds, rd, nxt, 0, dma, true, p, m_base, n_base,
-                          kt + T::STAGES, lds0 + cur);
+      // stage cur is free now: refill it with k-tile kt+STAGES
+      substep<T, LAZY>(acc, gram, f1, f0, lds, rd, nxt, 0, dma, kt + T::STAGES < nk, p, m_base,
+                       n_base, kt + T::STAGES, lds0 + cur);
       cur_s = nxt_s;
     }
-  }
-  for (; kt < nk; ++kt) {
-    const int nxt_s = cur_s + 1 == T::STAGES ? 0 : cur_s + 1;
-    const uint32_t cur = (uint32_t)cur_s * T::STAGE;
-    const uint32_t nxt = (uint32_t)nxt_s * T::STAGE;
-    substep<T, LAZY, 2>(acc, gram, f0, f1, lds, rd, cur, 1, dma, false, p, m_base, n_base, 0, 0);
-    wait_next(kt);
-    __syncthreads();
-    // stage cur is free now: refill it with k-tile kt+STAGES
-    substep<T, LAZY>(acc, gram, f1, f0, lds, rd, nxt, 0, dma, kt + T::STAGES < nk, p, m_base,
-                     n_base, kt + T::STAGES, lds0 + cur);
-    cur_s = nxt_s;
   }
   // every wave is done with the stages before they are reused
   __syncthreads();
