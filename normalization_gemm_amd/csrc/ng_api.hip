@@ -52,7 +52,10 @@ constexpr int64_t kMaxDim = int64_t(1) << 24;
 //           the other's epilogue: the N <= 128 shapes are HBM-bound.
 //           (Measured on 65536x512x128 against 256 x 128 tiles of 8 waves
 //           with three stages, one workgroup per CU: 3 % faster; 128 x 128
-//           with three stages, 64 x 128 and 8-wave 128 x 128 were slower.)
+//           with three stages, 64 x 128 and 8-wave 128 x 128 were slower, and
+//           so were 32-deep k-tiles in 3 or 4 stages and persistent grids of
+//           64- or 128-row tiles.)  Each row block of A has one reader, so A
+//           is fetched nontemporally (19.1 against 19.8 us on that shape).
 //   Row256: 128 x 256, 2x2 waves (128 < N <= 256).
 template <bool KN> struct TLargeSel {
   using type = ng::Tile<256, 256, 4, 2, false, 2>;
@@ -61,7 +64,7 @@ template <> struct TLargeSel<true> {
   using type = ng::Tile<256, 256, 4, 2, true, 4, false, 0, 32>;
 };
 template <bool KN> using TLarge = typename TLargeSel<KN>::type;
-template <bool KN> using TRow128 = ng::Tile<128, 128, 4, 1, KN, 2>;
+template <bool KN> using TRow128 = ng::Tile<128, 128, 4, 1, KN, 2, false, 0, 64, true>;
 template <bool KN> using TRow256 = ng::Tile<128, 256, 2, 2, KN>;
 //   Wgrad: the 256x256 tile with A stored [K, M] (the reduction over the
 //          forward rows) and the normalized A rebuilt on the A (RS 1) or B

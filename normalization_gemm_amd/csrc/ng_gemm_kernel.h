@@ -128,10 +128,13 @@ struct GemmParams {
 // row_rstd and rounded to bf16 in registers before the MFMAs (the
 // normalized A of Lazy Pre-Norm rebuilt from A and its saved rstd).
 // BK: k-tile depth (64, or 32 for deeper pipelines within the LDS budget).
+// ANT: A is fetched with nontemporal loads (tiles whose workgroup is the only
+// reader of its rows of A: one column tile per row block).
 template <int BM_, int BN_, int WM_, int WN_, bool KN_, int STAGES_ = 2, bool AKM_ = false,
-          int RS_ = 0, int BK_ = 64>
+          int RS_ = 0, int BK_ = 64, bool ANT_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+  static constexpr bool ANT = ANT_;
   static constexpr bool KN = KN_;
   static constexpr bool AKM = AKM_;
   static constexpr int RS = RS_;
@@ -274,7 +277,7 @@ struct DmaPlan {
         make_rsrc(p.A + off, ((uint64_t)p.M * p.K - off) * 2u);
     const uint32_t v = (k0 + (int)a_kc < p.K) ? a_voff : kOOB;
     const uint32_t row0 = (uint32_t)((wave * A_INS + j) * (64 / T::CPR));
-    dma16(rs, st + (uint32_t)(wave * A_INS + j) * 1024u, v, row0 * a_row_bytes);
+    dma16<T::ANT>(rs, st + (uint32_t)(wave * A_INS + j) * 1024u, v, row0 * a_row_bytes);
   }
   // Transfer j of k-tile kt of B into the B region at LDS byte address `st`.
   __device__ __forceinline__ void issue_b(const GemmParams& p, int n_base, int kt, uint32_t st,
@@ -1018,8 +1021,8 @@ __device__ __forceinline__ void apply_store(const GemmParams& p, const f32x4 (&a
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.C + base, left);
       const uint32_t o0 = voff_c == kOOB ? kOOB : voff_c + (uint32_t)rr * row_bytes;
       const uint32_t o1 = voff_c == kOOB ? kOOB : voff_c + (uint32_t)(rr + 8) * row_bytes;
-      __builtin_amdgcn_raw_buffer_store_b128(v0, rs, o0, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(v1, rs, o1, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v0, rs, o0, 0, kStoreNT);
+      __builtin_amdgcn_raw_buffer_store_b128(v1, rs, o1, 0, kStoreNT);
     }
   }
 }
