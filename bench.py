@@ -81,6 +81,26 @@ def _pmc_rows(d, counter):
     return [(k, v) for _, k, v in rows]
 
 
+EPI_NUMBER = {"EPI_NONE": 0, "EPI_LAZY": 1, "EPI_ROW_RMS": 2, "EPI_ROW_LN": 3,
+              "EPI_LAZY_BIAS": 4, "EPI_ROW_RMS_RES": 5, "EPI_ROW_LN_RES": 6, "EPI_PRE_LN": 7,
+              "EPI_LAZY_BWD": 8}
+
+
+def is_fused_dispatch(kernel_name: str, w) -> bool:
+    """Whether a traced kernel symbol is the workload's fused kernel (not the
+    ng_gemm of the unfused pair, whose symbol has the same base name)."""
+    import re
+    label = kernel_label(w)
+    base = label.split("<")[0]
+    if base not in kernel_name:
+        return False
+    if base == "gemm_xwg_kernel":
+        return True
+    epi = label.rstrip(">").rsplit("<", 1)[-1].rsplit(", ", 1)[-1]
+    m = re.search(r",\s*(\d+)>\s*(\(|$)", kernel_name.strip())
+    return m is not None and int(m.group(1)) == EPI_NUMBER[epi]
+
+
 def summarize_pmc(fetch_dir, write_dir, w, copy_mib):
     """HBM bytes per launch of the fused kernel, each counter scaled by what
     it reads for a plain copy of known size (copy_mib read + written)."""
@@ -90,7 +110,7 @@ def summarize_pmc(fetch_dir, write_dir, w, copy_mib):
         rows = _pmc_rows(d, counter)
         # the calibration copies are the first three runtime copy kernels
         copies = [v for k, v in rows if "copybuffer" in k.lower()][:3]
-        fused = [v for k, v in rows if "gemm_kernel" in k or "gemm_xwg_kernel" in k]
+        fused = [v for k, v in rows if is_fused_dispatch(k, w)]
         if not copies or not fused:
             raise SystemExit("missing copy or fused kernel rows for %s" % counter)
         copy_kib = statistics.median(copies)
