@@ -492,14 +492,35 @@ constexpr bool lazy_split() { return T::WN == 2 && T::FM % 2 == 0; }
 template <class T>
 constexpr int lazy_slots() { return lazy_split<T>() ? T::FM / 2 : T::FM; }
 
+// Without the split (one wave per row set, the narrow-row tile) the Gram
+// MFMAs would add FM per FM*FN products, and the squares are taken on the
+// VALU instead: the lane's 8 elements of the fragment, one fmaf each, spread
+// over the products' slots, into register 0 of the slot's accumulator (the
+// lane's own row and k-group; the later lane-group sum adds the row's four
+// k-groups).  (Measured on 256x128x64: 4.9 against 5.2 us; on the 256x256
+// tile with the split, the Gram MFMAs are faster: 922-925 against
+// 937-942 us on 32768x4096x4096.)
+template <class T>
+constexpr bool lazy_valu() { return !lazy_split<T>(); }
+
 // Gram accumulator g belongs to slot (lazy_split ? 2g : g); each is updated
-// once per sub-step, after the last product MFMA that shares its fragment.
+// once per sub-step, after the last product MFMA that shares its fragment
+// (on the VALU path: one element every STEP/8 slots).
 template <class T>
 __device__ __forceinline__ void lazy_gram(int q, const Frags<T>& cur,
                                           f32x4 (&gram)[lazy_slots<T>()]) {
   constexpr int STEP = (T::FM * T::FN) / lazy_slots<T>();
   static_assert((T::FM * T::FN) % lazy_slots<T>() == 0, "Gram MFMA spacing");
-  if (q % STEP == STEP - 1) {
+  if constexpr (lazy_valu<T>()) {
+    static_assert(STEP % 8 == 0, "VALU squares: 8 elements per fragment");
+    if (q % (STEP / 8) == STEP / 8 - 1) {
+      const int g = q / STEP;
+      const int e = (q % STEP) / (STEP / 8);  // element 0..7 of the lane's 8
+      const uint32_t w = cur.a[g][e >> 1];
+      const float x = (e & 1) ? bf16_hi(w) : bf16_lo(w);
+      gram[g][0] = fmaf(x, x, gram[g][0]);
+    }
+  } else if (q % STEP == STEP - 1) {
     const int g = q / STEP;
     const int k = lazy_split<T>() ? 2 * g : g;
     gram[g] = mfma_16x16x32(cur.a[k], cur.a[k], gram[g]);
@@ -719,14 +740,15 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   __syncthreads();
   if constexpr (LAZY) {
     // the Gram diagonal: row l16 of a slot in lane group l16 >> 2, register
-    // l16 & 3; the other lane groups contribute zero to the later lane-group sum
+    // l16 & 3; the other lane groups contribute zero to the later lane-group
+    // sum (VALU path: every lane holds its k-group's partial in register 0)
     const int l16 = lane & 15, g = lane >> 4;
     const int r = l16 & 3;
 #pragma unroll
     for (int gi = 0; gi < lazy_slots<T>(); ++gi) {
       const f32x4 d = gram[gi];
       const float v = r == 0 ? d[0] : r == 1 ? d[1] : r == 2 ? d[2] : d[3];
-      ss[lazy_split<T>() ? 2 * gi : gi] = g == (l16 >> 2) ? v : 0.f;
+      ss[lazy_split<T>() ? 2 * gi : gi] = lazy_valu<T>() ? d[0] : (g == (l16 >> 2) ? v : 0.f);
     }
   }
 }
