@@ -87,14 +87,14 @@ __device__ __forceinline__ void wait_all_mem() {
 
 __device__ __forceinline__ float xor_shfl(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
-// Raw buffer resource over `bytes` bytes from `base`: loads at offsets at or
-// beyond the size return zero.  Sizes are clamped below 2^31 so that offset
 // Cache policy of the output stores: nontemporal (nt), for streamed results
 // that the kernel never reads back.  (Measured on MI355X: the 16 MiB output
 // of a 65536 x 512 x 128 GEMM + LayerNorm stores ~3.5 us sooner than with the
 // default policy, 19.5 against 23.1 us per call.)
 constexpr int kStoreNT = 2;
 
+// Raw buffer resource over `bytes` bytes from `base`: loads at offsets at or
+// beyond the size return zero.  Sizes are clamped below 2^31 so that offset
 // kOOB is always out of range.
 constexpr uint32_t kOOB = 0x80000000u;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
