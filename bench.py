@@ -5,8 +5,9 @@
 
 A step is one call of the fused kernel over one batch of the workload's
 synthetic bf16 inputs (seeded, see workloads/).  The default workload is the
-GEMM + LayerNorm epilogue case (A 65536x512 @ B 512x128, N = 128: the
-single-workgroup row tile).  Inputs sit in HBM before the timed region;
+largest one, GEMM + LayerNorm(gamma, beta) epilogue over full rows of 16384
+columns (A 8192x8192 @ B 8192x16384: the cross-workgroup row reduction,
+MFMA-bound).  Inputs sit in HBM before the timed region;
 several input/output copies are rotated so that the 256 MB Infinity Cache
 cannot serve a step from the previous step's data.  The fused call and the
 unfused baseline (ng_gemm, ng_norm, and the pair) are timed round-robin over
@@ -40,7 +41,7 @@ MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 ROUNDS = 5  # round-robin timing rounds per callable (median reported)
 RIDGE_FLOP_PER_BYTE = MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-DEFAULT_WORKLOAD = workloads.WORKLOADS[1].name
+DEFAULT_WORKLOAD = workloads.WORKLOADS[4].name
 ROTATE_BYTES = 768 << 20     # input+output copies rotated per step exceed this
 METRIC = ("fused norm-GEMM bf16 TFLOP/s (% MFMA peak) + % norm latency hidden vs unfused")
 
@@ -425,18 +426,138 @@ class Bench:
         return per, wall, mean
 
 
+def _read(path):
+    try:
+        with open(path) as f:
+            return f.read().strip()
+    except OSError:
+        return None
+
+
+def _sysfs_card():
+    """sysfs device directory of the GPU torch sees as cuda:0 (matched by PCI
+    address), or None."""
+    import glob
+    torch = __import__("torch")
+    prop = torch.cuda.get_device_properties(0)
+    bus = getattr(prop, "pci_bus_id", None)
+    dev = getattr(prop, "pci_device_id", None)
+    dom = getattr(prop, "pci_domain_id", 0) or 0
+    if bus is None or dev is None:
+        return None
+    slot = "%04x:%02x:%02x." % (dom, bus, dev)
+    for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+        ue = _read(os.path.join(d, "uevent")) or ""
+        for line in ue.splitlines():
+            if line.startswith("PCI_SLOT_NAME=") and line.split("=", 1)[1].lower().startswith(slot):
+                return d
+    return None
+
+
+def power_and_clocks():
+    """Shader clock and power readings of cuda:0 from sysfs (hwmon: sclk in
+    MHz, socket power and its cap in W; the current DPM level of pp_dpm_sclk),
+    falling back to rocm-smi's JSON.  Best effort: missing readings are None."""
+    import glob
+    out = {}
+    d = _sysfs_card()
+    if d:
+        for hw in glob.glob(os.path.join(d, "hwmon", "hwmon*")):
+            f = _read(os.path.join(hw, "freq1_input"))
+            if f and f.isdigit():
+                out["sclk_mhz"] = round(int(f) / 1e6)
+            for name, key in (("power1_average", "power_w"), ("power1_input", "power_w"),
+                              ("power1_cap", "power_cap_w")):
+                v = _read(os.path.join(hw, name))
+                if v and v.isdigit() and key not in out:
+                    out[key] = round(int(v) / 1e6, 1)
+        lv = _read(os.path.join(d, "pp_dpm_sclk"))
+        if lv:
+            cur = [ln for ln in lv.splitlines() if ln.rstrip().endswith("*")]
+            if cur:
+                out["sclk_dpm_level"] = cur[0].rstrip(" *")
+    if "sclk_mhz" not in out or "power_cap_w" not in out:
+        import subprocess
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--showmaxpower",
+                                "--json"], capture_output=True, text=True, timeout=20)
+            rec = json.loads(r.stdout)
+            card = next(iter(rec.values())) if len(rec) == 1 else None
+            if isinstance(card, dict):
+                out["rocm_smi"] = {k: v for k, v in card.items()
+                                   if "sclk" in k.lower() or "power" in k.lower()}
+        except Exception:  # pragma: no cover - best effort
+            pass
+    return out
+
+
+def readings_under_load(fn, n_launches):
+    """Enqueue n_launches calls of fn (about a second of GPU work) and take
+    power_and_clocks() from a thread while they run."""
+    import threading
+    torch = __import__("torch")
+    res = {}
+
+    def sample():
+        time.sleep(0.25)
+        res.update(power_and_clocks())
+
+    th = threading.Thread(target=sample)
+    th.start()
+    for i in range(n_launches):
+        fn(i)
+    th.join()
+    torch.cuda.synchronize()
+    return res
+
+
+def source_hash() -> str:
+    """Hash of the sources a result depends on (kernels, header, bench), for
+    runs made where git is not available."""
+    h = hashlib.sha256()
+    for rel in ("include/normgemm.h", "bench.py"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    h.update(kernel_source_hash().encode())
+    return h.hexdigest()[:16]
+
+
+def git_sha():
+    import subprocess
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                           text=True, timeout=10)
+        return r.stdout.strip() or None
+    except Exception:  # pragma: no cover - best effort
+        return None
+
+
 def device_info():
-    """Name, CU count and maximum shader clock of the device, and the ROCm
-    version of the runtime (for the record; not used in any figure)."""
+    """Name, CU count and maximum shader clock of the device, the HIP runtime
+    the process loaded (PyTorch's) and the ROCm install the library was built
+    with (for the record; not used in any figure)."""
     torch = __import__("torch")
     prop = torch.cuda.get_device_properties(0)
     info = {"name": prop.name, "arch": getattr(prop, "gcnArchName", ""),
             "cus": prop.multi_processor_count,
-            "hip": getattr(torch.version, "hip", None)}
+            "hip_runtime": getattr(torch.version, "hip", None),
+            "rocm_install": _read("/opt/rocm/.info/version")}
     clk = getattr(prop, "clock_rate", None)
     if clk:
         info["max_sclk_mhz"] = round(clk / 1000.0)
     return info
+
+
+def blas_info():
+    """BLAS library NumPy runs the oracle's products on (threadpoolctl)."""
+    try:
+        from threadpoolctl import threadpool_info
+        for d in threadpool_info():
+            if d.get("user_api") == "blas":
+                return "%s %s" % (d.get("internal_api"), d.get("version"))
+    except Exception:  # pragma: no cover
+        pass
+    return None
 
 
 def cpu_baseline(w: workloads.Workload, target_s: float):
@@ -491,7 +612,7 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
     products = 2 if w.op == workloads.OP_LAZY_BWD else 1
     flops = 2.0 * products * done_rows * w.N * w.K
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "kind": "oracle", "blas": blas_info(),
             "sample": "%d output rows of %s in passes of up to %d rows (fp64 NumPy GEMM%s + "
                       "explicit norm, %.1f s)" % (done_rows, w.name, rows,
                                                   "s" if products == 2 else "", t_total)}
@@ -537,6 +658,8 @@ def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: f
     roof["avg_launch_us"] = round(t_fused * 1e3, 2)
     roof["algorithmic_bytes"] = algorithmic_bytes(w)
     hidden = (t_gemm + t_norm - t_fused) / t_norm * 100.0
+    # clock and power while the fused kernel runs (about a second of calls)
+    load = readings_under_load(b.fused, max(50, int(1.0 / max(t_fused * 1e-3, 1e-6))))
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -563,6 +686,9 @@ def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: f
                     "fused_p90_us": round(float(np.percentile(per, 90)) * 1e3, 2)},
         "roofline": roof,
         "device": device_info(),
+        "under_load": load,
+        "git_sha": git_sha(),
+        "source_hash": source_hash(),
     }
     del b
     torch_mod.cuda.empty_cache()

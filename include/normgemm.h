@@ -13,6 +13,12 @@
  *   - M >= 0 (M == 0 is a no-op that returns NG_OK), N >= 1, K >= 1 and each
  *     at most 2^24;
  *   - N and K must be multiples of 8 (16-byte rows) -> else NG_ERR_UNSUPPORTED;
+ *   - K at most 2^22 -> else NG_ERR_UNSUPPORTED (a tile reads up to 256 rows
+ *     of A [M, K], or of B stored [N, K], through 32-bit offsets from one
+ *     base, which must stay below 2 GiB); the weight-gradient products
+ *     (ng_gemm_at, ng_rmsnorm_gemm_lazy_backward_weight), which read no rows
+ *     of length K, take K up to 2^24;
+ *   - no matrix with 2^34 or more elements -> else NG_ERR_UNSUPPORTED;
  *   - eps finite and >= 0;
  *   - every matrix pointer non-NULL (A and C, or X and Y, may be NULL when
  *     M, or rows, is 0) and 16-byte aligned; gamma/beta (when given) 16-byte
@@ -39,6 +45,7 @@ extern "C" {
 
 typedef uint16_t ng_bf16; /* raw bfloat16 bits */
 
+/* Every entry point that returns a status returns one of these values. */
 typedef enum {
   NG_OK = 0,
   NG_ERR_INVALID_ARG = 1, /* NULL/misaligned pointer, bad size, bad eps or enum */
@@ -72,7 +79,7 @@ enum {
  * A: [M, K]; B: see b_layout; C: [M, N] bf16 out.
  * rstd_out: float32 [M] or NULL.  Needs no workspace.
  */
-int ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N,
+ng_status ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N,
                          int64_t K, int b_layout, float eps, float* rstd_out, void* stream);
 
 /*
@@ -95,11 +102,11 @@ int ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t
  * ng_rmsnorm_gemm_lazy).  bias: fp32 [N], 16-byte aligned, or NULL (no bias).
  * rstd_out: float32 [M] or NULL.  Needs no workspace.
  */
-int ng_lazy_fold_affine(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
+ng_status ng_lazy_fold_affine(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
                         ng_bf16* B_folded, float* bias, int64_t K, int64_t N, int b_layout,
                         void* stream);
 
-int ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded, const float* bias,
+ng_status ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded, const float* bias,
                                 ng_bf16* C, int64_t M, int64_t N, int64_t K, int b_layout,
                                 float eps, float* rstd_out, void* stream);
 
@@ -120,7 +127,7 @@ int ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded, const
  * (ng_workspace_bytes(NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT, M, N, K) bytes; the
  * same rules as for ng_gemm_rmsnorm).  dA must not overlap the inputs.
  */
-int ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
+ng_status ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
                                          const float* rstd, ng_bf16* dA, int64_t M, int64_t N,
                                          int64_t K, int b_layout, void* workspace,
                                          size_t workspace_bytes, void* stream);
@@ -148,11 +155,11 @@ int ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, con
  * required (the pre-pass writes them, the product reads them).  K at most
  * 65536 (else NG_ERR_UNSUPPORTED).  Needs no workspace.
  */
-int ng_layernorm_gemm_fold(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
+ng_status ng_layernorm_gemm_fold(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
                            ng_bf16* B_folded, float* colsum, float* bias, int64_t K, int64_t N,
                            int b_layout, void* stream);
 
-int ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, const float* colsum,
+ng_status ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, const float* colsum,
                               const float* bias, ng_bf16* C, int64_t M, int64_t N, int64_t K,
                               int b_layout, float eps, float* mean, float* rstd, void* stream);
 
@@ -172,15 +179,12 @@ int ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, const f
  * grid of at most as many workgroups as the device holds at once, whose
  * workgroups wait for each other: two such calls must not run concurrently
  * on one device (e.g. on two streams).  If they do, a wait may give up after
- * about a second; ng_workspace_status then reports NG_ERR_TIMEOUT and the
- * output of that call is undefined.  (The environment variable NG_WAIT_SPINS,
- * read on every call, replaces the bound of 2^20 polls of ~1 us;
- * NG_ROW_LOCAL_MAX, also read on every call and by ng_workspace_bytes,
- * lowers the widest row reduced inside one workgroup from 256, so that the
- * cross-workgroup path can be run on narrow rows for comparison.)
+ * about a second (2^20 polls of ~1 us; see ng_set_debug_option);
+ * ng_workspace_status then reports NG_ERR_TIMEOUT, and every output element
+ * and statistic of a row whose exchange failed is NaN.
  * gamma: bf16 [N] or NULL.  rstd_out: float32 [M] or NULL.
  */
-int ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,
+ng_status ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,
                     int64_t M, int64_t N, int64_t K, int b_layout, float eps, float* rstd_out,
                     void* workspace, size_t workspace_bytes, void* stream);
 
@@ -195,7 +199,7 @@ int ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng
  * Workspace rules as for ng_gemm_rmsnorm with NG_OP_GEMM_LAYERNORM.
  * mean_out, rstd_out: float32 [M] or NULL.
  */
-int ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
+ng_status ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
                       const ng_bf16* beta, ng_bf16* C, int64_t M, int64_t N, int64_t K,
                       int b_layout, float eps, float* mean_out, float* rstd_out, void* workspace,
                       size_t workspace_bytes, void* stream);
@@ -216,22 +220,26 @@ int ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
  * workspace rules as for ng_gemm_rmsnorm / ng_gemm_layernorm, with
  * ng_workspace_bytes(NG_OP_GEMM_ADD_RMSNORM / NG_OP_GEMM_ADD_LAYERNORM, ...).
  */
-int ng_gemm_add_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
+ng_status ng_gemm_add_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
                         const ng_bf16* gamma, ng_bf16* C, ng_bf16* S_out, int64_t M, int64_t N,
                         int64_t K, int b_layout, float eps, float* rstd_out, void* workspace,
                         size_t workspace_bytes, void* stream);
 
-int ng_gemm_add_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
+ng_status ng_gemm_add_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
                           const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* C, ng_bf16* S_out,
                           int64_t M, int64_t N, int64_t K, int b_layout, float eps,
                           float* mean_out, float* rstd_out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
 /*
- * Plain GEMM, the matrix half of the unfused baseline: C = A @ B (bf16 out,
- * fp32 accumulation).
+ * Plain GEMM, the matrix half of the unfused baseline that the fused forms
+ * are measured against ("Free normalization fusion", section "why
+ * normalization is a performance problem": a GEMM tiles both dimensions, so
+ * no tile sees a whole row and the norm, a reduction over the row, runs as a
+ * kernel of its own without the matrix units):  C = A @ B (bf16 out, fp32
+ * accumulation).  A: [M, K]; B: see b_layout; C: [M, N] bf16 out.
  */
-int ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+ng_status ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
             int b_layout, void* stream);
 
 /*
@@ -243,7 +251,7 @@ int ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N
  * most 65536 (else NG_ERR_UNSUPPORTED).  mean_out (LayerNorm only) and
  * rstd_out: float32 [rows] or NULL.
  */
-int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* Y,
+ng_status ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* Y,
             int64_t rows, int64_t cols, int kind, float eps, float* mean_out, float* rstd_out,
             void* stream);
 
@@ -256,7 +264,7 @@ int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16
  * may equal X or R (in-place updates: each element is read before the same
  * element is written); S_out and Y must differ.  Limits as for ng_norm.
  */
-int ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng_bf16* beta,
+ng_status ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng_bf16* beta,
                 ng_bf16* Y, ng_bf16* S_out, int64_t rows, int64_t cols, int kind, float eps,
                 float* mean_out, float* rstd_out, void* stream);
 
@@ -271,7 +279,7 @@ int ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const 
  * NG_B_KN, [N, K] for NG_B_NK), bf16.  M may be any size (M == 0 writes
  * zeros).  dB must not overlap the inputs.
  */
-int ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* dC, const float* rstd,
+ng_status ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* dC, const float* rstd,
                                           ng_bf16* dB, int64_t M, int64_t N, int64_t K,
                                           int b_layout, void* stream);
 
@@ -282,7 +290,7 @@ int ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* dC, co
  * bf16 out, fp32 accumulation.  M and N multiples of 8 (else
  * NG_ERR_UNSUPPORTED); K any size >= 1.
  */
-int ng_gemm_at(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+ng_status ng_gemm_at(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
                void* stream);
 
 /*
@@ -293,27 +301,51 @@ int ng_gemm_at(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_
  * (the chain rule of y = x * rstd).  bf16 in and out; cols a multiple of 8
  * and at most 65536 (else NG_ERR_UNSUPPORTED).  dX may equal dY.
  */
-int ng_rmsnorm_backward(const ng_bf16* dY, const ng_bf16* X, const float* rstd, ng_bf16* dX,
+ng_status ng_rmsnorm_backward(const ng_bf16* dY, const ng_bf16* X, const float* rstd, ng_bf16* dX,
                         int64_t rows, int64_t cols, void* stream);
 
 /* Workspace bytes `op` needs for this shape (0 when it needs none). */
 size_t ng_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /* Zero-fill a workspace on `stream` with a fill kernel (graph-capture safe). */
-int ng_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
+ng_status ng_workspace_reset(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Synchronizes `stream`, then reads the workspace's error word: NG_OK, or
  * NG_ERR_TIMEOUT if a cross-workgroup wait in an earlier call gave up (its
  * output is then undefined and the workspace must be reset).
  */
-int ng_workspace_status(const void* workspace, void* stream);
+ng_status ng_workspace_status(const void* workspace, void* stream);
 
 /* Static description of a status code. */
-const char* ng_status_string(int status);
+const char* ng_status_string(ng_status status);
 
 /* Detail of the last error on the calling thread ("" if none). */
 const char* ng_last_error(void);
+
+/*
+ * Diagnostics, process-wide, for tests and experiments (no effect on results
+ * unless stated):
+ *   NG_DEBUG_WAIT_SPINS     bound of each cross-workgroup wait, in polls of
+ *                           ~1 us: 0 .. 2^30, or -1 for the default 2^20.
+ *                           A bound of 0 makes every wait that does not find
+ *                           its entry at once give up (NG_ERR_TIMEOUT, NaN
+ *                           output), with no wave left waiting.
+ *   NG_DEBUG_ROW_LOCAL_MAX  widest row reduced inside one workgroup: 0 .. 256,
+ *                           or -1 for the default 256.  Lower values send
+ *                           narrow rows through the cross-workgroup exchange
+ *                           (so both strategies can be compared on one
+ *                           shape); ng_workspace_bytes follows it.
+ *   NG_DEBUG_TILE_ORDER     order in which the grids take their output tiles:
+ *                           NG_TILE_ORDER_NATURAL (default), _REVERSED or
+ *                           _SHUFFLED (a fixed permutation).  Outputs are
+ *                           bit-identical in every order.
+ * Returns NG_ERR_INVALID_ARG for an unknown option or value.  Calls already
+ * enqueued keep the values they were launched with.
+ */
+enum { NG_DEBUG_WAIT_SPINS = 0, NG_DEBUG_ROW_LOCAL_MAX = 1, NG_DEBUG_TILE_ORDER = 2 };
+enum { NG_TILE_ORDER_NATURAL = 0, NG_TILE_ORDER_REVERSED = 1, NG_TILE_ORDER_SHUFFLED = 2 };
+ng_status ng_set_debug_option(int option, int64_t value);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,9 @@ from ._lib import (  # noqa: F401
     ng_lazy_fold_affine, ng_norm, ng_rmsnorm_backward, ng_rmsnorm_gemm_lazy_backward_input,
     ng_rmsnorm_gemm_lazy_backward_weight, ng_gemm_at,
     ng_rmsnorm_gemm_lazy, ng_rmsnorm_gemm_lazy_affine, ng_status_string, ng_workspace_bytes,
-    ng_workspace_reset, ng_workspace_status,
+    ng_workspace_reset, ng_workspace_status, ng_set_debug_option,
+    NG_DEBUG_ROW_LOCAL_MAX, NG_DEBUG_TILE_ORDER, NG_DEBUG_WAIT_SPINS, NG_TILE_ORDER_NATURAL,
+    NG_TILE_ORDER_REVERSED, NG_TILE_ORDER_SHUFFLED,
 )
 
 __all__ = [
@@ -33,7 +35,7 @@ __all__ = [
     "add_norm", "layernorm_gemm_fold", "layernorm_gemm_prenorm",
     "rmsnorm_gemm_lazy_backward_input", "rmsnorm_gemm_lazy_backward_weight", "rmsnorm_backward",
     "gemm_at",
-    "Workspace", "library_path",
+    "Workspace", "library_path", "debug_option",
 ]
 
 
@@ -41,6 +43,26 @@ class NormGemmError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__("%s: %s (%s)" % (where, ng_status_string(status), ng_last_error()))
+
+
+class debug_option:
+    """Context manager: set a diagnostic option of the library (see
+    ng_set_debug_option) for the duration of a block, then restore `reset`
+    (the option's default)."""
+
+    _DEFAULT = {NG_DEBUG_WAIT_SPINS: -1, NG_DEBUG_ROW_LOCAL_MAX: -1,
+                NG_DEBUG_TILE_ORDER: NG_TILE_ORDER_NATURAL}
+
+    def __init__(self, option: int, value: int):
+        self.option, self.value = option, value
+
+    def __enter__(self):
+        _check(ng_set_debug_option(self.option, self.value), "ng_set_debug_option")
+        return self
+
+    def __exit__(self, *exc):
+        _check(ng_set_debug_option(self.option, self._DEFAULT[self.option]), "ng_set_debug_option")
+        return False
 
 
 def library_path() -> str:
@@ -106,15 +128,25 @@ def _shapes(A, B, lay):
 
 
 class Workspace:
-    """Device scratch for the cross-workgroup epilogue (zeroed once here; the
-    kernels leave it ready for the next call).  One workspace must not serve
-    two calls that can run at the same time."""
+    """Device scratch for the cross-workgroup epilogue.  It is zero-filled on
+    `stream` (default: the current stream) by the library's fill kernel, so
+    the fill is ordered before any call on that stream; the kernels leave it
+    ready for the next call.  One workspace must not serve two calls that can
+    run at the same time (e.g. on two streams without an ordering between
+    them)."""
 
-    def __init__(self, nbytes: int, device=None):
+    def __init__(self, nbytes: int, device=None, stream=None):
         torch = _torch()
-        self.nbytes = max(int(nbytes), 256)
-        self.buf = torch.zeros(self.nbytes, dtype=torch.uint8,
-                               device=device if device is not None else "cuda")
+        dev = torch.device(device if device is not None else "cuda")
+        self.nbytes = max(256, (int(nbytes) + 255) // 256 * 256)
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=dev)
+        handle = _stream(stream)
+        if stream is not None and handle != torch.cuda.current_stream(dev).cuda_stream:
+            # used on another stream than the one that allocated it: the
+            # allocator must not hand the block out again before that stream
+            # has passed every call made on it
+            self.buf.record_stream(torch.cuda.ExternalStream(handle, device=dev))
+        _check(ng_workspace_reset(self.ptr(), self.nbytes, handle), "ng_workspace_reset")
 
     def ptr(self):
         return self.buf.data_ptr()
@@ -123,19 +155,26 @@ class Workspace:
         return ng_workspace_status(self.ptr(), _stream(stream))
 
 
+# Workspaces the tensor helpers create, one per (device, stream): calls on one
+# stream run in order, so they can share one; calls on different streams get
+# different workspaces.
 _ws_cache = {}
 
 
-def _workspace(op, M, N, K, device, workspace):
+def _workspace(op, M, N, K, device, workspace, stream):
     need = ng_workspace_bytes(op, M, N, K)
     if need == 0:
         return None, 0
     if workspace is not None:
         return workspace.ptr(), workspace.nbytes
-    key = (str(device),)
+    handle = _stream(stream)
+    key = (str(device), handle)
     ws = _ws_cache.get(key)
     if ws is None or ws.nbytes < need:
-        ws = Workspace(need, device)
+        # (a replaced workspace's block is held back by the allocator until
+        # the stream has passed the calls that used it: record_stream above,
+        # or the stream that allocated it)
+        ws = Workspace(need, device, stream=handle)
         _ws_cache[key] = ws
     return ws.ptr(), ws.nbytes
 
@@ -266,7 +305,7 @@ def rmsnorm_gemm_lazy_backward_input(dC, B, A, rstd, *, b_layout="kn", out=None,
     _f32_vec(rstd, M, "rstd")
     dA = out if out is not None else torch.empty((M, K), dtype=torch.bfloat16, device=A.device)
     _dev_bf16(dA, "out")
-    ws, wsb = _workspace(NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT, M, N, K, A.device, workspace)
+    ws, wsb = _workspace(NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT, M, N, K, A.device, workspace, stream)
     _check(ng_rmsnorm_gemm_lazy_backward_input(_ptr(dC), _ptr(B), _ptr(A), _ptr(rstd), _ptr(dA),
                                                M, N, K, lay, ws, wsb, _stream(stream)),
            "ng_rmsnorm_gemm_lazy_backward_input")
@@ -335,7 +374,7 @@ def gemm_rmsnorm(A, B, gamma=None, *, eps: float = 1e-6, b_layout="kn", out=None
     M, N, K = _shapes(A, B, lay)
     C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     _dev_bf16(C, "out")
-    ws, wsb = _workspace(NG_OP_GEMM_RMSNORM, M, N, K, A.device, workspace)
+    ws, wsb = _workspace(NG_OP_GEMM_RMSNORM, M, N, K, A.device, workspace, stream)
     _check(ng_gemm_rmsnorm(_ptr(A), _ptr(B), _ptr(gamma), _ptr(C), M, N, K, lay, float(eps),
                            _ptr(rstd_out), ws, wsb, _stream(stream)), "ng_gemm_rmsnorm")
     return C
@@ -355,7 +394,7 @@ def gemm_layernorm(A, B, gamma=None, beta=None, *, eps: float = 1e-5, b_layout="
     M, N, K = _shapes(A, B, lay)
     C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     _dev_bf16(C, "out")
-    ws, wsb = _workspace(NG_OP_GEMM_LAYERNORM, M, N, K, A.device, workspace)
+    ws, wsb = _workspace(NG_OP_GEMM_LAYERNORM, M, N, K, A.device, workspace, stream)
     _check(ng_gemm_layernorm(_ptr(A), _ptr(B), _ptr(gamma), _ptr(beta), _ptr(C), M, N, K, lay,
                              float(eps), _ptr(mean_out), _ptr(rstd_out), ws, wsb,
                              _stream(stream)), "ng_gemm_layernorm")
@@ -387,7 +426,7 @@ def gemm_add_rmsnorm(A, B, R, gamma=None, *, eps: float = 1e-6, b_layout="kn", o
     _residual(R, s_out, M, N)
     C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     _dev_bf16(C, "out")
-    ws, wsb = _workspace(NG_OP_GEMM_ADD_RMSNORM, M, N, K, A.device, workspace)
+    ws, wsb = _workspace(NG_OP_GEMM_ADD_RMSNORM, M, N, K, A.device, workspace, stream)
     _check(ng_gemm_add_rmsnorm(_ptr(A), _ptr(B), _ptr(R), _ptr(gamma), _ptr(C), _ptr(s_out), M, N,
                                K, lay, float(eps), _ptr(rstd_out), ws, wsb, _stream(stream)),
            "ng_gemm_add_rmsnorm")
@@ -410,7 +449,7 @@ def gemm_add_layernorm(A, B, R, gamma=None, beta=None, *, eps: float = 1e-5, b_l
     _residual(R, s_out, M, N)
     C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
     _dev_bf16(C, "out")
-    ws, wsb = _workspace(NG_OP_GEMM_ADD_LAYERNORM, M, N, K, A.device, workspace)
+    ws, wsb = _workspace(NG_OP_GEMM_ADD_LAYERNORM, M, N, K, A.device, workspace, stream)
     _check(ng_gemm_add_layernorm(_ptr(A), _ptr(B), _ptr(R), _ptr(gamma), _ptr(beta), _ptr(C),
                                  _ptr(s_out), M, N, K, lay, float(eps), _ptr(mean_out),
                                  _ptr(rstd_out), ws, wsb, _stream(stream)),

@@ -33,6 +33,13 @@ NG_OP_GEMM_ADD_RMSNORM = 5
 NG_OP_GEMM_ADD_LAYERNORM = 6
 NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT = 7
 
+NG_DEBUG_WAIT_SPINS = 0
+NG_DEBUG_ROW_LOCAL_MAX = 1
+NG_DEBUG_TILE_ORDER = 2
+NG_TILE_ORDER_NATURAL = 0
+NG_TILE_ORDER_REVERSED = 1
+NG_TILE_ORDER_SHUFFLED = 2
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I = ctypes.c_int
@@ -64,6 +71,7 @@ _SIGNATURES = {
     "ng_workspace_status": (_I, [_P, _P]),
     "ng_status_string": (ctypes.c_char_p, [_I]),
     "ng_last_error": (ctypes.c_char_p, []),
+    "ng_set_debug_option": (_I, [_I, _I64]),
 }
 
 _lib = None
@@ -94,96 +102,18 @@ def _call(name, *args):
     return getattr(load(), name)(*args)
 
 
-def ng_rmsnorm_gemm_lazy(A, B, C, M, N, K, b_layout, eps, rstd_out, stream):
-    return _call("ng_rmsnorm_gemm_lazy", A, B, C, M, N, K, b_layout, eps, rstd_out, stream)
+def _delegate(name):
+    def fn(*args):
+        return getattr(load(), name)(*args)
+    fn.__name__ = fn.__qualname__ = name
+    fn.__doc__ = "C entry point %s (include/normgemm.h); returns what it returns." % name
+    return fn
 
 
-def ng_lazy_fold_affine(B, gamma, beta, B_folded, bias, K, N, b_layout, stream):
-    return _call("ng_lazy_fold_affine", B, gamma, beta, B_folded, bias, K, N, b_layout, stream)
-
-
-def ng_rmsnorm_gemm_lazy_affine(A, B_folded, bias, C, M, N, K, b_layout, eps, rstd_out, stream):
-    return _call("ng_rmsnorm_gemm_lazy_affine", A, B_folded, bias, C, M, N, K, b_layout, eps,
-                 rstd_out, stream)
-
-
-def ng_gemm_rmsnorm(A, B, gamma, C, M, N, K, b_layout, eps, rstd_out, workspace,
-                    workspace_bytes, stream):
-    return _call("ng_gemm_rmsnorm", A, B, gamma, C, M, N, K, b_layout, eps, rstd_out,
-                 workspace, workspace_bytes, stream)
-
-
-def ng_gemm_layernorm(A, B, gamma, beta, C, M, N, K, b_layout, eps, mean_out, rstd_out,
-                      workspace, workspace_bytes, stream):
-    return _call("ng_gemm_layernorm", A, B, gamma, beta, C, M, N, K, b_layout, eps, mean_out,
-                 rstd_out, workspace, workspace_bytes, stream)
-
-
-def ng_gemm_add_rmsnorm(A, B, R, gamma, C, S_out, M, N, K, b_layout, eps, rstd_out, workspace,
-                        workspace_bytes, stream):
-    return _call("ng_gemm_add_rmsnorm", A, B, R, gamma, C, S_out, M, N, K, b_layout, eps,
-                 rstd_out, workspace, workspace_bytes, stream)
-
-
-def ng_gemm_add_layernorm(A, B, R, gamma, beta, C, S_out, M, N, K, b_layout, eps, mean_out,
-                          rstd_out, workspace, workspace_bytes, stream):
-    return _call("ng_gemm_add_layernorm", A, B, R, gamma, beta, C, S_out, M, N, K, b_layout, eps,
-                 mean_out, rstd_out, workspace, workspace_bytes, stream)
-
-
-def ng_layernorm_gemm_fold(B, gamma, beta, B_folded, colsum, bias, K, N, b_layout, stream):
-    return _call("ng_layernorm_gemm_fold", B, gamma, beta, B_folded, colsum, bias, K, N, b_layout,
-                 stream)
-
-
-def ng_layernorm_gemm_prenorm(A, B_folded, colsum, bias, C, M, N, K, b_layout, eps, mean, rstd,
-                              stream):
-    return _call("ng_layernorm_gemm_prenorm", A, B_folded, colsum, bias, C, M, N, K, b_layout, eps,
-                 mean, rstd, stream)
-
-
-def ng_rmsnorm_gemm_lazy_backward_input(dC, B, A, rstd, dA, M, N, K, b_layout, workspace,
-                                         workspace_bytes, stream):
-    return _call("ng_rmsnorm_gemm_lazy_backward_input", dC, B, A, rstd, dA, M, N, K, b_layout,
-                 workspace, workspace_bytes, stream)
-
-
-def ng_rmsnorm_gemm_lazy_backward_weight(A, dC, rstd, dB, M, N, K, b_layout, stream):
-    return _call("ng_rmsnorm_gemm_lazy_backward_weight", A, dC, rstd, dB, M, N, K, b_layout,
-                 stream)
-
-
-def ng_gemm_at(A, B, C, M, N, K, stream):
-    return _call("ng_gemm_at", A, B, C, M, N, K, stream)
-
-
-def ng_rmsnorm_backward(dY, X, rstd, dX, rows, cols, stream):
-    return _call("ng_rmsnorm_backward", dY, X, rstd, dX, rows, cols, stream)
-
-
-def ng_gemm(A, B, C, M, N, K, b_layout, stream):
-    return _call("ng_gemm", A, B, C, M, N, K, b_layout, stream)
-
-
-def ng_norm(X, gamma, beta, Y, rows, cols, kind, eps, mean_out, rstd_out, stream):
-    return _call("ng_norm", X, gamma, beta, Y, rows, cols, kind, eps, mean_out, rstd_out, stream)
-
-
-def ng_add_norm(X, R, gamma, beta, Y, S_out, rows, cols, kind, eps, mean_out, rstd_out, stream):
-    return _call("ng_add_norm", X, R, gamma, beta, Y, S_out, rows, cols, kind, eps, mean_out,
-                 rstd_out, stream)
-
-
-def ng_workspace_bytes(op, M, N, K):
-    return _call("ng_workspace_bytes", op, M, N, K)
-
-
-def ng_workspace_reset(workspace, workspace_bytes, stream):
-    return _call("ng_workspace_reset", workspace, workspace_bytes, stream)
-
-
-def ng_workspace_status(workspace, stream):
-    return _call("ng_workspace_status", workspace, stream)
+# One Python function per C entry point, same name and argument order.
+for _name in _SIGNATURES:
+    globals()[_name] = _delegate(_name)
+del _name
 
 
 def ng_status_string(status):

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
 #include <mutex>
 
 #include "../../include/normgemm.h"
@@ -21,7 +22,7 @@ namespace {
 
 thread_local char g_err[512];
 
-int fail(int code, const char* fmt, ...) {
+ng_status fail(ng_status code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof(g_err), fmt, ap);
@@ -29,7 +30,7 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-int ok() {
+ng_status ok() {
   g_err[0] = '\0';
   return NG_OK;
 }
@@ -37,6 +38,11 @@ int ok() {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 constexpr int64_t kMaxDim = int64_t(1) << 24;
+// Longest row of A [M, K] (and of B stored [N, K]) that a tile can read: the
+// tile addresses its (up to 256) rows from one base through 32-bit buffer
+// offsets that must stay inside the buffer range (clamped below 2 GiB), and
+// 255 * 2K + 2 * 64 <= 0x7FFFFFF0 holds for every K <= 2^22.
+constexpr int64_t kMaxRowK = int64_t(1) << 22;
 
 // Tile configurations.
 //   Large: 256x256 macro tile, 8 waves (4 along M x 2 along N) of 64x128, two
@@ -71,7 +77,7 @@ template <bool KN> using TRow256 = ng::Tile<128, 256, 2, 2, KN>;
 //          (RS 2) side.
 template <int RS> using TWgrad = ng::Tile<256, 256, 4, 2, true, 2, true, RS>;
 
-int check_gemm(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
+ng_status check_gemm(const void* A, const void* B, const void* C, int64_t M, int64_t N, int64_t K,
                int b_layout) {
   // A and C are empty when M == 0 and may then be NULL.
   if (!B || (M != 0 && (!A || !C)))
@@ -88,55 +94,73 @@ int check_gemm(const void* A, const void* B, const void* C, int64_t M, int64_t N
   if (N % 8 != 0 || K % 8 != 0)
     return fail(NG_ERR_UNSUPPORTED, "N and K must be multiples of 8 (got N=%lld K=%lld)",
                 (long long)N, (long long)K);
+  if (K > kMaxRowK)
+    return fail(NG_ERR_UNSUPPORTED, "K must be at most 2^22 (got K=%lld)", (long long)K);
   if ((M * K) >= (int64_t(1) << 31) * 8 || (N * K) >= (int64_t(1) << 31) * 8 ||
       (M * N) >= (int64_t(1) << 31) * 8)
     return fail(NG_ERR_UNSUPPORTED, "a matrix has more than 2^34 elements");
   return NG_OK;
 }
 
-int check_eps(float eps) {
+ng_status check_eps(float eps) {
   if (!std::isfinite(eps) || eps < 0.f)
     return fail(NG_ERR_INVALID_ARG, "eps must be finite and >= 0");
   return NG_OK;
 }
 
-int check_vec(const void* p, const char* name, size_t align) {
+ng_status check_vec(const void* p, const char* name, size_t align) {
   if (p && !aligned(p, align))
     return fail(NG_ERR_INVALID_ARG, "%s must be %zu-byte aligned", name, align);
   return NG_OK;
 }
 
-int launched(const char* what) {
+ng_status launched(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(NG_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
   return ok();
 }
 
-// Bound of the cross-workgroup waits, in polls of ~1 us: 2^20 (about a
-// second) unless NG_WAIT_SPINS holds a non-negative integer (read on every
-// call, so a process can lower it to exercise the timeout report).
+// Diagnostic options (ng_set_debug_option), process-wide.
+//   wait bound of the cross-workgroup waits, in polls of ~1 us (-1: 2^20,
+//     about a second);
+//   widest row reduced inside one workgroup (-1: 256);
+//   tile order of the grids (NG_TILE_ORDER_*).
+std::atomic<int> g_wait_spins{-1};
+std::atomic<int> g_row_local_max{-1};
+std::atomic<int> g_tile_order{NG_TILE_ORDER_NATURAL};
+
 int wait_spins() {
-  const char* e = getenv("NG_WAIT_SPINS");
-  if (e && *e) {
-    char* end = nullptr;
-    const long v = strtol(e, &end, 10);
-    if (end && *end == '\0' && v >= 0 && v <= (1L << 30)) return (int)v;
-  }
-  return 1 << 20;
+  const int v = g_wait_spins.load(std::memory_order_relaxed);
+  return v < 0 ? (1 << 20) : v;
 }
 
-// Widest row reduced inside one workgroup: 256 unless NG_ROW_LOCAL_MAX holds
-// a smaller non-negative integer (read on every call; a diagnostic that puts
-// narrow rows on the cross-workgroup path, so that both strategies can be
-// compared on one shape).
 int64_t row_local_max() {
-  const char* e = getenv("NG_ROW_LOCAL_MAX");
-  if (e && *e) {
-    char* end = nullptr;
-    const long v = strtol(e, &end, 10);
-    if (end && *end == '\0' && v >= 0 && v < 256) return v;
+  const int v = g_row_local_max.load(std::memory_order_relaxed);
+  return v < 0 ? 256 : v;
+}
+
+// (a, c) of the tile walk t -> (a t + c) mod total for the current tile-order
+// option: natural (1, 0); reversed (total - 1, total - 1), i.e. total - 1 - t;
+// shuffled: a a prime that does not divide total (so a is coprime to it) and
+// an offset of a third of the walk.
+void tile_order(int64_t total, int* a, int* c) {
+  const int mode = g_tile_order.load(std::memory_order_relaxed);
+  *a = 1;
+  *c = 0;
+  if (total <= 1 || mode == NG_TILE_ORDER_NATURAL) return;
+  if (mode == NG_TILE_ORDER_REVERSED) {
+    *a = (int)(total - 1);
+    *c = (int)(total - 1);
+    return;
   }
-  return 256;
+  static const int64_t primes[] = {15485863, 104729, 7919, 9973};
+  for (int64_t q : primes) {
+    if (total % q != 0) {
+      *a = (int)(q % total);
+      break;
+    }
+  }
+  *c = (int)(total / 3);
 }
 
 ng::GemmParams make_params(const void* A, const void* B, void* C, int64_t M, int64_t N, int64_t K,
@@ -150,21 +174,24 @@ ng::GemmParams make_params(const void* A, const void* B, void* C, int64_t M, int
   p.K = (int)K;
   p.eps = eps;
   p.spin_limit = wait_spins();
+  p.order_a = 1;
+  p.order_c = 0;
   return p;
 }
 
 template <class T, int EPI>
-int launch_grid(ng::GemmParams p, hipStream_t s, const char* what) {
+ng_status launch_grid(ng::GemmParams p, hipStream_t s, const char* what) {
   p.tiles_m = (p.M + T::BM - 1) / T::BM;
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
   const unsigned grid = (unsigned)p.tiles_m * (unsigned)p.tiles_n;
+  tile_order(grid, &p.order_a, &p.order_c);
   hipLaunchKernelGGL((ng::gemm_kernel<T, EPI>), dim3(grid), dim3(T::NT), 0, s, p);
   return launched(what);
 }
 
 // Co-resident workgroups per device for a persistent kernel (cached per
 // kernel and device).
-int resident_capacity(const void* kernel, int threads, int* cap) {
+ng_status resident_capacity(const void* kernel, int threads, int* cap) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(NG_ERR_HIP, "hipGetDevice failed");
   struct Entry {
@@ -194,24 +221,25 @@ int resident_capacity(const void* kernel, int threads, int* cap) {
 }
 
 template <class T, int EPI>
-int launch_persistent(ng::GemmParams p, hipStream_t s, const char* what) {
+ng_status launch_persistent(ng::GemmParams p, hipStream_t s, const char* what) {
   p.tiles_m = (p.M + T::BM - 1) / T::BM;
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
   const long long total = (long long)p.tiles_m * p.tiles_n;
   int cap = 0;
-  int st = resident_capacity((const void*)ng::gemm_persistent_kernel<T, EPI>, T::NT, &cap);
+  ng_status st = resident_capacity((const void*)ng::gemm_persistent_kernel<T, EPI>, T::NT, &cap);
   if (st) return st;
   const unsigned grid = (unsigned)(total < cap ? total : cap);
+  tile_order(total, &p.order_a, &p.order_c);
   hipLaunchKernelGGL((ng::gemm_persistent_kernel<T, EPI>), dim3(grid), dim3(T::NT), 0, s, p);
   return launched(what);
 }
 
 template <class T, bool LN, bool RES, bool BWD = false>
-int launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
+ng_status launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   p.tiles_m = (p.M + T::BM - 1) / T::BM;
   p.tiles_n = (p.N + T::BN - 1) / T::BN;
   int cap = 0;
-  int st = resident_capacity((const void*)ng::gemm_xwg_kernel<T, LN, RES, BWD>, T::NT, &cap);
+  ng_status st = resident_capacity((const void*)ng::gemm_xwg_kernel<T, LN, RES, BWD>, T::NT, &cap);
   if (st) return st;
   if (p.tiles_n > cap)
     return fail(NG_ERR_UNSUPPORTED, "row of %d tiles exceeds %d co-resident workgroups",
@@ -220,6 +248,7 @@ int launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   if (R > p.tiles_m) R = p.tiles_m;
   p.iters = (p.tiles_m + R - 1) / R;
   const unsigned grid = (unsigned)(R * p.tiles_n);
+  tile_order(grid, &p.order_a, &p.order_c);
   // A plain launch: the grid never exceeds what the device holds at once, so
   // on a device not shared with another such grid all workgroups become
   // resident.  (A cooperative launch would guarantee it even then, but was
@@ -239,7 +268,7 @@ size_t xwg_bytes(int64_t M, int64_t N) {
 // per row block, N <= 256 one 128 x 256 workgroup, wider rows the
 // cross-workgroup grid.
 template <bool LN, bool RES>
-int launch_norm(ng::GemmParams p, bool kn, bool local, hipStream_t s, const char* what) {
+ng_status launch_norm(ng::GemmParams p, bool kn, bool local, hipStream_t s, const char* what) {
   constexpr int EPI = RES ? (LN ? ng::EPI_ROW_LN_RES : ng::EPI_ROW_RMS_RES)
                           : (LN ? ng::EPI_ROW_LN : ng::EPI_ROW_RMS);
   if (local && p.N <= 128)
@@ -254,11 +283,11 @@ int launch_norm(ng::GemmParams p, bool kn, bool local, hipStream_t s, const char
 
 // Shared by ng_gemm_rmsnorm / ng_gemm_layernorm and the residual forms
 // (R non-NULL).
-int gemm_norm(const void* A, const void* B, const void* R, const void* gamma, const void* beta,
+ng_status gemm_norm(const void* A, const void* B, const void* R, const void* gamma, const void* beta,
               void* C, void* S_out, int64_t M, int64_t N, int64_t K, int b_layout, float eps,
               float* mean_out, float* rstd_out, void* ws, size_t ws_bytes, hipStream_t s,
               int kind, bool residual, const char* what) {
-  int st = check_gemm(A, B, C, M, N, K, b_layout);
+  ng_status st = check_gemm(A, B, C, M, N, K, b_layout);
   if (!st) st = check_eps(eps);
   if (!st) st = check_vec(gamma, "gamma", 16);
   if (!st) st = check_vec(beta, "beta", 16);
@@ -302,9 +331,9 @@ int gemm_norm(const void* A, const void* B, const void* R, const void* gamma, co
 
 extern "C" {
 
-int ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N,
+ng_status ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N,
                          int64_t K, int b_layout, float eps, float* rstd_out, void* stream) {
-  int st = check_gemm(A, B, C, M, N, K, b_layout);
+  ng_status st = check_gemm(A, B, C, M, N, K, b_layout);
   if (!st) st = check_eps(eps);
   if (!st) st = check_vec(rstd_out, "rstd_out", 4);
   if (st) return st;
@@ -320,7 +349,7 @@ int ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t
             : launch_persistent<TLarge<false>, ng::EPI_LAZY>(p, s, "ng_rmsnorm_gemm_lazy");
 }
 
-int ng_lazy_fold_affine(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
+ng_status ng_lazy_fold_affine(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
                         ng_bf16* B_folded, float* bias, int64_t K, int64_t N, int b_layout,
                         void* stream) {
   if (!B || !B_folded) return fail(NG_ERR_INVALID_ARG, "B and B_folded must be non-NULL");
@@ -331,7 +360,7 @@ int ng_lazy_fold_affine(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* b
                 (long long)N);
   if (b_layout != NG_B_KN && b_layout != NG_B_NK)
     return fail(NG_ERR_INVALID_ARG, "b_layout must be NG_B_KN or NG_B_NK (got %d)", b_layout);
-  int st = check_vec(gamma, "gamma", 16);
+  ng_status st = check_vec(gamma, "gamma", 16);
   if (!st) st = check_vec(beta, "beta", 16);
   if (!st) st = check_vec(bias, "bias", 4);
   if (st) return st;
@@ -364,10 +393,10 @@ int ng_lazy_fold_affine(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* b
   return launched("ng_lazy_fold_affine");
 }
 
-int ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded, const float* bias,
+ng_status ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded, const float* bias,
                                 ng_bf16* C, int64_t M, int64_t N, int64_t K, int b_layout,
                                 float eps, float* rstd_out, void* stream) {
-  int st = check_gemm(A, B_folded, C, M, N, K, b_layout);
+  ng_status st = check_gemm(A, B_folded, C, M, N, K, b_layout);
   if (!st) st = check_eps(eps);
   if (!st) st = check_vec(bias, "bias", 16);
   if (!st) st = check_vec(rstd_out, "rstd_out", 4);
@@ -393,7 +422,7 @@ int ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded, const
             : launch_persistent<TLarge<false>, ng::EPI_LAZY_BIAS>(p, s, what);
 }
 
-int ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,
+ng_status ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,
                     int64_t M, int64_t N, int64_t K, int b_layout, float eps, float* rstd_out,
                     void* workspace, size_t workspace_bytes, void* stream) {
   return gemm_norm(A, B, nullptr, gamma, nullptr, C, nullptr, M, N, K, b_layout, eps, nullptr,
@@ -401,7 +430,7 @@ int ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng
                    "ng_gemm_rmsnorm");
 }
 
-int ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
+ng_status ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
                       const ng_bf16* beta, ng_bf16* C, int64_t M, int64_t N, int64_t K,
                       int b_layout, float eps, float* mean_out, float* rstd_out, void* workspace,
                       size_t workspace_bytes, void* stream) {
@@ -410,7 +439,7 @@ int ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
                    "ng_gemm_layernorm");
 }
 
-int ng_gemm_add_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
+ng_status ng_gemm_add_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
                         const ng_bf16* gamma, ng_bf16* C, ng_bf16* S_out, int64_t M, int64_t N,
                         int64_t K, int b_layout, float eps, float* rstd_out, void* workspace,
                         size_t workspace_bytes, void* stream) {
@@ -419,7 +448,7 @@ int ng_gemm_add_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
                    "ng_gemm_add_rmsnorm");
 }
 
-int ng_gemm_add_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
+ng_status ng_gemm_add_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
                           const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* C, ng_bf16* S_out,
                           int64_t M, int64_t N, int64_t K, int b_layout, float eps,
                           float* mean_out, float* rstd_out, void* workspace,
@@ -429,9 +458,9 @@ int ng_gemm_add_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
                    "ng_gemm_add_layernorm");
 }
 
-int ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+ng_status ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
             int b_layout, void* stream) {
-  int st = check_gemm(A, B, C, M, N, K, b_layout);
+  ng_status st = check_gemm(A, B, C, M, N, K, b_layout);
   if (st) return st;
   if (M == 0) return ok();
   ng::GemmParams p = make_params(A, B, C, M, N, K, 0.f);
@@ -449,7 +478,7 @@ int ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N
 namespace {
 
 // Launch shape of the norm kernel for p.cols (rows of up to 65536 columns).
-int launch_norm_rows(const ng::NormParams& p, hipStream_t s, bool residual, const char* what) {
+ng_status launch_norm_rows(const ng::NormParams& p, hipStream_t s, bool residual, const char* what) {
   const int64_t rows = p.rows;
   const int64_t nch = p.cols / 8;
 #define NG_NORM_LAUNCH(LPR, CPL)                                                              \
@@ -475,7 +504,7 @@ int launch_norm_rows(const ng::NormParams& p, hipStream_t s, bool residual, cons
 }
 
 // Shared by ng_norm and ng_add_norm (R non-NULL).
-int norm_rows(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng_bf16* beta,
+ng_status norm_rows(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng_bf16* beta,
               ng_bf16* Y, ng_bf16* S_out, int64_t rows, int64_t cols, int kind, float eps,
               float* mean_out, float* rstd_out, hipStream_t s, bool residual, const char* what) {
   if (rows != 0 && (!X || !Y)) return fail(NG_ERR_INVALID_ARG, "X and Y must be non-NULL");
@@ -494,7 +523,7 @@ int norm_rows(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng
     return fail(NG_ERR_INVALID_ARG, "kind must be NG_NORM_RMS or NG_NORM_LAYER");
   if (kind == NG_NORM_RMS && mean_out)
     return fail(NG_ERR_INVALID_ARG, "RMSNorm has no mean output");
-  int st = check_eps(eps);
+  ng_status st = check_eps(eps);
   if (!st) st = check_vec(gamma, "gamma", 16);
   if (!st) st = check_vec(beta, "beta", 16);
   if (!st) st = check_vec(mean_out, "mean_out", 4);
@@ -523,21 +552,21 @@ int norm_rows(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng
 
 extern "C" {
 
-int ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* Y,
+ng_status ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* Y,
             int64_t rows, int64_t cols, int kind, float eps, float* mean_out, float* rstd_out,
             void* stream) {
   return norm_rows(X, nullptr, gamma, beta, Y, nullptr, rows, cols, kind, eps, mean_out,
                    rstd_out, (hipStream_t)stream, false, "ng_norm");
 }
 
-int ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng_bf16* beta,
+ng_status ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng_bf16* beta,
                 ng_bf16* Y, ng_bf16* S_out, int64_t rows, int64_t cols, int kind, float eps,
                 float* mean_out, float* rstd_out, void* stream) {
   return norm_rows(X, R, gamma, beta, Y, S_out, rows, cols, kind, eps, mean_out, rstd_out,
                    (hipStream_t)stream, true, "ng_add_norm");
 }
 
-int ng_layernorm_gemm_fold(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
+ng_status ng_layernorm_gemm_fold(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
                            ng_bf16* B_folded, float* colsum, float* bias, int64_t K, int64_t N,
                            int b_layout, void* stream) {
   if (!colsum) return fail(NG_ERR_INVALID_ARG, "colsum must be non-NULL");
@@ -545,7 +574,7 @@ int ng_layernorm_gemm_fold(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16
   if (bias && !aligned(bias, 16)) return fail(NG_ERR_INVALID_ARG, "bias must be 16-byte aligned");
   if (beta && !bias) return fail(NG_ERR_INVALID_ARG, "beta needs a bias output");
   // bias = beta^T B (before B_folded may overwrite B), then B' = diag(gamma) B
-  int st = ng_lazy_fold_affine(B, gamma, beta, B_folded, bias, K, N, b_layout, stream);
+  ng_status st = ng_lazy_fold_affine(B, gamma, beta, B_folded, bias, K, N, b_layout, stream);
   if (st) return st;
   // colsum = 1^T B' over the folded (bf16-rounded) weights the product uses
   ng::FoldParams p{};
@@ -560,10 +589,10 @@ int ng_layernorm_gemm_fold(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16
   return launched("ng_layernorm_gemm_fold");
 }
 
-int ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, const float* colsum,
+ng_status ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, const float* colsum,
                               const float* bias, ng_bf16* C, int64_t M, int64_t N, int64_t K,
                               int b_layout, float eps, float* mean, float* rstd, void* stream) {
-  int st = check_gemm(A, B_folded, C, M, N, K, b_layout);
+  ng_status st = check_gemm(A, B_folded, C, M, N, K, b_layout);
   if (!st) st = check_eps(eps);
   if (st) return st;
   if (!colsum || !aligned(colsum, 16))
@@ -601,7 +630,7 @@ int ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, const f
             : launch_persistent<TLarge<false>, ng::EPI_PRE_LN>(p, s, what);
 }
 
-int ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
+ng_status ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
                                          const float* rstd, ng_bf16* dA, int64_t M, int64_t N,
                                          int64_t K, int b_layout, void* workspace,
                                          size_t workspace_bytes, void* stream) {
@@ -611,7 +640,7 @@ int ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, con
   if (b_layout != NG_B_KN && b_layout != NG_B_NK)
     return fail(NG_ERR_INVALID_ARG, "b_layout must be NG_B_KN or NG_B_NK (got %d)", b_layout);
   const int lay = b_layout == NG_B_KN ? NG_B_NK : NG_B_KN;
-  int st = check_gemm(dC, B, dA, M, K, N, lay);
+  ng_status st = check_gemm(dC, B, dA, M, K, N, lay);
   if (st) return st;
   if (M != 0 && (!A || !rstd)) return fail(NG_ERR_INVALID_ARG, "A and rstd must be non-NULL");
   if (!aligned(A, 16)) return fail(NG_ERR_INVALID_ARG, "A must be 16-byte aligned");
@@ -641,7 +670,7 @@ int ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, con
             : launch_xwg<TLarge<false>, false, false, true>(p, s, what);
 }
 
-int ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* dC, const float* rstd,
+ng_status ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* dC, const float* rstd,
                                           ng_bf16* dB, int64_t M, int64_t N, int64_t K,
                                           int b_layout, void* stream) {
   if (M != 0 && (!A || !dC || !rstd)) return fail(NG_ERR_INVALID_ARG, "A, dC and rstd must be non-NULL");
@@ -680,7 +709,7 @@ int ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* dC, co
   p.row_rstd = rstd;
   p.C = (uint16_t*)dB;
   p.K = (int)M;
-  p.spin_limit = 1 << 20;
+  p.spin_limit = wait_spins();
   if (b_layout == NG_B_KN) {
     p.A = (const uint16_t*)A;
     p.B = (const uint16_t*)dC;
@@ -695,7 +724,7 @@ int ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* dC, co
   return launch_persistent<TWgrad<2>, ng::EPI_NONE>(p, s, what);
 }
 
-int ng_gemm_at(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+ng_status ng_gemm_at(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
                void* stream) {
   if (M != 0 && N != 0 && (!A || !B || !C))
     return fail(NG_ERR_INVALID_ARG, "A, B and C must be non-NULL");
@@ -719,11 +748,11 @@ int ng_gemm_at(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
-  p.spin_limit = 1 << 20;
+  p.spin_limit = wait_spins();
   return launch_persistent<TWgrad<0>, ng::EPI_NONE>(p, (hipStream_t)stream, "ng_gemm_at");
 }
 
-int ng_rmsnorm_backward(const ng_bf16* dY, const ng_bf16* X, const float* rstd, ng_bf16* dX,
+ng_status ng_rmsnorm_backward(const ng_bf16* dY, const ng_bf16* X, const float* rstd, ng_bf16* dX,
                         int64_t rows, int64_t cols, void* stream) {
   if (rows != 0 && (!dY || !X || !rstd || !dX))
     return fail(NG_ERR_INVALID_ARG, "dY, X, rstd and dX must be non-NULL");
@@ -773,7 +802,7 @@ size_t ng_workspace_bytes(int op, int64_t M, int64_t N, int64_t K) {
   return xwg_bytes(M, N);
 }
 
-int ng_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
+ng_status ng_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
   if (!workspace || !aligned(workspace, 256))
     return fail(NG_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
   if (workspace_bytes % 4 != 0) return fail(NG_ERR_INVALID_ARG, "workspace size must be a multiple of 4");
@@ -789,7 +818,7 @@ int ng_workspace_reset(void* workspace, size_t workspace_bytes, void* stream) {
   return launched("ng_workspace_reset");
 }
 
-int ng_workspace_status(const void* workspace, void* stream) {
+ng_status ng_workspace_status(const void* workspace, void* stream) {
   if (!workspace || !aligned(workspace, 256))
     return fail(NG_ERR_INVALID_ARG, "workspace must be non-NULL and 256-byte aligned");
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);
@@ -801,7 +830,7 @@ int ng_workspace_status(const void* workspace, void* stream) {
   return ok();
 }
 
-const char* ng_status_string(int status) {
+const char* ng_status_string(ng_status status) {
   switch (status) {
     case NG_OK: return "NG_OK";
     case NG_ERR_INVALID_ARG: return "NG_ERR_INVALID_ARG";
@@ -814,5 +843,28 @@ const char* ng_status_string(int status) {
 }
 
 const char* ng_last_error(void) { return g_err; }
+
+ng_status ng_set_debug_option(int option, int64_t value) {
+  switch (option) {
+    case NG_DEBUG_WAIT_SPINS:
+      if (value < -1 || value > (int64_t(1) << 30))
+        return fail(NG_ERR_INVALID_ARG, "wait bound must be -1 or in 0 .. 2^30");
+      g_wait_spins.store((int)value, std::memory_order_relaxed);
+      return ok();
+    case NG_DEBUG_ROW_LOCAL_MAX:
+      if (value < -1 || value > 256)
+        return fail(NG_ERR_INVALID_ARG, "row-local maximum must be -1 or in 0 .. 256");
+      g_row_local_max.store((int)value, std::memory_order_relaxed);
+      return ok();
+    case NG_DEBUG_TILE_ORDER:
+      if (value != NG_TILE_ORDER_NATURAL && value != NG_TILE_ORDER_REVERSED &&
+          value != NG_TILE_ORDER_SHUFFLED)
+        return fail(NG_ERR_INVALID_ARG, "unknown tile order %lld", (long long)value);
+      g_tile_order.store((int)value, std::memory_order_relaxed);
+      return ok();
+    default:
+      return fail(NG_ERR_INVALID_ARG, "unknown debug option %d", option);
+  }
+}
 
 }  // extern "C"

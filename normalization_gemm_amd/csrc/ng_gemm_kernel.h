@@ -120,7 +120,19 @@ struct GemmParams {
   int tiles_m, tiles_n;
   int iters;       // persistent grid: tile rounds
   int spin_limit;  // persistent grid: bounded wait (iterations of ~1 us)
+  // Order in which the grid walks its tiles: tile t is taken as
+  // (order_a * t + order_c) mod total, a bijection since order_a is coprime
+  // to total.  (1, 0) is the natural order; other values exist to check that
+  // results do not depend on which workgroup reaches a tile first.
+  int order_a, order_c;
 };
+
+// Tile index t of a walk over `total` tiles in the launch's tile order.
+__device__ __forceinline__ int ordered_tile(const GemmParams& p, int t, int total) {
+  if (p.order_a == 1 && p.order_c == 0) return t;
+  return (int)(((uint64_t)(uint32_t)p.order_a * (uint64_t)(uint32_t)t + (uint32_t)p.order_c) %
+               (uint64_t)(uint32_t)total);
+}
 
 // KN: B stored [K, N] (else [N, K]).  AKM: A stored [K, M] (the reduction
 // index is A's storage row: the weight-gradient products), read like B[K, N].
@@ -1281,7 +1293,7 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(16))) char smem[T::LDS];
   lds_char* lds = lds_base(smem);
   const int total = p.tiles_m * p.tiles_n;
-  const int t = xcd_contiguous(blockIdx.x, total);
+  const int t = ordered_tile(p, xcd_contiguous(blockIdx.x, total), total);
   int tm, tn;
   grouped_tile(t, p.tiles_m, p.tiles_n, 4, tm, tn);
   process_tile<T, EPI>(p, lds, tm, tn);
@@ -1306,7 +1318,7 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     int tm, tn;
-    grouped_tile(first, p.tiles_m, p.tiles_n, 4, tm, tn);
+    grouped_tile(ordered_tile(p, first, total), p.tiles_m, p.tiles_n, 4, tm, tn);
     issue_prologue<T>(p, lds0, tm * T::BM, tn * T::BN, tid);
   }
   for (int t = first; t < total; t += G) {
@@ -1317,7 +1329,7 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / T::WN, wn = wave % T::WN;
     int tm, tn;
-    grouped_tile(t, p.tiles_m, p.tiles_n, 4, tm, tn);
+    grouped_tile(ordered_tile(p, t, total), p.tiles_m, p.tiles_n, 4, tm, tn);
     const int m_base = tm * T::BM, n_base = tn * T::BN;
     const int ax = (epi_lazy(EPI) && lazy_split<T>()) ? wn : 0;
     f32x4 acc[T::FM][T::FN];
@@ -1332,7 +1344,7 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     tile_scale<T, EPI>(p, acc, ss, lds, m_base, n_base, tn, wm, wn, lane, ax, mean, rstd);
     if (t + G < total) {
       int tm2, tn2;
-      grouped_tile(t + G, p.tiles_m, p.tiles_n, 4, tm2, tn2);
+      grouped_tile(ordered_tile(p, t + G, total), p.tiles_m, p.tiles_n, 4, tm2, tn2);
       issue_prologue<T>(p, lds0, tm2 * T::BM, tn2 * T::BN, tid);
     }
     tile_store<T, EPI>(p, acc, mean, rstd, aff, bias, lds, m_base, n_base, wave, wm, wn, lane,
@@ -1376,8 +1388,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t xwg_fin_rsrc(const GemmParams&
   return make_rsrc(p.ws + XwgLayout::fin_off(p.tiles_m, p.tiles_n, T::BM) + (size_t)tm * blk, blk);
 }
 
-// 16-byte sc1 load of a tagged entry, repeated until both halves carry `tag`
-// (or the bounded wait gives up and raises the error word).
+// 16-byte sc1 load of a tagged entry, repeated until both halves carry `tag`.
+// If the bounded wait gives up, the error word is raised and the entry reads
+// as NaN, so that every statistic and output element that depends on it is
+// NaN: an output of a failed exchange can never look plausible.
 __device__ __forceinline__ u32x4 xwg_poll(const GemmParams& p, __amdgpu_buffer_rsrc_t rs,
                                           uint32_t off, uint32_t tag) {
   u32x4 v;
@@ -1387,6 +1401,7 @@ __device__ __forceinline__ u32x4 xwg_poll(const GemmParams& p, __amdgpu_buffer_r
     if (v[1] == tag && v[3] == tag) break;
     if (++spins > p.spin_limit) {
       store_agent((int*)(p.ws + XwgLayout::kErr), 1);
+      v = u32x4{0x7FC00000u, tag, 0x7FC00000u, tag};
       break;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -1504,7 +1519,7 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
   const uint32_t lds0 = lds_addr_of(lds);
   const int G = gridDim.x;
   const int R = G / p.tiles_n;
-  const int j = (G % 8 == 0) ? xcd_contiguous(blockIdx.x, G) : (int)blockIdx.x;
+  const int j = ordered_tile(p, (G % 8 == 0) ? xcd_contiguous(blockIdx.x, G) : (int)blockIdx.x, G);
   const int gh = (R % 4 == 0) ? 4 : ((R % 2 == 0) ? 2 : 1);
   int rb_in, tn;
   grouped_tile(j, R, p.tiles_n, gh, rb_in, tn);

@@ -53,7 +53,7 @@ def _f64(x) -> np.ndarray:
     x = np.asarray(x)
     if x.dtype == np.uint16:
         return bf16_to_f64(x)
-    return x.astype(np.float64)
+    return np.asarray(x, dtype=np.float64)
 
 
 def gemm(A, B) -> np.ndarray:

@@ -284,3 +284,63 @@ def test_package_has_no_cpu_fallback():
         ng.rmsnorm_gemm_lazy(A, A)
     with pytest.raises(ValueError):
         ng.norm(A, "rms")
+
+
+K_MAX = 1 << 22  # longest row of A [M, K] or B [N, K] a tile reads (header)
+
+
+@pytest.mark.parametrize("lay", [0, 1])
+def test_k_limit_at_the_boundary(lay):
+    # 255 * 2K + 128 must stay below the 2 GiB buffer range of a 256-row tile
+    assert 255 * 2 * K_MAX + 128 <= 0x7FFFFFF0
+    M, N = 64, 64
+    # just inside: validation passes (M = 0 stops before any launch)
+    assert lazy(M=0, N=N, K=K_MAX, lay=lay) == 0
+    assert _lib.ng_gemm(P, P2, P3, 0, N, K_MAX, lay, None) == 0
+    # just outside: unsupported, for every entry point that reads rows of length K
+    assert lazy(M=0, N=N, K=K_MAX + 8, lay=lay) == 2
+    assert "2^22" in _lib.ng_last_error()
+    assert lazy(M=M, N=N, K=K_MAX + 8, lay=lay) == 2
+    assert _lib.ng_gemm(P, P2, P3, M, N, K_MAX + 8, lay, None) == 2
+    assert _lib.ng_rmsnorm_gemm_lazy_affine(P, P2, None, P3, M, N, K_MAX + 8, lay, 1e-6, None,
+                                            None) == 2
+    assert _lib.ng_gemm_rmsnorm(P, P2, None, P3, M, N, K_MAX + 8, lay, 1e-6, None, None, 0,
+                                None) == 2
+    assert _lib.ng_gemm_layernorm(P, P2, None, None, P3, M, 4096, K_MAX + 8, lay, 1e-5, None,
+                                  None, P, 1 << 20, None) == 2
+    assert _lib.ng_gemm_add_rmsnorm(P, P2, P4, None, P3, None, M, N, K_MAX + 8, lay, 1e-6, None,
+                                    None, 0, None) == 2
+    # the input gradient's product reads rows of dC, of length N (forward)
+    assert _lib.ng_rmsnorm_gemm_lazy_backward_input(P, P2, P5, P4, P3, M, K_MAX + 8, 64, lay,
+                                                    None, 0, None) == 2
+
+
+def test_weight_gradient_products_take_long_reductions():
+    # A stored [K, M] (the reduction over storage rows): K up to 2^24 passes
+    # validation (K reaches no row offset); checked without a launch (M, N
+    # fail on alignment instead when they are set wrong)
+    assert _lib.ng_gemm_at(P, P2, P3, 64, 64, (1 << 24) + 1, None) == 1   # K > 2^24
+    assert _lib.ng_gemm_at(P, P2, P3, 60, 64, 1 << 24, None) == 2         # M % 8, K ok
+    assert _lib.ng_rmsnorm_gemm_lazy_backward_weight(P, P2, P3, P4, 1 << 24, 100, 64, 0,
+                                                     None) == 2           # N % 8, M ok
+
+
+def test_debug_options():
+    f = _lib.ng_set_debug_option
+    assert f(_lib.NG_DEBUG_WAIT_SPINS, -2) == 1
+    assert f(_lib.NG_DEBUG_WAIT_SPINS, (1 << 30) + 1) == 1
+    assert f(_lib.NG_DEBUG_ROW_LOCAL_MAX, 257) == 1
+    assert f(_lib.NG_DEBUG_TILE_ORDER, 3) == 1
+    assert f(99, 0) == 1
+    # the row-local maximum moves the workspace boundary, and is restored
+    assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 1000, 256, 64) == 0
+    assert f(_lib.NG_DEBUG_ROW_LOCAL_MAX, 0) == 0
+    try:
+        assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 1000, 256, 64) > 0
+    finally:
+        assert f(_lib.NG_DEBUG_ROW_LOCAL_MAX, -1) == 0
+    assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 1000, 256, 64) == 0
+    for v in (1, 2, 0):
+        assert f(_lib.NG_DEBUG_TILE_ORDER, v) == 0
+    assert f(_lib.NG_DEBUG_WAIT_SPINS, 0) == 0
+    assert f(_lib.NG_DEBUG_WAIT_SPINS, -1) == 0
