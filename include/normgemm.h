@@ -205,6 +205,29 @@ ng_status ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* g
                       size_t workspace_bytes, void* stream);
 
 /*
+ * ng_gemm_layernorm for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same operation, arguments and results, with no workspace
+ * argument.  Rows wider than one workgroup tile exchange their statistics
+ * through a scratch array of NG_NOALLOC_SCRATCH_BYTES (16 MiB) that the
+ * library keeps in static device memory, one per device, until the process
+ * ends.  The call allocates nothing.  Shapes whose exchange needs more than
+ * that (ng_workspace_bytes(NG_OP_GEMM_LAYERNORM, M, N, K) > 16 MiB, e.g.
+ * more than 16128 rows at N = 16384) return NG_ERR_UNSUPPORTED.  The first
+ * call on a device takes the array's address there and, unless the stream is
+ * being captured, zero-fills it on `stream`.  Every call on one device shares
+ * that device's array: calls that may overlap on one device (e.g. on two
+ * streams without an ordering) race and must not be made; calls on one
+ * stream are ordered and fine.  A wait that gives up leaves NaN in the rows
+ * it affects (no status word is exposed for this variant).
+ */
+#define NG_NOALLOC_SCRATCH_BYTES (16u << 20)
+ng_status ng_gemm_layernorm_noalloc(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
+                                    const ng_bf16* beta, ng_bf16* C, int64_t M, int64_t N,
+                                    int64_t K, int b_layout, float eps, float* mean_out,
+                                    float* rstd_out, void* stream);
+
+/*
  * Residual connection followed by a post-norm ("Free normalization fusion",
  * section "FlashNormAttention": residual add, then the post-norm, the residual
  * added to the product's accumulator; norm formulas as above):

@@ -72,6 +72,7 @@ _SIGNATURES = {
     "ng_status_string": (ctypes.c_char_p, [_I]),
     "ng_last_error": (ctypes.c_char_p, []),
     "ng_set_debug_option": (_I, [_I, _I64]),
+    "ng_gemm_layernorm_noalloc": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P]),
 }
 
 _lib = None

@@ -18,6 +18,14 @@
 #include "ng_norm_kernel.h"
 #include "ng_fold_kernel.h"
 
+// Scratch of ng_gemm_layernorm_noalloc: the cross-workgroup exchange's
+// workspace in static device memory, one copy per device, held until the
+// process ends.  Zero when the code object is loaded (static storage).  Host
+// code never uses the name as an address: each device's address comes from
+// hipGetSymbolAddress (noalloc_scratch below).
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
 namespace {
 
 thread_local char g_err[512];
@@ -283,10 +291,11 @@ ng_status launch_norm(ng::GemmParams p, bool kn, bool local, hipStream_t s, cons
 
 // Shared by ng_gemm_rmsnorm / ng_gemm_layernorm and the residual forms
 // (R non-NULL).
-ng_status gemm_norm(const void* A, const void* B, const void* R, const void* gamma, const void* beta,
-              void* C, void* S_out, int64_t M, int64_t N, int64_t K, int b_layout, float eps,
-              float* mean_out, float* rstd_out, void* ws, size_t ws_bytes, hipStream_t s,
-              int kind, bool residual, const char* what) {
+// Argument checks of the epilogue norms (everything but the workspace).
+ng_status check_gemm_norm(const void* A, const void* B, const void* R, const void* gamma,
+                          const void* beta, const void* C, const void* S_out, int64_t M, int64_t N,
+                          int64_t K, int b_layout, float eps, const float* mean_out,
+                          const float* rstd_out, bool residual) {
   ng_status st = check_gemm(A, B, C, M, N, K, b_layout);
   if (!st) st = check_eps(eps);
   if (!st) st = check_vec(gamma, "gamma", 16);
@@ -301,6 +310,16 @@ ng_status gemm_norm(const void* A, const void* B, const void* R, const void* gam
     if (S_out && M != 0 && S_out == C)
       return fail(NG_ERR_INVALID_ARG, "S_out and C must be different buffers");
   }
+  return NG_OK;
+}
+
+ng_status gemm_norm(const void* A, const void* B, const void* R, const void* gamma, const void* beta,
+              void* C, void* S_out, int64_t M, int64_t N, int64_t K, int b_layout, float eps,
+              float* mean_out, float* rstd_out, void* ws, size_t ws_bytes, hipStream_t s,
+              int kind, bool residual, const char* what) {
+  ng_status st = check_gemm_norm(A, B, R, gamma, beta, C, S_out, M, N, K, b_layout, eps, mean_out,
+                                 rstd_out, residual);
+  if (st) return st;
   const bool local = N <= row_local_max();
   if (!local && M > 0) {
     const size_t need = xwg_bytes(M, N);
@@ -327,9 +346,83 @@ ng_status gemm_norm(const void* A, const void* B, const void* R, const void* gam
             : launch_norm<false, false>(p, kn, local, s, what);
 }
 
+// Per-device address of `scratch`, taken once per device on the first
+// no-allocation call there (with that device current), followed by a zero
+// fill on the caller's stream unless the stream is being captured into a
+// graph (the array is zero from the load anyway; the fill makes the start
+// state explicit without putting a fill into a captured graph).
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+  const char* step = "";
+};
+ScratchSlot g_scratch_slot[64];
+
+ng_status noalloc_scratch(hipStream_t s, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(NG_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(NG_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  ScratchSlot& sl = g_scratch_slot[dev];
+  std::call_once(sl.once, [&] {
+    void* p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      sl.err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      sl.step = "hipGetSymbolAddress";
+      return;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+      (void)hipGetLastError();
+      cs = hipStreamCaptureStatusActive;  // unknown: do not enqueue the fill
+    }
+    if (cs == hipStreamCaptureStatusNone) {
+      hipLaunchKernelGGL(ng::fill_zero_kernel, dim3(1024), dim3(256), 0, s, (ng::u32x4*)p,
+                         kNoallocScratchBytes / 16, (uint32_t*)nullptr, (size_t)0);
+      e = hipGetLastError();
+      if (e != hipSuccess) {
+        sl.err = e;
+        sl.step = "zero fill";
+        return;
+      }
+    }
+    sl.ptr = p;
+  });
+  if (sl.err != hipSuccess)
+    return fail(NG_ERR_HIP, "scratch set-up (%s) failed: %s", sl.step, hipGetErrorString(sl.err));
+  *out = sl.ptr;
+  return NG_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+ng_status ng_gemm_layernorm_noalloc(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
+                                    const ng_bf16* beta, ng_bf16* C, int64_t M, int64_t N,
+                                    int64_t K, int b_layout, float eps, float* mean_out,
+                                    float* rstd_out, void* stream) {
+  ng_status st = check_gemm_norm(A, B, nullptr, gamma, beta, C, nullptr, M, N, K, b_layout, eps,
+                                 mean_out, rstd_out, false);
+  if (st) return st;
+  void* ws = nullptr;
+  size_t wsb = 0;
+  if (M > 0 && N > row_local_max()) {
+    const size_t need = xwg_bytes(M, N);
+    if (need > kNoallocScratchBytes)
+      return fail(NG_ERR_UNSUPPORTED,
+                  "this shape's row exchange needs %zu bytes; the no-allocation variant holds %zu "
+                  "(use ng_gemm_layernorm with a workspace)",
+                  need, kNoallocScratchBytes);
+    st = noalloc_scratch((hipStream_t)stream, &ws);
+    if (st) return st;
+    wsb = kNoallocScratchBytes;
+  }
+  return gemm_norm(A, B, nullptr, gamma, beta, C, nullptr, M, N, K, b_layout, eps, mean_out,
+                   rstd_out, ws, wsb, (hipStream_t)stream, ng::NORM_LAYER, false,
+                   "ng_gemm_layernorm_noalloc");
+}
 
 ng_status ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N,
                          int64_t K, int b_layout, float eps, float* rstd_out, void* stream) {
