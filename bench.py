@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="workload name, or 'all' for one line per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-load-readings", action="store_true",
+                    help="skip the clock/power readings under load (about a second of extra "
+                         "fused calls; for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -618,7 +621,8 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
                                                   "s" if products == 2 else "", t_total)}
 
 
-def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: float):
+def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: float,
+        load_readings: bool = True):
     import numpy as np
     torch_mod = __import__("torch")
     b = Bench(w)
@@ -659,7 +663,8 @@ def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: f
     roof["algorithmic_bytes"] = algorithmic_bytes(w)
     hidden = (t_gemm + t_norm - t_fused) / t_norm * 100.0
     # clock and power while the fused kernel runs (about a second of calls)
-    load = readings_under_load(b.fused, max(50, int(1.0 / max(t_fused * 1e-3, 1e-6))))
+    load = (readings_under_load(b.fused, max(50, int(1.0 / max(t_fused * 1e-3, 1e-6))))
+            if load_readings else None)
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -722,7 +727,8 @@ def main():
         small = w.flops < 1e11
         steps = args.steps if args.steps is not None else (200 if small else 30)
         warmup = args.warmup if args.warmup is not None else 20
-        line = run(w, steps, warmup, not args.no_cpu_baseline, args.cpu_seconds)
+        line = run(w, steps, warmup, not args.no_cpu_baseline, args.cpu_seconds,
+                   not args.no_load_readings)
         print(json.dumps(line), flush=True)
 
 
