@@ -237,7 +237,13 @@ ng_status launch_persistent(ng::GemmParams p, hipStream_t s, const char* what) {
   ng_status st = resident_capacity((const void*)ng::gemm_persistent_kernel<T, EPI>, T::NT, &cap);
   if (st) return st;
   const unsigned grid = (unsigned)(total < cap ? total : cap);
-  tile_order(total, &p.order_a, &p.order_c);
+  // the Lazy kernels walk strips of column tiles (one row block each); the
+  // tile order permutes the strips
+  const long long walked =
+      ng::epi_lazy(EPI)
+          ? (long long)p.tiles_m * ((p.tiles_n + ng::kLazyStrip - 1) / ng::kLazyStrip)
+          : total;
+  tile_order(walked, &p.order_a, &p.order_c);
   hipLaunchKernelGGL((ng::gemm_persistent_kernel<T, EPI>), dim3(grid), dim3(T::NT), 0, s, p);
   return launched(what);
 }

@@ -1299,6 +1299,103 @@ __global__ void __launch_bounds__(T::NT) gemm_kernel(GemmParams p) {
   process_tile<T, EPI>(p, lds, tm, tn);
 }
 
+// Lazy Pre-Norm's walk of the persistent grid.  Every column tile of a row
+// block needs the same row scales, so each workgroup takes "strips" of
+// kLazyStrip consecutive column tiles of one row block and computes the sums
+// of squares (the Gram MFMAs) only on a strip's first tile; the strip's later
+// tiles reuse its rstd, computed from the same rows of A in the same order,
+// so the result does not depend on which tile computed it.  Strips are
+// numbered over the (row block, column group) grid in groups 8 row blocks
+// high, column-major inside a group, and workgroup w walks strips w, w + G,
+// ...: the 32 workgroups of an XCD then hold 8 row blocks x 4 column groups,
+// which reads as many A and B panels per round (12) as the 4 x 8 blocks of
+// the other walks.
+constexpr int kLazyStrip = 4;
+
+// The walk's tile number idx (strip idx / kLazyStrip, position idx %
+// kLazyStrip) of the workgroup whose first strip is `first`, advanced past
+// the positions of short strips (the last column group of a row) that fall
+// outside the matrix.  Returns false past the end of the walk.
+__device__ __forceinline__ bool lazy_strip_tile(const GemmParams& p, int first, int G, int& idx,
+                                                int& tm, int& tn) {
+  const int n_cg = (p.tiles_n + kLazyStrip - 1) / kLazyStrip;
+  const int strips = p.tiles_m * n_cg;
+  while (true) {
+    const int s = first + (idx / kLazyStrip) * G;
+    if (s >= strips) return false;
+    int cg;
+    grouped_tile(ordered_tile(p, s, strips), p.tiles_m, n_cg, 8, tm, cg);
+    tn = cg * kLazyStrip + idx % kLazyStrip;
+    if (tn < p.tiles_n) return true;
+    idx = (idx / kLazyStrip + 1) * kLazyStrip;  // rest of a short strip
+  }
+}
+
+// Persistent grid for Lazy Pre-Norm (EPI_LAZY, EPI_LAZY_BIAS) on the strip
+// walk above: a tile whose row block is the previous tile's runs the plain
+// k-loop and reuses the previous rstd (kept per accumulator fragment).
+template <class T, int EPI>
+__device__ __forceinline__ void lazy_persistent(const GemmParams& p, lds_char* lds) {
+  const uint32_t lds0 = lds_addr_of(lds);
+  const int G = gridDim.x;
+  const int first = (G % 8 == 0) ? xcd_contiguous(blockIdx.x, G) : (int)blockIdx.x;
+  int idx = 0, tm = 0, tn = 0;
+  bool have = lazy_strip_tile(p, first, G, idx, tm, tn);
+  if (have) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    issue_prologue<T>(p, lds0, tm * T::BM, tn * T::BN, tid);
+  }
+  int tm_prev = -1;
+  float rs_frag[T::FM];  // rstd of this lane's row in accumulator fragment f
+  bool first_tile = true;
+  while (have) {
+    // opaque thread id: keeps lane-dependent addresses from being hoisted
+    // out of the tile loop (where they would be spilled)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / T::WN, wn = wave % T::WN;
+    const int m_base = tm * T::BM, n_base = tn * T::BN;
+    const bool reuse = tm == tm_prev;
+    f32x4 acc[T::FM][T::FN];
+    float ss[T::FM];
+    float mean[T::FM], rstd[T::FM];
+    int ax;
+    if (reuse) {
+      mainloop<T, false>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, !first_tile);
+      ax = 0;
+      const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) {
+        mean[i] = 0.f;
+        rstd[i] = rs_frag[i];
+        const int m = m_base + wm * T::WTM + 16 * i + l16;
+        if (p.rstd_out && tn == 0 && wn == 0 && g == 0 && m < p.M) p.rstd_out[m] = rstd[i];
+      }
+    } else {
+      mainloop<T, true>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, !first_tile);
+      ax = lazy_split<T>() ? wn : 0;
+      tile_scale<T, EPI>(p, acc, ss, lds, m_base, n_base, tn, wm, wn, lane, ax, mean, rstd);
+#pragma unroll
+      for (int i = 0; i < T::FM; ++i) rs_frag[i ^ ax] = rstd[i];
+      tm_prev = tm;
+    }
+    Affine<T> aff;
+    Bias<T> bias;
+    load_columns<T, EPI>(p, n_base, wn, lane, aff, bias);
+    int idx2 = idx + 1, tm2 = 0, tn2 = 0;
+    const bool have2 = lazy_strip_tile(p, first, G, idx2, tm2, tn2);
+    if (have2) issue_prologue<T>(p, lds0, tm2 * T::BM, tn2 * T::BN, tid);
+    tile_store<T, EPI>(p, acc, mean, rstd, aff, bias, lds, m_base, n_base, wave, wm, wn, lane, ax);
+    idx = idx2;
+    tm = tm2;
+    tn = tn2;
+    have = have2;
+    first_tile = false;
+  }
+}
+
 // Persistent grid: gridDim.x workgroups (at most one round of resident
 // workgroups) walk the tile order with stride gridDim.x.  After a tile's
 // k-loop a workgroup computes the tile's row scales, issues the LDS transfers
@@ -1310,6 +1407,10 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
   static_assert(T::STG_OWN, "persistent tiles need their own output staging");
   __shared__ __attribute__((aligned(16))) char smem[T::LDS];
   lds_char* lds = lds_base(smem);
+  if constexpr (epi_lazy(EPI)) {
+    lazy_persistent<T, EPI>(p, lds);
+    return;
+  }
   const uint32_t lds0 = lds_addr_of(lds);
   const int G = gridDim.x;
   const int total = p.tiles_m * p.tiles_n;
