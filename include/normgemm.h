@@ -172,7 +172,8 @@ ng_status ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, c
  * that several workgroups share, then applying.)  Rows with N <= 256 are
  * normalized inside one workgroup; wider rows merge per-row fp32 partials
  * across workgroups through `workspace`, which must hold
- * ng_workspace_bytes(NG_OP_GEMM_RMSNORM, M, N, K) bytes (0 means none needed),
+ * ng_workspace_bytes(NG_OP_GEMM_RMSNORM, M, N, K) bytes (0 means none needed;
+ * at most ~7 MB: it holds one round of row blocks and stops growing with M),
  * be 256-byte aligned and be zero-filled before its first use (see
  * ng_workspace_reset); calls leave it ready for the next call.  One workspace
  * must not be used by two calls that may run concurrently.  Wide rows run a
@@ -211,9 +212,10 @@ ng_status ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* g
  * argument.  Rows wider than one workgroup tile exchange their statistics
  * through a scratch array of NG_NOALLOC_SCRATCH_BYTES (16 MiB) that the
  * library keeps in static device memory, one per device, until the process
- * ends.  The call allocates nothing.  Shapes whose exchange needs more than
- * that (ng_workspace_bytes(NG_OP_GEMM_LAYERNORM, M, N, K) > 16 MiB, e.g.
- * more than 16128 rows at N = 16384) return NG_ERR_UNSUPPORTED.  The first
+ * ends.  The call allocates nothing.  The array holds the exchange of every
+ * shape the other entry points accept (ng_workspace_bytes(
+ * NG_OP_GEMM_LAYERNORM, M, N, K) <= 16 MiB for any M); a shape that would
+ * need more returns NG_ERR_UNSUPPORTED.  The first
  * call on a device takes the array's address there and, unless the stream is
  * being captured, zero-fills it on `stream`.  Every call on one device shares
  * that device's array: calls that may overlap on one device (e.g. on two

@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <atomic>
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/normgemm.h"
@@ -255,10 +256,13 @@ ng_status launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   int cap = 0;
   ng_status st = resident_capacity((const void*)ng::gemm_xwg_kernel<T, LN, RES, BWD>, T::NT, &cap);
   if (st) return st;
-  if (p.tiles_n > cap)
+  const int resident = std::min(cap, ng::kXwgMaxResident);
+  if (p.tiles_n > resident)
     return fail(NG_ERR_UNSUPPORTED, "row of %d tiles exceeds %d co-resident workgroups",
-                p.tiles_n, cap);
-  int R = cap / p.tiles_n;  // row blocks per round
+                p.tiles_n, resident);
+  // row blocks per round (the workspace holds one slot per row block of a
+  // round, for at most kXwgMaxResident workgroups)
+  int R = resident / p.tiles_n;
   if (R > p.tiles_m) R = p.tiles_m;
   p.iters = (p.tiles_m + R - 1) / R;
   const unsigned grid = (unsigned)(R * p.tiles_n);
@@ -271,11 +275,16 @@ ng_status launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   return launched(what);
 }
 
+// Workspace of the cross-workgroup grid: one slot per row block of a round,
+// for as many row blocks as a round can hold (at most kXwgMaxResident
+// workgroups, and no more than the matrix has), one partial per row and
+// column tile.  It does not grow with M past one round.
 size_t xwg_bytes(int64_t M, int64_t N) {
   using T = TLarge<true>;
   const int tm = (int)((M + T::BM - 1) / T::BM);
   const int tn = (int)((N + T::BN - 1) / T::BN);
-  return ng::XwgLayout::bytes(tm, tn, T::BM);
+  const int slots = std::max(1, std::min(tm, ng::kXwgMaxResident / tn));
+  return ng::XwgLayout::bytes(slots, tn, T::BM);
 }
 
 // Strategy choice of the epilogue norms: N <= 128 one 256 x 128 workgroup

@@ -72,29 +72,38 @@ constexpr bool epi_ln(int e) { return e == EPI_ROW_LN || e == EPI_ROW_LN_RES; }
 constexpr bool epi_res(int e) { return e == EPI_ROW_RMS_RES || e == EPI_ROW_LN_RES; }
 enum NormKind { NORM_RMS = 0, NORM_LAYER = 1 };
 
-// Workspace layout of the cross-workgroup row norm (byte offsets).
+// Workspace layout of the cross-workgroup row norm (byte offsets).  A round
+// of the persistent grid covers R row blocks, one per "slot"; the entries of
+// a round go to its slots and the next round reuses them (safe: a workgroup
+// writes its next round's entries only after it has read every final of
+// this round's row block, which the other workgroups of the block publish
+// only after reading all of its partials).
 //   [0]        int error word (0 = ok, 1 = a wait timed out)
-//   [4]        uint call counter: a call's tag is its value + 1; the last
-//              workgroup of a call to finish stores the tag back
+//   [4]        uint tag base: round `it` of a call tags its entries base +
+//              1 + it; the last workgroup of a call to finish stores base +
+//              rounds back
 //   [8]        uint number of workgroups of the running call that finished
-//   [256]      partial[row_blocks][BM][tiles_n], 16 bytes per (row, column
+//   [256]      partial[slots][BM][tiles_n], 16 bytes per (row, column
 //              tile): {mean_t, tag, M2_t, tag} (LayerNorm) or
 //              {0, tag, sum x^2, tag} (RMSNorm)
-//   [fin_off]  final[row_blocks][BM], 16 bytes per row: {mean, tag, rstd, tag}
-// Each 8-byte half of an entry carries the tag of the call that wrote it, and
-// 8-byte accesses are single transactions, so a reader that finds its own
-// call's tag in both halves holds the whole entry.  Entries of earlier calls
-// never match, so nothing needs resetting between calls.
+//   [fin_off]  final[slots][BM], 16 bytes per row: {mean, tag, rstd, tag}
+// Each 8-byte half of an entry carries the tag of the round that wrote it,
+// and 8-byte accesses are single transactions, so a reader that finds its own
+// round's tag in both halves holds the whole entry.  Entries of earlier
+// rounds and calls never match, so nothing needs resetting between rounds or
+// calls.  The host sizes the workspace for min(tiles_m, kXwgMaxResident /
+// tiles_n) slots, at least as many as any launch uses.
+constexpr int kXwgMaxResident = 1024;
 struct XwgLayout {
   static constexpr size_t kErr = 0;
   static constexpr size_t kTag = 4;
   static constexpr size_t kDone = 8;
   static constexpr size_t kPart = 256;
-  static __host__ __device__ size_t fin_off(int row_blocks, int tiles_n, int bm) {
-    return kPart + (size_t)row_blocks * bm * tiles_n * 16u;
+  static __host__ __device__ size_t fin_off(int slots, int parts, int bm) {
+    return kPart + (size_t)slots * bm * parts * 16u;
   }
-  static __host__ __device__ size_t bytes(int row_blocks, int tiles_n, int bm) {
-    return fin_off(row_blocks, tiles_n, bm) + (size_t)row_blocks * bm * 16u;
+  static __host__ __device__ size_t bytes(int slots, int parts, int bm) {
+    return fin_off(slots, parts, bm) + (size_t)slots * bm * 16u;
   }
 };
 
@@ -788,10 +797,24 @@ __device__ __forceinline__ void combine_waves(float (&out)[T::FM], lds_char* lds
 // mode 0: sum x;  mode 1: sum (x - center[i])^2;  mode 2: sum x^2.
 // Result: out[i] for row wm*WTM + 16i + (lane & 15), same in all lanes of the group.
 template <class T>
+__device__ __forceinline__ void wave_row_sums(const f32x4 (&acc)[T::FM][T::FN],
+                                              const bool (&colv)[T::FN], int mode,
+                                              const float (&center)[T::FM], float (&out)[T::FM]);
+
+template <class T>
 __device__ __forceinline__ void tile_row_sums(const f32x4 (&acc)[T::FM][T::FN],
                                               const bool (&colv)[T::FN], int mode,
                                               const float (&center)[T::FM], float (&out)[T::FM],
                                               lds_char* lds, int wm, int wn, int lane) {
+  wave_row_sums<T>(acc, colv, mode, center, out);
+  combine_waves<T>(out, lds, wm, wn, lane);
+}
+
+// The same sums over this wave's columns only (no exchange between waves).
+template <class T>
+__device__ __forceinline__ void wave_row_sums(const f32x4 (&acc)[T::FM][T::FN],
+                                              const bool (&colv)[T::FN], int mode,
+                                              const float (&center)[T::FM], float (&out)[T::FM]) {
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
     float s = 0.f;
@@ -808,7 +831,6 @@ __device__ __forceinline__ void tile_row_sums(const f32x4 (&acc)[T::FM][T::FN],
     }
     out[i] = reduce_lane_groups(s);
   }
-  combine_waves<T>(out, lds, wm, wn, lane);
 }
 
 // Sum of per-wave row partials over the WN waves that share rows, through
@@ -902,12 +924,11 @@ __device__ __forceinline__ u32x2 tile_lds_frag(lds_char* lds, uint32_t region, i
                        8u * (uint32_t)(g & 1));
 }
 
-// Per-row sums of acc * X over the workgroup's columns, X the staged tile
-// (zero past N), combined across the waves sharing rows.
+// Per-row sums of acc * X over this wave's columns, X the staged tile (zero
+// past N).
 template <class T>
-__device__ __forceinline__ void tile_dot_sums(const f32x4 (&acc)[T::FM][T::FN], lds_char* lds,
-                                              int wave, int wm, int wn, int lane,
-                                              float (&out)[T::FM]) {
+__device__ __forceinline__ void wave_dot_sums(const f32x4 (&acc)[T::FM][T::FN], lds_char* lds,
+                                              int wave, int lane, float (&out)[T::FM]) {
   const uint32_t region = tile_lds_region<T>(wave);
 #pragma unroll
   for (int i = 0; i < T::FM; ++i) {
@@ -922,6 +943,15 @@ __device__ __forceinline__ void tile_dot_sums(const f32x4 (&acc)[T::FM][T::FN], 
     }
     out[i] = reduce_lane_groups(s);
   }
+}
+
+// The same sums over the workgroup's columns, combined across the waves
+// sharing rows.
+template <class T>
+__device__ __forceinline__ void tile_dot_sums(const f32x4 (&acc)[T::FM][T::FN], lds_char* lds,
+                                              int wave, int wm, int wn, int lane,
+                                              float (&out)[T::FM]) {
+  wave_dot_sums<T>(acc, lds, wave, lane, out);
   combine_waves<T>(out, lds, wm, wn, lane);
 }
 
@@ -1477,16 +1507,21 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
 // written and read with agent-scope (sc1) accesses, which bypass the per-XCD
 // L2.
 
-// sc1 buffer views of the row block's partials and final statistics.
+// sc1 buffer views of a slot's partials and final statistics (R slots,
+// parts partials per row).
 template <class T>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t xwg_part_rsrc(const GemmParams& p, int tm) {
-  const size_t blk = (size_t)T::BM * p.tiles_n * 16u;
-  return make_rsrc(p.ws + XwgLayout::kPart + (size_t)tm * blk, blk);
+__device__ __forceinline__ int xwg_parts(const GemmParams& p) { return p.tiles_n; }
+template <class T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xwg_part_rsrc(const GemmParams& p, int slot) {
+  const size_t blk = (size_t)T::BM * xwg_parts<T>(p) * 16u;
+  return make_rsrc(p.ws + XwgLayout::kPart + (size_t)slot * blk, blk);
 }
 template <class T>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t xwg_fin_rsrc(const GemmParams& p, int tm) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xwg_fin_rsrc(const GemmParams& p, int slot,
+                                                              int slots) {
   const size_t blk = (size_t)T::BM * 16u;
-  return make_rsrc(p.ws + XwgLayout::fin_off(p.tiles_m, p.tiles_n, T::BM) + (size_t)tm * blk, blk);
+  return make_rsrc(p.ws + XwgLayout::fin_off(slots, xwg_parts<T>(p), T::BM) + (size_t)slot * blk,
+                   blk);
 }
 
 // 16-byte sc1 load of a tagged entry, repeated until both halves carry `tag`.
@@ -1522,10 +1557,13 @@ __device__ __forceinline__ void chan_combine(float& n_a, float& mu_a, float& m2_
   n_a = nn;
 }
 
-// Step 2.  BWD: (0, sum acc * X) per row, X the staged forward input.
+// Step 2: the workgroup's slice of every row (its BN columns), reduced over
+// the tile: LayerNorm (mean_t, M2_t), RMSNorm (0, sum x^2); BWD (0, sum
+// acc * X), X the staged forward input.
 template <class T, bool LN, bool BWD = false>
 __device__ __forceinline__ void xwg_publish(const GemmParams& p, const f32x4 (&acc)[T::FM][T::FN],
-                                            lds_char* lds, int tm, int tn, int tid, uint32_t tag) {
+                                            lds_char* lds, int slot, int tn, int tid,
+                                            uint32_t tag) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int l16 = lane & 15, g = lane >> 4;
@@ -1537,45 +1575,47 @@ __device__ __forceinline__ void xwg_publish(const GemmParams& p, const f32x4 (&a
   } else {
     tile_stats<T, LN>(p, acc, lds, tn * T::BN, wm, wn, lane, s1, s2);
   }
-  const __amdgpu_buffer_rsrc_t prs = xwg_part_rsrc<T>(p, tm);
+  const int parts = xwg_parts<T>(p);
+  const __amdgpu_buffer_rsrc_t prs = xwg_part_rsrc<T>(p, slot);
   if (wn == 0 && g == 0) {
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
       const int r = wm * T::WTM + 16 * i + l16;
       const u32x4 v = {__float_as_uint(s1[i]), tag, __float_as_uint(s2[i]), tag};
-      __builtin_amdgcn_raw_buffer_store_b128(v, prs, (uint32_t)(r * p.tiles_n + tn) * 16u, 0, 16);
+      __builtin_amdgcn_raw_buffer_store_b128(v, prs, (uint32_t)(r * parts + tn) * 16u, 0, 16);
     }
   }
 }
 
 // Step 4.  Rows r0 .. r1-1 of the row block belong to this workgroup.  A row
-// is merged by `cpl` lanes (a power of two, at most 64, at least tiles_n when
-// tiles_n <= 64): lane li takes column tiles li, li+cpl, ... in order, then
-// the lanes combine pairwise, lower lanes first.  BWD: the row's plain sum is
-// published as is (in the rstd slot).
+// is merged by `cpl` lanes (a power of two, at most 64, at least tiles_n
+// when tiles_n <= 64): lane li takes column tiles li, li+cpl, ... in order,
+// then the lanes combine pairwise, lower lanes first.  BWD: the row's plain
+// sum is published as is (in the rstd slot).
 template <class T, bool LN, bool BWD = false>
-__device__ __forceinline__ void xwg_merge_rows(const GemmParams& p, int tm, int tn, int tid,
-                                               uint32_t tag) {
+__device__ __forceinline__ void xwg_merge_rows(const GemmParams& p, int slot, int slots, int tm,
+                                               int tn, int tid, uint32_t tag) {
   constexpr int NW = T::NT / 64;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_n = p.tiles_n;
+  const int parts = xwg_parts<T>(p);
   const int rpw = (T::BM + tiles_n - 1) / tiles_n;
   const int r0 = tn * rpw, r1 = min(T::BM, r0 + rpw);
   int cpl = 1;
-  while (cpl < tiles_n && cpl < 64) cpl <<= 1;
+  while (cpl < parts && cpl < 64) cpl <<= 1;
   const int rows_per_pass = 64 / cpl;
   const int sub = lane / cpl, li = lane % cpl;
-  const __amdgpu_buffer_rsrc_t prs = xwg_part_rsrc<T>(p, tm);
-  const __amdgpu_buffer_rsrc_t frs = xwg_fin_rsrc<T>(p, tm);
+  const __amdgpu_buffer_rsrc_t prs = xwg_part_rsrc<T>(p, slot);
+  const __amdgpu_buffer_rsrc_t frs = xwg_fin_rsrc<T>(p, slot, slots);
   const float inv_n = 1.0f / (float)p.N;
   for (int rb = r0 + wave * rows_per_pass; rb < r1; rb += NW * rows_per_pass) {
     const int row = rb + sub;
     const bool active = row < r1;
     float n = 0.f, mu = 0.f, m2 = 0.f;
     if (active) {
-      for (int t = li; t < tiles_n; t += cpl) {
-        const u32x4 v = xwg_poll(p, prs, (uint32_t)(row * tiles_n + t) * 16u, tag);
+      for (int t = li; t < parts; t += cpl) {
+        const u32x4 v = xwg_poll(p, prs, (uint32_t)(row * parts + t) * 16u, tag);
         if constexpr (LN) {
           chan_combine(n, mu, m2, (float)min(T::BN, p.N - t * T::BN), __uint_as_float(v[0]),
                        __uint_as_float(v[2]));
@@ -1624,9 +1664,9 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
   const int gh = (R % 4 == 0) ? 4 : ((R % 2 == 0) ? 2 : 1);
   int rb_in, tn;
   grouped_tile(j, R, p.tiles_n, gh, rb_in, tn);
-  const uint32_t tag =
-      __builtin_amdgcn_readfirstlane((uint32_t)load_agent((const int*)(p.ws + XwgLayout::kTag))) +
-      1u;
+  // tag base of this call; round `it` tags its entries base + 1 + it
+  const uint32_t base =
+      __builtin_amdgcn_readfirstlane((uint32_t)load_agent((const int*)(p.ws + XwgLayout::kTag)));
   if (rb_in < p.tiles_m) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
@@ -1643,6 +1683,7 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
     const int wm = wave / T::WN, wn = wave % T::WN;
     const int l16 = lane & 15;
     const int m_base = tm * T::BM, n_base = tn * T::BN;
+    const uint32_t tag = base + 1u + (uint32_t)it;
     f32x4 acc[T::FM][T::FN];
     float ss[T::FM];
     // (BWD: the previous tile's output stores precede this tile's first
@@ -1650,16 +1691,16 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
     mainloop<T, false>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, !BWD && it > 0);
     if constexpr (RES) add_residual<T>(p, acc, lds, lds0, m_base, n_base, wave, wm, wn, lane);
     if constexpr (BWD) load_tile_lds<T>(p, p.Xin, lds0, m_base, n_base, wave, wn, lane);
-    xwg_publish<T, LN, BWD>(p, acc, lds, tm, tn, tid, tag);
+    xwg_publish<T, LN, BWD>(p, acc, lds, rb_in, tn, tid, tag);
     Affine<T> aff;
     if constexpr (!BWD) {
       load_affine<T>(p, n_base, wn, lane, aff);
       if (tm + R < p.tiles_m) issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid);
     }
-    xwg_merge_rows<T, LN, BWD>(p, tm, tn, tid, tag);
+    xwg_merge_rows<T, LN, BWD>(p, rb_in, R, tm, tn, tid, tag);
     // step 5: (mean, rstd) of this wave's rows; BWD: (c, rstd) from the row's
     // sum of acc * X and the saved rstd
-    const __amdgpu_buffer_rsrc_t frs = xwg_fin_rsrc<T>(p, tm);
+    const __amdgpu_buffer_rsrc_t frs = xwg_fin_rsrc<T>(p, rb_in, R);
     float mean[T::FM], rstd[T::FM];
 #pragma unroll
     for (int i = 0; i < T::FM; ++i) {
@@ -1690,7 +1731,7 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
   if (threadIdx.x == 0) {
     int* done = (int*)(p.ws + XwgLayout::kDone);
     if (add_agent(done, 1) == G - 1) {
-      store_agent((int*)(p.ws + XwgLayout::kTag), (int)tag);
+      store_agent((int*)(p.ws + XwgLayout::kTag), (int)(base + (uint32_t)p.iters));
       store_agent(done, 0);
     }
   }

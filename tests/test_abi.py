@@ -112,16 +112,32 @@ def test_gemm_norm_workspace_checks():
     assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM, 1000, 4096, 512) == 0
 
 
+def _ws_formula(M, N):
+    # 256-byte header; then per slot (a row block of one round: at most
+    # 1024 co-resident workgroups, and no more than the matrix has) one
+    # 16-byte tagged partial per (row, column tile) and one 16-byte tagged
+    # (mean, rstd) per row
+    rb, tn = -(-M // 256), -(-N // 256)
+    slots = max(1, min(rb, 1024 // tn))
+    return 256 + slots * 256 * tn * 16 + slots * 256 * 16
+
+
 def test_workspace_size_formula():
-    # 256-byte header, then one 16-byte tagged partial per (row block, row,
-    # column tile) and one 16-byte tagged (mean, rstd) per row
-    M, N = 16384, 8192
-    rb, tn = M // 256, N // 256
-    expect = 256 + rb * 256 * tn * 16 + rb * 256 * 16
-    assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_RMSNORM, M, N, 4096) == expect
-    # ragged: 1000 rows -> 4 row blocks, 4100 columns -> 17 column tiles
-    expect = 256 + 4 * 256 * 17 * 16 + 4 * 256 * 16
-    assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 1000, 4100, 64) == expect
+    for M, N in [(16384, 8192), (8192, 16384), (1000, 4100), (300, 2048), (1 << 24, 512),
+                 (1 << 20, 65536)]:
+        assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_RMSNORM, M, N, 4096) == _ws_formula(M, N)
+    # it stops growing with M once a round's row blocks are covered
+    assert (_lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 1 << 24, 16384, 64) ==
+            _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 4096, 16384, 64))
+
+
+def test_no_allocation_scratch_holds_every_shape():
+    # the static scratch of ng_gemm_layernorm_noalloc (16 MiB) holds the
+    # exchange of every accepted shape (rows up to 2^24, rows of up to 65536
+    # columns)
+    worst = max(_lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 1 << 24, 8 * n, 64)
+                for n in range(33, 8193))
+    assert worst <= 16 << 20, worst
 
 
 def test_gemm_norm_argument_checks():
