@@ -634,17 +634,29 @@ __device__ __forceinline__ void wait_ktile(int after) {
   else wait_vmcnt<X>();
 }
 
-// prologue_issued: the first STAGES k-tiles were issued by the caller.
-// stores_after: the caller then issued exactly T::C_STORES further
+// prologue_issued: the first STAGES k-tiles were issued by the caller (or by
+// the previous tile's k-loop, see below).
+// stores_after: the caller then issued at least T::C_STORES further
 // vector-memory operations (the previous tile's output) before this call.
 // LAZY: ss[i] receives this lane's share of slot i's row sums of squares
 // (summed over the 4 lane groups they give the row's total over this wave's
 // A fragments; zero for slots the wave did not take).
+// Cross-tile prefetch (32-deep k-tiles only, nk >= STAGES): with nx_m >= 0
+// the sub-steps whose refill would lie past the end of this tile's k-loop
+// issue the first STAGES k-tiles of the next tile (m_base nx_m, n_base nx_n)
+// instead, into the stages this tile vacates, so that they land during this
+// tile's last k-tiles rather than behind its epilogue.  k-tile j of a tile
+// sits in stage (j + srot) % STAGES; the next tile's srot is (srot + nk) %
+// STAGES.  Every sub-step then issues STAGES - 2 k-tiles' worth of
+// transfers after the one awaited, tile after tile.  (A tile's epilogue
+// polls and loads wait for every earlier transfer, so transfers issued after
+// the k-loop would hold them up.)
 template <class T, bool LAZY>
 __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM][T::FN],
                                          float (&ss)[T::FM], lds_char* lds, uint32_t lds0,
                                          int m_base, int n_base, int tid,
-                                         bool prologue_issued = false, bool stores_after = false) {
+                                         bool prologue_issued = false, bool stores_after = false,
+                                         int srot = 0, int nx_m = -1, int nx_n = 0) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WN, wn = wave % T::WN;
@@ -664,6 +676,9 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   constexpr int ND = DmaPlan<T>::INS;
   constexpr int NR = FragReader<T>::ITEMS;
   const int nk = (p.K + T::BK - 1) / T::BK;
+  const bool xt = T::KK == 1 && nx_m >= 0 && nk >= T::STAGES;
+  // LDS byte offset of the stage that holds k-tile k
+  auto stg = [&](int k) { return (uint32_t)((k + srot) % T::STAGES) * T::STAGE; };
 
   if (!prologue_issued) issue_prologue<T>(p, lds0, m_base, n_base, tid);
   if (stores_after) wait_ktile<ND, T::STAGES, T::C_STORES>(min(nk, T::STAGES) - 1);
@@ -672,7 +687,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   __syncthreads();
   Frags<T> f0, f1;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) rd.read(f0, r, lds, 0, T::A_BYTES, 0);
+  for (int r = 0; r < NR; ++r) rd.read(f0, r, lds, stg(0), stg(0) + T::A_BYTES, 0);
   if constexpr (T::RS == 1) {
     float r0s[8];
     load_scales<T>(lds, 0, 0, rd, r0s);
@@ -688,7 +703,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   // (and, while kt+1 is a prologue k-tile, the caller's stores after them)
   auto wait_next = [&](int kt) {
     if (kt + 1 < nk) {
-      const int after = min(nk - 1, kt + T::STAGES - 1) - (kt + 1);
+      const int after = xt ? T::STAGES - 2 : min(nk - 1, kt + T::STAGES - 1) - (kt + 1);
       if (stores_after && kt + 1 < T::STAGES) wait_ktile<ND, T::STAGES, T::C_STORES>(after);
       else wait_ktile<ND, T::STAGES>(after);
       if constexpr (T::RS == 2)
@@ -703,9 +718,9 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
     // the two fragment sets in fixed registers.
     // steady state, peeled: both k-tiles of a trip refill a stage
     for (; kt + 1 + T::STAGES < nk; kt += 2) {
-      const uint32_t s0 = (uint32_t)(kt % T::STAGES) * T::STAGE;
-      const uint32_t s1 = (uint32_t)((kt + 1) % T::STAGES) * T::STAGE;
-      const uint32_t s2 = (uint32_t)((kt + 2) % T::STAGES) * T::STAGE;
+      const uint32_t s0 = stg(kt);
+      const uint32_t s1 = stg(kt + 1);
+      const uint32_t s2 = stg(kt + 2);
       wait_next(kt);
       __syncthreads();
       substep<T, LAZY, 1>(acc, gram, f0, f1, lds, rd, s1, 0, dma, true, p, m_base, n_base,
@@ -715,17 +730,39 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
       substep<T, LAZY, 1>(acc, gram, f1, f0, lds, rd, s2, 0, dma, true, p, m_base, n_base,
                           kt + 1 + T::STAGES, lds0 + s1);
     }
+    // the last sub-steps: refills of this tile while there are k-tiles left,
+    // then (cross-tile prefetch) the next tile's first k-tiles
+    bool switched = false;
+    auto refill = [&](int u, bool& on, int& mb, int& nb, int& uk) {
+      on = u < nk;
+      mb = m_base;
+      nb = n_base;
+      uk = u;
+      if (!on && xt) {
+        if (!switched) {
+          dma.init(p, nx_m, nx_n, lane, wave);
+          switched = true;
+        }
+        on = true;
+        mb = nx_m;
+        nb = nx_n;
+        uk = u - nk;
+      }
+    };
     for (; kt < nk; kt += 2) {
+      bool on;
+      int mb, nb, uk;
       wait_next(kt);
       __syncthreads();
-      substep<T, LAZY>(acc, gram, f0, f1, lds, rd, (uint32_t)((kt + 1) % T::STAGES) * T::STAGE, 0,
-                       dma, kt + T::STAGES < nk, p, m_base, n_base, kt + T::STAGES,
-                       lds0 + (uint32_t)(kt % T::STAGES) * T::STAGE);
+      refill(kt + T::STAGES, on, mb, nb, uk);
+      substep<T, LAZY>(acc, gram, f0, f1, lds, rd, stg(kt + 1), 0, dma, on, p, mb, nb, uk,
+                       lds0 + stg(kt));
       if (kt + 1 >= nk) break;
       wait_next(kt + 1);
       __syncthreads();
-      substep<T, LAZY, 2>(acc, gram, f1, f0, lds, rd, (uint32_t)((kt + 2) % T::STAGES) * T::STAGE,
-                          0, dma, false, p, m_base, n_base, 0, 0);
+      refill(kt + 1 + T::STAGES, on, mb, nb, uk);
+      substep<T, LAZY>(acc, gram, f1, f0, lds, rd, stg(kt + 2), 0, dma, on, p, mb, nb, uk,
+                       lds0 + stg(kt + 1));
     }
   } else {
     if constexpr (!LAZY) {
@@ -1452,6 +1489,11 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     grouped_tile(ordered_tile(p, first, total), p.tiles_m, p.tiles_n, 4, tm, tn);
     issue_prologue<T>(p, lds0, tm * T::BM, tn * T::BN, tid);
   }
+  // cross-tile prefetch: not for the epilogues that stage data through the
+  // stages or load per-row data after the k-loop
+  constexpr bool kCross = T::KK == 1 && EPI == EPI_NONE;
+  const int nk = (p.K + T::BK - 1) / T::BK;
+  int srot = 0;
   for (int t = first; t < total; t += G) {
     // opaque thread id: keeps lane-dependent addresses from being hoisted
     // out of the tile loop (where they would be spilled)
@@ -1463,9 +1505,14 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     grouped_tile(ordered_tile(p, t, total), p.tiles_m, p.tiles_n, 4, tm, tn);
     const int m_base = tm * T::BM, n_base = tn * T::BN;
     const int ax = (epi_lazy(EPI) && lazy_split<T>()) ? wn : 0;
+    const bool has_next = t + G < total;
+    int tm2 = 0, tn2 = 0;
+    if (has_next) grouped_tile(ordered_tile(p, t + G, total), p.tiles_m, p.tiles_n, 4, tm2, tn2);
+    const bool xt = kCross && has_next && nk >= T::STAGES;
     f32x4 acc[T::FM][T::FN];
     float ss[T::FM];
-    mainloop<T, epi_lazy(EPI)>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, t != first);
+    mainloop<T, epi_lazy(EPI)>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, t != first, srot,
+                               xt ? tm2 * T::BM : -1, tn2 * T::BN);
     if constexpr (epi_res(EPI))
       add_residual<T>(p, acc, lds, lds0, m_base, n_base, wave, wm, wn, lane);
     Affine<T> aff;
@@ -1473,13 +1520,10 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     load_columns<T, EPI>(p, n_base, wn, lane, aff, bias);
     float mean[T::FM], rstd[T::FM];
     tile_scale<T, EPI>(p, acc, ss, lds, m_base, n_base, tn, wm, wn, lane, ax, mean, rstd);
-    if (t + G < total) {
-      int tm2, tn2;
-      grouped_tile(ordered_tile(p, t + G, total), p.tiles_m, p.tiles_n, 4, tm2, tn2);
-      issue_prologue<T>(p, lds0, tm2 * T::BM, tn2 * T::BN, tid);
-    }
+    if (has_next && !xt) issue_prologue<T>(p, lds0, tm2 * T::BM, tn2 * T::BN, tid);
     tile_store<T, EPI>(p, acc, mean, rstd, aff, bias, lds, m_base, n_base, wave, wm, wn, lane,
                        ax);
+    srot = xt ? (srot + nk) % T::STAGES : 0;
   }
 }
 
@@ -1672,6 +1716,12 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
     asm volatile("" : "+v"(tid));
     issue_prologue<T>(p, lds0, rb_in * T::BM, tn * T::BN, tid);
   }
+  // cross-tile prefetch of the next round's first k-tiles inside the k-loop
+  // (not with the residual or the backward, which stage data through the
+  // stages after the k-loop)
+  constexpr bool kCross = T::KK == 1 && !RES && !BWD;
+  const int nk = (p.K + T::BK - 1) / T::BK;
+  int srot = 0;
   for (int it = 0; it < p.iters; ++it) {
     const int tm = it * R + rb_in;
     if (tm >= p.tiles_m) break;
@@ -1688,14 +1738,16 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
     float ss[T::FM];
     // (BWD: the previous tile's output stores precede this tile's first
     // transfers, so they are not counted after them)
-    mainloop<T, false>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, !BWD && it > 0);
+    const bool xt = kCross && tm + R < p.tiles_m && nk >= T::STAGES;
+    mainloop<T, false>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, !BWD && it > 0, srot,
+                       xt ? (tm + R) * T::BM : -1, n_base);
     if constexpr (RES) add_residual<T>(p, acc, lds, lds0, m_base, n_base, wave, wm, wn, lane);
     if constexpr (BWD) load_tile_lds<T>(p, p.Xin, lds0, m_base, n_base, wave, wn, lane);
     xwg_publish<T, LN, BWD>(p, acc, lds, rb_in, tn, tid, tag);
     Affine<T> aff;
     if constexpr (!BWD) {
       load_affine<T>(p, n_base, wn, lane, aff);
-      if (tm + R < p.tiles_m) issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid);
+      if (tm + R < p.tiles_m && !xt) issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid);
     }
     xwg_merge_rows<T, LN, BWD>(p, rb_in, R, tm, tn, tid, tag);
     // step 5: (mean, rstd) of this wave's rows; BWD: (c, rstd) from the row's
@@ -1725,6 +1777,7 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
         issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid);
       }
     }
+    srot = xt ? (srot + nk) % T::STAGES : 0;
   }
   // the last workgroup to finish advances the call counter (every workgroup
   // read it at its start)
