@@ -173,7 +173,7 @@ ng_status ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, c
  * normalized inside one workgroup; wider rows merge per-row fp32 partials
  * across workgroups through `workspace`, which must hold
  * ng_workspace_bytes(NG_OP_GEMM_RMSNORM, M, N, K) bytes (0 means none needed;
- * at most ~7 MB: it holds one round of row blocks and stops growing with M),
+ * at most ~6.3 MB: it holds one round of row blocks and stops growing with M),
  * be 256-byte aligned and be zero-filled before its first use (see
  * ng_workspace_reset); calls leave it ready for the next call.  One workspace
  * must not be used by two calls that may run concurrently.  Wide rows run a
@@ -182,7 +182,9 @@ ng_status ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, c
  * on one device (e.g. on two streams).  If they do, a wait may give up after
  * about a second (2^20 polls of ~1 us; see ng_set_debug_option);
  * ng_workspace_status then reports NG_ERR_TIMEOUT, and every output element
- * and statistic of a row whose exchange failed is NaN.
+ * and statistic of a row whose exchange failed is NaN.  A row may span at
+ * most as many 256-column tiles as the device holds such workgroups at once
+ * (N <= 65536 on a 256-CU device); wider rows return NG_ERR_UNSUPPORTED.
  * gamma: bf16 [N] or NULL.  rstd_out: float32 [M] or NULL.
  */
 ng_status ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,
