@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--no-load-readings", action="store_true",
                     help="skip the clock/power readings under load (about a second of extra "
                          "fused calls; for profiler runs)")
+    ap.add_argument("--no-library-gemm", action="store_true",
+                    help="skip timing torch.matmul (hipBLASLt) on the same operands as a "
+                         "reference point for the plain product")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -391,6 +394,18 @@ class Bench:
     def norm_only(self, i):
         self._call(self._norm, i)
 
+    # The vendor library's GEMM on the same operands (torch.matmul, which
+    # ROCm serves from hipBLASLt): a reference point for the plain product on
+    # the same board at the same clock and power cap, not part of any
+    # measured path.  Only for the forward products C = A @ B.
+    def has_library_gemm(self):
+        return self.w.op not in (workloads.OP_LAZY_BWD, workloads.OP_LAZY_BWD_W)
+
+    def library_gemm(self, i):
+        r = i % self.R
+        A = self.An[r] if prenorm(self.w) else self.A[r]
+        self.torch.matmul(A, self.B, out=self.C[r])
+
     def pair(self, i):
         if prenorm(self.w):
             self.norm_only(i)
@@ -622,7 +637,7 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
 
 
 def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: float,
-        load_readings: bool = True):
+        load_readings: bool = True, library_reference: bool = True):
     import numpy as np
     torch_mod = __import__("torch")
     b = Bench(w)
@@ -633,9 +648,21 @@ def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: f
     # otherwise penalize whichever callable is timed first.
     rounds = {"fused": [], "gemm": [], "norm": [], "pair": []}
     fns = {"fused": b.fused, "gemm": b.gemm_only, "norm": b.norm_only, "pair": b.pair}
+    with_lib = library_reference and b.has_library_gemm() and w.flops >= 1e11
+    if with_lib:
+        rounds["library"] = []
+        fns["library"] = b.library_gemm
     for _ in range(ROUNDS):
         for k, fn in fns.items():
             rounds[k].append(b.time_launches(fn, steps, warmup))
+
+    # a cross-workgroup exchange that gave up would have left NaN in the
+    # output and raised the workspace's error word: a timing of such calls
+    # is not reported
+    if b.ws is not None:
+        st = b.ws.status()
+        if st != 0:
+            raise b.ng.NormGemmError(st, "cross-workgroup exchange during the timed calls")
 
     def median_round(k):
         rs = sorted(rounds[k], key=lambda r: r[2])
@@ -690,6 +717,10 @@ def run(w: workloads.Workload, steps: int, warmup: int, with_cpu: bool, cpu_s: f
                     "fused_p10_us": round(float(np.percentile(per, 10)) * 1e3, 2),
                     "fused_p90_us": round(float(np.percentile(per, 90)) * 1e3, 2)},
         "roofline": roof,
+        "library_gemm": ({"callable": "torch.matmul (hipBLASLt)",
+                          "us": round(median_round("library")[2] * 1e3, 2),
+                          "tflops": round(flops / (median_round("library")[2] * 1e-3) / 1e12, 1)}
+                         if with_lib else None),
         "device": device_info(),
         "under_load": load,
         "git_sha": git_sha(),
@@ -728,7 +759,7 @@ def main():
         steps = args.steps if args.steps is not None else (200 if small else 30)
         warmup = args.warmup if args.warmup is not None else 20
         line = run(w, steps, warmup, not args.no_cpu_baseline, args.cpu_seconds,
-                   not args.no_load_readings)
+                   not args.no_load_readings, not args.no_library_gemm)
         print(json.dumps(line), flush=True)
 
 

@@ -347,6 +347,27 @@ def test_gemm_add_norm_cross_workgroup_rounds_ragged():
         _check_stat("xwg residual rstd", rstd, rref)
 
 
+def test_gemm_add_norm_cross_workgroup_deep_k():
+    # k-loops of 8 or more 32-deep k-tiles stream R into the stages under
+    # their last k-tiles (B[K,N]); 10 column tiles, 2 rounds, ragged M, N, K
+    M, N, K = 256 * 30 + 100, 256 * 9 + 24, 520
+    for kind, layout in (("layer", "kn"), ("rms", "kn"), ("rms", "nk")):
+        log("xwg residual deep k %s M=%d N=%d K=%d %s" % (kind, M, N, K, layout))
+        x = workloads.make_inputs(M, N, K, seed=29, gamma=True, beta=kind == "layer",
+                                  residual=True)
+        eps = 1e-5 if kind == "layer" else 1e-6
+        S_dev = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        C, mean, rstd = _residual_call(kind, x, layout, eps, s_out=S_dev)
+        torch.cuda.synchronize()
+        Y, mref, rref, S = _residual_ref(kind, x, eps)
+        _check("xwg residual deep k %s" % kind, down(C), Y)
+        _check("xwg residual deep k s_out", down(S_dev), S)
+        _check_stat("xwg residual deep k rstd", rstd, rref)
+        if mean is not None:
+            got_mean = mean.cpu().numpy().astype(np.float64)
+            assert np.max(np.abs(got_mean - mref) / (1.0 + np.abs(mref))) <= 1e-3
+
+
 def test_gemm_add_norm_zero_residual_matches_plain():
     # R = 0: the residual forms give exactly the plain epilogue's result
     for N in (128, 1000):
@@ -493,6 +514,19 @@ def test_lazy_backward_input_small(M, N, K, layout):
     _check_stat("lazy backward rstd (forward)", rstd, rref)
 
 
+def test_lazy_backward_input_cross_workgroup_deep_product():
+    # the product dC @ B^T runs over N = 520 (17 k-tiles): with B stored [N, K]
+    # the forward input streams into the stages under the last k-tiles
+    M, N, K = 256 * 30 + 100, 520, 256 * 9 + 24
+    for layout in ("nk", "kn"):
+        log("lazy backward xwg deep product M=%d N=%d K=%d %s" % (M, N, K, layout))
+        x = workloads.make_inputs(M, N, K, seed=37, row_scale=True, upstream=True)
+        dA, _ = _lazy_bwd(x, layout, 1e-6)
+        torch.cuda.synchronize()
+        ref = oracle.rmsnorm_gemm_lazy_backward(x.A, x.B, x.dC, 1e-6)[0]
+        _check("lazy backward xwg deep product", down(dA), ref)
+
+
 def test_lazy_backward_input_cross_workgroup_rounds_ragged():
     # 10 column tiles of dA -> 25 row blocks per round; 31 row blocks -> 2 rounds
     M, N, K = 256 * 30 + 100, 136, 256 * 9 + 24
@@ -629,6 +663,14 @@ def _order_cases():
                                                                       eps=1e-6)],
                                  lambda x: oracle.gemm_add_rmsnorm(x.A, x.B, x.R, 1e-6,
                                                                    x.gamma)[0]),
+        # the same with R streamed in under the last of 17 k-tiles
+        "xwg_residual_layernorm_deep_k": ((6000, 2056, 520),
+                                          dict(gamma=True, beta=True, residual=True),
+                                          lambda x, A, B: [ng.gemm_add_layernorm(
+                                              A, B, up(x.R), up(x.gamma), up(x.beta),
+                                              eps=1e-5)],
+                                          lambda x: oracle.gemm_add_layernorm(
+                                              x.A, x.B, x.R, 1e-5, x.gamma, x.beta)[0]),
         # persistent 256x256 grid with more tiles than slots (two rounds)
         "persistent_lazy": ((5000, 4000, 264), dict(row_scale=True),
                             lambda x, A, B: [ng.rmsnorm_gemm_lazy(A, B, eps=1e-6)],
