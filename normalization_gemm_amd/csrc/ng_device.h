@@ -106,7 +106,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // ... lds): lane l's data lands at LDS byte address lds_addr + 16*l; lds_addr
 // must be wave-uniform.  Issued through inline asm so that the compiler does
 // not add a full vmcnt wait before unrelated LDS reads; callers order the
-// transfer with wait_vmcnt() and a barrier.  M0 is saved and restored.
+// transfer with wait_vmcnt() and a barrier.  M0 is left holding the LDS
+// address: nothing else in the library's kernels reads M0 (no s_movrel,
+// s_sendmsg, GWS, ds_*_addtid or compiler-issued LDS transfers; a CPU test
+// scans the compiled code for them), and saving and restoring it put two
+// more scalar instructions beside every transfer of the k-loop (~0.7 % on
+// the large shapes).
 // NT: nontemporal load, for data that no other workgroup reads (a row block
 // of A whose rows fit one column tile); data shared through L2 must not use
 // it (measured ~10 % slower on the large shapes, whose A panels are re-read
@@ -114,25 +119,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 template <bool NT = false>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t lds_addr, uint32_t voff,
                                       uint32_t soff) {
-  uint32_t tmp;
   if constexpr (NT) {
     asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
+        "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, %4 offen nt lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(tmp)
+        "buffer_load_dwordx4 %1, %2, %3 offen nt lds"
+        :
         : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff)
         : "memory");
   } else {
     asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
+        "s_mov_b32 m0, %0\n\t"
         "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(tmp)
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
         : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff)
         : "memory");
   }
