@@ -242,6 +242,12 @@ struct DmaPlan {
   uint32_t a_km[T::AKM ? A_INS : 1];  // A[K,M]: lane part per instruction (M tail folded in)
   uint32_t r_voff;          // RS: this lane's 16 bytes of the scales (lanes 0..15)
   uint32_t a_row_bytes;     // K * 2
+  // Bytes of the tile's rows from the start of their k-tile 0 (A, and B
+  // stored [N, K]: at most 256 rows of 2K bytes, at most 2^31 under the
+  // K limit); B stored [K, N]: bytes of a whole k-tile and of the last one
+  // from its first column, each at most 0x7FFFFFF0.  A k-tile's buffer size
+  // follows from these with 32-bit scalar arithmetic.
+  uint32_t a_tile_bytes, b_tile_bytes, b_kt_bytes, b_last_bytes;
 
   // Blocked-layout slot (16 bytes) -> (k row, column) of a [K, X] tile of
   // width W (B[K,N], or A[K,M]).
@@ -263,6 +269,17 @@ struct DmaPlan {
     a_kc = 8u * c;
     a_voff = (uint32_t)row_in * a_row_bytes + 16u * c;
     r_voff = lane < 16 ? 16u * (uint32_t)lane : kOOB;
+    if constexpr (!T::AKM) a_tile_bytes = (uint32_t)min(p.M - m_base, T::BM) * a_row_bytes;
+    if constexpr (T::KN && !T::AKM) {
+      const int nk = (p.K + T::BK - 1) / T::BK;
+      const int last_rows = p.K - (nk - 1) * T::BK;
+      const uint64_t full = ((uint64_t)T::BK * p.N - n_base) * 2u;
+      const uint64_t last = ((uint64_t)last_rows * p.N - n_base) * 2u;
+      b_kt_bytes = full > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)full;
+      b_last_bytes = last > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)last;
+    } else if constexpr (!T::KN) {
+      b_tile_bytes = (uint32_t)min(p.N - n_base, T::BN) * a_row_bytes;
+    }
     if constexpr (T::AKM) {
 #pragma unroll
       for (int j = 0; j < A_INS; ++j) {
@@ -297,7 +314,7 @@ struct DmaPlan {
     }
     const uint64_t off = (uint64_t)m_base * p.K + k0;
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(p.A + off, ((uint64_t)p.M * p.K - off) * 2u);
+        make_rsrc_n(p.A + off, umin32(uniform(a_tile_bytes) - 2u * (uint32_t)k0, 0x7FFFFFF0u));
     const uint32_t v = (k0 + (int)a_kc < p.K) ? a_voff : kOOB;
     const uint32_t row0 = (uint32_t)((wave * A_INS + j) * (64 / T::CPR));
     dma16<T::ANT>(rs, st + (uint32_t)(wave * A_INS + j) * 1024u, v, row0 * a_row_bytes);
@@ -308,13 +325,17 @@ struct DmaPlan {
     const int k0 = kt * T::BK;
     if constexpr (T::KN) {
       const uint64_t off = (uint64_t)k0 * p.N + n_base;
+      // (the weight-gradient tiles, short of scalar registers, size it the
+      // long way from the kernel arguments)
       const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(p.B + off, ((uint64_t)p.K * p.N - off) * 2u);
+          T::AKM ? make_rsrc(p.B + off, ((uint64_t)p.K * p.N - off) * 2u)
+                 : make_rsrc_n(p.B + off,
+                               uniform(k0 + T::BK <= p.K ? b_kt_bytes : b_last_bytes));
       dma16(rs, st + (uint32_t)(wave * B_INS + j) * 1024u, b_voff[j], 0u);
     } else {
       const uint64_t off = (uint64_t)n_base * p.K + k0;
       const __amdgpu_buffer_rsrc_t rs =
-          make_rsrc(p.B + off, ((uint64_t)p.N * p.K - off) * 2u);
+          make_rsrc_n(p.B + off, umin32(uniform(b_tile_bytes) - 2u * (uint32_t)k0, 0x7FFFFFF0u));
       const uint32_t v = (k0 + (int)a_kc < p.K) ? a_voff : kOOB;
       const uint32_t row0 = (uint32_t)((wave * B_INS + j) * (64 / T::CPR));
       dma16(rs, st + (uint32_t)(wave * B_INS + j) * 1024u, v, row0 * a_row_bytes);
