@@ -706,6 +706,30 @@ def test_tile_order_does_not_change_results(case, order):
 
 
 # ------------------------------------------------------------ edge cases
+def test_longest_rows_of_length_k():
+    # K = 2^22, the longest row the products read: a full 256-row tile spans
+    # 255 * 2K + 64 bytes from its first row, just inside the 2 GiB buffer
+    # range; a second, 4-row tile and two column tiles (the last ragged)
+    M, N, K = 260, 264, 1 << 22
+    log("longest rows M=%d N=%d K=%d" % (M, N, K))
+    x = workloads.make_inputs(M, N, K, seed=3)
+    ref = oracle.gemm(x.A, x.B)
+    ref_lazy, rref = oracle.rmsnorm_gemm_lazy(x.A, x.B, 1e-6)
+    A = up(x.A)
+    for layout in ("kn", "nk"):
+        B = up(b_for_layout(x.B, layout))
+        C = ng.gemm(A, B, b_layout=layout)
+        rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+        L = ng.rmsnorm_gemm_lazy(A, B, eps=1e-6, b_layout=layout, rstd_out=rstd)
+        torch.cuda.synchronize()
+        _check("gemm K=2^22 %s" % layout, down(C), ref)
+        _check("lazy K=2^22 %s" % layout, down(L), ref_lazy)
+        _check_stat("lazy K=2^22 rstd %s" % layout, rstd, rref)
+        del B, C, L
+    del A
+    torch.cuda.empty_cache()
+
+
 def test_empty_M_is_a_no_op():
     # M == 0: the calls return NG_OK without touching any buffer (A and C may
     # be NULL), and the helpers return empty outputs
