@@ -145,9 +145,11 @@ __device__ __forceinline__ int ordered_tile(const GemmParams& p, int t, int tota
 
 // KN: B stored [K, N] (else [N, K]).  AKM: A stored [K, M] (the reduction
 // index is A's storage row: the weight-gradient products), read like B[K, N].
-// RS: the A (1) or B (2) fragments are scaled per reduction index by
-// row_rstd and rounded to bf16 in registers before the MFMAs (the
-// normalized A of Lazy Pre-Norm rebuilt from A and its saved rstd).
+// RS: one operand is scaled per reduction index by row_rstd and rounded to
+// bf16 before the MFMAs (the normalized A of Lazy Pre-Norm rebuilt from A
+// and its saved rstd): 1 = the A k-tile, 2 = the B k-tile, in LDS one k-tile
+// ahead of its use (32-deep k-tiles in 4 stages; both operands stored with
+// the reduction index as their row).
 // BK: k-tile depth (64, or 32 for deeper pipelines within the LDS budget).
 // ANT: A is fetched with nontemporal loads (tiles whose workgroup is the only
 // reader of its rows of A: one column tile per row block).
@@ -168,7 +170,7 @@ struct Tile {
   static constexpr int FM = WTM / 16, FN = WTN / 16;
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int B_BYTES = BN * BK * 2;
-  // RS: the k-tile's 64 fp32 scales, in a 1 KB slot after B
+  // RS: the k-tile's scales, in a 1 KB slot after B
   static constexpr int R_BYTES = RS ? 1024 : 0;
   static constexpr int STAGE = A_BYTES + B_BYTES + R_BYTES;
   static constexpr int A_PER = BM * BK / 8 / NT;  // 16-byte chunks per thread
@@ -190,12 +192,13 @@ struct Tile {
   static_assert(FN % 4 == 0, "64-column output groups");
   static_assert(STAGES >= 2 && STAGES <= 4, "pipeline depth");
   static_assert(BK == 64 || BK == 32, "k-tile depth");
-  static_assert(RS == 0 || BK == 64, "scaled operands use 64-deep k-tiles");
+  static_assert(RS == 0 || (BK == 32 && STAGES == 4), "scaled operands: 32-deep k-tiles in 4 stages");
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tile");
   static_assert((BM * BK / 8) % NT == 0 && (BN * BK / 8) % NT == 0, "loader split");
   static_assert((BN & (BN - 1)) == 0 && BN >= 16, "BN power of two");
   static_assert(!AKM || ((BM & (BM - 1)) == 0 && BM >= 16), "BM power of two");
   static_assert(RS >= 0 && RS <= 2, "scale side");
+  static_assert(RS == 0 || (RS == 1 ? AKM : KN), "scaled operand: a blocked [K, X] tile");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -230,7 +233,10 @@ template <class T>
 struct DmaPlan {
   static constexpr int A_INS = T::A_BYTES / 1024 / (T::NT / 64);  // instructions per wave
   static constexpr int B_INS = T::B_BYTES / 1024 / (T::NT / 64);
-  static constexpr int R_INS = T::RS ? 1 : 0;  // the scales: one transfer per wave
+  // RS: one more transfer, the k-tile's scales, issued by wave 0 only (the
+  // other waves read them after the barrier that follows every wave's wait
+  // for the k-tile); INS counts wave 0's transfers.
+  static constexpr int R_INS = T::RS ? 1 : 0;
   static constexpr int INS = A_INS + B_INS + R_INS;
   static_assert(A_INS * 1024 * (T::NT / 64) == T::A_BYTES, "A tile split");
   static_assert(B_INS * 1024 * (T::NT / 64) == T::B_BYTES, "B tile split");
@@ -240,7 +246,7 @@ struct DmaPlan {
   uint32_t a_kc;            // k offset (elements) of this lane's chunk within the k-tile
   uint32_t b_voff[B_INS];   // B[K,N]: lane part per instruction (N tail folded in)
   uint32_t a_km[T::AKM ? A_INS : 1];  // A[K,M]: lane part per instruction (M tail folded in)
-  uint32_t r_voff;          // RS: this lane's 16 bytes of the scales (lanes 0..15)
+  uint32_t r_voff;          // RS: this lane's 16 bytes of the scales (lanes 0 .. BK/4-1)
   uint32_t a_row_bytes;     // K * 2
   // Bytes of the tile's rows from the start of their k-tile 0 (A, and B
   // stored [N, K]: at most 256 rows of 2K bytes, at most 2^31 under the
@@ -268,7 +274,7 @@ struct DmaPlan {
     const uint32_t c = (uint32_t)(pos ^ a_swz<T>(row_in));
     a_kc = 8u * c;
     a_voff = (uint32_t)row_in * a_row_bytes + 16u * c;
-    r_voff = lane < 16 ? 16u * (uint32_t)lane : kOOB;
+    r_voff = lane < T::BK / 4 ? 16u * (uint32_t)lane : kOOB;
     if constexpr (!T::AKM) a_tile_bytes = (uint32_t)min(p.M - m_base, T::BM) * a_row_bytes;
     if constexpr (T::KN && !T::AKM) {
       const int nk = (p.K + T::BK - 1) / T::BK;
@@ -341,9 +347,8 @@ struct DmaPlan {
       dma16(rs, st + (uint32_t)(wave * B_INS + j) * 1024u, v, row0 * a_row_bytes);
     }
   }
-  // RS: the k-tile's 64 scales (lanes 0..15, 16 bytes each; the other lanes
-  // write zeros into the rest of the 1 KB slot).  Every wave moves the same
-  // bytes, so that each wave issues the same number of transfers per k-tile.
+  // RS: the k-tile's BK scales (16 bytes per lane; the other lanes write
+  // zeros into the rest of the 1 KB slot).
   __device__ __forceinline__ void issue_r(const GemmParams& p, int kt, uint32_t st) const {
     const int k0 = kt * T::BK;
     const __amdgpu_buffer_rsrc_t rs =
@@ -351,12 +356,12 @@ struct DmaPlan {
     dma16(rs, st, r_voff, 0u);
   }
   // Transfer number d (0 .. INS-1) of k-tile kt into the stage at `st` (A
-  // region first, then B, then the scales).
+  // region first, then B, then, from wave 0, the scales).
   __device__ __forceinline__ void issue(const GemmParams& p, int m_base, int n_base, int kt,
                                         uint32_t st, int d) const {
     if (d < A_INS) issue_a(p, m_base, kt, st, d);
     else if (d < A_INS + B_INS) issue_b(p, n_base, kt, st + T::A_BYTES, d - A_INS);
-    else issue_r(p, kt, st + T::A_BYTES + T::B_BYTES);
+    else if (wave == 0) issue_r(p, kt, st + T::A_BYTES + T::B_BYTES);
   }
 };
 
@@ -385,13 +390,11 @@ struct FragReader {
   uint32_t a_odd[T::KK];   // per kk: base for odd slots
   uint32_t b_base[T::KK];  // per kk: B fragment 0 (half 0) of this lane, from the B region
   uint32_t b_odd[T::KK];   // KN: base for odd fragments (the XOR in b_blk_off)
-  uint32_t r_off[T::KK];   // RS: per kk, this lane's 8 scales in the stage's scale slot
 
   __device__ __forceinline__ void init(int wm, int wn, int lane, int a_xor = 0) {
     const int l16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int kk = 0; kk < T::KK; ++kk) {
-      r_off[kk] = (uint32_t)(T::A_BYTES + T::B_BYTES + (kk * 32 + 8 * g) * 4);
       const int row = wm * T::WTM + l16;
       // (row = l16 modulo 16, which is all the swizzle looks at)
       const uint32_t a0 = (uint32_t)(row * T::RB + (((kk * 4 + g) ^ a_swz<T>(l16)) << 4));
@@ -458,65 +461,82 @@ struct FragReader {
   }
 };
 
-// RS 1: the A fragments are multiplied by their reduction index's scale and
-// rounded to bf16 in registers after their LDS reads.  Element e of a fragment is reduction
-// index kk*32 + 8*(lane >> 4) + e (the MFMA operand layout), whatever LDS
-// read produced it; the k-tile's 64 scales sit in its stage's scale slot.
-template <class T>
-__device__ __forceinline__ void load_scales(lds_char* lds, uint32_t st, int kk,
-                                            const FragReader<T>& rd, float (&r)[8]) {
-  const uint32_t o = st + rd.r_off[kk];
-  const f32x4 r0 = *(lds_f32x4*)(lds + o);
-  const f32x4 r1 = *(lds_f32x4*)(lds + o + 16);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { r[e] = r0[e]; r[4 + e] = r1[e]; }
-}
-
 __device__ __forceinline__ uint32_t scale_pair(uint32_t w, float r_lo, float r_hi) {
   return pack_bf16x2(bf16_lo(w) * r_lo, bf16_hi(w) * r_hi);
 }
 
-// RS 2 (B side): a B fragment is held by the WM waves of a column, so the
-// k-tile is scaled in LDS instead, once per workgroup: each wave scales the
-// 16-byte chunks that its own transfers wrote, right after its own wait for
-// the k-tile and before the barrier that publishes it.  In the blocked
-// [K, N] layout a chunk holds 8 elements of one k row, which share one scale.
-// (Measured on 32768x4096x4096: 1030 us against 1216 us for scaling the
-// fragments in registers; on the A side, held by only WN waves, registers
-// win.)  The per-lane offsets are recomputed from an opaque lane index so
-// that they are not kept live across the k-loop.
+// RS: the scaled operand's k-tile is scaled in LDS, once per workgroup (a
+// fragment is held by several waves: WN of them for A, WM for B), each wave
+// the 16-byte chunks that its own transfers wrote.  In the blocked [K, X]
+// layout a chunk holds 8 elements of one k row, which share one scale.
+template <class T>
+constexpr bool scale_b_side() { return T::RS == 2; }
+template <class T>
+constexpr bool scale_ahead() { return T::RS != 0; }
+
+template <class T>
+struct ChunkScaler {
+  static constexpr bool BS = scale_b_side<T>();
+  static constexpr int INS = BS ? DmaPlan<T>::B_INS : DmaPlan<T>::A_INS;
+  static constexpr int W = BS ? T::BN : T::BM;
+  static constexpr uint32_t REGION = BS ? (uint32_t)T::A_BYTES : 0u;
+  static constexpr uint32_t RSLOT = (uint32_t)(T::A_BYTES + T::B_BYTES);
+  // A wave's transfer j moves slots (wave*INS + j)*64 + lane, i.e. 16-byte
+  // block (wave*INS + j)*8 + lane/8 of the blocked layout (W/16 blocks per
+  // row of 4 k rows).  When a block row holds a whole number of waves'
+  // blocks, all INS chunks of a lane sit in one block row, at k row
+  // 4*kb + (lane % 8)/2 with kb = (wave*INS*8) / (W/16): a wave needs the
+  // four scales of k rows 4*kb .. 4*kb+3, one per lane.
+  static_assert(T::RS == 0 || (W / 16) % (INS * 8) == 0, "a wave's chunks share their k rows");
+  static __device__ __forceinline__ int kb(int wave) { return (wave * INS * 8) / (W / 16); }
+  u32x4 v;
+  float r;
+  uint32_t o;  // LDS byte offset of chunk 0
+  // chunk 0's bytes and the lane's scale, from the stage at `st`
+  __device__ __forceinline__ void load_first(lds_char* lds, uint32_t st, int wave, int lane) {
+    r = *(lds_float*)(lds + st + RSLOT + 16u * (uint32_t)kb(wave) + (uint32_t)((lane & 6) << 1));
+    o = st + REGION + (uint32_t)(wave * INS) * 1024u + (uint32_t)lane * 16u;
+    v = lds_read16(lds, o);
+  }
+  // chunk j (> 0): 1 KB after chunk j-1
+  __device__ __forceinline__ void load(lds_char* lds, int j) {
+    v = lds_read16(lds, o + (uint32_t)j * 1024u);
+  }
+  // dword w (0 .. 3) of the loaded chunk: its bf16 pair times the scale
+  __device__ __forceinline__ void scale(int w) { v[w] = scale_pair(v[w], r, r); }
+  __device__ __forceinline__ void store(lds_char* lds, int j) const {
+    lds_write16(lds, o + (uint32_t)j * 1024u, v);
+  }
+};
+
 template <class T>
 __device__ __forceinline__ void scale_own_chunks(lds_char* lds, uint32_t st, int wave, int lane) {
-  static_assert(T::RS == 2 && T::KN, "B stored [K, N] scaled in LDS");
-  constexpr int INS = DmaPlan<T>::B_INS;
+  static_assert(scale_ahead<T>(), "scaled operand");
   int ln = lane;
   asm volatile("" : "+v"(ln));
-  const uint32_t region = st + (uint32_t)T::A_BYTES;
-  const uint32_t rslot = st + (uint32_t)(T::A_BYTES + T::B_BYTES);
+  ChunkScaler<T> sc;
 #pragma unroll
-  for (int j = 0; j < INS; ++j) {
-    const int slot = (wave * INS + j) * 64 + ln;
-    int kr, xc;
-    DmaPlan<T>::template blk_slot<T::BN>(slot, kr, xc);
-    const float r = *(lds_float*)(lds + rslot + (uint32_t)kr * 4u);
-    const uint32_t o = region + (uint32_t)slot * 16u;
-    u32x4 v = lds_read16(lds, o);
+  for (int j = 0; j < ChunkScaler<T>::INS; ++j) {
+    if (j == 0) sc.load_first(lds, st, wave, ln);
+    else sc.load(lds, j);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) v[w] = scale_pair(v[w], r, r);
-    lds_write16(lds, o, v);
+    for (int w = 0; w < 4; ++w) sc.scale(w);
+    sc.store(lds, j);
   }
 }
 
-// RS 1 (A side): one packed pair (dword) of the next sub-step's A fragments
-// per MFMA slot over the last 4*FM slots of the sequence, so that each
-// slot's few VALU operations sit under an MFMA in flight.  By then the A
-// reads (the first items) have been issued and the first rows of the
-// current fragments are dead, which leaves registers for the scales (loaded
-// one slot before the first use).
+// The sub-step that computes k-tile kt scales the chunks of k-tile
+// kt+2 that this wave's own transfers wrote (they have landed: the wait
+// before the sub-step covers kt+2), one chunk at a time: read at slot
+// SC_GAP*j, scaled one dword per slot from SC_GAP*j + SC_LAT on, written back
+// at the slot after; the barrier before the next sub-step publishes them,
+// and the sub-step after that reads them as fragments.  No wave touches
+// k-tile kt+2's stage in between: the reads of the sub-step are of kt+1, its
+// transfers refill kt's.
 template <class T>
-constexpr int scale_first_slot() {
-  return T::FM * T::FN - 4 * T::FM;
-}
+constexpr int sc_lat() { return 6; }
+template <class T>
+constexpr int sc_gap() { return sc_lat<T>() + 5; }
 
 // Lazy Pre-Norm sum of squares on the matrix cores.  For an A fragment F
 // (16 rows x 32 k of the sub-step), one MFMA of F with itself gives the 16x16
@@ -577,31 +597,39 @@ __device__ __forceinline__ void lazy_gram(int q, const Frags<T>& cur,
 // fragments join the sequence.
 // DM: 0 = issue the transfers when dma_on, 1 = always, 2 = never (the last
 // two make the choice at compile time, without a branch per transfer).
-template <class T, bool LAZY, int DM = 0>
+// SC (scaled operands): 0 = no scaling ahead, 1 = scale the stage at sc_st,
+// 2 = do so when sc_on.
+template <class T, bool LAZY, int DM = 0, int SC = 0>
 __device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN],
                                         f32x4 (&gram)[lazy_slots<T>()],
                                         const Frags<T>& cur, Frags<T>& nxt, lds_char* lds,
                                         const FragReader<T>& rd, uint32_t rd_st, int rd_kk,
                                         const DmaPlan<T>& dma,
                                         bool dma_on, const GemmParams& p, int m_base,
-                                        int n_base, int dma_kt, uint32_t dma_st) {
+                                        int n_base, int dma_kt, uint32_t dma_st,
+                                        uint32_t sc_st = 0, bool sc_on = false, int lane = 0) {
   constexpr int NM = T::FM * T::FN;
   constexpr int NR = FragReader<T>::ITEMS;
   constexpr int ND = DmaPlan<T>::INS;
-  float rsc[8];
-  static_assert(T::RS != 1 || (scale_first_slot<T>() >= NM / 2 &&
-                               FragReader<T>::A_ITEMS * NM / NR < scale_first_slot<T>() - 1),
-                "scale slots");
+  ChunkScaler<T> sc;
+  constexpr int SCJ = ChunkScaler<T>::INS;
+  static_assert(!scale_ahead<T>() || sc_gap<T>() * SCJ <= NM, "scale-ahead slots");
 #pragma unroll
   for (int q = 0; q < NM; ++q) {
     const int i = q / T::FN, j = q % T::FN;
     acc[i][j] = mfma_16x16x32(cur.b[j], cur.a[i], acc[i][j]);
-    if constexpr (T::RS == 1) {
-      constexpr int S0 = scale_first_slot<T>();
-      if (q == S0 - 1) load_scales<T>(lds, rd_st, rd_kk, rd, rsc);
-      if (q >= S0) {
-        const int f = (q - S0) >> 2, w = (q - S0) & 3;
-        nxt.a[f][w] = scale_pair(nxt.a[f][w], rsc[2 * w], rsc[2 * w + 1]);
+    if constexpr (scale_ahead<T>() && SC != 0) {
+      if (SC == 1 || sc_on) {
+        constexpr int G = sc_gap<T>(), L = sc_lat<T>();
+        const int j = q / G, u = q % G;
+        if (j < SCJ) {
+          if (u == 0) {
+            if (j == 0) sc.load_first(lds, sc_st, dma.wave, lane);
+            else sc.load(lds, j);
+          }
+          if (u >= L && u < L + 4) sc.scale(u - L);
+          if (u == L + 4) sc.store(lds, j);
+        }
       }
     }
     if constexpr (LAZY) lazy_gram<T>(q, cur, gram);
@@ -697,38 +725,57 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   constexpr int ND = DmaPlan<T>::INS;
   constexpr int NR = FragReader<T>::ITEMS;
   const int nk = (p.K + T::BK - 1) / T::BK;
-  const bool xt = T::KK == 1 && nx_m >= 0 && nk >= T::STAGES;
+  const bool xt = T::KK == 1 && !scale_ahead<T>() && nx_m >= 0 && nk >= T::STAGES;
   // LDS byte offset of the stage that holds k-tile k
   auto stg = [&](int k) { return (uint32_t)((k + srot) % T::STAGES) * T::STAGE; };
+  // Wait until a k-tile has landed with `after` later k-tiles (and, with
+  // st_after, the caller's output stores) still allowed in flight.  With a
+  // scaled operand only wave 0 issues the scale transfers.
+  auto waitk = [&](int after, bool st_after) {
+    constexpr int NDW = ND - DmaPlan<T>::R_INS;  // transfers per k-tile of waves 1..
+    if (DmaPlan<T>::R_INS && wave == 0) {
+      if (st_after) wait_ktile<ND, T::STAGES, T::C_STORES>(after);
+      else wait_ktile<ND, T::STAGES>(after);
+    } else {
+      if (st_after) wait_ktile<NDW, T::STAGES, T::C_STORES>(after);
+      else wait_ktile<NDW, T::STAGES>(after);
+    }
+  };
 
   if (!prologue_issued) issue_prologue<T>(p, lds0, m_base, n_base, tid);
-  if (stores_after) wait_ktile<ND, T::STAGES, T::C_STORES>(min(nk, T::STAGES) - 1);
-  else wait_ktile<ND, T::STAGES>(min(nk, T::STAGES) - 1);
-  if constexpr (T::RS == 2) scale_own_chunks<T>(lds, 0, wave, lane);
+  if constexpr (scale_ahead<T>()) {
+    // k-tiles 0 and 1 are scaled here, the later ones one k-tile ahead
+    const int after = nk >= 2 ? min(nk, T::STAGES) - 2 : 0;
+    waitk(after, stores_after);
+    // (wave 0's scale transfers have landed for every wave after a barrier)
+    __syncthreads();
+    scale_own_chunks<T>(lds, stg(0), wave, lane);
+    if (nk >= 2) scale_own_chunks<T>(lds, stg(1), wave, lane);
+  } else {
+    waitk(min(nk, T::STAGES) - 1, stores_after);
+  }
   __syncthreads();
   Frags<T> f0, f1;
 #pragma unroll
   for (int r = 0; r < NR; ++r) rd.read(f0, r, lds, stg(0), stg(0) + T::A_BYTES, 0);
-  if constexpr (T::RS == 1) {
-    float r0s[8];
-    load_scales<T>(lds, 0, 0, rd, r0s);
-#pragma unroll
-    for (int i = 0; i < T::FM; ++i)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) f0.a[i][w] = scale_pair(f0.a[i][w], r0s[2 * w], r0s[2 * w + 1]);
-  }
 
   int cur_s = 0;
   int kt = 0;
   // k-tile kt+1 must have landed; k-tiles kt+2 .. kt+STAGES-1 may still fly
   // (and, while kt+1 is a prologue k-tile, the caller's stores after them)
   auto wait_next = [&](int kt) {
+    if constexpr (scale_ahead<T>()) {
+      // k-tile kt+1 was awaited (and scaled) one sub-step earlier; kt+2 is
+      // scaled during this one
+      if (kt + 2 < nk) {
+        const int after = min(nk - 1, kt + T::STAGES - 1) - (kt + 2);
+        waitk(after, stores_after && kt + 2 < T::STAGES);
+      }
+      return;
+    }
     if (kt + 1 < nk) {
       const int after = xt ? T::STAGES - 2 : min(nk - 1, kt + T::STAGES - 1) - (kt + 1);
-      if (stores_after && kt + 1 < T::STAGES) wait_ktile<ND, T::STAGES, T::C_STORES>(after);
-      else wait_ktile<ND, T::STAGES>(after);
-      if constexpr (T::RS == 2)
-        scale_own_chunks<T>(lds, (uint32_t)((kt + 1) % T::STAGES) * T::STAGE, wave, lane);
+      waitk(after, stores_after && kt + 1 < T::STAGES);
     }
   };
   if constexpr (T::KK == 1) {
@@ -744,12 +791,12 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
       const uint32_t s2 = stg(kt + 2);
       wait_next(kt);
       __syncthreads();
-      substep<T, LAZY, 1>(acc, gram, f0, f1, lds, rd, s1, 0, dma, true, p, m_base, n_base,
-                          kt + T::STAGES, lds0 + s0);
+      substep<T, LAZY, 1, 1>(acc, gram, f0, f1, lds, rd, s1, 0, dma, true, p, m_base, n_base,
+                             kt + T::STAGES, lds0 + s0, s2, true, lane);
       wait_next(kt + 1);
       __syncthreads();
-      substep<T, LAZY, 1>(acc, gram, f1, f0, lds, rd, s2, 0, dma, true, p, m_base, n_base,
-                          kt + 1 + T::STAGES, lds0 + s1);
+      substep<T, LAZY, 1, 1>(acc, gram, f1, f0, lds, rd, s2, 0, dma, true, p, m_base, n_base,
+                             kt + 1 + T::STAGES, lds0 + s1, stg(kt + 3), true, lane);
     }
     // the last sub-steps: refills of this tile while there are k-tiles left,
     // then (cross-tile prefetch) the next tile's first k-tiles
@@ -776,14 +823,22 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
       wait_next(kt);
       __syncthreads();
       refill(kt + T::STAGES, on, mb, nb, uk);
-      substep<T, LAZY>(acc, gram, f0, f1, lds, rd, stg(kt + 1), 0, dma, on, p, mb, nb, uk,
-                       lds0 + stg(kt));
+      if constexpr (scale_ahead<T>())
+        substep<T, LAZY, 0, 2>(acc, gram, f0, f1, lds, rd, stg(kt + 1), 0, dma, on, p, mb, nb,
+                               uk, lds0 + stg(kt), stg(kt + 2), kt + 2 < nk, lane);
+      else
+        substep<T, LAZY>(acc, gram, f0, f1, lds, rd, stg(kt + 1), 0, dma, on, p, mb, nb, uk,
+                         lds0 + stg(kt));
       if (kt + 1 >= nk) break;
       wait_next(kt + 1);
       __syncthreads();
       refill(kt + 1 + T::STAGES, on, mb, nb, uk);
-      substep<T, LAZY>(acc, gram, f1, f0, lds, rd, stg(kt + 2), 0, dma, on, p, mb, nb, uk,
-                       lds0 + stg(kt + 1));
+      if constexpr (scale_ahead<T>())
+        substep<T, LAZY, 0, 2>(acc, gram, f1, f0, lds, rd, stg(kt + 2), 0, dma, on, p, mb, nb,
+                               uk, lds0 + stg(kt + 1), stg(kt + 3), kt + 3 < nk, lane);
+      else
+        substep<T, LAZY>(acc, gram, f1, f0, lds, rd, stg(kt + 2), 0, dma, on, p, mb, nb, uk,
+                         lds0 + stg(kt + 1));
     }
   } else {
     if constexpr (!LAZY) {
@@ -1512,7 +1567,7 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
   }
   // cross-tile prefetch: not for the epilogues that stage data through the
   // stages or load per-row data after the k-loop
-  constexpr bool kCross = T::KK == 1 && EPI == EPI_NONE;
+  constexpr bool kCross = T::KK == 1 && EPI == EPI_NONE && !scale_ahead<T>();
   const int nk = (p.K + T::BK - 1) / T::BK;
   int srot = 0;
   for (int t = first; t < total; t += G) {
@@ -1740,7 +1795,7 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
   // cross-tile prefetch of the next round's first k-tiles inside the k-loop
   // (not with the residual or the backward, which stage data through the
   // stages after the k-loop)
-  constexpr bool kCross = T::KK == 1 && !RES && !BWD;
+  constexpr bool kCross = T::KK == 1 && !RES && !BWD && !scale_ahead<T>();
   const int nk = (p.K + T::BK - 1) / T::BK;
   int srot = 0;
   for (int it = 0; it < p.iters; ++it) {
