@@ -162,6 +162,11 @@ def algorithmic_bytes(w: workloads.Workload) -> int:
     if w.op == workloads.OP_LAZY_BWD:
         # dC [M, N], B, A [M, K] and dA [M, K], fp32 rstd [M]
         return 2 * (w.M * w.N + w.K * w.N + 2 * w.M * w.K) + 4 * w.M
+    if w.op == workloads.OP_LAZY_BWD_RG:
+        # as the input gradient, plus dB [K, N] written and the intermediate
+        # rstd * dC [M, N] written once and read once
+        return (2 * (w.M * w.N + w.K * w.N + 2 * w.M * w.K) + 4 * w.M + 2 * w.K * w.N
+                + 4 * w.M * w.N)
     b += 2 * w.N * (int(w.gamma) + int(w.beta))
     if w.residual:
         b += 2 * w.M * w.N
@@ -171,7 +176,11 @@ def algorithmic_bytes(w: workloads.Workload) -> int:
 def norm_bytes(w: workloads.Workload) -> int:
     """Standalone norm of the unfused pair: read + write the normalized matrix
     (and read R for the residual forms)."""
-    rows, cols = (w.M, w.K) if prenorm(w) or w.op == workloads.OP_LAZY_BWD else (w.M, w.N)
+    rows, cols = (w.M, w.K) if prenorm(w) or w.op in (workloads.OP_LAZY_BWD,
+                                                       workloads.OP_LAZY_BWD_RG) else (w.M, w.N)
+    if w.op == workloads.OP_LAZY_BWD_RG:
+        # the norm's backward (dA_hat, A -> dA) and the stored A_hat (A -> A_hat)
+        return 10 * rows * cols
     return (6 if w.residual or w.op == workloads.OP_LAZY_BWD else 4) * rows * cols
 
 
@@ -189,9 +198,12 @@ def kernel_label(w: workloads.Workload) -> str:
            workloads.OP_GEMM_ADD_RMSNORM: "EPI_ROW_RMS_RES",
            workloads.OP_GEMM_ADD_LAYERNORM: "EPI_ROW_LN_RES",
            workloads.OP_PRENORM_LN: "EPI_PRE_LN", workloads.OP_LAZY_BWD: "EPI_LAZY_BWD",
-           workloads.OP_LAZY_BWD_W: "EPI_NONE"}[w.op]
+           workloads.OP_LAZY_BWD_W: "EPI_NONE", workloads.OP_LAZY_BWD_RG: "EPI_LAZY_BWD"}[w.op]
     if w.op == workloads.OP_LAZY_BWD_W:
         return "gemm_persistent_kernel<Tile<..., A stored [K,M], RS 1>, EPI_NONE>"
+    if w.op == workloads.OP_LAZY_BWD_RG:
+        return ("%s<EPI_LAZY_BWD> writing rstd*dC, then gemm_persistent_kernel<Tile<..., "
+                "A stored [K,M]>, EPI_NONE>" % ("gemm_kernel" if w.K <= 256 else "gemm_xwg_kernel"))
     if w.op == workloads.OP_LAZY_BWD:
         return "%s<%s>" % ("gemm_kernel" if w.K <= 256 else "gemm_xwg_kernel", epi)
     if prenorm(w):
@@ -244,6 +256,9 @@ class Bench:
         per_copy += 2 * w.M * w.N if w.residual else 0
         if w.op == workloads.OP_LAZY_BWD:
             per_copy = 2 * (w.M * w.N + 3 * w.M * w.K)  # dC, A, dA, dA_hat
+        if w.op == workloads.OP_LAZY_BWD_RG:
+            # dC, A, dA, dA_hat, A_hat, rstd * dC, dB
+            per_copy = 2 * (2 * w.M * w.N + 4 * w.M * w.K + w.K * w.N)
         self.R = max(1, min(8, math.ceil(ROTATE_BYTES / per_copy)))
         A0 = up(x.A)
         self.A = [A0] + [A0.clone() for _ in range(self.R - 1)]
@@ -262,6 +277,24 @@ class Bench:
             self.dC = [G0] + [G0.clone() for _ in range(self.R - 1)]
             self.C = [torch.empty((w.K, w.N), dtype=torch.bfloat16, device=dev)
                       for _ in range(self.R)]
+        if w.op == workloads.OP_LAZY_BWD_RG:
+            # the forward pass's saved rstd (untimed); outputs dA [M, K] and
+            # dB [K, N], the scratch rstd * dC [M, N]; the unfused pair's
+            # dA_hat and A_hat
+            self.rstd = torch.empty(w.M, dtype=torch.float32, device=dev)
+            ng.rmsnorm_gemm_lazy(A0, self.B, eps=w.eps, rstd_out=self.rstd)
+            G0 = up(x.dC)
+            self.dC = [G0] + [G0.clone() for _ in range(self.R - 1)]
+            self.C = [torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev)
+                      for _ in range(self.R)]
+            self.dAh = [torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev)
+                        for _ in range(self.R)]
+            self.dB = [torch.empty((w.K, w.N), dtype=torch.bfloat16, device=dev)
+                       for _ in range(self.R)]
+            self.scratch = [torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+                            for _ in range(self.R)]
+            An0 = ng.norm(A0, "rms", eps=w.eps)
+            self.An = [An0] + [An0.clone() for _ in range(self.R - 1)]
         if w.op == workloads.OP_LAZY_BWD:
             # the forward pass's saved rstd (untimed); outputs are [M, K]
             self.rstd = torch.empty(w.M, dtype=torch.float32, device=dev)
@@ -290,6 +323,7 @@ class Bench:
               workloads.OP_LAZY_AFFINE: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_PRENORM_LN: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_LAZY_BWD: ng.NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT,
+              workloads.OP_LAZY_BWD_RG: ng.NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT,
               workloads.OP_LAZY_BWD_W: ng.NG_OP_RMSNORM_GEMM_LAZY,
               workloads.OP_GEMM_RMSNORM: ng.NG_OP_GEMM_RMSNORM,
               workloads.OP_GEMM_LAYERNORM: ng.NG_OP_GEMM_LAYERNORM,
@@ -331,6 +365,19 @@ class Bench:
                 # unfused: A_hat stored by ng_norm, then dB = A_hat^T @ dC
                 self._gemm.append((lib.ng_gemm_at, (An, G, C, K, N, M, st)))
                 self._norm.append((lib.ng_norm, (A, None, None, An, M, K, 0, eps, None, None, st)))
+            elif w.op == workloads.OP_LAZY_BWD_RG:
+                G, dAh, rs = self.dC[r].data_ptr(), self.dAh[r].data_ptr(), self.rstd.data_ptr()
+                dB, sc, An = (self.dB[r].data_ptr(), self.scratch[r].data_ptr(),
+                              self.An[r].data_ptr())
+                self._fused.append((lib.ng_rmsnorm_gemm_lazy_backward,
+                                    (G, B, A, rs, C, dB, sc, M, N, K, 0, ws, wsb, st)))
+                # unfused: dA_hat = dC @ B^T and dB = A_hat^T @ dC (A_hat stored
+                # by ng_norm); the norm's backward and the norm itself
+                self._gemm.append([(lib.ng_gemm, (G, B, dAh, M, K, N, 1, st)),
+                                   (lib.ng_gemm_at, (An, G, dB, K, N, M, st))])
+                self._norm.append([(lib.ng_rmsnorm_backward, (dAh, A, rs, C, M, K, st)),
+                                   (lib.ng_norm, (A, None, None, An, M, K, 0, eps, None, None,
+                                                  st))])
             elif w.op == workloads.OP_LAZY_BWD:
                 G, dAh, rs = self.dC[r].data_ptr(), self.dAh[r].data_ptr(), self.rstd.data_ptr()
                 self._fused.append((lib.ng_rmsnorm_gemm_lazy_backward_input,
@@ -380,10 +427,11 @@ class Bench:
                 self._norm.append((lib.ng_norm, (C, g, b, C, M, N, 1, eps, None, None, st)))
 
     def _call(self, table, i):
-        fn, args = table[i % self.R]
-        status = fn(*args)
-        if status != 0:
-            raise self.ng.NormGemmError(status, fn.__name__)
+        entry = table[i % self.R]
+        for fn, args in (entry if isinstance(entry, list) else [entry]):
+            status = fn(*args)
+            if status != 0:
+                raise self.ng.NormGemmError(status, fn.__name__)
 
     def fused(self, i):
         self._call(self._fused, i)
@@ -399,7 +447,8 @@ class Bench:
     # the same board at the same clock and power cap, not part of any
     # measured path.  Only for the forward products C = A @ B.
     def has_library_gemm(self):
-        return self.w.op not in (workloads.OP_LAZY_BWD, workloads.OP_LAZY_BWD_W)
+        return self.w.op not in (workloads.OP_LAZY_BWD, workloads.OP_LAZY_BWD_W,
+                                 workloads.OP_LAZY_BWD_RG)
 
     def library_gemm(self, i):
         r = i % self.R
@@ -607,7 +656,7 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
             oracle.rmsnorm_gemm_lazy_affine(x.A, x.B, w.eps, x.gamma, x.beta)
         elif w.op == workloads.OP_PRENORM_LN:
             oracle.layernorm_gemm_prenorm(x.A, x.B, w.eps, x.gamma, x.beta)
-        elif w.op == workloads.OP_LAZY_BWD:
+        elif w.op in (workloads.OP_LAZY_BWD, workloads.OP_LAZY_BWD_RG):
             oracle.rmsnorm_gemm_lazy_backward(x.A, x.B, x.dC, w.eps)
         elif w.op == workloads.OP_LAZY_BWD_W:
             oracle.lazy_backward_weight(x.A, x.dC, w.eps)
@@ -627,7 +676,7 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
             rows = min(w.M, rows * 4)
             x = sample(rows)
     # the backward oracle also forms the weight gradient: two products per row
-    products = 2 if w.op == workloads.OP_LAZY_BWD else 1
+    products = 2 if w.op in (workloads.OP_LAZY_BWD, workloads.OP_LAZY_BWD_RG) else 1
     flops = 2.0 * products * done_rows * w.N * w.K
     return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores),
             "kind": "oracle", "blas": blas_info(),

@@ -311,6 +311,32 @@ ng_status ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* 
                                           int b_layout, void* stream);
 
 /*
+ * Both gradients of Lazy Pre-Norm (C = rmsnorm(A) @ B, RMSNorm without
+ * affine), with the weight gradient regrouped ("Towards Free Normalization"
+ * summary page, its abstract: backward passes get epilogue fusion by fusing
+ * the norm with a different matmul than in the forward pass).  Since
+ * dB = A_hat^T @ dC = A^T @ (rstd * dC), the row scale moves from the forward
+ * input onto the upstream gradient: the input-gradient kernel (as in
+ * ng_rmsnorm_gemm_lazy_backward_input, same arguments, workspace and rules)
+ * also writes dC_scaled = rstd * dC, rounded to bf16, while it runs, and dB
+ * is then the plain product over the forward rows (as ng_gemm_at):
+ *   dA as in ng_rmsnorm_gemm_lazy_backward_input;
+ *   dC_scaled[m, n] = bf16(rstd[m] * dC[m, n])        (bf16 [M, N], written);
+ *   dB = A^T @ dC_scaled                               (bf16, B's layout).
+ * dB is written in B's layout ([K, N] for NG_B_KN, [N, K] for NG_B_NK);
+ * M == 0 writes dB = 0.  dC_scaled is caller-owned scratch of M * N * 2
+ * bytes that must not overlap any other argument (NG_ERR_INVALID_ARG); dA
+ * and dB must not overlap the inputs.  Against ng_rmsnorm_gemm_lazy_backward_weight,
+ * which keeps no intermediate, this trades M * N * 2 bytes of scratch for a
+ * weight gradient at the speed of the plain product.
+ */
+ng_status ng_rmsnorm_gemm_lazy_backward(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
+                                   const float* rstd, ng_bf16* dA, ng_bf16* dB,
+                                   ng_bf16* dC_scaled, int64_t M, int64_t N, int64_t K,
+                                   int b_layout, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * Plain GEMM with the first operand stored transposed, the product half of
  * the weight gradient's unfused baseline: C [M, N] = A^T @ B with A stored
  * [K, M] and B stored [K, N] (the reduction runs over both matrices' rows),

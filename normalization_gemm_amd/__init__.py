@@ -21,7 +21,8 @@ from ._lib import (  # noqa: F401
     NG_OP_GEMM_RMSNORM, NG_OP_NORM, NG_OP_RMSNORM_GEMM_LAZY, NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT,
     ng_gemm, ng_gemm_add_layernorm, ng_gemm_add_rmsnorm, ng_gemm_layernorm, ng_gemm_rmsnorm,
     ng_add_norm, ng_last_error, ng_layernorm_gemm_fold, ng_layernorm_gemm_prenorm,
-    ng_lazy_fold_affine, ng_norm, ng_rmsnorm_backward, ng_rmsnorm_gemm_lazy_backward_input,
+    ng_lazy_fold_affine, ng_norm, ng_rmsnorm_backward, ng_rmsnorm_gemm_lazy_backward,
+    ng_rmsnorm_gemm_lazy_backward_input,
     ng_rmsnorm_gemm_lazy_backward_weight, ng_gemm_at,
     ng_rmsnorm_gemm_lazy, ng_rmsnorm_gemm_lazy_affine, ng_status_string, ng_workspace_bytes,
     ng_workspace_reset, ng_workspace_status, ng_set_debug_option,
@@ -33,7 +34,8 @@ __all__ = [
     "NormGemmError", "rmsnorm_gemm_lazy", "lazy_fold_affine", "rmsnorm_gemm_lazy_affine",
     "gemm_rmsnorm", "gemm_layernorm", "gemm_add_rmsnorm", "gemm_add_layernorm", "gemm", "norm",
     "add_norm", "layernorm_gemm_fold", "layernorm_gemm_prenorm",
-    "rmsnorm_gemm_lazy_backward_input", "rmsnorm_gemm_lazy_backward_weight", "rmsnorm_backward",
+    "rmsnorm_gemm_lazy_backward_input", "rmsnorm_gemm_lazy_backward_weight",
+    "rmsnorm_gemm_lazy_backward", "rmsnorm_backward",
     "gemm_at",
     "Workspace", "library_path", "debug_option",
 ]
@@ -332,6 +334,41 @@ def rmsnorm_gemm_lazy_backward_weight(A, dC, rstd, *, b_layout="kn", out=None, s
                                                 lay, _stream(stream)),
            "ng_rmsnorm_gemm_lazy_backward_weight")
     return dB
+
+
+def rmsnorm_gemm_lazy_backward(dC, B, A, rstd, *, b_layout="kn", out_dA=None, out_dB=None,
+                               scratch=None, workspace: Optional[Workspace] = None, stream=None):
+    """(dA, dB) for C = rmsnorm(A) @ B (no affine) given dC, the weight
+    gradient regrouped: the input-gradient kernel also writes rstd * dC into
+    `scratch` (bf16 [M, N]) and dB = A^T @ scratch is a plain product; dB in
+    B's layout."""
+    torch = _torch()
+    _dev_bf16(dC, "dC"); _dev_bf16(B, "B"); _dev_bf16(A, "A")
+    lay = _layout(b_layout)
+    M, N, K = _shapes(A, B, lay)
+    if tuple(dC.shape) != (M, N):
+        raise ValueError("dC must be [%d, %d] (got %s)" % (M, N, tuple(dC.shape)))
+    _f32_vec(rstd, M, "rstd")
+    dA = out_dA if out_dA is not None else torch.empty((M, K), dtype=torch.bfloat16,
+                                                       device=A.device)
+    _dev_bf16(dA, "out_dA")
+    shape = (K, N) if lay == NG_B_KN else (N, K)
+    dB = out_dB if out_dB is not None else torch.empty(shape, dtype=torch.bfloat16,
+                                                       device=A.device)
+    _dev_bf16(dB, "out_dB")
+    if tuple(dB.shape) != shape:
+        raise ValueError("out_dB must be %s" % (shape,))
+    sc = scratch if scratch is not None else torch.empty((M, N), dtype=torch.bfloat16,
+                                                         device=A.device)
+    _dev_bf16(sc, "scratch")
+    if sc.numel() != M * N:
+        raise ValueError("scratch must hold %d bf16 values" % (M * N))
+    ws, wsb = _workspace(NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT, M, N, K, A.device, workspace, stream)
+    _check(ng_rmsnorm_gemm_lazy_backward(_ptr(dC), _ptr(B), _ptr(A), _ptr(rstd), _ptr(dA),
+                                         _ptr(dB), _ptr(sc), M, N, K, lay, ws, wsb,
+                                         _stream(stream)),
+           "ng_rmsnorm_gemm_lazy_backward")
+    return dA, dB
 
 
 def gemm_at(A, B, *, out=None, stream=None):

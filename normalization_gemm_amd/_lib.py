@@ -58,6 +58,8 @@ _SIGNATURES = {
     "ng_layernorm_gemm_prenorm": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _F, _P, _P, _P]),
     "ng_rmsnorm_gemm_lazy_backward_input": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P,
                                                  _SZ, _P]),
+    "ng_rmsnorm_gemm_lazy_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P,
+                                           _SZ, _P]),
     "ng_rmsnorm_backward": (_I, [_P, _P, _P, _P, _I64, _I64, _P]),
     "ng_rmsnorm_gemm_lazy_backward_weight": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "ng_gemm_at": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),

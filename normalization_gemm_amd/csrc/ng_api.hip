@@ -743,10 +743,13 @@ ng_status ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, c
             : launch_persistent<TLarge<false>, ng::EPI_PRE_LN>(p, s, what);
 }
 
-ng_status ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
-                                         const float* rstd, ng_bf16* dA, int64_t M, int64_t N,
-                                         int64_t K, int b_layout, void* workspace,
-                                         size_t workspace_bytes, void* stream) {
+// The input gradient; with scaled_out, the kernel also writes rstd * dC
+// (the regrouped weight gradient's operand).
+static ng_status lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
+                                     const float* rstd, ng_bf16* dA, ng_bf16* scaled_out,
+                                     int64_t M, int64_t N, int64_t K, int b_layout,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     const char* what) {
   // dA_hat = dC [M, N] @ B^T [N, K]: the product's output width is the
   // forward K and its reduction the forward N; B^T is B read in the other
   // layout
@@ -769,10 +772,10 @@ ng_status ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* 
   ng::GemmParams p = make_params(dC, B, dA, M, K, N, 0.f);
   p.Xin = A;
   p.row_rstd = rstd;
+  p.scaled_out = (uint16_t*)scaled_out;
   p.ws = (char*)workspace;
   hipStream_t s = (hipStream_t)stream;
   const bool kn = lay == NG_B_KN;
-  const char* what = "ng_rmsnorm_gemm_lazy_backward_input";
   if (local && K <= 128)
     return kn ? launch_grid<TRow128<true>, ng::EPI_LAZY_BWD>(p, s, what)
               : launch_grid<TRow128<false>, ng::EPI_LAZY_BWD>(p, s, what);
@@ -781,6 +784,70 @@ ng_status ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* 
               : launch_grid<TRow256<false>, ng::EPI_LAZY_BWD>(p, s, what);
   return kn ? launch_xwg<TLarge<true>, false, false, true>(p, s, what)
             : launch_xwg<TLarge<false>, false, false, true>(p, s, what);
+}
+
+ng_status ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
+                                         const float* rstd, ng_bf16* dA, int64_t M, int64_t N,
+                                         int64_t K, int b_layout, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  return lazy_backward_input(dC, B, A, rstd, dA, nullptr, M, N, K, b_layout, workspace,
+                             workspace_bytes, stream, "ng_rmsnorm_gemm_lazy_backward_input");
+}
+
+ng_status ng_rmsnorm_gemm_lazy_backward(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
+                                   const float* rstd, ng_bf16* dA, ng_bf16* dB,
+                                   ng_bf16* dC_scaled, int64_t M, int64_t N, int64_t K,
+                                   int b_layout, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  const char* what = "ng_rmsnorm_gemm_lazy_backward";
+  if (!dB || (M != 0 && !dC_scaled))
+    return fail(NG_ERR_INVALID_ARG, "dB and dC_scaled must be non-NULL");
+  if (!aligned(dB, 16) || !aligned(dC_scaled, 16))
+    return fail(NG_ERR_INVALID_ARG, "dB and dC_scaled must be 16-byte aligned");
+  if (M > 0 && N > 0 && K > 0 && M <= kMaxDim && N <= kMaxDim && K <= kMaxDim) {
+    // the scratch is distinct from every other argument
+    const uintptr_t sc = (uintptr_t)dC_scaled, sce = sc + (uintptr_t)(M * N * 2);
+    const struct { const void* p; int64_t bytes; } others[] = {
+        {dC, M * N * 2}, {B, K * N * 2}, {A, M * K * 2}, {rstd, M * 4}, {dA, M * K * 2},
+        {dB, K * N * 2}};
+    for (const auto& o : others) {
+      const uintptr_t b = (uintptr_t)o.p, e = b + (uintptr_t)o.bytes;
+      if (o.p && b < sce && sc < e)
+        return fail(NG_ERR_INVALID_ARG, "dC_scaled must not overlap the other arguments");
+    }
+  }
+  // dA, and rstd * dC into dC_scaled (the checks of the input gradient apply)
+  ng_status st = lazy_backward_input(dC, B, A, rstd, dA, dC_scaled, M, N, K, b_layout, workspace,
+                                     workspace_bytes, stream, what);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (M == 0) {
+    // an empty sum over rows: dB = 0
+    const size_t n16 = (size_t)(K * N) / 8;
+    size_t blocks = (n16 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(ng::fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (ng::u32x4*)dB, n16, (uint32_t*)nullptr, (size_t)0);
+    return launched(what);
+  }
+  // dB = A^T (rstd * dC) over the forward rows: [K, N] = gemm_at(A, dC_scaled)
+  // for B stored [K, N]; [N, K] = gemm_at(dC_scaled, A) for B stored [N, K]
+  ng::GemmParams p{};
+  p.C = (uint16_t*)dB;
+  p.K = (int)M;
+  p.spin_limit = wait_spins();
+  if (b_layout == NG_B_KN) {
+    p.A = (const uint16_t*)A;
+    p.B = (const uint16_t*)dC_scaled;
+    p.M = (int)K;
+    p.N = (int)N;
+  } else {
+    p.A = (const uint16_t*)dC_scaled;
+    p.B = (const uint16_t*)A;
+    p.M = (int)N;
+    p.N = (int)K;
+  }
+  return launch_persistent<TWgrad<0>, ng::EPI_NONE>(p, s, what);
 }
 
 ng_status ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* dC, const float* rstd,

@@ -120,6 +120,7 @@ struct GemmParams {
   const float* row_mean;  // EPI_PRE_LN: fp32 [M] mean of each row of A
   const float* row_rstd;  // EPI_PRE_LN: fp32 [M] rstd of each row of A; EPI_LAZY_BWD: saved rstd
   const uint16_t* Xin;    // EPI_LAZY_BWD: the forward input A, bf16 [M][N]
+  uint16_t* scaled_out;   // EPI_LAZY_BWD, optional: bf16 [M][K] rstd * (this product's A)
   float* mean_out;
   float* rstd_out;
   char* ws;
@@ -463,6 +464,48 @@ struct FragReader {
 
 __device__ __forceinline__ uint32_t scale_pair(uint32_t w, float r_lo, float r_hi) {
   return pack_bf16x2(bf16_lo(w) * r_lo, bf16_hi(w) * r_hi);
+}
+
+// Regrouped Lazy Pre-Norm weight gradient.  dB = A_hat^T dC with A_hat =
+// rstd * A equals A^T (rstd * dC): the scale can sit on the upstream
+// gradient instead, so that the weight gradient becomes a plain product.  The
+// input-gradient kernel, whose own A operand is dC ([M, K] here), writes
+// rstd * dC, rounded to bf16, for the rows of each row block, split by rows
+// over the row block's `parts` workgroups (rows past M are skipped).  It
+// runs in the epilogue, after the k-loop's transfers have all landed, so its
+// loads and stores are the compiler's to count.
+template <class T>
+__device__ __forceinline__ void write_scaled_rows(const GemmParams& p, int m_base, int part,
+                                                  int parts, int tid) {
+  const int rows = min(T::BM, p.M - m_base);
+  const int rpp = (rows + parts - 1) / parts;
+  const int r0 = part * rpp, r1 = min(rows, r0 + rpp);
+  const int cpr = p.K / 8;  // 16-byte chunks per row
+  constexpr int RB = 4;     // rows in flight per lane
+  for (int c = tid; c < cpr; c += T::NT) {
+    for (int r = r0; r < r1; r += RB) {
+      u32x4 v[RB];
+      float sc[RB];
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        if (r + b < r1) {
+          const size_t off = (size_t)(m_base + r + b) * (size_t)p.K + 8u * (size_t)c;
+          v[b] = *(const u32x4*)(p.A + off);
+          sc[b] = p.row_rstd[m_base + r + b];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        if (r + b < r1) {
+          const size_t off = (size_t)(m_base + r + b) * (size_t)p.K + 8u * (size_t)c;
+          u32x4 w = v[b];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) w[q] = scale_pair(w[q], sc[b], sc[b]);
+          *(u32x4*)(p.scaled_out + off) = w;
+        }
+      }
+    }
+  }
 }
 
 // RS: the scaled operand's k-tile is scaled in LDS, once per workgroup (a
@@ -1407,6 +1450,8 @@ __device__ __forceinline__ void process_tile(const GemmParams& p, lds_char* lds,
   float mean[T::FM], rstd[T::FM];
   tile_scale<T, EPI>(p, acc, ss, lds, m_base, n_base, tn, wm, wn, lane, ax, mean, rstd);
   tile_store<T, EPI>(p, acc, mean, rstd, aff, bias, lds, m_base, n_base, wave, wm, wn, lane, ax);
+  if constexpr (EPI == EPI_LAZY_BWD)
+    if (p.scaled_out) write_scaled_rows<T>(p, m_base, tn, p.tiles_n, tid);
 }
 
 // Tile order shared by the grids: tiles grouped 4 tile-rows high, column-major
@@ -1826,6 +1871,10 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
       if (tm + R < p.tiles_m && !xt) issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid);
     }
     xwg_merge_rows<T, LN, BWD>(p, rb_in, R, tm, tn, tid, tag);
+    // (regrouped weight gradient: this workgroup's rows of rstd * dC, while
+    // the other workgroups of the row block merge)
+    if constexpr (BWD)
+      if (p.scaled_out) write_scaled_rows<T>(p, m_base, tn, p.tiles_n, tid);
     // step 5: (mean, rstd) of this wave's rows; BWD: (c, rstd) from the row's
     // sum of acc * X and the saved rstd
     const __amdgpu_buffer_rsrc_t frs = xwg_fin_rsrc<T>(p, rb_in, R);

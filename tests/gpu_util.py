@@ -28,8 +28,9 @@ def wgrad_excess(got, ref, A_hat, dC):
     A_hat) exceeds its bar, per element (<= 0 everywhere means it passes).
 
     The kernel multiplies A_hat rounded to bf16 (nearest even, the rounding a
-    stored A_hat has), so each product a_m * g_m carries an independent
-    relative error of at most 2^-9, roughly uniform: the sum over the M rows
+    stored A_hat has) -- or, regrouped, A times rstd * dC rounded to bf16 --
+    so each product a_m * g_m carries an independent relative error of at
+    most 2^-9, roughly uniform: the sum over the M rows
     errs by about 2^-9 / sqrt(3) * sqrt(sum_m (a_m g_m)^2) (one standard
     deviation).  The bar is the plain 1e-2 * (1 + |ref|) plus 8 * 2^-9 times
     that root sum of squares (about 14 standard deviations, so a correct

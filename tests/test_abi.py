@@ -35,7 +35,8 @@ def test_header_declares_expected_entry_points():
               "ng_rmsnorm_gemm_lazy_affine", "ng_gemm_add_rmsnorm", "ng_gemm_add_layernorm",
               "ng_add_norm", "ng_layernorm_gemm_fold", "ng_layernorm_gemm_prenorm",
               "ng_rmsnorm_gemm_lazy_backward_input", "ng_rmsnorm_backward",
-              "ng_rmsnorm_gemm_lazy_backward_weight", "ng_gemm_at"):
+              "ng_rmsnorm_gemm_lazy_backward_weight", "ng_gemm_at",
+              "ng_rmsnorm_gemm_lazy_backward"):
         assert n in names
 
 
@@ -189,6 +190,7 @@ def test_lazy_affine_argument_checks():
 
 P4 = P + 0x300000
 P5 = P + 0x400000
+P6 = P + 0x500000
 
 
 def test_residual_argument_checks():
@@ -274,6 +276,19 @@ def test_lazy_backward_argument_checks():
     assert w(P, P2, P3 + 2, P4, 64, 128, 64, 0, None) == 1       # rstd misaligned
     assert w(P, P2, P3, P4, 64, 128, 64, 2, None) == 1           # layout
     assert w(P, P2, P3, P4, 64, 100, 64, 0, None) == 2           # N % 8
+    b = _lib.ng_rmsnorm_gemm_lazy_backward
+    SC = 1 << 44  # scratch of 64 * 128 * 2 bytes, away from the other arguments
+    assert b(P, P2, P5, P4, P3, None, SC, 64, 128, 64, 0, None, 0, None) == 1   # dB NULL
+    assert b(P, P2, P5, P4, P3, P6, None, 64, 128, 64, 0, None, 0, None) == 1   # scratch NULL
+    assert b(P, P2, P5, P4, P3, P6, SC + 8, 64, 128, 64, 0, None, 0, None) == 1  # misaligned
+    # the scratch overlapping the input gradient, or starting inside dC
+    assert b(P, P2, P5, P4, P3, P6, P3 - 1024, 64, 128, 64, 0, None, 0, None) == 1
+    assert "overlap" in _lib.ng_last_error()
+    assert b(P, P2, P5, P4, P3, P6, P + 4096, 64, 128, 64, 0, None, 0, None) == 1
+    # then the input gradient's checks
+    assert b(P, P2, None, P4, P3, P6, SC, 64, 128, 64, 0, None, 0, None) == 1   # A NULL
+    assert b(P, P2, P5, P4, P3, P6, SC, 64, 128, 60, 0, None, 0, None) == 2     # K % 8
+    assert b(P, P2, P5, P4, P3, P6, SC, 64, 128, 4096, 0, None, 0, None) == 3   # workspace
     at = _lib.ng_gemm_at
     assert at(None, P2, P3, 64, 64, 8, None) == 1
     assert at(P, P2, P3, 60, 64, 8, None) == 2                   # M % 8

@@ -539,6 +539,53 @@ def test_lazy_backward_input_cross_workgroup_rounds_ragged():
         _check("lazy backward xwg rounds", down(dA), ref)
 
 
+def _check_scaled(name, got_bits, dC_bits, rstd_ref):
+    # rstd * dC rounded once to bf16: within one bf16 rounding (2^-8
+    # relative, nearest even) of the fp64 product, plus the fp32 rstd's error
+    ref = rstd_ref[:, None] * oracle.bf16_to_f64(dC_bits)
+    got = oracle.bf16_to_f64(got_bits)
+    err = np.abs(got - ref) - (2.0 ** -8 + 1e-5) * np.abs(ref)
+    log("%s: worst excess over one rounding %.3e" % (name, err.max()))
+    assert np.all(err <= 0), (name, err.max())
+
+
+# the regrouped backward: forward (M, N, K) over the input gradient's three
+# strategies (rows of length K <= 128, <= 256, wider: one and several rounds)
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("M,N,K", [(300, 136, 128), (77, 72, 200), (513, 264, 520), (1, 8, 8),
+                                   (260, 96, 1000), (256 * 30 + 100, 136, 256 * 9 + 24)])
+def test_lazy_backward_regrouped(M, N, K, layout):
+    log("lazy backward regrouped M=%d N=%d K=%d %s" % (M, N, K, layout))
+    x = workloads.make_inputs(M, N, K, seed=7 * M + N + K, row_scale=True, upstream=True)
+    A, B = up(x.A), up(b_for_layout(x.B, layout))
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    ng.rmsnorm_gemm_lazy(A, B, eps=1e-6, b_layout=layout, rstd_out=rstd)
+    scratch = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dA, dB = ng.rmsnorm_gemm_lazy_backward(up(x.dC), B, A, rstd, b_layout=layout,
+                                           scratch=scratch)
+    torch.cuda.synchronize()
+    dA_ref, _, rref = oracle.rmsnorm_gemm_lazy_backward(x.A, x.B, x.dC, 1e-6)
+    _check("regrouped dA", down(dA), dA_ref)
+    _check_scaled("regrouped rstd * dC", down(scratch), x.dC, rref)
+    ref = oracle.lazy_backward_weight(x.A, x.dC, 1e-6)
+    got = down(dB) if layout == "kn" else np.ascontiguousarray(down(dB).T)
+    _check_wgrad("regrouped dB %s" % layout, got, ref, x.A, x.dC, 1e-6)
+
+
+def test_lazy_backward_regrouped_empty_rows():
+    dC = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((128, 64), dtype=torch.bfloat16, device="cuda")
+    rstd = torch.zeros(0, dtype=torch.float32, device="cuda")
+    dB = torch.full((128, 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    dA, dB = ng.rmsnorm_gemm_lazy_backward(dC, B, A, rstd, out_dB=dB,
+                                           scratch=torch.empty(0, dtype=torch.bfloat16,
+                                                               device="cuda"))
+    torch.cuda.synchronize()
+    assert tuple(dA.shape) == (0, 128)
+    assert int(torch.count_nonzero(dB)) == 0
+
+
 # forward (M, N, K): M (the reduction here) ragged and short; N, K over tiles
 @pytest.mark.parametrize("layout", ["kn", "nk"])
 @pytest.mark.parametrize("M,N,K", [(300, 136, 200), (77, 264, 520), (1000, 64, 128), (1, 8, 8),
@@ -889,6 +936,25 @@ def _workload_case(w, layout="kn"):
         ref = oracle.lazy_backward_weight(x.A, x.dC, w.eps)
         _check_wgrad(w.name + " (every element)", down(C), ref, x.A, x.dC, w.eps)
         return
+    elif w.op == workloads.OP_LAZY_BWD_RG:
+        rstd = _f32(M)
+        ng.rmsnorm_gemm_lazy(A, B, eps=w.eps, b_layout=layout, rstd_out=rstd)
+        scratch = torch.empty((M, w.N), dtype=torch.bfloat16, device="cuda")
+        C, dB = ng.rmsnorm_gemm_lazy_backward(up(x.dC), B, A, rstd, b_layout=layout,
+                                              scratch=scratch)
+        if layout == "nk":
+            dB = dB.t().contiguous()
+        torch.cuda.synchronize()
+        ref = oracle.lazy_backward_weight(x.A, x.dC, w.eps)
+        _check_wgrad(w.name + " dB (every element)", down(dB), ref, x.A, x.dC, w.eps)
+        del ref
+        _check_scaled(w.name + " rstd * dC (every element)", down(scratch), x.dC,
+                      oracle.rms_norm_rows(x.A, w.eps)[1])
+        stats = {"rstd": rstd}
+
+        def ref_rows(r0, r1):
+            dA, _, r = oracle.rmsnorm_gemm_lazy_backward(x.A[r0:r1], B64, x.dC[r0:r1], w.eps)
+            return dA, {"rstd": r}
     elif w.op == workloads.OP_PRENORM_LN:
         C, mean, rstd = _prenorm_case(x, layout, w.eps)[:3]
         stats = {"mean": mean, "rstd": rstd}

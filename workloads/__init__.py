@@ -46,6 +46,7 @@ OP_GEMM_ADD_LAYERNORM = "gemm_add_layernorm"
 OP_PRENORM_LN = "layernorm_gemm_prenorm"
 OP_LAZY_BWD = "rmsnorm_gemm_lazy_backward_input"
 OP_LAZY_BWD_W = "rmsnorm_gemm_lazy_backward_weight"
+OP_LAZY_BWD_RG = "rmsnorm_gemm_lazy_backward"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -66,7 +67,8 @@ class Workload:
 
     @property
     def flops(self) -> int:
-        return 2 * self.M * self.N * self.K
+        # both gradients of the regrouped backward: two products
+        return (4 if self.op == OP_LAZY_BWD_RG else 2) * self.M * self.N * self.K
 
 
 WORKLOADS = [
@@ -108,6 +110,11 @@ NEXT_WORKLOADS = [
              row_scale=True, upstream=True,
              description="Lazy Pre-Norm weight gradient: A_hat^T @ dC over 32768 rows, A_hat "
                          "rebuilt from A (32768x4096) and rstd"),
+    Workload("lazy_rms_bwd_regrouped_32768x4096x4096", OP_LAZY_BWD_RG, 32768, 4096, 4096, 1e-6,
+             row_scale=True, upstream=True,
+             description="Lazy Pre-Norm backward, both gradients, the weight gradient "
+                         "regrouped: the input gradient over rows of A (32768x4096) also "
+                         "writes rstd * dC, then dB = A^T @ (rstd * dC)"),
     Workload("gemm_add_ln_65536x512x128", OP_GEMM_ADD_LAYERNORM, 65536, 128, 512, 1e-5,
              residual=True,
              description="GEMM + residual add + LayerNorm epilogue (no affine), "
