@@ -604,6 +604,26 @@ def test_lazy_backward_weight_small(M, N, K, layout):
     _check_wgrad("lazy backward dB %s" % layout, got, ref, x.A, x.dC, 1e-6)
 
 
+# the scaled operand's pipeline (32-deep k-tiles, 4 stages, scaling one
+# k-tile ahead) with 2, 4, 5, 6 and 7 k-tiles over the forward rows: the
+# prologue and tail paths around the steady loop
+@pytest.mark.parametrize("layout", ["kn", "nk"])
+@pytest.mark.parametrize("M", [40, 128, 150, 170, 200])
+def test_lazy_backward_weight_short_reductions(M, layout):
+    N, K = 264, 136
+    log("lazy backward weight short M=%d %s" % (M, layout))
+    x = workloads.make_inputs(M, N, K, seed=5 * M + 3, row_scale=True, upstream=True)
+    A = up(x.A)
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    ng.rmsnorm_gemm_lazy(A, up(b_for_layout(x.B, layout)), eps=1e-6, b_layout=layout,
+                         rstd_out=rstd)
+    dB = ng.rmsnorm_gemm_lazy_backward_weight(A, up(x.dC), rstd, b_layout=layout)
+    torch.cuda.synchronize()
+    ref = oracle.lazy_backward_weight(x.A, x.dC, 1e-6)
+    got = down(dB) if layout == "kn" else np.ascontiguousarray(down(dB).T)
+    _check_wgrad("lazy backward dB short %s" % layout, got, ref, x.A, x.dC, 1e-6)
+
+
 def test_lazy_backward_weight_empty_rows_give_zero():
     dC = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
     A = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
