@@ -624,6 +624,29 @@ def test_lazy_backward_weight_short_reductions(M, layout):
     _check_wgrad("lazy backward dB short %s" % layout, got, ref, x.A, x.dC, 1e-6)
 
 
+def test_weight_gradient_products_many_tiles():
+    # 17 x 17 = 289 output tiles on a 256-workgroup grid: some workgroups take
+    # a second tile, whose first k-tiles are issued before the first tile's
+    # output is stored (the scaled pipeline's waits count those stores)
+    M, N, K = 100, 4352, 4352
+    x = workloads.make_inputs(M, N, K, seed=41, row_scale=True, upstream=True)
+    A, G = up(x.A), up(x.dC)
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    ng.rmsnorm_gemm_lazy(A, up(x.B), eps=1e-6, rstd_out=rstd)
+    ref = oracle.lazy_backward_weight(x.A, x.dC, 1e-6)
+    for layout in ("kn", "nk"):
+        log("weight gradient many tiles %s" % layout)
+        dB = ng.rmsnorm_gemm_lazy_backward_weight(A, G, rstd, b_layout=layout)
+        torch.cuda.synchronize()
+        got = down(dB) if layout == "kn" else np.ascontiguousarray(down(dB).T)
+        _check_wgrad("weight gradient many tiles %s" % layout, got, ref, x.A, x.dC, 1e-6)
+    # the plain transposed product on the same tiles: A^T @ dC
+    C = ng.gemm_at(A, G)
+    torch.cuda.synchronize()
+    _check("gemm_at many tiles", down(C),
+           oracle.gemm(np.ascontiguousarray(x.A.T), x.dC))
+
+
 def test_lazy_backward_weight_empty_rows_give_zero():
     dC = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
     A = torch.zeros((0, 128), dtype=torch.bfloat16, device="cuda")
