@@ -129,6 +129,17 @@ def summarize_pmc(fetch_dir, write_dir, w, copy_mib):
            "copy_mib": copy_mib, "counters": out,
            "bytes_per_launch": int(out["FETCH_SIZE"]["fused_bytes"] + out["WRITE_SIZE"]["fused_bytes"]),
            "algorithmic_bytes": algorithmic_bytes(w)}
+    # the vendor library's product on the same operands, when the run timed it
+    # (hipBLASLt kernels are named Cijk_...): the same counters, same scaling
+    lib = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [(k, v) for k, v in _pmc_rows(d, counter) if k.startswith("Cijk_")]
+        if rows:
+            lib[counter] = statistics.median(v for _, v in rows) * 1024.0 * out[counter]["factor"]
+            lib["kernel"] = rows[0][0].split("(")[0][:80]
+    if "FETCH_SIZE" in lib and "WRITE_SIZE" in lib:
+        lib["bytes_per_launch"] = int(lib["FETCH_SIZE"] + lib["WRITE_SIZE"])
+        rec["library_gemm"] = lib
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % w.name)
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
