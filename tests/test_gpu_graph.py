@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import TOL, b_for_layout, down, log, up
+from gpu_util import TOL, b_for_layout, down, log, up, wgrad_excess
 
 pytestmark = pytest.mark.gpu
 
@@ -100,6 +100,45 @@ def test_graph_replays_a_chain_of_forms():
         _check("chain replay %d: residual rmsnorm" % rep, down(Y), ref_y)
         _check("chain replay %d: lazy" % rep, down(C), ref_c)
         _check("chain replay %d: lazy input gradient" % rep, down(dA), ref_da)
+    assert ws.status() == 0
+
+
+def test_graph_replays_the_backward():
+    # one graph: the Lazy forward (saving rstd), both gradients regrouped
+    # (wide rows: the input gradient also writes rstd * dC, then the plain
+    # product), and the weight gradient rebuilt on chip
+    M, N, K = 700, 264, 520
+    x = workloads.make_inputs(M, N, K, seed=63, row_scale=True, upstream=True)
+    A, B, G = up(x.A), up(x.B), up(x.dC)
+    ws = ng.Workspace(ng.ng_workspace_bytes(ng.NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT, M, N, K))
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dB = torch.empty((K, N), dtype=torch.bfloat16, device="cuda")
+    dB2 = torch.empty((K, N), dtype=torch.bfloat16, device="cuda")
+    sc = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+
+    def chain():
+        ng.rmsnorm_gemm_lazy(A, B, eps=1e-6, out=C, rstd_out=rstd)
+        ng.rmsnorm_gemm_lazy_backward(G, B, A, rstd, out_dA=dA, out_dB=dB, scratch=sc,
+                                      workspace=ws)
+        ng.rmsnorm_gemm_lazy_backward_weight(A, G, rstd, out=dB2)
+
+    ref_da = oracle.rmsnorm_gemm_lazy_backward(x.A, x.B, x.dC, 1e-6)[0]
+    ref_db = oracle.lazy_backward_weight(x.A, x.dC, 1e-6)
+    A_hat, _ = oracle.rms_norm_rows(x.A, 1e-6)
+    G64 = oracle.bf16_to_f64(x.dC)
+    graph = _capture(chain)
+    for rep in range(3):
+        for t in (dA, dB, dB2):
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        _check("backward replay %d: dA" % rep, down(dA), ref_da)
+        for name, t in (("regrouped dB", dB), ("rebuilt dB", dB2)):
+            excess = wgrad_excess(oracle.bf16_to_f64(down(t)), ref_db, A_hat, G64)
+            log("backward replay %d: %s worst excess %.3e" % (rep, name, excess.max()))
+            assert np.all(excess <= 0), (rep, name)
     assert ws.status() == 0
 
 
