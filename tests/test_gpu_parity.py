@@ -1052,6 +1052,17 @@ def test_named_workload_nk_layout_large():
     _workload_case(workloads.WORKLOAD_BY_NAME["gemm_rms_16384x4096x8192"], layout="nk")
 
 
+# B stored [N, K] (a Linear weight) at full size on the other large forms: the
+# 2-stage 64-deep tiles forward, and the backward's products in the other
+# layout (the input gradient then reads B as [K, N] on 32-deep tiles, whose
+# regrouped copy runs in the epilogue)
+@pytest.mark.parametrize("name", ["lazy_rms_32768x4096x4096", "gemm_ln_8192x8192x16384",
+                                  "lazy_rms_bwd_32768x4096x4096",
+                                  "lazy_rms_bwd_regrouped_32768x4096x4096"])
+def test_workload_nk_layout_full_size(name):
+    _workload_case(workloads.WORKLOAD_BY_NAME[name], layout="nk")
+
+
 # The unfused pairs the hidden-latency metric is measured against, at full
 # size, every element.
 def test_unfused_pairs_full_size_epilogue_forms():
