@@ -108,6 +108,22 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+def _empty(shape, dtype, device, stream):
+    """A new tensor for a call launched on `stream`.  torch's allocator ties a
+    block to the stream current at allocation; when the call runs on another
+    stream the block is recorded on that one too, so that it is not handed
+    out again (after the caller drops a temporary or an output) before the
+    launch stream has passed the call."""
+    torch = _torch()
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None:
+        dev = torch.device(device)
+        handle = _stream(stream)
+        if handle != torch.cuda.current_stream(dev).cuda_stream:
+            t.record_stream(torch.cuda.ExternalStream(handle, device=dev))
+    return t
+
+
 def _layout(b_layout):
     if b_layout in ("kn", NG_B_KN):
         return NG_B_KN
@@ -188,7 +204,7 @@ def rmsnorm_gemm_lazy(A, B, *, eps: float = 1e-6, b_layout="kn", out=None, rstd_
     _dev_bf16(A, "A"); _dev_bf16(B, "B")
     lay = _layout(b_layout)
     M, N, K = _shapes(A, B, lay)
-    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    C = out if out is not None else _empty((M, N), torch.bfloat16, A.device, stream)
     _dev_bf16(C, "out")
     _check(ng_rmsnorm_gemm_lazy(_ptr(A), _ptr(B), _ptr(C), M, N, K, lay, float(eps),
                                 _ptr(rstd_out), _stream(stream)), "ng_rmsnorm_gemm_lazy")
@@ -209,10 +225,9 @@ def lazy_fold_affine(B, gamma=None, beta=None, *, b_layout="kn", out=None, bias_
         _dev_bf16(gamma, "gamma")
     if beta is not None:
         _dev_bf16(beta, "beta")
-    Bf = out if out is not None else torch.empty_like(B)
+    Bf = out if out is not None else _empty(B.shape, B.dtype, B.device, stream)
     _dev_bf16(Bf, "out")
-    bias = bias_out if bias_out is not None else torch.empty(N, dtype=torch.float32,
-                                                             device=B.device)
+    bias = bias_out if bias_out is not None else _empty(N, torch.float32, B.device, stream)
     _check(ng_lazy_fold_affine(_ptr(B), _ptr(gamma), _ptr(beta), _ptr(Bf), _ptr(bias), K, N, lay,
                                _stream(stream)), "ng_lazy_fold_affine")
     return Bf, bias
@@ -229,7 +244,7 @@ def rmsnorm_gemm_lazy_affine(A, B_folded, bias=None, *, eps: float = 1e-6, b_lay
     if bias is not None and (bias.dtype != torch.float32 or bias.device.type != "cuda"
                              or not bias.is_contiguous()):
         raise ValueError("bias must be a contiguous float32 GPU tensor")
-    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    C = out if out is not None else _empty((M, N), torch.bfloat16, A.device, stream)
     _dev_bf16(C, "out")
     _check(ng_rmsnorm_gemm_lazy_affine(_ptr(A), _ptr(B_folded), _ptr(bias), _ptr(C), M, N, K, lay,
                                        float(eps), _ptr(rstd_out), _stream(stream)),
@@ -251,10 +266,10 @@ def layernorm_gemm_fold(B, gamma=None, beta=None, *, b_layout="kn", out=None, st
         _dev_bf16(gamma, "gamma")
     if beta is not None:
         _dev_bf16(beta, "beta")
-    Bf = out if out is not None else torch.empty_like(B)
+    Bf = out if out is not None else _empty(B.shape, B.dtype, B.device, stream)
     _dev_bf16(Bf, "out")
-    colsum = torch.empty(N, dtype=torch.float32, device=B.device)
-    bias = torch.empty(N, dtype=torch.float32, device=B.device)
+    colsum = _empty(N, torch.float32, B.device, stream)
+    bias = _empty(N, torch.float32, B.device, stream)
     _check(ng_layernorm_gemm_fold(_ptr(B), _ptr(gamma), _ptr(beta), _ptr(Bf), _ptr(colsum),
                                   _ptr(bias), K, N, lay, _stream(stream)), "ng_layernorm_gemm_fold")
     return Bf, colsum, bias
@@ -275,11 +290,9 @@ def layernorm_gemm_prenorm(A, B_folded, colsum, bias=None, *, eps: float = 1e-5,
             raise ValueError("%s must be a contiguous float32 GPU tensor of %d values" % (name, N))
     if colsum is None:
         raise ValueError("colsum is required")
-    mean = mean_out if mean_out is not None else torch.empty(M, dtype=torch.float32,
-                                                             device=A.device)
-    rstd = rstd_out if rstd_out is not None else torch.empty(M, dtype=torch.float32,
-                                                             device=A.device)
-    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    mean = mean_out if mean_out is not None else _empty(M, torch.float32, A.device, stream)
+    rstd = rstd_out if rstd_out is not None else _empty(M, torch.float32, A.device, stream)
+    C = out if out is not None else _empty((M, N), torch.bfloat16, A.device, stream)
     _dev_bf16(C, "out")
     _check(ng_layernorm_gemm_prenorm(_ptr(A), _ptr(B_folded), _ptr(colsum), _ptr(bias), _ptr(C),
                                      M, N, K, lay, float(eps), _ptr(mean), _ptr(rstd),
@@ -305,7 +318,7 @@ def rmsnorm_gemm_lazy_backward_input(dC, B, A, rstd, *, b_layout="kn", out=None,
     if tuple(dC.shape) != (M, N):
         raise ValueError("dC must be [%d, %d] (got %s)" % (M, N, tuple(dC.shape)))
     _f32_vec(rstd, M, "rstd")
-    dA = out if out is not None else torch.empty((M, K), dtype=torch.bfloat16, device=A.device)
+    dA = out if out is not None else _empty((M, K), torch.bfloat16, A.device, stream)
     _dev_bf16(dA, "out")
     ws, wsb = _workspace(NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT, M, N, K, A.device, workspace, stream)
     _check(ng_rmsnorm_gemm_lazy_backward_input(_ptr(dC), _ptr(B), _ptr(A), _ptr(rstd), _ptr(dA),
@@ -326,7 +339,7 @@ def rmsnorm_gemm_lazy_backward_weight(A, dC, rstd, *, b_layout="kn", out=None, s
     N = dC.shape[1]
     _f32_vec(rstd, M, "rstd")
     shape = (K, N) if lay == NG_B_KN else (N, K)
-    dB = out if out is not None else torch.empty(shape, dtype=torch.bfloat16, device=A.device)
+    dB = out if out is not None else _empty(shape, torch.bfloat16, A.device, stream)
     _dev_bf16(dB, "out")
     if tuple(dB.shape) != shape:
         raise ValueError("out must be %s" % (shape,))
@@ -349,17 +362,14 @@ def rmsnorm_gemm_lazy_backward(dC, B, A, rstd, *, b_layout="kn", out_dA=None, ou
     if tuple(dC.shape) != (M, N):
         raise ValueError("dC must be [%d, %d] (got %s)" % (M, N, tuple(dC.shape)))
     _f32_vec(rstd, M, "rstd")
-    dA = out_dA if out_dA is not None else torch.empty((M, K), dtype=torch.bfloat16,
-                                                       device=A.device)
+    dA = out_dA if out_dA is not None else _empty((M, K), torch.bfloat16, A.device, stream)
     _dev_bf16(dA, "out_dA")
     shape = (K, N) if lay == NG_B_KN else (N, K)
-    dB = out_dB if out_dB is not None else torch.empty(shape, dtype=torch.bfloat16,
-                                                       device=A.device)
+    dB = out_dB if out_dB is not None else _empty(shape, torch.bfloat16, A.device, stream)
     _dev_bf16(dB, "out_dB")
     if tuple(dB.shape) != shape:
         raise ValueError("out_dB must be %s" % (shape,))
-    sc = scratch if scratch is not None else torch.empty((M, N), dtype=torch.bfloat16,
-                                                         device=A.device)
+    sc = scratch if scratch is not None else _empty((M, N), torch.bfloat16, A.device, stream)
     _dev_bf16(sc, "scratch")
     if sc.numel() != M * N:
         raise ValueError("scratch must hold %d bf16 values" % (M * N))
@@ -379,7 +389,7 @@ def gemm_at(A, B, *, out=None, stream=None):
         raise ValueError("A [K, M] and B [K, N] must share K")
     K, M = A.shape
     N = B.shape[1]
-    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    C = out if out is not None else _empty((M, N), torch.bfloat16, A.device, stream)
     _dev_bf16(C, "out")
     _check(ng_gemm_at(_ptr(A), _ptr(B), _ptr(C), M, N, K, _stream(stream)), "ng_gemm_at")
     return C
@@ -393,7 +403,7 @@ def rmsnorm_backward(dY, X, rstd, *, out=None, stream=None):
         raise ValueError("dY and X must be 2-D of one shape")
     rows, cols = X.shape
     _f32_vec(rstd, rows, "rstd")
-    dX = out if out is not None else torch.empty_like(X)
+    dX = out if out is not None else _empty(X.shape, X.dtype, X.device, stream)
     _dev_bf16(dX, "out")
     _check(ng_rmsnorm_backward(_ptr(dY), _ptr(X), _ptr(rstd), _ptr(dX), rows, cols,
                                _stream(stream)), "ng_rmsnorm_backward")
@@ -409,7 +419,7 @@ def gemm_rmsnorm(A, B, gamma=None, *, eps: float = 1e-6, b_layout="kn", out=None
         _dev_bf16(gamma, "gamma")
     lay = _layout(b_layout)
     M, N, K = _shapes(A, B, lay)
-    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    C = out if out is not None else _empty((M, N), torch.bfloat16, A.device, stream)
     _dev_bf16(C, "out")
     ws, wsb = _workspace(NG_OP_GEMM_RMSNORM, M, N, K, A.device, workspace, stream)
     _check(ng_gemm_rmsnorm(_ptr(A), _ptr(B), _ptr(gamma), _ptr(C), M, N, K, lay, float(eps),
@@ -429,7 +439,7 @@ def gemm_layernorm(A, B, gamma=None, beta=None, *, eps: float = 1e-5, b_layout="
         _dev_bf16(beta, "beta")
     lay = _layout(b_layout)
     M, N, K = _shapes(A, B, lay)
-    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    C = out if out is not None else _empty((M, N), torch.bfloat16, A.device, stream)
     _dev_bf16(C, "out")
     ws, wsb = _workspace(NG_OP_GEMM_LAYERNORM, M, N, K, A.device, workspace, stream)
     _check(ng_gemm_layernorm(_ptr(A), _ptr(B), _ptr(gamma), _ptr(beta), _ptr(C), M, N, K, lay,
@@ -461,7 +471,7 @@ def gemm_add_rmsnorm(A, B, R, gamma=None, *, eps: float = 1e-6, b_layout="kn", o
     lay = _layout(b_layout)
     M, N, K = _shapes(A, B, lay)
     _residual(R, s_out, M, N)
-    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    C = out if out is not None else _empty((M, N), torch.bfloat16, A.device, stream)
     _dev_bf16(C, "out")
     ws, wsb = _workspace(NG_OP_GEMM_ADD_RMSNORM, M, N, K, A.device, workspace, stream)
     _check(ng_gemm_add_rmsnorm(_ptr(A), _ptr(B), _ptr(R), _ptr(gamma), _ptr(C), _ptr(s_out), M, N,
@@ -484,7 +494,7 @@ def gemm_add_layernorm(A, B, R, gamma=None, beta=None, *, eps: float = 1e-5, b_l
     lay = _layout(b_layout)
     M, N, K = _shapes(A, B, lay)
     _residual(R, s_out, M, N)
-    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    C = out if out is not None else _empty((M, N), torch.bfloat16, A.device, stream)
     _dev_bf16(C, "out")
     ws, wsb = _workspace(NG_OP_GEMM_ADD_LAYERNORM, M, N, K, A.device, workspace, stream)
     _check(ng_gemm_add_layernorm(_ptr(A), _ptr(B), _ptr(R), _ptr(gamma), _ptr(beta), _ptr(C),
@@ -500,7 +510,7 @@ def gemm(A, B, *, b_layout="kn", out=None, stream=None):
     _dev_bf16(A, "A"); _dev_bf16(B, "B")
     lay = _layout(b_layout)
     M, N, K = _shapes(A, B, lay)
-    C = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    C = out if out is not None else _empty((M, N), torch.bfloat16, A.device, stream)
     _dev_bf16(C, "out")
     _check(ng_gemm(_ptr(A), _ptr(B), _ptr(C), M, N, K, lay, _stream(stream)), "ng_gemm")
     return C
@@ -518,7 +528,7 @@ def norm(X, kind: str, gamma=None, beta=None, *, eps: float = 1e-5, out=None, me
         _dev_bf16(gamma, "gamma")
     if beta is not None:
         _dev_bf16(beta, "beta")
-    Y = out if out is not None else torch.empty_like(X)
+    Y = out if out is not None else _empty(X.shape, X.dtype, X.device, stream)
     _dev_bf16(Y, "out")
     rows, cols = X.shape
     _check(ng_norm(_ptr(X), _ptr(gamma), _ptr(beta), _ptr(Y), rows, cols, k, float(eps),
@@ -541,7 +551,7 @@ def add_norm(X, R, kind: str, gamma=None, beta=None, *, eps: float = 1e-5, out=N
         _dev_bf16(gamma, "gamma")
     if beta is not None:
         _dev_bf16(beta, "beta")
-    Y = out if out is not None else torch.empty_like(X)
+    Y = out if out is not None else _empty(X.shape, X.dtype, X.device, stream)
     _dev_bf16(Y, "out")
     _check(ng_add_norm(_ptr(X), _ptr(R), _ptr(gamma), _ptr(beta), _ptr(Y), _ptr(s_out), rows, cols,
                        k, float(eps), _ptr(mean_out), _ptr(rstd_out), _stream(stream)),

@@ -586,6 +586,43 @@ def test_lazy_backward_regrouped_empty_rows():
     assert int(torch.count_nonzero(dB)) == 0
 
 
+def test_calls_on_a_side_stream_match_the_current_stream():
+    # every output and temporary the helpers allocate themselves (the
+    # regrouped backward's scratch, the pre-norm statistics, the per-stream
+    # workspace of the wide-row epilogue) for calls launched on another
+    # stream than the current one; the kernels are deterministic, so the
+    # results equal the same calls on the current stream bit for bit
+    M, N, K = 700, 1040, 264
+    x = workloads.make_inputs(M, N, K, seed=83, row_scale=True, row_shift=True, gamma=True,
+                              beta=True, gamma_len=K, upstream=True)
+    A, B, dC = up(x.A), up(x.B), up(x.dC)
+    g, b = up(x.gamma), up(x.beta)
+    xn = workloads.make_inputs(M, N, K, seed=84, gamma=True, beta=True)
+    An, Bn, gn, bn = up(xn.A), up(xn.B), up(xn.gamma), up(xn.beta)
+
+    def run(stream):
+        rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+        out = [ng.rmsnorm_gemm_lazy(A, B, eps=1e-6, rstd_out=rstd, stream=stream)]
+        out += list(ng.rmsnorm_gemm_lazy_backward(dC, B, A, rstd, stream=stream))
+        Bf, colsum, bias = ng.layernorm_gemm_fold(B, g, b, stream=stream)
+        out.append(ng.layernorm_gemm_prenorm(A, Bf, colsum, bias, eps=1e-5, stream=stream))
+        out.append(ng.gemm_layernorm(An, Bn, gn, bn, eps=1e-5, stream=stream))
+        return out
+
+    ref = run(None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = run(side)
+    side.synchronize()
+    torch.cuda.synchronize()
+    names = ["lazy", "regrouped dA", "regrouped dB", "prenorm", "wide-row layernorm"]
+    for name, r, o in zip(names, ref, got):
+        assert torch.equal(r.view(torch.int16), o.view(torch.int16)), name
+    c_ref, _, _ = oracle.gemm_layernorm(xn.A, xn.B, 1e-5, xn.gamma, xn.beta)
+    _check("wide-row layernorm on a side stream", down(got[4]), c_ref)
+
+
 # forward (M, N, K): M (the reduction here) ragged and short; N, K over tiles
 @pytest.mark.parametrize("layout", ["kn", "nk"])
 @pytest.mark.parametrize("M,N,K", [(300, 136, 200), (77, 264, 520), (1000, 64, 128), (1, 8, 8),
