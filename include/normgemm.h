@@ -49,7 +49,7 @@ typedef uint16_t ng_bf16; /* raw bfloat16 bits */
 typedef enum {
   NG_OK = 0,
   NG_ERR_INVALID_ARG = 1, /* NULL/misaligned pointer, bad size, bad eps or enum */
-  NG_ERR_UNSUPPORTED = 2, /* valid request the library does not tile (N or K not a multiple of 8, ...) */
+  NG_ERR_UNSUPPORTED = 2, /* a valid request the library does not tile (see the limits) */
   NG_ERR_WORKSPACE = 3,   /* workspace NULL, too small or misaligned */
   NG_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
   NG_ERR_TIMEOUT = 5      /* a cross-workgroup wait gave up (reported by ng_workspace_status) */
@@ -80,7 +80,7 @@ enum {
  * rstd_out: float32 [M] or NULL.  Needs no workspace.
  */
 ng_status ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N,
-                         int64_t K, int b_layout, float eps, float* rstd_out, void* stream);
+                               int64_t K, int b_layout, float eps, float* rstd_out, void* stream);
 
 /*
  * Lazy Pre-Norm with a per-column affine on the normalized A (gamma, beta of
@@ -103,12 +103,12 @@ ng_status ng_rmsnorm_gemm_lazy(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, i
  * rstd_out: float32 [M] or NULL.  Needs no workspace.
  */
 ng_status ng_lazy_fold_affine(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
-                        ng_bf16* B_folded, float* bias, int64_t K, int64_t N, int b_layout,
-                        void* stream);
+                              ng_bf16* B_folded, float* bias, int64_t K, int64_t N, int b_layout,
+                              void* stream);
 
 ng_status ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded, const float* bias,
-                                ng_bf16* C, int64_t M, int64_t N, int64_t K, int b_layout,
-                                float eps, float* rstd_out, void* stream);
+                                      ng_bf16* C, int64_t M, int64_t N, int64_t K, int b_layout,
+                                      float eps, float* rstd_out, void* stream);
 
 /*
  * Input gradient of Lazy Pre-Norm (C = rmsnorm(A) @ B, RMSNorm without
@@ -128,9 +128,9 @@ ng_status ng_rmsnorm_gemm_lazy_affine(const ng_bf16* A, const ng_bf16* B_folded,
  * same rules as for ng_gemm_rmsnorm).  dA must not overlap the inputs.
  */
 ng_status ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
-                                         const float* rstd, ng_bf16* dA, int64_t M, int64_t N,
-                                         int64_t K, int b_layout, void* workspace,
-                                         size_t workspace_bytes, void* stream);
+                                              const float* rstd, ng_bf16* dA, int64_t M, int64_t N,
+                                              int64_t K, int b_layout, void* workspace,
+                                              size_t workspace_bytes, void* stream);
 
 /*
  * Pre-LayerNorm fused with the following product: C = LayerNorm(A) @ B with
@@ -156,12 +156,13 @@ ng_status ng_rmsnorm_gemm_lazy_backward_input(const ng_bf16* dC, const ng_bf16* 
  * 65536 (else NG_ERR_UNSUPPORTED).  Needs no workspace.
  */
 ng_status ng_layernorm_gemm_fold(const ng_bf16* B, const ng_bf16* gamma, const ng_bf16* beta,
-                           ng_bf16* B_folded, float* colsum, float* bias, int64_t K, int64_t N,
-                           int b_layout, void* stream);
+                                 ng_bf16* B_folded, float* colsum, float* bias, int64_t K,
+                                 int64_t N, int b_layout, void* stream);
 
 ng_status ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, const float* colsum,
-                              const float* bias, ng_bf16* C, int64_t M, int64_t N, int64_t K,
-                              int b_layout, float eps, float* mean, float* rstd, void* stream);
+                                    const float* bias, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+                                    int b_layout, float eps, float* mean, float* rstd,
+                                    void* stream);
 
 /*
  * GEMM with an RMSNorm epilogue over each full output row (H = N):
@@ -188,8 +189,8 @@ ng_status ng_layernorm_gemm_prenorm(const ng_bf16* A, const ng_bf16* B_folded, c
  * gamma: bf16 [N] or NULL.  rstd_out: float32 [M] or NULL.
  */
 ng_status ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma, ng_bf16* C,
-                    int64_t M, int64_t N, int64_t K, int b_layout, float eps, float* rstd_out,
-                    void* workspace, size_t workspace_bytes, void* stream);
+                          int64_t M, int64_t N, int64_t K, int b_layout, float eps, float* rstd_out,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * GEMM with a LayerNorm epilogue over each full output row (H = N):
@@ -203,9 +204,9 @@ ng_status ng_gemm_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gam
  * mean_out, rstd_out: float32 [M] or NULL.
  */
 ng_status ng_gemm_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* gamma,
-                      const ng_bf16* beta, ng_bf16* C, int64_t M, int64_t N, int64_t K,
-                      int b_layout, float eps, float* mean_out, float* rstd_out, void* workspace,
-                      size_t workspace_bytes, void* stream);
+                            const ng_bf16* beta, ng_bf16* C, int64_t M, int64_t N, int64_t K,
+                            int b_layout, float eps, float* mean_out, float* rstd_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * ng_gemm_layernorm for callers that cannot allocate device memory (code
@@ -243,20 +244,21 @@ ng_status ng_gemm_layernorm_noalloc(const ng_bf16* A, const ng_bf16* B, const ng
  * above).  R: [M, N] bf16, required; S_out: [M, N] bf16 or NULL.  R may be
  * the very buffer of C or of S_out (an in-place update: every element of R
  * is read before the same element of C or S_out is written); S_out and C
- * must differ, and no other overlap is allowed.  mean_out/rstd_out describe S.  Strategies and
- * workspace rules as for ng_gemm_rmsnorm / ng_gemm_layernorm, with
+ * must differ, and no other overlap is allowed.  mean_out/rstd_out describe
+ * S.  Strategies and workspace rules as for ng_gemm_rmsnorm /
+ * ng_gemm_layernorm, with
  * ng_workspace_bytes(NG_OP_GEMM_ADD_RMSNORM / NG_OP_GEMM_ADD_LAYERNORM, ...).
  */
 ng_status ng_gemm_add_rmsnorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
-                        const ng_bf16* gamma, ng_bf16* C, ng_bf16* S_out, int64_t M, int64_t N,
-                        int64_t K, int b_layout, float eps, float* rstd_out, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                              const ng_bf16* gamma, ng_bf16* C, ng_bf16* S_out, int64_t M,
+                              int64_t N, int64_t K, int b_layout, float eps, float* rstd_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 ng_status ng_gemm_add_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf16* R,
-                          const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* C, ng_bf16* S_out,
-                          int64_t M, int64_t N, int64_t K, int b_layout, float eps,
-                          float* mean_out, float* rstd_out, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                                const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* C,
+                                ng_bf16* S_out, int64_t M, int64_t N, int64_t K, int b_layout,
+                                float eps, float* mean_out, float* rstd_out, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * Plain GEMM, the matrix half of the unfused baseline that the fused forms
@@ -267,7 +269,7 @@ ng_status ng_gemm_add_layernorm(const ng_bf16* A, const ng_bf16* B, const ng_bf1
  * accumulation).  A: [M, K]; B: see b_layout; C: [M, N] bf16 out.
  */
 ng_status ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
-            int b_layout, void* stream);
+                  int b_layout, void* stream);
 
 /*
  * Standalone row norm, the other half of the unfused baseline.  X, Y: [rows,
@@ -279,8 +281,8 @@ ng_status ng_gemm(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int
  * rstd_out: float32 [rows] or NULL.
  */
 ng_status ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, ng_bf16* Y,
-            int64_t rows, int64_t cols, int kind, float eps, float* mean_out, float* rstd_out,
-            void* stream);
+                  int64_t rows, int64_t cols, int kind, float eps, float* mean_out, float* rstd_out,
+                  void* stream);
 
 /*
  * Standalone residual add and row norm, the norm half of the unfused
@@ -292,8 +294,8 @@ ng_status ng_norm(const ng_bf16* X, const ng_bf16* gamma, const ng_bf16* beta, n
  * element is written); S_out and Y must differ.  Limits as for ng_norm.
  */
 ng_status ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, const ng_bf16* beta,
-                ng_bf16* Y, ng_bf16* S_out, int64_t rows, int64_t cols, int kind, float eps,
-                float* mean_out, float* rstd_out, void* stream);
+                      ng_bf16* Y, ng_bf16* S_out, int64_t rows, int64_t cols, int kind, float eps,
+                      float* mean_out, float* rstd_out, void* stream);
 
 /*
  * Weight gradient of Lazy Pre-Norm: dB = A_hat^T @ dC with A_hat = rstd * A
@@ -301,14 +303,15 @@ ng_status ng_add_norm(const ng_bf16* X, const ng_bf16* R, const ng_bf16* gamma, 
  * normalization fusion", section "Lazy Pre-Norm": the normalized A is never
  * stored, so backward rebuilds it).  The product runs over the forward rows:
  * each k-tile of A is read on chip, its elements scaled by their row's rstd
- * and rounded to bf16 (the rounding of a stored A_hat), then multiplied.  M, N, K and b_layout are the forward product's: A [M, K],
- * dC [M, N], rstd float32 [M]; dB is written in B's layout ([K, N] for
- * NG_B_KN, [N, K] for NG_B_NK), bf16.  M may be any size (M == 0 writes
- * zeros).  dB must not overlap the inputs.
+ * and rounded to bf16 (the rounding of a stored A_hat), then multiplied.
+ * M, N, K and b_layout are the forward product's: A [M, K], dC [M, N], rstd
+ * float32 [M]; dB is written in B's layout ([K, N] for NG_B_KN, [N, K] for
+ * NG_B_NK), bf16.  M may be any size (M == 0 writes zeros).  dB must not
+ * overlap the inputs.
  */
-ng_status ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* dC, const float* rstd,
-                                          ng_bf16* dB, int64_t M, int64_t N, int64_t K,
-                                          int b_layout, void* stream);
+ng_status ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* dC,
+                                               const float* rstd, ng_bf16* dB, int64_t M, int64_t N,
+                                               int64_t K, int b_layout, void* stream);
 
 /*
  * Both gradients of Lazy Pre-Norm (C = rmsnorm(A) @ B, RMSNorm without
@@ -326,15 +329,16 @@ ng_status ng_rmsnorm_gemm_lazy_backward_weight(const ng_bf16* A, const ng_bf16* 
  * dB is written in B's layout ([K, N] for NG_B_KN, [N, K] for NG_B_NK);
  * M == 0 writes dB = 0.  dC_scaled is caller-owned scratch of M * N * 2
  * bytes that must not overlap any other argument (NG_ERR_INVALID_ARG); dA
- * and dB must not overlap the inputs.  Against ng_rmsnorm_gemm_lazy_backward_weight,
- * which keeps no intermediate, this trades M * N * 2 bytes of scratch for a
- * weight gradient at the speed of the plain product.
+ * and dB must not overlap the inputs.  Against
+ * ng_rmsnorm_gemm_lazy_backward_weight, which keeps no intermediate, this
+ * trades M * N * 2 bytes of scratch for a weight gradient at the speed of the
+ * plain product.
  */
 ng_status ng_rmsnorm_gemm_lazy_backward(const ng_bf16* dC, const ng_bf16* B, const ng_bf16* A,
-                                   const float* rstd, ng_bf16* dA, ng_bf16* dB,
-                                   ng_bf16* dC_scaled, int64_t M, int64_t N, int64_t K,
-                                   int b_layout, void* workspace, size_t workspace_bytes,
-                                   void* stream);
+                                        const float* rstd, ng_bf16* dA, ng_bf16* dB,
+                                        ng_bf16* dC_scaled, int64_t M, int64_t N, int64_t K,
+                                        int b_layout, void* workspace, size_t workspace_bytes,
+                                        void* stream);
 
 /*
  * Plain GEMM with the first operand stored transposed, the product half of
@@ -343,8 +347,8 @@ ng_status ng_rmsnorm_gemm_lazy_backward(const ng_bf16* dC, const ng_bf16* B, con
  * bf16 out, fp32 accumulation.  M and N multiples of 8 (else
  * NG_ERR_UNSUPPORTED); K any size >= 1.
  */
-ng_status ng_gemm_at(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N, int64_t K,
-               void* stream);
+ng_status ng_gemm_at(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, int64_t N,
+                     int64_t K, void* stream);
 
 /*
  * Standalone RMSNorm backward (no affine), the norm half of the unfused
@@ -355,7 +359,7 @@ ng_status ng_gemm_at(const ng_bf16* A, const ng_bf16* B, ng_bf16* C, int64_t M, 
  * and at most 65536 (else NG_ERR_UNSUPPORTED).  dX may equal dY.
  */
 ng_status ng_rmsnorm_backward(const ng_bf16* dY, const ng_bf16* X, const float* rstd, ng_bf16* dX,
-                        int64_t rows, int64_t cols, void* stream);
+                              int64_t rows, int64_t cols, void* stream);
 
 /* Workspace bytes `op` needs for this shape (0 when it needs none). */
 size_t ng_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
