@@ -375,3 +375,15 @@ def test_debug_options():
         assert f(_lib.NG_DEBUG_TILE_ORDER, v) == 0
     assert f(_lib.NG_DEBUG_WAIT_SPINS, 0) == 0
     assert f(_lib.NG_DEBUG_WAIT_SPINS, -1) == 0
+
+
+def test_autograd_op_has_no_cpu_fallback():
+    # the differentiable op routes to the library only: CPU tensors are
+    # refused before any call, never computed another way
+    torch = pytest.importorskip("torch")
+    from normalization_gemm_amd.autograd import lazy_rmsnorm_linear, lazy_rmsnorm_matmul
+    x = torch.zeros((4, 16), dtype=torch.bfloat16, requires_grad=True)
+    with pytest.raises(ValueError, match="GPU"):
+        lazy_rmsnorm_linear(x, torch.zeros((8, 16), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="GPU"):
+        lazy_rmsnorm_matmul(x, torch.zeros((16, 8), dtype=torch.bfloat16))
