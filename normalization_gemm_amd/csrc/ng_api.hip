@@ -809,7 +809,7 @@ ng_status ng_rmsnorm_gemm_lazy_backward(const ng_bf16* dC, const ng_bf16* B, con
     const uintptr_t sc = (uintptr_t)dC_scaled, sce = sc + (uintptr_t)(M * N * 2);
     const struct { const void* p; int64_t bytes; } others[] = {
         {dC, M * N * 2}, {B, K * N * 2}, {A, M * K * 2}, {rstd, M * 4}, {dA, M * K * 2},
-        {dB, K * N * 2}};
+        {dB, K * N * 2}, {workspace, (int64_t)workspace_bytes}};
     for (const auto& o : others) {
       const uintptr_t b = (uintptr_t)o.p, e = b + (uintptr_t)o.bytes;
       if (o.p && b < sce && sc < e)

@@ -285,6 +285,11 @@ def test_lazy_backward_argument_checks():
     assert b(P, P2, P5, P4, P3, P6, P3 - 1024, 64, 128, 64, 0, None, 0, None) == 1
     assert "overlap" in _lib.ng_last_error()
     assert b(P, P2, P5, P4, P3, P6, P + 4096, 64, 128, 64, 0, None, 0, None) == 1
+    # ... or the workspace (K = 4096 needs one)
+    wsb = _lib.ng_workspace_bytes(_lib.NG_OP_RMSNORM_GEMM_LAZY_BWD_INPUT, 64, 128, 4096)
+    WS = 1 << 45
+    assert b(P, P2, P5, P4, P3, P6, WS + 256, 64, 128, 4096, 0, WS, wsb, None) == 1
+    assert "overlap" in _lib.ng_last_error()
     # then the input gradient's checks
     assert b(P, P2, None, P4, P3, P6, SC, 64, 128, 64, 0, None, 0, None) == 1   # A NULL
     assert b(P, P2, P5, P4, P3, P6, SC, 64, 128, 60, 0, None, 0, None) == 2     # K % 8
