@@ -316,6 +316,12 @@ class Bench:
                       for _ in range(self.R)]
             self.dAh = [torch.empty((w.M, w.K), dtype=torch.bfloat16, device=dev)
                         for _ in range(self.R)]
+        # the library reference's transposed operands (B^T for dC @ B^T, the
+        # normalized A transposed for A_hat^T @ dC), outside the timed calls
+        if w.op in (workloads.OP_LAZY_BWD, workloads.OP_LAZY_BWD_RG):
+            self.Bt = self.B.t().contiguous()
+        if w.op in (workloads.OP_LAZY_BWD_W, workloads.OP_LAZY_BWD_RG):
+            self.At = ng.norm(A0, "rms", eps=w.eps).t().contiguous()
         # unfused pair intermediates: the normalized A of the lazy form's
         # pair holds real values (the GEMM's speed depends on its data)
         if lazy:
@@ -454,15 +460,25 @@ class Bench:
         self._call(self._norm, i)
 
     # The vendor library's GEMM on the same operands (torch.matmul, which
-    # ROCm serves from hipBLASLt): a reference point for the plain product on
-    # the same board at the same clock and power cap, not part of any
-    # measured path.  Only for the forward products C = A @ B.
+    # ROCm serves from hipBLASLt): a reference point for the plain product(s)
+    # on the same board at the same clock and power cap, not part of any
+    # measured path.  Forward: C = A @ B.  Backward: dA_hat = dC @ B^T and/or
+    # dB = A_hat^T @ dC, the transposed operands materialized once outside
+    # the timed calls (the library then multiplies contiguous matrices).
     def has_library_gemm(self):
-        return self.w.op not in (workloads.OP_LAZY_BWD, workloads.OP_LAZY_BWD_W,
-                                 workloads.OP_LAZY_BWD_RG)
+        return True
 
     def library_gemm(self, i):
         r = i % self.R
+        op = self.w.op
+        if op in (workloads.OP_LAZY_BWD, workloads.OP_LAZY_BWD_RG):
+            self.torch.matmul(self.dC[r], self.Bt, out=self.dAh[r])
+        if op == workloads.OP_LAZY_BWD_W:
+            self.torch.matmul(self.At, self.dC[r], out=self.C[r])
+        if op == workloads.OP_LAZY_BWD_RG:
+            self.torch.matmul(self.At, self.dC[r], out=self.dB[r])
+        if op in (workloads.OP_LAZY_BWD, workloads.OP_LAZY_BWD_W, workloads.OP_LAZY_BWD_RG):
+            return
         A = self.An[r] if prenorm(self.w) else self.A[r]
         self.torch.matmul(A, self.B, out=self.C[r])
 
