@@ -1611,8 +1611,11 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     issue_prologue<T>(p, lds0, tm * T::BM, tn * T::BN, tid);
   }
   // cross-tile prefetch: not for the epilogues that stage data through the
-  // stages or load per-row data after the k-loop
-  constexpr bool kCross = T::KK == 1 && EPI == EPI_NONE && !scale_ahead<T>();
+  // stages (the pre-norm epilogue's per-row loads wait for the prefetched
+  // transfers, which are older, but the next k-loop then starts on landed
+  // k-tiles)
+  constexpr bool kCross =
+      T::KK == 1 && (EPI == EPI_NONE || EPI == EPI_PRE_LN) && !scale_ahead<T>();
   const int nk = (p.K + T::BK - 1) / T::BK;
   int srot = 0;
   for (int t = first; t < total; t += G) {
