@@ -397,11 +397,27 @@ const char* ng_last_error(void);
  *                           NG_TILE_ORDER_NATURAL (default), _REVERSED or
  *                           _SHUFFLED (a fixed permutation).  Outputs are
  *                           bit-identical in every order.
+ *   NG_DEBUG_K_WALK         k-tile walk of the persistent grids of ng_gemm
+ *                           and of the cross-workgroup RMSNorm/LayerNorm
+ *                           epilogues (without residual): NG_K_WALK_AUTO
+ *                           (default: every second round of tiles walks K
+ *                           downwards when one round's operands and output
+ *                           exceed 192 MiB), _UPWARD (always upwards) or
+ *                           _ALTERNATE (every second round downwards whenever
+ *                           there is more than one round).  The fp32 sums
+ *                           over K then run in another order: outputs agree
+ *                           within rounding, not bit for bit.
  * Returns NG_ERR_INVALID_ARG for an unknown option or value.  Calls already
  * enqueued keep the values they were launched with.
  */
-enum { NG_DEBUG_WAIT_SPINS = 0, NG_DEBUG_ROW_LOCAL_MAX = 1, NG_DEBUG_TILE_ORDER = 2 };
+enum {
+  NG_DEBUG_WAIT_SPINS = 0,
+  NG_DEBUG_ROW_LOCAL_MAX = 1,
+  NG_DEBUG_TILE_ORDER = 2,
+  NG_DEBUG_K_WALK = 3
+};
 enum { NG_TILE_ORDER_NATURAL = 0, NG_TILE_ORDER_REVERSED = 1, NG_TILE_ORDER_SHUFFLED = 2 };
+enum { NG_K_WALK_AUTO = 0, NG_K_WALK_UPWARD = 1, NG_K_WALK_ALTERNATE = 2 };
 ng_status ng_set_debug_option(int option, int64_t value);
 
 #ifdef __cplusplus

@@ -27,7 +27,8 @@ from ._lib import (  # noqa: F401
     ng_rmsnorm_gemm_lazy, ng_rmsnorm_gemm_lazy_affine, ng_status_string, ng_workspace_bytes,
     ng_workspace_reset, ng_workspace_status, ng_set_debug_option,
     NG_DEBUG_ROW_LOCAL_MAX, NG_DEBUG_TILE_ORDER, NG_DEBUG_WAIT_SPINS, NG_TILE_ORDER_NATURAL,
-    NG_TILE_ORDER_REVERSED, NG_TILE_ORDER_SHUFFLED,
+    NG_TILE_ORDER_REVERSED, NG_TILE_ORDER_SHUFFLED, NG_DEBUG_K_WALK, NG_K_WALK_AUTO,
+    NG_K_WALK_UPWARD, NG_K_WALK_ALTERNATE,
 )
 
 __all__ = [
@@ -53,7 +54,7 @@ class debug_option:
     (the option's default)."""
 
     _DEFAULT = {NG_DEBUG_WAIT_SPINS: -1, NG_DEBUG_ROW_LOCAL_MAX: -1,
-                NG_DEBUG_TILE_ORDER: NG_TILE_ORDER_NATURAL}
+                NG_DEBUG_TILE_ORDER: NG_TILE_ORDER_NATURAL, NG_DEBUG_K_WALK: NG_K_WALK_AUTO}
 
     def __init__(self, option: int, value: int):
         self.option, self.value = option, value

@@ -39,6 +39,10 @@ NG_DEBUG_TILE_ORDER = 2
 NG_TILE_ORDER_NATURAL = 0
 NG_TILE_ORDER_REVERSED = 1
 NG_TILE_ORDER_SHUFFLED = 2
+NG_DEBUG_K_WALK = 3
+NG_K_WALK_AUTO = 0
+NG_K_WALK_UPWARD = 1
+NG_K_WALK_ALTERNATE = 2
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64

@@ -138,8 +138,10 @@ ng_status launched(const char* what) {
 //   wait bound of the cross-workgroup waits, in polls of ~1 us (-1: 2^20,
 //     about a second);
 //   widest row reduced inside one workgroup (-1: 256);
-//   tile order of the grids (NG_TILE_ORDER_*).
+//   tile order of the grids (NG_TILE_ORDER_*);
+//   k-tile walk of the cross-workgroup grid (NG_K_WALK_*).
 std::atomic<int> g_wait_spins{-1};
+std::atomic<int> g_k_walk{NG_K_WALK_AUTO};
 std::atomic<int> g_row_local_max{-1};
 std::atomic<int> g_tile_order{NG_TILE_ORDER_NATURAL};
 
@@ -234,6 +236,22 @@ ng_status resident_capacity(const void* kernel, int threads, int* cap) {
   return NG_OK;
 }
 
+// Bytes that one round of a persistent grid reads and writes (all of B, the
+// round's A panels and its output rows) above which its odd rounds walk the
+// k-tiles downwards: past this size the next round's first k-tiles have left
+// the 256 MB Infinity Cache when read upwards again.
+constexpr uint64_t kWalkBytes = uint64_t(192) << 20;
+
+// rb: row blocks that one round covers.
+bool alternate_walk(const ng::GemmParams& p, int rb, int BM, bool several_rounds) {
+  const int mode = g_k_walk.load(std::memory_order_relaxed);
+  if (!several_rounds) return false;
+  if (mode != NG_K_WALK_AUTO) return mode == NG_K_WALK_ALTERNATE;
+  const uint64_t round_bytes = 2ull * ((uint64_t)p.N * p.K + (uint64_t)rb * BM * p.K +
+                                       (uint64_t)rb * BM * p.N);
+  return round_bytes > kWalkBytes;
+}
+
 template <class T, int EPI>
 ng_status launch_persistent(ng::GemmParams p, hipStream_t s, const char* what) {
   p.tiles_m = (p.M + T::BM - 1) / T::BM;
@@ -250,6 +268,17 @@ ng_status launch_persistent(ng::GemmParams p, hipStream_t s, const char* what) {
           ? (long long)p.tiles_m * ((p.tiles_n + ng::kLazyStrip - 1) / ng::kLazyStrip)
           : total;
   tile_order(walked, &p.order_a, &p.order_c);
+  if constexpr (EPI == ng::EPI_NONE && !T::AKM) {
+    const int rb = std::max(1, std::min(p.tiles_m, (int)grid / p.tiles_n));
+    if (alternate_walk(p, rb, T::BM, total > (long long)grid)) {
+      int cap2 = 0;
+      st = resident_capacity((const void*)ng::gemm_persistent_kernel<T, EPI, true>, T::NT, &cap2);
+      if (st) return st;
+      hipLaunchKernelGGL((ng::gemm_persistent_kernel<T, EPI, true>),
+                         dim3((unsigned)std::min<long long>(grid, cap2)), dim3(T::NT), 0, s, p);
+      return launched(what);
+    }
+  }
   hipLaunchKernelGGL((ng::gemm_persistent_kernel<T, EPI>), dim3(grid), dim3(T::NT), 0, s, p);
   return launched(what);
 }
@@ -275,7 +304,22 @@ ng_status launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   // A plain launch: the grid never exceeds what the device holds at once, so
   // on a device not shared with another such grid all workgroups become
   // resident.  (A cooperative launch would guarantee it even then, but was
-  // measured to add ~18 us per call.)
+  // measured to add ~18 us per call.)  Both k-walk variants have the same
+  // resources (checked by the occupancy query of each).
+  if constexpr (!RES && !BWD) {
+    if (alternate_walk(p, R, T::BM, p.iters > 1)) {
+      int cap2 = 0;
+      st = resident_capacity((const void*)ng::gemm_xwg_kernel<T, LN, RES, BWD, true>, T::NT,
+                             &cap2);
+      if (st) return st;
+      if (cap2 < (int)grid)
+        return fail(NG_ERR_UNSUPPORTED, "alternating k-walk grid of %u workgroups exceeds %d",
+                    grid, cap2);
+      hipLaunchKernelGGL((ng::gemm_xwg_kernel<T, LN, RES, BWD, true>), dim3(grid), dim3(T::NT),
+                         0, s, p);
+      return launched(what);
+    }
+  }
   hipLaunchKernelGGL((ng::gemm_xwg_kernel<T, LN, RES, BWD>), dim3(grid), dim3(T::NT), 0, s, p);
   return launched(what);
 }
@@ -1041,6 +1085,11 @@ ng_status ng_set_debug_option(int option, int64_t value) {
           value != NG_TILE_ORDER_SHUFFLED)
         return fail(NG_ERR_INVALID_ARG, "unknown tile order %lld", (long long)value);
       g_tile_order.store((int)value, std::memory_order_relaxed);
+      return ok();
+    case NG_DEBUG_K_WALK:
+      if (value != NG_K_WALK_AUTO && value != NG_K_WALK_UPWARD && value != NG_K_WALK_ALTERNATE)
+        return fail(NG_ERR_INVALID_ARG, "unknown k-walk mode %lld", (long long)value);
+      g_k_walk.store((int)value, std::memory_order_relaxed);
       return ok();
     default:
       return fail(NG_ERR_INVALID_ARG, "unknown debug option %d", option);

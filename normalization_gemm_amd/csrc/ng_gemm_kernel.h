@@ -693,10 +693,12 @@ __device__ __forceinline__ void substep(f32x4 (&acc)[T::FM][T::FN],
 //   sub-step 1: MFMAs on (kt, k 32..63) while reading (kt+1, k 0..31) and
 //               issuing k-tile kt+STAGES's transfers into stage s (no wave
 //               reads stage s any more after the barrier).
-// LDS transfers of the first two k-tiles of the tile at (m_base, n_base).
+// LDS transfers of the first STAGES k-tiles of the tile at (m_base, n_base):
+// k-tiles 0, 1, ..., or with `rev` (the tile's k-loop walks downwards) the
+// last ones, nk-1, nk-2, ....
 template <class T>
 __device__ __forceinline__ void issue_prologue(const GemmParams& p, uint32_t lds0, int m_base,
-                                               int n_base, int tid) {
+                                               int n_base, int tid, bool rev = false) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   DmaPlan<T> dma;
@@ -707,7 +709,8 @@ __device__ __forceinline__ void issue_prologue(const GemmParams& p, uint32_t lds
   for (int st = 0; st < T::STAGES; ++st) {
     if (st < nk) {
 #pragma unroll
-      for (int d = 0; d < ND; ++d) dma.issue(p, m_base, n_base, st, lds0 + st * T::STAGE, d);
+      for (int d = 0; d < ND; ++d)
+        dma.issue(p, m_base, n_base, rev ? nk - 1 - st : st, lds0 + st * T::STAGE, d);
     }
   }
 }
@@ -743,12 +746,16 @@ __device__ __forceinline__ void wait_ktile(int after) {
 // transfers after the one awaited, tile after tile.  (A tile's epilogue
 // polls and loads wait for every earlier transfer, so transfers issued after
 // the k-loop would hold them up.)
-template <class T, bool LAZY>
+// REV: the k-tiles are walked downwards (k-tile nk-1 first); nx_rev: the
+// next tile's walk, for its prefetched first k-tiles.  The sum over k then
+// runs in the other order, which changes the fp32 rounding, not the result.
+template <class T, bool LAZY, bool REV = false>
 __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM][T::FN],
                                          float (&ss)[T::FM], lds_char* lds, uint32_t lds0,
                                          int m_base, int n_base, int tid,
                                          bool prologue_issued = false, bool stores_after = false,
-                                         int srot = 0, int nx_m = -1, int nx_n = 0) {
+                                         int srot = 0, int nx_m = -1, int nx_n = 0,
+                                         bool nx_rev = false) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / T::WN, wn = wave % T::WN;
@@ -769,6 +776,8 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
   constexpr int NR = FragReader<T>::ITEMS;
   const int nk = (p.K + T::BK - 1) / T::BK;
   const bool xt = !scale_ahead<T>() && nx_m >= 0 && nk >= T::STAGES;
+  // global k-tile of the walk's k-th k-tile
+  auto kmap = [&](int k) { return REV ? nk - 1 - k : k; };
   // LDS byte offset of the stage that holds k-tile k
   auto stg = [&](int k) { return (uint32_t)((k + srot) % T::STAGES) * T::STAGE; };
   // Wait until a k-tile has landed with `after` later k-tiles (and, with
@@ -785,7 +794,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
     }
   };
 
-  if (!prologue_issued) issue_prologue<T>(p, lds0, m_base, n_base, tid);
+  if (!prologue_issued) issue_prologue<T>(p, lds0, m_base, n_base, tid, REV);
   if constexpr (scale_ahead<T>()) {
     // k-tiles 0 and 1 are scaled here, the later ones one k-tile ahead
     const int after = nk >= 2 ? min(nk, T::STAGES) - 2 : 0;
@@ -835,11 +844,11 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
       wait_next(kt);
       __syncthreads();
       substep<T, LAZY, 1, 1>(acc, gram, f0, f1, lds, rd, s1, 0, dma, true, p, m_base, n_base,
-                             kt + T::STAGES, lds0 + s0, s2, true, lane);
+                             kmap(kt + T::STAGES), lds0 + s0, s2, true, lane);
       wait_next(kt + 1);
       __syncthreads();
       substep<T, LAZY, 1, 1>(acc, gram, f1, f0, lds, rd, s2, 0, dma, true, p, m_base, n_base,
-                             kt + 1 + T::STAGES, lds0 + s1, stg(kt + 3), true, lane);
+                             kmap(kt + 1 + T::STAGES), lds0 + s1, stg(kt + 3), true, lane);
     }
     // the last sub-steps: refills of this tile while there are k-tiles left,
     // then (cross-tile prefetch) the next tile's first k-tiles
@@ -848,7 +857,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
       on = u < nk;
       mb = m_base;
       nb = n_base;
-      uk = u;
+      uk = kmap(u);
       if (!on && xt) {
         if (!switched) {
           dma.init(p, nx_m, nx_n, lane, wave);
@@ -857,7 +866,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
         on = true;
         mb = nx_m;
         nb = nx_n;
-        uk = u - nk;
+        uk = nx_rev ? 2 * nk - 1 - u : u - nk;
       }
     };
     for (; kt < nk; kt += 2) {
@@ -896,7 +905,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
         wait_next(kt);
         __syncthreads();
         substep<T, LAZY, 1>(acc, gram, f1, f0, lds, rd, nxt, 0, dma, true, p, m_base, n_base,
-                            kt + T::STAGES, lds0 + cur);
+                            kmap(kt + T::STAGES), lds0 + cur);
         cur_s = nxt_s;
       }
     }
@@ -912,7 +921,9 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
       // prefetch) with the next tile's first k-tiles
       int u = kt + T::STAGES, mb = m_base, nb = n_base;
       bool on = u < nk;
-      if (!on && xt) {
+      if (on) {
+        u = kmap(u);
+      } else if (xt) {
         if (!switched) {
           dma.init(p, nx_m, nx_n, lane, wave);
           switched = true;
@@ -920,7 +931,7 @@ __device__ __forceinline__ void mainloop(const GemmParams& p, f32x4 (&acc)[T::FM
         on = true;
         mb = nx_m;
         nb = nx_n;
-        u -= nk;
+        u = nx_rev ? 2 * nk - 1 - u : u - nk;
       }
       substep<T, LAZY>(acc, gram, f1, f0, lds, rd, nxt, 0, dma, on, p, mb, nb, u, lds0 + cur);
       cur_s = nxt_s;
@@ -1603,8 +1614,11 @@ __device__ __forceinline__ void lazy_persistent(const GemmParams& p, lds_char* l
 // that start its next tile, then scales and stores the finished tile, so the
 // next tile's first k-tiles stream in behind the epilogue.  All epilogues
 // whose tile holds what it needs (EPI_NONE, EPI_LAZY*, EPI_ROW_*, EPI_PRE_LN).
-template <class T, int EPI>
+// KW (plain GEMM): every second pass over the tile order (gridDim.x tiles)
+// walks the k-tiles downwards, as in the cross-workgroup grid.
+template <class T, int EPI, bool KW = false>
 __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
+  static_assert(!KW || EPI == EPI_NONE, "alternating k-walk: plain GEMM only");
   static_assert(T::STG_OWN, "persistent tiles need their own output staging");
   __shared__ __attribute__((aligned(16))) char smem[T::LDS];
   lds_char* lds = lds_base(smem);
@@ -1647,8 +1661,14 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     const bool xt = kCross && has_next && nk >= T::STAGES;
     f32x4 acc[T::FM][T::FN];
     float ss[T::FM];
-    mainloop<T, epi_lazy(EPI)>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, t != first, srot,
-                               xt ? tm2 * T::BM : -1, tn2 * T::BN);
+    const int pass = (t - first) / G;
+    const bool rev = KW && (pass & 1), nx_rev = KW && !(pass & 1);
+    if (rev)
+      mainloop<T, false, KW>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, t != first, srot,
+                             xt ? tm2 * T::BM : -1, tn2 * T::BN, nx_rev);
+    else
+      mainloop<T, epi_lazy(EPI)>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, t != first,
+                                 srot, xt ? tm2 * T::BM : -1, tn2 * T::BN, nx_rev);
     if constexpr (epi_res(EPI))
       add_residual<T>(p, acc, lds, lds0, m_base, n_base, wave, wm, wn, lane);
     Affine<T> aff;
@@ -1656,7 +1676,7 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     load_columns<T, EPI>(p, n_base, wn, lane, aff, bias);
     float mean[T::FM], rstd[T::FM];
     tile_scale<T, EPI>(p, acc, ss, lds, m_base, n_base, tn, wm, wn, lane, ax, mean, rstd);
-    if (has_next && !xt) issue_prologue<T>(p, lds0, tm2 * T::BM, tn2 * T::BN, tid);
+    if (has_next && !xt) issue_prologue<T>(p, lds0, tm2 * T::BM, tn2 * T::BN, tid, nx_rev);
     tile_store<T, EPI>(p, acc, mean, rstd, aff, bias, lds, m_base, n_base, wave, wm, wn, lane,
                        ax);
     srot = xt ? (srot + nk) % T::STAGES : 0;
@@ -1832,8 +1852,12 @@ __device__ __forceinline__ void xwg_merge_rows(const GemmParams& p, int slot, in
   }
 }
 
-template <class T, bool LN, bool RES = false, bool BWD = false>
+// KW: the k-loops of odd rounds walk the k-tiles downwards, so that a round
+// starts on the k-tiles of B (and A) that the last one read most recently --
+// those still in the Infinity Cache when one round's operands exceed it.
+template <class T, bool LN, bool RES = false, bool BWD = false, bool KW = false>
 __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
+  static_assert(!KW || (!RES && !BWD), "alternating k-walk: plain norm epilogues only");
   static_assert(T::STG_OWN, "persistent tiles need their own output staging");
   __shared__ __attribute__((aligned(16))) char smem[T::LDS];
   lds_char* lds = lds_base(smem);
@@ -1877,15 +1901,21 @@ __global__ void __launch_bounds__(T::NT) gemm_xwg_kernel(GemmParams p) {
     // (BWD: the previous tile's output stores precede this tile's first
     // transfers, so they are not counted after them)
     const bool xt = kCross && tm + R < p.tiles_m && nk >= T::STAGES;
-    mainloop<T, false>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, !BWD && it > 0, srot,
-                       xt ? (tm + R) * T::BM : -1, n_base);
+    const bool rev = KW && (it & 1), nx_rev = KW && !(it & 1);
+    if (rev)
+      mainloop<T, false, KW>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, it > 0, srot,
+                             xt ? (tm + R) * T::BM : -1, n_base, nx_rev);
+    else
+      mainloop<T, false>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, !BWD && it > 0, srot,
+                         xt ? (tm + R) * T::BM : -1, n_base, nx_rev);
     if constexpr (RES) add_residual<T>(p, acc, lds, lds0, m_base, n_base, wave, wm, wn, lane);
     if constexpr (BWD) load_tile_lds<T>(p, p.Xin, lds0, m_base, n_base, wave, wn, lane);
     xwg_publish<T, LN, BWD>(p, acc, lds, rb_in, tn, tid, tag);
     Affine<T> aff;
     if constexpr (!BWD) {
       load_affine<T>(p, n_base, wn, lane, aff);
-      if (tm + R < p.tiles_m && !xt) issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid);
+      if (tm + R < p.tiles_m && !xt)
+        issue_prologue<T>(p, lds0, (tm + R) * T::BM, n_base, tid, nx_rev);
     }
     xwg_merge_rows<T, LN, BWD>(p, rb_in, R, tm, tn, tid, tag);
     // (regrouped weight gradient: this workgroup's rows of rstd * dC, while

@@ -367,6 +367,8 @@ def test_debug_options():
     assert f(_lib.NG_DEBUG_WAIT_SPINS, (1 << 30) + 1) == 1
     assert f(_lib.NG_DEBUG_ROW_LOCAL_MAX, 257) == 1
     assert f(_lib.NG_DEBUG_TILE_ORDER, 3) == 1
+    assert f(_lib.NG_DEBUG_K_WALK, 3) == 1
+    assert f(_lib.NG_DEBUG_K_WALK, -1) == 1
     assert f(99, 0) == 1
     # the row-local maximum moves the workspace boundary, and is restored
     assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 1000, 256, 64) == 0
@@ -378,6 +380,8 @@ def test_debug_options():
     assert _lib.ng_workspace_bytes(_lib.NG_OP_GEMM_LAYERNORM, 1000, 256, 64) == 0
     for v in (1, 2, 0):
         assert f(_lib.NG_DEBUG_TILE_ORDER, v) == 0
+    for v in (_lib.NG_K_WALK_UPWARD, _lib.NG_K_WALK_ALTERNATE, _lib.NG_K_WALK_AUTO):
+        assert f(_lib.NG_DEBUG_K_WALK, v) == 0
     assert f(_lib.NG_DEBUG_WAIT_SPINS, 0) == 0
     assert f(_lib.NG_DEBUG_WAIT_SPINS, -1) == 0
 

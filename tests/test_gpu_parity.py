@@ -832,6 +832,41 @@ def test_tile_order_does_not_change_results(case, order):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), case
 
 
+@pytest.mark.parametrize("kind,layout,K", [("layer", "kn", 200), ("rms", "nk", 200),
+                                           ("layer", "nk", 72), ("rms", "kn", 520)])
+def test_alternating_k_walk(kind, layout, K):
+    # 10 column tiles -> 25 row blocks per round; 61 row blocks -> 3 rounds,
+    # the middle one walking K downwards (ragged last k-tile first), with the
+    # next round's first k-tiles prefetched in both directions (K = 72 on the
+    # 64-deep tiles: fewer k-tiles than the prefetch needs)
+    M, N = 256 * 60 + 100, 256 * 9 + 24
+    log("alternating k-walk %s M=%d N=%d K=%d %s" % (kind, M, N, K, layout))
+    x = workloads.make_inputs(M, N, K, seed=K + 5, gamma=True, beta=kind == "layer")
+    A, B = up(x.A), up(b_for_layout(x.B, layout))
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+
+    def run():
+        if kind == "layer":
+            return ng.gemm_layernorm(A, B, up(x.gamma), up(x.beta), eps=1e-5, b_layout=layout,
+                                     rstd_out=rstd)
+        return ng.gemm_rmsnorm(A, B, up(x.gamma), eps=1e-6, b_layout=layout, rstd_out=rstd)
+
+    with ng.debug_option(ng.NG_DEBUG_K_WALK, ng.NG_K_WALK_ALTERNATE):
+        C1 = run()
+        C2 = run()
+        # the plain product's persistent grid: 610 tiles, 3 passes of 256
+        P = ng.gemm(A, B, b_layout=layout)
+        torch.cuda.synchronize()
+    if kind == "layer":
+        ref, _, rref = oracle.gemm_layernorm(x.A, x.B, 1e-5, x.gamma, x.beta)
+    else:
+        ref, rref = oracle.gemm_rmsnorm(x.A, x.B, 1e-6, x.gamma)
+    _check("alternating k-walk %s %s K=%d" % (kind, layout, K), down(C1), ref)
+    _check_stat("alternating k-walk rstd", rstd, rref)
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+    _check("alternating k-walk gemm %s K=%d" % (layout, K), down(P), oracle.gemm(x.A, x.B))
+
+
 # ------------------------------------------------------------ edge cases
 def test_longest_rows_of_length_k():
     # K = 2^22, the longest row the products read: a full 256-row tile spans
