@@ -104,7 +104,8 @@ def is_fused_dispatch(kernel_name: str, w) -> bool:
     if base == "gemm_xwg_kernel":
         return True
     epi = label.rstrip(">").rsplit("<", 1)[-1].rsplit(", ", 1)[-1]
-    m = re.search(r",\s*(\d+)>\s*(\(|$)", kernel_name.strip())
+    # (the plain product's grid may carry a trailing k-walk flag)
+    m = re.search(r",\s*(\d+)(?:,\s*(?:true|false))?>\s*(\(|$)", kernel_name.strip())
     return m is not None and int(m.group(1)) == EPI_NUMBER[epi]
 
 

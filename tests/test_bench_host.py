@@ -39,6 +39,10 @@ def test_fused_dispatch_large_shapes():
     rms = workloads.WORKLOAD_BY_NAME["gemm_rms_16384x4096x8192"]
     assert bench.is_fused_dispatch(XWG, rms)
     assert not bench.is_fused_dispatch(LAZY.replace(", 1>(", ", 0>("), rms)
+    # the persistent grids' symbols carry the k-walk flag after the epilogue
+    assert bench.is_fused_dispatch(LAZY.replace(", 1>(", ", 1, false>("), lazy)
+    assert not bench.is_fused_dispatch(LAZY.replace(", 1>(", ", 0, true>("), lazy)
+    assert not bench.is_fused_dispatch(LAZY.replace(", 1>(", ", 0, false>("), lazy)
 
 
 def test_algorithmic_bytes_of_the_default_workload():
