@@ -242,13 +242,15 @@ ng_status resident_capacity(const void* kernel, int threads, int* cap) {
 // the 256 MB Infinity Cache when read upwards again.
 constexpr uint64_t kWalkBytes = uint64_t(192) << 20;
 
-// rb: row blocks that one round covers.
-bool alternate_walk(const ng::GemmParams& p, int rb, int BM, bool several_rounds) {
+// rb x cb: row blocks x column tiles (of BM x BN) that one round covers.
+bool alternate_walk(const ng::GemmParams& p, int rb, int cb, int BM, int BN,
+                    bool several_rounds) {
   const int mode = g_k_walk.load(std::memory_order_relaxed);
   if (!several_rounds) return false;
   if (mode != NG_K_WALK_AUTO) return mode == NG_K_WALK_ALTERNATE;
-  const uint64_t round_bytes = 2ull * ((uint64_t)p.N * p.K + (uint64_t)rb * BM * p.K +
-                                       (uint64_t)rb * BM * p.N);
+  const uint64_t rows = std::min<uint64_t>((uint64_t)rb * BM, (uint64_t)p.M);
+  const uint64_t cols = std::min<uint64_t>((uint64_t)cb * BN, (uint64_t)p.N);
+  const uint64_t round_bytes = 2ull * (cols * p.K + rows * p.K + rows * cols);
   return round_bytes > kWalkBytes;
 }
 
@@ -269,8 +271,10 @@ ng_status launch_persistent(ng::GemmParams p, hipStream_t s, const char* what) {
           : total;
   tile_order(walked, &p.order_a, &p.order_c);
   if constexpr (EPI == ng::EPI_NONE && !T::AKM) {
-    const int rb = std::max(1, std::min(p.tiles_m, (int)grid / p.tiles_n));
-    if (alternate_walk(p, rb, T::BM, total > (long long)grid)) {
+    // a round: grid tiles, whole rows of tiles where they fit
+    const int cb = std::min(p.tiles_n, (int)grid);
+    const int rb = std::max(1, std::min(p.tiles_m, (int)grid / cb));
+    if (alternate_walk(p, rb, cb, T::BM, T::BN, total > (long long)grid)) {
       int cap2 = 0;
       st = resident_capacity((const void*)ng::gemm_persistent_kernel<T, EPI, true>, T::NT, &cap2);
       if (st) return st;
@@ -307,7 +311,7 @@ ng_status launch_xwg(ng::GemmParams p, hipStream_t s, const char* what) {
   // measured to add ~18 us per call.)  Both k-walk variants have the same
   // resources (checked by the occupancy query of each).
   if constexpr (!RES && !BWD) {
-    if (alternate_walk(p, R, T::BM, p.iters > 1)) {
+    if (alternate_walk(p, R, p.tiles_n, T::BM, T::BN, p.iters > 1)) {
       int cap2 = 0;
       st = resident_capacity((const void*)ng::gemm_xwg_kernel<T, LN, RES, BWD, true>, T::NT,
                              &cap2);

@@ -1614,8 +1614,10 @@ __device__ __forceinline__ void lazy_persistent(const GemmParams& p, lds_char* l
 // that start its next tile, then scales and stores the finished tile, so the
 // next tile's first k-tiles stream in behind the epilogue.  All epilogues
 // whose tile holds what it needs (EPI_NONE, EPI_LAZY*, EPI_ROW_*, EPI_PRE_LN).
-// KW (plain GEMM): every second pass over the tile order (gridDim.x tiles)
-// walks the k-tiles downwards, as in the cross-workgroup grid.
+// KW (plain GEMM): the tiles of every second pass over the tile order
+// (gridDim.x tiles) walk the k-tiles downwards, as in the cross-workgroup
+// grid.  The direction follows the tile's place in the natural order, so a
+// permuted order (a diagnostic) gives the same sums.
 template <class T, int EPI, bool KW = false>
 __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
   static_assert(!KW || EPI == EPI_NONE, "alternating k-walk: plain GEMM only");
@@ -1634,8 +1636,9 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     int tm, tn;
-    grouped_tile(ordered_tile(p, first, total), p.tiles_m, p.tiles_n, 4, tm, tn);
-    issue_prologue<T>(p, lds0, tm * T::BM, tn * T::BN, tid);
+    const int j = ordered_tile(p, first, total);
+    grouped_tile(j, p.tiles_m, p.tiles_n, 4, tm, tn);
+    issue_prologue<T>(p, lds0, tm * T::BM, tn * T::BN, tid, KW && ((j / G) & 1));
   }
   // cross-tile prefetch (both k-loop shapes): not for the epilogues that
   // stage data through the stages (the pre-norm epilogue's per-row loads
@@ -1652,17 +1655,20 @@ __global__ void __launch_bounds__(T::NT) gemm_persistent_kernel(GemmParams p) {
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / T::WN, wn = wave % T::WN;
     int tm, tn;
-    grouped_tile(ordered_tile(p, t, total), p.tiles_m, p.tiles_n, 4, tm, tn);
+    const int j = ordered_tile(p, t, total);
+    grouped_tile(j, p.tiles_m, p.tiles_n, 4, tm, tn);
     const int m_base = tm * T::BM, n_base = tn * T::BN;
     const int ax = (epi_lazy(EPI) && lazy_split<T>()) ? wn : 0;
     const bool has_next = t + G < total;
-    int tm2 = 0, tn2 = 0;
-    if (has_next) grouped_tile(ordered_tile(p, t + G, total), p.tiles_m, p.tiles_n, 4, tm2, tn2);
+    int tm2 = 0, tn2 = 0, j2 = 0;
+    if (has_next) {
+      j2 = ordered_tile(p, t + G, total);
+      grouped_tile(j2, p.tiles_m, p.tiles_n, 4, tm2, tn2);
+    }
     const bool xt = kCross && has_next && nk >= T::STAGES;
     f32x4 acc[T::FM][T::FN];
     float ss[T::FM];
-    const int pass = (t - first) / G;
-    const bool rev = KW && (pass & 1), nx_rev = KW && !(pass & 1);
+    const bool rev = KW && ((j / G) & 1), nx_rev = KW && has_next && ((j2 / G) & 1);
     if (rev)
       mainloop<T, false, KW>(p, acc, ss, lds, lds0, m_base, n_base, tid, true, t != first, srot,
                              xt ? tm2 * T::BM : -1, tn2 * T::BN, nx_rev);

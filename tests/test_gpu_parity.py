@@ -856,7 +856,14 @@ def test_alternating_k_walk(kind, layout, K):
         C2 = run()
         # the plain product's persistent grid: 610 tiles, 3 passes of 256
         P = ng.gemm(A, B, b_layout=layout)
+        # each tile keeps its walk when the grids take the tiles in another
+        # order: the same sums, bit for bit
+        with ng.debug_option(ng.NG_DEBUG_TILE_ORDER, ng.NG_TILE_ORDER_SHUFFLED):
+            C3 = run()
+            P3 = ng.gemm(A, B, b_layout=layout)
         torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int16), C3.view(torch.int16))
+    assert torch.equal(P.view(torch.int16), P3.view(torch.int16))
     if kind == "layer":
         ref, _, rref = oracle.gemm_layernorm(x.A, x.B, 1e-5, x.gamma, x.beta)
     else:
