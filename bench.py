@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run 3 plain device copies of this many MiB (a known-size "
                          "kernel for scaling profiler byte counters)")
+    ap.add_argument("--k-walk", choices=("auto", "upward", "alternate"), default="auto",
+                    help="direction of the k-loops from round to round in the library's "
+                         "persistent grids (diagnostic; default: the library's own choice)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --calibrate-copy-mib 512` into profiles/traffic_<workload>.json")
@@ -826,6 +829,11 @@ def main():
         sys.exit(1)
     if args.calibrate_copy_mib:
         copy_calibration(args.calibrate_copy_mib)
+    if args.k_walk != "auto":
+        import normalization_gemm_amd as ng
+        mode = {"upward": ng.NG_K_WALK_UPWARD, "alternate": ng.NG_K_WALK_ALTERNATE}[args.k_walk]
+        if ng.ng_set_debug_option(ng.NG_DEBUG_K_WALK, mode) != 0:
+            raise SystemExit("ng_set_debug_option failed")
     if args.workload == "all":
         names = [w.name for w in workloads.WORKLOADS + workloads.NEXT_WORKLOADS]
     else:
@@ -837,6 +845,8 @@ def main():
         warmup = args.warmup if args.warmup is not None else 20
         line = run(w, steps, warmup, not args.no_cpu_baseline, args.cpu_seconds,
                    not args.no_load_readings, not args.no_library_gemm)
+        if args.k_walk != "auto":
+            line["k_walk"] = args.k_walk
         print(json.dumps(line), flush=True)
 
 
