@@ -47,6 +47,15 @@ def test_library_exports_every_declared_symbol():
     assert sorted(_lib.exported_names()) == header_functions()
 
 
+def test_binding_constants_match_the_header():
+    # every enumerator the header defines has the same value in the binding
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    consts = dict(re.findall(r"\b(NG_[A-Z0-9_]+)\s*=\s*(-?\d+)", text))
+    assert len(consts) > 20
+    for name, value in consts.items():
+        assert getattr(_lib, name) == int(value), name
+
+
 def test_binding_signatures_match_the_header():
     # argument counts of every prototype in the header against the ctypes
     # table (a mismatch would pass arguments in the wrong slots)
